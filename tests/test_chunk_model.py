@@ -1,0 +1,46 @@
+"""(A') the chunk equations of the prefill kernel equal the token recurrence."""
+import numpy as np
+import pytest
+
+import oracle
+from tests import chunk_model
+
+
+def _case(T, dk, dv, seed, s0=True, extreme=None):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, dk)); q /= np.linalg.norm(q, axis=1, keepdims=True)
+    k = rng.standard_normal((T, dk)); k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((T, dv))
+    la = -np.exp(rng.uniform(-4, 0)) * np.log1p(np.exp(rng.standard_normal(T)))
+    b = 1 / (1 + np.exp(-rng.standard_normal(T)))
+    if extreme == "no_decay":
+        la[:] = 0.0
+    elif extreme == "strong_decay":
+        la[:] = -30.0
+    elif extreme == "beta_one":
+        b[:] = 1.0
+    elif extreme == "repeated_keys":
+        k[1::2] = k[0::2][: len(k[1::2])]
+    S0 = rng.standard_normal((dk, dv)) * 0.02 if s0 else np.zeros((dk, dv))
+    return q, k, v, la, b, S0
+
+
+@pytest.mark.parametrize("T,C", [(1, 64), (63, 64), (64, 64), (65, 64), (200, 64), (130, 16),
+                                 (77, 1), (90, 90)])
+@pytest.mark.parametrize("extreme", [None, "no_decay", "strong_decay", "beta_one", "repeated_keys"])
+def test_chunk_model_equals_recurrence(T, C, extreme):
+    q, k, v, la, b, S0 = _case(T, 16, 12, seed=T * 7 + C, extreme=extreme)
+    y, S = chunk_model.chunk_fwd(q, k, v, la, b, S0, C=C)
+    yo, So = oracle.gdn_fwd(q[:, None], k[:, None], v[:, None], la[:, None], b[:, None],
+                            S0[None, None])
+    scale_y = max(np.abs(yo).max(), 1e-3)
+    assert np.abs(y - yo[:, 0]).max() / scale_y < 1e-11
+    assert np.abs(S - So[0, 0]).max() / max(np.abs(So).max(), 1e-3) < 1e-11
+
+
+def test_blocked_inverse_equals_dense():
+    rng = np.random.default_rng(3)
+    for C in (1, 15, 16, 17, 64):
+        A = np.tril(rng.uniform(-1, 1, (C, C)), -1)
+        T = chunk_model.unit_lower_inverse_blocked(A)
+        assert np.abs(T @ (np.eye(C) + A) - np.eye(C)).max() < 1e-9
