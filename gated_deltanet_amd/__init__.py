@@ -1,0 +1,163 @@
+"""Python binding of libgdn, the Gated DeltaNet token mixer for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libgdn.so`` (built in-tree by ``gated_deltanet_amd.build``).
+PyTorch supplies device memory and the current stream. There is no fallback:
+if the library is missing or the GPU is absent, calls raise.
+
+Functions carry the names of the C entry points declared in include/gdn.h:
+
+* ``gdn_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None,
+  out_dtype=None, S_T=None, y=None)`` -> (y, S_T)
+* ``gdn_decode_step(q, k, v, log_alpha, beta, S, out_dtype=None, y=None)`` -> y
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32 = 0
+GDN_BF16 = 1
+GDN_OK = 0
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libgdn.so and declare the C signatures. Raises if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise GdnError("libgdn.so not built (%s); run `python -m gated_deltanet_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, fp, ip, i32 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32
+    lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, ip, i32, i32, i32, i32, i32,
+                                  i32, i32, vp]
+    lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i32, i32, i32, i32, i32, i32,
+                                    vp]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_version.argtypes = []
+    lib.gdn_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return GDN_BF16
+    if t == torch.float32:
+        return GDN_F32
+    raise GdnError("unsupported dtype %s (bf16 or fp32)" % t)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(rc, lib, name):
+    if rc != GDN_OK:
+        raise GdnError("%s: %s (%s)" % (name, lib.gdn_status_string(rc).decode(),
+                                        lib.gdn_last_error().decode()))
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, dtype=None):
+    if not t.is_cuda:
+        raise GdnError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise GdnError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise GdnError("%s must be %s" % (name, dtype))
+
+
+def gdn_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, out_dtype=None,
+                  S_T=None, y=None, want_state=True, N=None):
+    """Chunked prefill. q, k [rows, H, dk]; v [rows, H, dv] (bf16 or fp32);
+    log_alpha, beta fp32 [rows, H]; S0 fp32 [N, H, dk, dv] or None; cu_seqlens
+    int32 [N+1] (device) or None. Without cu_seqlens the rows hold N
+    equal-length sequences back to back: N is taken from a 4-D q [N, T, H, dk],
+    else from the argument N, else from S0, else 1. Returns (y, S_T) with y
+    shaped like v."""
+    lib = load_library()
+    in_dtype = q.dtype
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, in_dtype)
+    _need(log_alpha, "log_alpha", torch.float32)
+    _need(beta, "beta", torch.float32)
+    dk, dv = q.shape[-1], v.shape[-1]
+    H = q.shape[-2]
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+        T = q.numel() // (H * dk)  # total rows
+    elif q.dim() == 4:
+        N, T = q.shape[0], q.shape[1]
+    else:
+        rows = q.shape[0]
+        if N is None:
+            N = S0.shape[0] if S0 is not None else 1
+        if N <= 0 or rows % N:
+            raise GdnError("rows (%d) must be a multiple of N (%d)" % (rows, N))
+        T = rows // N
+    if S0 is not None:
+        _need(S0, "S0", torch.float32)
+        if tuple(S0.shape) != (N, H, dk, dv):
+            raise GdnError("S0 must be [N, H, dk, dv] = %s" % ((N, H, dk, dv),))
+    if y is None:
+        y = torch.empty(v.shape, dtype=out_dtype, device=v.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=v.device)
+    rc = lib.gdn_chunk_fwd(_p(q), _p(k), _p(v), _p(log_alpha), _p(beta), _p(S0), _p(y), _p(S_T),
+                           _p(cu_seqlens), N, T, H, dk, dv, _dt(in_dtype), _dt(out_dtype),
+                           _stream(v.device))
+    _check(rc, lib, "gdn_chunk_fwd")
+    return y, S_T
+
+
+def gdn_decode_step(q, k, v, log_alpha, beta, S, out_dtype=None, y=None):
+    """One decode token per (sequence, head), updating S in place.
+    q, k [N, H, dk]; v [N, H, dv]; gates fp32 [N, H]; S fp32 [N, H, dk, dv]."""
+    lib = load_library()
+    in_dtype = q.dtype
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, in_dtype)
+    _need(log_alpha, "log_alpha", torch.float32)
+    _need(beta, "beta", torch.float32)
+    _need(S, "S", torch.float32)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=out_dtype, device=v.device)
+    rc = lib.gdn_decode_step(_p(q), _p(k), _p(v), _p(log_alpha), _p(beta), _p(S), _p(y), N, H,
+                             dk, dv, _dt(in_dtype), _dt(out_dtype), _stream(v.device))
+    _check(rc, lib, "gdn_decode_step")
+    return y
+
+
+def gdn_version() -> int:
+    return int(load_library().gdn_version())
+
+
+# short aliases
+chunk_fwd = gdn_chunk_fwd
+decode_step = gdn_decode_step

@@ -1,0 +1,171 @@
+// C ABI of libgdn: argument validation and dispatch to the kernels.
+// Every check runs before anything is enqueued, so an error return means no
+// kernel was launched and no output was written.
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512];
+
+int fail(int status, const char *fmt, const char *what) {
+  snprintf(g_last_error, sizeof(g_last_error), fmt, what);
+  return status;
+}
+
+bool misaligned(const void *p, uintptr_t a = 16) {
+  return p && (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
+}
+
+bool head_size_ok(int d) { return d == 64 || d == 128; }
+
+bool dtype_ok(int t) { return t == GDN_F32 || t == GDN_BF16; }
+
+size_t esize(int t) { return t == GDN_BF16 ? 2 : 4; }
+
+// half-open byte ranges [a, a+na) and [b, b+nb) overlap?
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int hip_status(hipError_t e, const char *where) {
+  if (e == hipSuccess) return GDN_OK;
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(e));
+  return GDN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+GDN_API const char *gdn_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_MISALIGNED: return "GDN_ERR_MISALIGNED";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+    default: return "GDN_ERR_UNKNOWN";
+  }
+}
+
+GDN_API const char *gdn_last_error(void) { return g_last_error; }
+
+GDN_API int gdn_version(void) { return 100; }
+
+GDN_API int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const float *beta, const float *S0, void *y, float *S_T,
+                          const int32_t *cu_seqlens, int32_t N, int32_t T, int32_t H,
+                          int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype,
+                          void *stream) {
+  g_last_error[0] = '\0';
+  if (N < 0 || T < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N, T must be >= 0 and H > 0");
+  if (!head_size_ok(dk) || !head_size_ok(dv))
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dk and dv must be 64 or 128");
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32 or GDN_BF16");
+  const int64_t rows = cu_seqlens ? static_cast<int64_t>(T) : static_cast<int64_t>(N) * T;
+  if (static_cast<int64_t>(N) * H > (int64_t{1} << 31) / 8)
+    return fail(GDN_ERR_INVALID_ARG, "%s", "N * H too large");
+  if (rows * H * (dk > dv ? dk : dv) >= (int64_t{1} << 40))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "input too large");
+  const bool any_rows = rows > 0;
+  if (any_rows && (!q || !k || !v || !log_alpha || !beta || !y))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "null input or output pointer");
+  if (N > 0 && !S_T && !y) return fail(GDN_ERR_INVALID_ARG, "%s", "no output requested");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(y) || misaligned(S0) ||
+      misaligned(S_T) || misaligned(log_alpha, 4) || misaligned(beta, 4) ||
+      misaligned(cu_seqlens, 4))
+    return fail(GDN_ERR_MISALIGNED, "%s", "q, k, v, y, S0, S_T need 16-byte alignment, the rest 4");
+  const size_t in_b = esize(in_dtype);
+  const size_t nq = static_cast<size_t>(rows) * H * dk * in_b;
+  const size_t nv = static_cast<size_t>(rows) * H * dv * in_b;
+  const size_t ny = static_cast<size_t>(rows) * H * dv * esize(out_dtype);
+  const size_t ns = static_cast<size_t>(N) * H * dk * dv * 4;
+  const size_t ng = static_cast<size_t>(rows) * H * 4;
+  const void *ins[5] = {q, k, v, log_alpha, beta};
+  const size_t in_n[5] = {nq, nq, nv, ng, ng};
+  for (int i = 0; i < 5; ++i) {
+    if (overlap(ins[i], in_n[i], y, ny) || overlap(ins[i], in_n[i], S_T, ns))
+      return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps an output");
+  }
+  if (overlap(y, ny, S_T, ns)) return fail(GDN_ERR_INVALID_ARG, "%s", "y overlaps S_T");
+  if (S0 && S0 != S_T && overlap(S0, ns, S_T, ns))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "S0 partially overlaps S_T");
+  if (S0 && overlap(S0, ns, y, ny)) return fail(GDN_ERR_INVALID_ARG, "%s", "S0 overlaps y");
+
+  gdn::ChunkArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_alpha = log_alpha;
+  a.beta = beta;
+  a.S0 = S0;
+  a.y = y;
+  a.S_T = S_T;
+  a.cu_seqlens = cu_seqlens;
+  a.N = N;
+  a.T = T;
+  a.H = H;
+  a.dk = dk;
+  a.dv = dv;
+  a.in_dtype = in_dtype;
+  a.out_dtype = out_dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_chunk_fwd(a), "gdn_chunk_fwd launch");
+}
+
+GDN_API int gdn_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                            const float *beta, float *S, void *y, int32_t N, int32_t H,
+                            int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype,
+                            void *stream) {
+  g_last_error[0] = '\0';
+  if (N < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N must be >= 0 and H > 0");
+  if (!head_size_ok(dk) || !head_size_ok(dv))
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dk and dv must be 64 or 128");
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32 or GDN_BF16");
+  if (static_cast<int64_t>(N) * H >= (int64_t{1} << 31))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "N * H too large");
+  if (N > 0 && (!q || !k || !v || !log_alpha || !beta || !S || !y))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "null pointer");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(y) || misaligned(S) ||
+      misaligned(log_alpha, 4) || misaligned(beta, 4))
+    return fail(GDN_ERR_MISALIGNED, "%s", "q, k, v, y, S need 16-byte alignment, the gates 4");
+  const size_t in_b = esize(in_dtype);
+  const size_t units = static_cast<size_t>(N) * H;
+  const size_t ns = units * dk * dv * 4;
+  const size_t ny = units * dv * esize(out_dtype);
+  const void *ins[5] = {q, k, v, log_alpha, beta};
+  const size_t in_n[5] = {units * dk * in_b, units * dk * in_b, units * dv * in_b, units * 4,
+                          units * 4};
+  for (int i = 0; i < 5; ++i) {
+    if (overlap(ins[i], in_n[i], S, ns) || overlap(ins[i], in_n[i], y, ny))
+      return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps an output");
+  }
+  if (overlap(S, ns, y, ny)) return fail(GDN_ERR_INVALID_ARG, "%s", "S overlaps y");
+
+  gdn::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_alpha = log_alpha;
+  a.beta = beta;
+  a.S = S;
+  a.y = y;
+  a.N = N;
+  a.H = H;
+  a.dk = dk;
+  a.dv = dv;
+  a.in_dtype = in_dtype;
+  a.out_dtype = out_dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_decode_step(a), "gdn_decode_step launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,240 @@
+// Device-side helpers shared by the libgdn kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 is carried as its 16 raw bits.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// round to nearest even; NaN stays NaN (quiet bit forced)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Element-type traits for global inputs and outputs.
+template <typename T>
+struct io;
+
+template <>
+struct io<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte access
+  __device__ static __forceinline__ void load16(const float *p, float *out) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+    out[0] = v[0];
+    out[1] = v[1];
+    out[2] = v[2];
+    out[3] = v[3];
+  }
+  __device__ static __forceinline__ float to_f32(float x) { return x; }
+  __device__ static __forceinline__ float from_f32(float x) { return x; }
+};
+
+template <>
+struct io<bf16_t> {
+  static constexpr int kVec = 8;
+  __device__ static __forceinline__ void load16(const bf16_t *p, float *out) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(v[i] << 16);
+      out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+  __device__ static __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x); }
+  __device__ static __forceinline__ bf16_t from_f32(float x) { return f32_to_bf16(x); }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA fragments.
+//
+// All products use the 16x16 output tile of the gfx950 matrix cores. A lane
+// l = 16*lg + lc of a wave owns, in an accumulator tile, rows 4*lg + i
+// (i = 0..3) of column lc. A "fragment" is the lane's share of a 32-deep
+// slice of an operand: 8 values, for row (A) or column (B) index lc, at the
+// contraction indices
+//     slot j < 4 : 4*lg + j          slot j >= 4 : 16 + 4*lg + (j - 4)
+// within the slice. Because the hardware sums slot-by-slot over the lanes of
+// one row/column, any bijection between slots and contraction indices that
+// A and B share gives the same product; this one makes the two accumulator
+// tiles that cover rows 0..15 and 16..31 of a 32-row block directly usable
+// as a B fragment (slots 0-3 from the first tile, 4-7 from the second), so
+// results chain into the next product without a trip through LDS.
+// ---------------------------------------------------------------------------
+
+template <typename MT>
+struct Frag;
+
+// fp16 operands: one v_mfma_f32_16x16x32_f16 per fragment pair.
+template <>
+struct Frag<_Float16> {
+  f16x8 v;
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (_Float16)0.0f;
+  }
+  // from two accumulator tiles (rows 0..15 and 16..31 of the slice)
+  __device__ __forceinline__ void from_acc(const f32x4 &a, const f32x4 &b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = (_Float16)a[j];
+      v[4 + j] = (_Float16)b[j];
+    }
+  }
+  __device__ __forceinline__ void from_acc_lo(const f32x4 &a) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = (_Float16)a[j];
+      v[4 + j] = (_Float16)0.0f;
+    }
+  }
+  // row-major LDS matrix, row `row`, slice starting at column c0
+  __device__ __forceinline__ void load_row(const _Float16 *base, int ld, int row, int c0,
+                                           int lg) {
+    const _Float16 *p = base + row * ld + c0 + 4 * lg;
+    const f16x4 a = *reinterpret_cast<const f16x4 *>(p);
+    const f16x4 b = *reinterpret_cast<const f16x4 *>(p + 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = a[j];
+      v[4 + j] = b[j];
+    }
+  }
+  // same, but contraction indices >= 16 of the slice are taken as zero
+  __device__ __forceinline__ void load_row_lo(const _Float16 *base, int ld, int row, int c0,
+                                              int lg) {
+    const _Float16 *p = base + row * ld + c0 + 4 * lg;
+    const f16x4 a = *reinterpret_cast<const f16x4 *>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = a[j];
+      v[4 + j] = (_Float16)0.0f;
+    }
+  }
+  // row-major fp32 LDS matrix, converted
+  __device__ __forceinline__ void load_row_f32(const float *base, int ld, int row, int c0,
+                                               int lg) {
+    const float *p = base + row * ld + c0 + 4 * lg;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = (_Float16)a[j];
+      v[4 + j] = (_Float16)b[j];
+    }
+  }
+  // column `col` of a row-major LDS matrix, slice starting at row r0
+  __device__ __forceinline__ void load_col(const _Float16 *base, int ld, int col, int r0,
+                                           int lg) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = base[(r0 + 4 * lg + j) * ld + col];
+      v[4 + j] = base[(r0 + 16 + 4 * lg + j) * ld + col];
+    }
+  }
+  __device__ __forceinline__ void load_col_lo(const _Float16 *base, int ld, int col, int r0,
+                                              int lg) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = base[(r0 + 4 * lg + j) * ld + col];
+      v[4 + j] = (_Float16)0.0f;
+    }
+  }
+};
+
+// fp32 operands: eight v_mfma_f32_16x16x4_f32 per fragment pair (slot j is
+// the lane's single contraction value of instruction j).
+template <>
+struct Frag<float> {
+  float v[8];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+  }
+  __device__ __forceinline__ void from_acc(const f32x4 &a, const f32x4 &b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = a[j];
+      v[4 + j] = b[j];
+    }
+  }
+  __device__ __forceinline__ void from_acc_lo(const f32x4 &a) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = a[j];
+      v[4 + j] = 0.0f;
+    }
+  }
+  __device__ __forceinline__ void load_row(const float *base, int ld, int row, int c0, int lg) {
+    const float *p = base + row * ld + c0 + 4 * lg;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = a[j];
+      v[4 + j] = b[j];
+    }
+  }
+  __device__ __forceinline__ void load_row_lo(const float *base, int ld, int row, int c0,
+                                              int lg) {
+    const float *p = base + row * ld + c0 + 4 * lg;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = a[j];
+      v[4 + j] = 0.0f;
+    }
+  }
+  __device__ __forceinline__ void load_row_f32(const float *base, int ld, int row, int c0,
+                                               int lg) {
+    load_row(base, ld, row, c0, lg);
+  }
+  __device__ __forceinline__ void load_col(const float *base, int ld, int col, int r0, int lg) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = base[(r0 + 4 * lg + j) * ld + col];
+      v[4 + j] = base[(r0 + 16 + 4 * lg + j) * ld + col];
+    }
+  }
+  __device__ __forceinline__ void load_col_lo(const float *base, int ld, int col, int r0,
+                                              int lg) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = base[(r0 + 4 * lg + j) * ld + col];
+      v[4 + j] = 0.0f;
+    }
+  }
+};
+
+// acc += A_slice * B_slice (16x32 times 32x16)
+__device__ __forceinline__ void mma(f32x4 &acc, const Frag<_Float16> &a,
+                                    const Frag<_Float16> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x4 &acc, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+  return z;
+}
+
+}  // namespace gdn

@@ -1,0 +1,35 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float *log_alpha, *beta;
+  float *S;
+  void *y;
+  int N, H, dk, dv;
+  int in_dtype, out_dtype;  // 0 = f32, 1 = bf16
+  hipStream_t stream;
+};
+
+struct ChunkArgs {
+  const void *q, *k, *v;
+  const float *log_alpha, *beta;
+  const float *S0;  // may be null (zeros)
+  void *y;
+  float *S_T;       // may be null
+  const int32_t *cu_seqlens;  // may be null
+  int N, T, H, dk, dv;
+  int in_dtype, out_dtype;
+  hipStream_t stream;
+};
+
+hipError_t launch_decode_step(const DecodeArgs &a);
+hipError_t launch_chunk_fwd(const ChunkArgs &a);
+
+}  // namespace gdn

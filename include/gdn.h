@@ -1,0 +1,130 @@
+/*
+ * libgdn — Gated DeltaNet token mixer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Every pointer argument is DEVICE memory unless stated otherwise; the
+ * caller owns every buffer, the library allocates nothing, keeps no pointer
+ * after a call returns and never synchronises: work is enqueued on `stream`
+ * (a hipStream_t passed as void*, NULL = the null stream) and completes in
+ * stream order. Errors found by argument validation are returned before any
+ * work is enqueued, so an error means nothing was written. Faults inside a
+ * kernel surface at the caller's next synchronisation on that stream.
+ * Results are bitwise deterministic for a given input and launch shape (no
+ * atomics). Calls are reentrant; the only library state is the thread-local
+ * error detail behind gdn_last_error().
+ *
+ * Notation (page "NLP——技术报告解读-Qwen3.8-Flash-Next", section
+ * "Gated DeltaNet 核心机制"): per head, q_t, k_t in R^dk, v_t in R^dv, state
+ * S in R^{dk x dv}, decay gate alpha_t in (0,1) (passed as log alpha_t) and
+ * write gate beta_t in (0,1). One token updates the state as
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ * equivalently: decay S by alpha_t, take the error e_t = v_t - S^T k_t
+ * against the decayed state, add beta_t k_t e_t^T; then y_t = S_t^T q_t
+ * (the post-update state, no 1/sqrt(dk) scale).
+ *
+ * Layouts (row-major, contiguous, token-major):
+ *   q, k           [rows, H, dk]
+ *   v, y           [rows, H, dv]
+ *   log_alpha, beta [rows, H]          float32
+ *   S0, S_T, S     [N, H, dk, dv]      float32
+ * where rows = N*T for equal-length batches (sequence n owns rows
+ * n*T .. n*T+T-1) or the packed total for varlen batches.
+ *
+ * Supported: dk, dv in {64, 128}; q/k/v dtype GDN_BF16 or GDN_F32; y dtype
+ * GDN_BF16 or GDN_F32. With bf16 inputs the matrix products run on fp16
+ * MFMA with fp32 accumulation and an fp32 state; with fp32 inputs every
+ * product runs on fp32 MFMA. Gates must satisfy log_alpha finite and <= 0,
+ * 0 <= beta <= 1; outside that domain the kernels still terminate and stay in
+ * bounds but the accuracy is not specified. With bf16 inputs the internal
+ * fp16 operands assume |v|, |S| and the intermediate errors stay below
+ * about 6e4.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_API __attribute__((visibility("default")))
+
+/* element types */
+enum gdn_dtype_e {
+  GDN_F32 = 0,
+  GDN_BF16 = 1,
+};
+
+/* return codes */
+enum gdn_status_e {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = -1, /* null pointer, bad size, aliasing */
+  GDN_ERR_UNSUPPORTED = -2, /* head size or dtype combination not built */
+  GDN_ERR_MISALIGNED = -3,  /* a pointer lacks its required alignment */
+  GDN_ERR_HIP = -4,         /* a HIP runtime call failed (see gdn_last_error) */
+};
+
+/*
+ * Chunked parallel prefill: runs the recurrence above over whole sequences
+ * and returns every y_t and the final state S_T.
+ *
+ *   q, k, v      inputs, dtype in_dtype, layouts above.
+ *   log_alpha    float32 [rows, H], log of the decay gate.
+ *   beta         float32 [rows, H], write gate.
+ *   S0           float32 [N, H, dk, dv] initial states, or NULL for zeros.
+ *   y            output [rows, H, dv], dtype out_dtype.
+ *   S_T          float32 [N, H, dk, dv] final states, or NULL to skip. May
+ *                equal S0 (in-place update); must not overlap anything else.
+ *   cu_seqlens   int32 [N+1] device array of sequence starts (cu_seqlens[0]
+ *                = 0, non-decreasing, cu_seqlens[N] = rows), or NULL for N
+ *                sequences of T tokens each.
+ *   N            number of sequences (>= 0).
+ *   T            tokens per sequence when cu_seqlens is NULL; otherwise the
+ *                total row count `rows` of the packed batch. Kernels clamp
+ *                every sequence to [0, rows) so bad offsets cannot address
+ *                memory outside the buffers.
+ *   H, dk, dv    heads and head sizes.
+ *
+ * Empty sequences (length 0) copy S0 to S_T. Inputs must not alias outputs.
+ * q, k, v, y, S0 and S_T must be 16-byte aligned; log_alpha, beta and
+ * cu_seqlens 4-byte aligned.
+ */
+GDN_API int gdn_chunk_fwd(const void *q, const void *k, const void *v,
+                          const float *log_alpha, const float *beta,
+                          const float *S0, void *y, float *S_T,
+                          const int32_t *cu_seqlens, int32_t N, int32_t T,
+                          int32_t H, int32_t dk, int32_t dv, int32_t in_dtype,
+                          int32_t out_dtype, void *stream);
+
+/*
+ * Single-token decode step, in place: for every (sequence n, head h) applies
+ * one token of the recurrence above to S[n, h] and writes y[n, h].
+ * The fixed-size state replaces a growing cache (page "NLP——技术报告解读-
+ * Qwen3.8-Flash-Next", section "Gated DeltaNet 核心机制").
+ *
+ *   q, k [N, H, dk]; v, y [N, H, dv]; log_alpha, beta float32 [N, H];
+ *   S float32 [N, H, dk, dv], read and overwritten.
+ * S must not overlap any other argument. q, k, v, y and S must be 16-byte
+ * aligned, the gates 4-byte aligned.
+ */
+GDN_API int gdn_decode_step(const void *q, const void *k, const void *v,
+                            const float *log_alpha, const float *beta,
+                            float *S, void *y, int32_t N, int32_t H,
+                            int32_t dk, int32_t dv, int32_t in_dtype,
+                            int32_t out_dtype, void *stream);
+
+/* Human-readable name of a return code (static string, never NULL). */
+GDN_API const char *gdn_status_string(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+GDN_API const char *gdn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+GDN_API int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every entry point declared in
+include/gdn.h, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+LIB = os.path.join(ROOT, "gated_deltanet_amd", "libgdn.so")
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        from gated_deltanet_amd import build
+        build.build(verbose=False)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"GDN_API\s+[\w\s\*]+?\b(gdn_\w+)\s*\(", text)
+
+
+def test_header_declares_entry_points():
+    syms = declared_symbols()
+    for s in ("gdn_chunk_fwd", "gdn_decode_step", "gdn_status_string", "gdn_last_error",
+              "gdn_version"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol():
+    _ensure_built()
+    lib = ctypes.CDLL(LIB)
+    missing = [s for s in declared_symbols() if not hasattr(lib, s)]
+    assert not missing, missing
+
+
+@pytest.fixture(scope="module")
+def lib():
+    _ensure_built()
+    lib = ctypes.CDLL(LIB)
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    v = ctypes.c_void_p
+    lib.gdn_chunk_fwd.argtypes = [v] * 9 + [ctypes.c_int32] * 7 + [v]
+    lib.gdn_decode_step.argtypes = [v] * 7 + [ctypes.c_int32] * 6 + [v]
+    return lib
+
+
+# fake, never dereferenced: validation must reject these calls before any launch
+A = 0x7F0000000000
+B = A + (1 << 30)
+
+
+def _chunk(lib, **kw):
+    args = dict(q=A, k=A + (1 << 26), v=A + (2 << 26), la=A + (3 << 26), b=A + (4 << 26), S0=None,
+                y=B, ST=B + (1 << 28), cu=None, N=1, T=64, H=2, dk=128, dv=128, it=1, ot=1)
+    args.update(kw)
+    return lib.gdn_chunk_fwd(args["q"], args["k"], args["v"], args["la"], args["b"], args["S0"],
+                             args["y"], args["ST"], args["cu"], args["N"], args["T"], args["H"],
+                             args["dk"], args["dv"], args["it"], args["ot"], None)
+
+
+def test_status_strings(lib):
+    assert lib.gdn_status_string(0) == b"GDN_OK"
+    assert lib.gdn_status_string(-2) == b"GDN_ERR_UNSUPPORTED"
+    assert lib.gdn_status_string(-99) == b"GDN_ERR_UNKNOWN"
+    assert lib.gdn_version() >= 100
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1),
+    (dict(y=None), -1),
+    (dict(N=-1), -1),
+    (dict(H=0), -1),
+    (dict(dk=96), -2),
+    (dict(dv=32), -2),
+    (dict(it=7), -2),
+    (dict(q=A + 4), -3),
+    (dict(ST=A + (1 << 26)), -1),   # S_T overlaps k
+    (dict(y=A), -1),                # y overlaps q
+    (dict(S0=B + (1 << 28) + 64), -1),  # S0 partially overlaps S_T
+])
+def test_chunk_fwd_rejects(lib, kw, code):
+    rc = _chunk(lib, **kw)
+    assert rc == code, (rc, lib.gdn_last_error())
+    assert lib.gdn_last_error() != b""
+
+
+def test_decode_rejects(lib):
+    rc = lib.gdn_decode_step(A, A + 4096, A + 8192, A + 12288, A + 16384, None, B, 4, 2, 128, 128,
+                             1, 1, None)
+    assert rc == -1
+    rc = lib.gdn_decode_step(A, A + 4096, A + 8192, A + 12288, A + 16384, B, B + 64, 4, 2, 128,
+                             128, 1, 1, None)
+    assert rc == -1  # S overlaps y
+    rc = lib.gdn_decode_step(A, A + 4096, A + 8192, A + 12288, A + 16384, B, B + (1 << 24), 4, 2,
+                             128, 100, 1, 1, None)
+    assert rc == -2

@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path against the fp64 oracle, element by element,
+through the C ABI (via the thin Python binding).
+
+Bar: relative L2 error <= 1e-5 for fp32 inputs and <= 2e-3 for bf16 inputs
+(fp32 state) on y and on the final state.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import oracle
+from tests.util import TOL, rel_l2, to_dev
+
+gpu = pytest.mark.gpu
+
+
+def _lib():
+    import gated_deltanet_amd as g
+    g.load_library()
+    return g
+
+
+def _run_chunk(inp, out_dtype=None):
+    g = _lib()
+    d = to_dev(inp)
+    y, S = g.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
+                           cu_seqlens=d["cu_seqlens"], out_dtype=out_dtype, N=d["N"])
+    torch.cuda.synchronize()
+    return y, S
+
+
+def _oracle_chunk(inp):
+    N = inp["N"]
+    return oracle.gdn_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"],
+                          cu_seqlens=inp["cu_seqlens"], N=N)
+
+
+def _flat(inp, y):
+    return y.reshape(-1, inp["H"], inp["dv"])
+
+
+def _check(inp, out_dtype=None, tol=None):
+    tol = TOL[inp["dtype"]] if tol is None else tol
+    y, S = _run_chunk(inp, out_dtype)
+    yo, So = _oracle_chunk(inp)
+    ey, es = rel_l2(_flat(inp, y), yo), rel_l2(S, So)
+    print("rel_l2 y=%.3e S=%.3e" % (ey, es), flush=True)
+    assert np.isfinite(ey) and np.isfinite(es)
+    assert ey <= tol and es <= tol, (ey, es)
+    return ey, es
+
+
+@gpu
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 256])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_small(T, d, dtype):
+    inp = gi.prefill_inputs(2, 3, T, d, d, dtype, s0_std=0.02, seed=T + d)
+    _check(inp, out_dtype=torch.float32)
+
+
+@gpu
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_rect_heads(dk, dv, dtype):
+    inp = gi.prefill_inputs(1, 2, 130, dk, dv, dtype, s0_std=0.02, seed=dk + 3 * dv)
+    _check(inp, out_dtype=torch.float32)
+
+
+@gpu
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_zero_state_bf16_out(dtype):
+    inp = gi.prefill_inputs(2, 2, 300, 128, 128, dtype, s0_std=0.0, seed=9)
+    _check(inp)  # y in the input dtype
+
+
+@gpu
+def test_workload_tiny_fwd():
+    """B=1, H=2, T=256, dk=dv=64, fp32, S0 = 0 (the oracle-sized workload)."""
+    inp = gi.workload_inputs(0)
+    _check(inp)
+
+
+@gpu
+@pytest.mark.parametrize("case", ["no_decay", "strong_decay", "beta0", "beta1", "repeated_keys",
+                                  "near_parallel"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_gate_extremes(case, dtype):
+    inp = gi.prefill_inputs(1, 2, 150, 128, 128, dtype, s0_std=0.02, seed=21)
+    if case == "no_decay":
+        inp["log_alpha"].zero_()
+    elif case == "strong_decay":
+        inp["log_alpha"].fill_(-30.0)
+    elif case == "beta0":
+        inp["beta"].zero_()
+    elif case == "beta1":
+        inp["beta"].fill_(1.0)
+    elif case == "repeated_keys":
+        inp["k"][1::2] = inp["k"][0::2][: inp["k"][1::2].shape[0]]
+    elif case == "near_parallel":
+        base = inp["k"][:1].float()
+        noise = gi.normal(inp["k"].shape, 77, 1) * 1e-2
+        kk = base + noise
+        inp["k"] = (kk / kk.norm(dim=-1, keepdim=True)).to(inp["k"].dtype)
+    _check(inp, out_dtype=torch.float32)
+
+
+@gpu
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_varlen(dtype):
+    lengths = [1, 2, 63, 64, 65, 1000, 0, 130]
+    inp = gi.prefill_inputs(0, 2, 0, 128, 128, dtype, s0_std=0.02, seed=31, lengths=lengths)
+    _check(inp, out_dtype=torch.float32)
+
+
+@gpu
+def test_chunk_in_place_state():
+    g = _lib()
+    inp = to_dev(gi.prefill_inputs(2, 2, 100, 128, 128, "bf16", s0_std=0.02, seed=41))
+    y_ref, S_ref = g.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                   inp["S0"])  # N from S0
+    S = inp["S0"].clone()
+    y2, S2 = g.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], S,
+                             S_T=S)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S_ref) and torch.equal(y2, y_ref)
+
+
+@gpu
+def test_chunk_deterministic():
+    g = _lib()
+    inp = to_dev(gi.prefill_inputs(2, 4, 333, 128, 128, "bf16", s0_std=0.02, seed=42))
+    outs = [g.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                            inp["S0"]) for _ in range(3)]
+    torch.cuda.synchronize()
+    for y, S in outs[1:]:
+        assert torch.equal(y, outs[0][0]) and torch.equal(S, outs[0][1])
+
+
+@gpu
+def test_chunk_split_resume():
+    """prefill(0..t0) -> S -> prefill(t0..T) equals one pass."""
+    g = _lib()
+    inp = to_dev(gi.prefill_inputs(1, 2, 300, 128, 128, "f32", s0_std=0.02, seed=43))
+    y, S = g.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
+    for t0 in (1, 64, 100):
+        sl = lambda x, a, b: x[a:b].contiguous()
+        y1, S1 = g.gdn_chunk_fwd(*(sl(inp[n], 0, t0) for n in ("q", "k", "v", "log_alpha", "beta")),
+                                 inp["S0"])
+        y2, S2 = g.gdn_chunk_fwd(*(sl(inp[n], t0, 300) for n in ("q", "k", "v", "log_alpha", "beta")),
+                                 S1)
+        torch.cuda.synchronize()
+        assert rel_l2(torch.cat([y1, y2]), y.cpu().double().numpy()) < 1e-5
+        assert rel_l2(S2, S.cpu().double().numpy()) < 1e-5
+
+
+@gpu
+def test_chunk_nan_isolated():
+    """A NaN in one (sequence, head) does not reach any other."""
+    g = _lib()
+    inp = gi.prefill_inputs(2, 3, 100, 128, 128, "bf16", s0_std=0.02, seed=44)
+    inp["v"][130, 1, 5] = float("nan")  # sequence 1, head 1
+    d = to_dev(inp)
+    y, S = g.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    torch.cuda.synchronize()
+    y = y.reshape(2, 100, 3, 128).cpu()
+    S = S.cpu()
+    for n in range(2):
+        for h in range(3):
+            bad = (n, h) == (1, 1)
+            assert torch.isfinite(S[n, h]).all() != bad
+            if not bad:
+                assert torch.isfinite(y[n, :, h]).all()
+
+
+# ---------------------------------------------------------------- decode ----
+@gpu
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_steps(dk, dv, dtype):
+    g = _lib()
+    inp = gi.decode_inputs(5, 3, dk, dv, steps=4, dtype=dtype, s0_std=0.02, seed=dk + dv)
+    S = inp["S0"].clone().cuda()
+    S_or = inp["S0"].double().numpy()
+    ys, ys_or = [], []
+    for t in range(4):
+        args = [inp[n][t].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")]
+        y = g.gdn_decode_step(*(a.cuda() for a in args), S, out_dtype=torch.float32)
+        yo, S_or = oracle.decode_step(*args, S_or)
+        ys.append(y.cpu())
+        ys_or.append(yo)
+    torch.cuda.synchronize()
+    ey = rel_l2(torch.stack(ys), np.stack(ys_or))
+    es = rel_l2(S, S_or)
+    print("rel_l2 y=%.3e S=%.3e" % (ey, es))
+    assert ey <= TOL[dtype] and es <= TOL[dtype]
+
+
+@gpu
+def test_decode_matches_prefill():
+    """T decode steps equal one prefill of T tokens (two GPU paths)."""
+    g = _lib()
+    T = 70
+    inp = to_dev(gi.prefill_inputs(3, 2, T, 128, 128, "f32", s0_std=0.02, seed=51))
+    y, S = g.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
+    Sd = inp["S0"].clone()  # N = 3 from S0
+    yd = []
+    for t in range(T):
+        rows = torch.arange(3, device="cuda") * T + t
+        args = [inp[n][rows].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")]
+        yd.append(g.gdn_decode_step(*args, Sd))
+    torch.cuda.synchronize()
+    yd = torch.stack(yd, 1).reshape(3 * T, 2, 128)
+    assert rel_l2(yd, y.cpu().double().numpy()) < 1e-5
+    assert rel_l2(Sd, S.cpu().double().numpy()) < 1e-5
