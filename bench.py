@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one gdn_chunk_fwd call (in-chunk gate cumsum, UT inverse, state
+scan and intra-chunk products) over the chunked-prefill workload
+B=4, H=16, T=4096, dk=dv=128, bf16 q/k/v, fp32 gates and state, S0 = 0,
+64-token chunks. `value` is prefill tokens/s (B*T per step). The same line
+also carries the decode-step workload (256 sequences x 32 heads x 128x128
+fp32 states, 128 consecutive steps) as state GB/s against the HBM peak,
+the roofline of the prefill kernel, and the fp64 CPU oracle timed on the
+host cores on the same prefill batch.
+
+Inputs are synthetic (seeded, generated on the CPU, resident in HBM before
+timing starts). Timing uses HIP events on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gdn_inputs as gi  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+CHUNK = 64
+
+
+def prefill_flops_per_token_head(dk, dv, C=CHUNK):
+    """Algorithmic work of chunked prefill per token per head (triangles
+    halved): 6 dk dv + C (3 dk + 2 dv) + C^2 / 3."""
+    return 6 * dk * dv + C * (3 * dk + 2 * dv) + C * C / 3.0
+
+
+def prefill_bytes(tokens, H, dk, dv, N, in_b=2, out_b=2, s0=False):
+    """Algorithmic HBM bytes: q, k, v read, y written, gates read, state
+    written (and read when S0 is given)."""
+    per_tok_head = (2 * dk + dv) * in_b + dv * out_b + 8
+    state = N * H * dk * dv * 4
+    return tokens * H * per_tok_head + state * (2 if s0 else 1)
+
+
+def decode_bytes_per_step(N, H, dk, dv, in_b=2, out_b=2):
+    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * in_b + dv * out_b + 8)
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def time_launches(fn, steps, warmup, stream):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)  # ms
+
+
+def bench_prefill(g, steps, warmup, copies=3):
+    w = gi.WORKLOADS[1]
+    inp = gi.workload_inputs(1)
+    N, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    tokens = N * T
+    dev = torch.device("cuda", 0)
+    # several copies of the inputs so consecutive steps do not hit the
+    # 256 MB last-level cache with the previous step's data
+    sets = []
+    for _ in range(copies):
+        sets.append({k: inp[k].to(dev) for k in ("q", "k", "v", "log_alpha", "beta")})
+    y = torch.empty((tokens, H, dv), dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    it = [0]
+
+    def step():
+        d = sets[it[0] % copies]
+        it[0] += 1
+        g.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None, y=y, S_T=S_T, N=N)
+
+    ms = time_launches(step, steps, warmup, stream)
+    ms_step = ms / steps
+    # one extra call on the first copy for the parity check
+    d = sets[0]
+    g.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None, y=y, S_T=S_T, N=N)
+    torch.cuda.synchronize()
+    return dict(inp=inp, ms_step=ms_step, tokens=tokens, N=N, H=H, T=T, dk=dk, dv=dv,
+                y=y.float().cpu(), S_T=S_T.cpu())
+
+
+def bench_decode(g, n_steps=128, reps=2):
+    w = gi.WORKLOADS[3]
+    N, H, dk, dv = w.B, w.H, w.dk, w.dv
+    dev = torch.device("cuda", 0)
+    inp = gi.workload_inputs(3, steps=n_steps)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    la, b = inp["log_alpha"].to(dev), inp["beta"].to(dev)
+    S = inp["S0"].to(dev)
+    y = torch.empty((n_steps, N, H, dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def one_pass():
+        for t in range(n_steps):
+            g.gdn_decode_step(q[t], k[t], v[t], la[t], b[t], S, y=y[t])
+
+    one_pass()  # warm-up (advances the state; the timing does not depend on values)
+    torch.cuda.synchronize()
+    ms = time_launches(one_pass, reps, 0, stream)
+    us_step = ms * 1e3 / (reps * n_steps)
+    bytes_step = decode_bytes_per_step(N, H, dk, dv)
+    gbs = bytes_step / (us_step * 1e-6) / 1e9
+    return dict(workload=w.name, us_per_step=us_step, GBps=gbs, frac_hbm=gbs / HBM_PEAK_GBS,
+                tokens_per_s=N / (us_step * 1e-6), bytes_per_step=bytes_step, steps=n_steps)
+
+
+def cpu_baseline(pf, max_seconds=30.0):
+    """The fp64 oracle on the host cores, on the same prefill batch: every
+    head of as many whole sequences as fit the time budget (starting with
+    one). Returns the record and the oracle outputs for the parity check."""
+    import oracle
+    inp = pf["inp"]
+    H, T = pf["H"], pf["T"]
+    threads = len(os.sched_getaffinity(0))
+    done = 0
+    spent = 0.0
+    outs = []
+    while done < pf["N"]:
+        rows = slice(done * T, (done + 1) * T)
+        t0 = time.perf_counter()
+        y, S = oracle.gdn_fwd(inp["q"][rows], inp["k"][rows], inp["v"][rows],
+                              inp["log_alpha"][rows], inp["beta"][rows], None, N=1,
+                              nthreads=threads)
+        spent += time.perf_counter() - t0
+        outs.append((done, y, S))
+        done += 1
+        if spent * (done + 1) / done > max_seconds:
+            break
+    tok_s = done * T / spent
+    rec = dict(value=tok_s, unit="tokens/s", cores=threads, kind="oracle",
+               sample="%d of %d sequences (all %d heads, %d tokens each), fp64 token recurrence, "
+                      "%.1f s" % (done, pf["N"], H, T, spent))
+    return rec, outs
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=128)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the GDN mixer shards over (sequence, head) with no "
+              "exchange, so --gpus %d is not a configuration this build runs." % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import gated_deltanet_amd as g
+    g.load_library()
+    torch.cuda.set_device(0)
+
+    print("[bench] prefill workload 1: B=4 H=16 T=4096 d=128 bf16", file=sys.stderr, flush=True)
+    pf = bench_prefill(g, args.steps, args.warmup)
+    ms = pf["ms_step"]
+    tokens, H, dk, dv, N = pf["tokens"], pf["H"], pf["dk"], pf["dv"], pf["N"]
+    value = tokens / (ms * 1e-3)
+    flops = tokens * H * prefill_flops_per_token_head(dk, dv)
+    nbytes = prefill_bytes(tokens, H, dk, dv, N)
+    achieved_gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "chunk_fwd_prefill_B4_H16_T4096_d128_traffic.json")
+    if os.path.exists(tfile):
+        try:
+            traffic = json.load(open(tfile)).get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    roofline = dict(kernel="chunk_fwd_kernel<128,64,bf16,bf16,f16>", bound="hbm",
+                    achieved=achieved_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=achieved_gbs / HBM_PEAK_GBS, traffic=traffic,
+                    alg_bytes_per_launch=nbytes, alg_flops_per_launch=flops,
+                    mfma_tflops=tflops, mfma_frac_bf16_peak=tflops / BF16_PEAK_TFLOPS)
+
+    rec = dict(metric="GDN prefill tokens/s (% bf16 MFMA peak); decode state GB/s (% HBM peak)",
+               value=value, unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+               ms_per_step=ms, higher_is_better=True, scaling="weak", vs_baseline=None,
+               dtype="bf16", data="synthetic",
+               config=dict(workload=gi.WORKLOADS[1].name, B=N, H=H, T=pf["T"], dk=dk, dv=dv,
+                           chunk=CHUNK, q_k_v="bf16", y="bf16", state="fp32", S0="zeros"),
+               pct_bf16_mfma_peak=100.0 * tflops / BF16_PEAK_TFLOPS,
+               roofline=roofline)
+
+    if not args.no_decode:
+        print("[bench] decode workload 3: 256 x 32 heads, %d steps" % args.decode_steps,
+              file=sys.stderr, flush=True)
+        rec["decode"] = bench_decode(g, args.decode_steps)
+
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cb, outs = cpu_baseline(pf)
+        rec["cpu_baseline"] = cb
+        ey, es = [], []
+        T = pf["T"]
+        for n, yo, So in outs:
+            ey.append(rel_l2(pf["y"][n * T:(n + 1) * T].numpy(), yo))
+            es.append(rel_l2(pf["S_T"][n].numpy(), So[0]))
+        rec["parity"] = dict(y_rel_l2=max(ey), S_T_rel_l2=max(es), sequences=len(outs),
+                             tolerance=2e-3)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()
