@@ -27,6 +27,9 @@ FLAGS = [
     "-ffp-contract=fast",
     # keep hipcc from emitting packed fp32 arithmetic in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: avoids AGPR<->VGPR copies around
+    # loop-carried accumulators
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(os.path.dirname(HERE), "include"),
 ]
 

@@ -30,6 +30,8 @@ struct ChunkArgs {
 };
 
 hipError_t launch_decode_step(const DecodeArgs &a);
-hipError_t launch_chunk_fwd(const ChunkArgs &a);
+hipError_t launch_chunk_fwd(const ChunkArgs &a);      // dispatches on in_dtype
+hipError_t launch_chunk_fwd_f32(const ChunkArgs &a);  // fp32 inputs
+hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a); // bf16 inputs
 
 }  // namespace gdn
