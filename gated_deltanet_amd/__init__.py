@@ -10,6 +10,9 @@ Functions carry the names of the C entry points declared in include/gdn.h:
 * ``gdn_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None,
   out_dtype=None, S_T=None, y=None)`` -> (y, S_T)
 * ``gdn_decode_step(q, k, v, log_alpha, beta, S, out_dtype=None, y=None)`` -> y
+* ``gdn_frontend_qkv(q_raw, k_raw, v_raw, conv_w, cu_seqlens=None, N=None,
+  l2_eps=1e-6, out_dtype=None)`` -> (q, k, v)
+* ``gdn_output_gate(y, z, norm_w=None, rms_eps=1e-6, out_dtype=None)`` -> o
 """
 from __future__ import annotations
 
@@ -47,6 +50,12 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i32, i32, i32, i32, i32, i32,
                                     vp]
     lib.gdn_decode_step.restype = ctypes.c_int
+    f32, i64 = ctypes.c_float, ctypes.c_int64
+    lib.gdn_frontend_qkv.argtypes = [vp, vp, vp, fp, ip, i32, i32, i32, i32, f32, vp, vp, vp,
+                                     i32, i32, vp]
+    lib.gdn_frontend_qkv.restype = ctypes.c_int
+    lib.gdn_output_gate.argtypes = [vp, vp, fp, f32, vp, i64, i32, i32, i32, vp]
+    lib.gdn_output_gate.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -152,6 +161,61 @@ def gdn_decode_step(q, k, v, log_alpha, beta, S, out_dtype=None, y=None):
                              dk, dv, _dt(in_dtype), _dt(out_dtype), _stream(v.device))
     _check(rc, lib, "gdn_decode_step")
     return y
+
+
+def gdn_frontend_qkv(q_raw, k_raw, v_raw, conv_w, cu_seqlens=None, N=None, l2_eps=1e-6,
+                     out_dtype=None, out=None):
+    """ShortConv -> SiLU -> L2Norm (q, k) / ShortConv -> SiLU (v) on raw
+    projections [rows, H, d]; conv_w fp32 [3, H*d, 4]. Sequence boundaries as
+    in gdn_chunk_fwd (cu_seqlens, or N equal-length sequences; default 1).
+    Returns (q, k, v)."""
+    lib = load_library()
+    in_dtype = q_raw.dtype
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    for t, nm in ((q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw")):
+        _need(t, nm, in_dtype)
+    _need(conv_w, "conv_w", torch.float32)
+    H, d = q_raw.shape[-2], q_raw.shape[-1]
+    rows = q_raw.numel() // (H * d)
+    if tuple(conv_w.shape) != (3, H * d, 4):
+        raise GdnError("conv_w must be [3, H*d, 4]")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        N, T = cu_seqlens.numel() - 1, rows
+    else:
+        N = 1 if N is None else N
+        if N <= 0 or rows % N:
+            raise GdnError("rows (%d) must be a multiple of N (%d)" % (rows, N))
+        T = rows // N
+    if out is None:
+        out = tuple(torch.empty(q_raw.shape, dtype=out_dtype, device=q_raw.device)
+                    for _ in range(3))
+    q, k, v = out
+    rc = lib.gdn_frontend_qkv(_p(q_raw), _p(k_raw), _p(v_raw), _p(conv_w), _p(cu_seqlens), N, T,
+                              H, d, float(l2_eps), _p(q), _p(k), _p(v), _dt(in_dtype),
+                              _dt(out_dtype), _stream(q_raw.device))
+    _check(rc, lib, "gdn_frontend_qkv")
+    return q, k, v
+
+
+def gdn_output_gate(y, z, norm_w=None, rms_eps=1e-6, out_dtype=None, o=None):
+    """o = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + norm_w) over the last
+    dimension (d in {64, 128}); y and z share a dtype."""
+    lib = load_library()
+    in_dtype = y.dtype
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    _need(y, "y", in_dtype)
+    _need(z, "z", in_dtype)
+    if norm_w is not None:
+        _need(norm_w, "norm_w", torch.float32)
+    d = y.shape[-1]
+    rows = y.numel() // d
+    if o is None:
+        o = torch.empty(y.shape, dtype=out_dtype, device=y.device)
+    rc = lib.gdn_output_gate(_p(y), _p(z), _p(norm_w), float(rms_eps), _p(o), rows, d,
+                             _dt(in_dtype), _dt(out_dtype), _stream(y.device))
+    _check(rc, lib, "gdn_output_gate")
+    return o
 
 
 def gdn_version() -> int:

@@ -168,4 +168,87 @@ GDN_API int gdn_decode_step(const void *q, const void *k, const void *v, const f
   return hip_status(gdn::launch_decode_step(a), "gdn_decode_step launch");
 }
 
+GDN_API int gdn_frontend_qkv(const void *q_raw, const void *k_raw, const void *v_raw,
+                             const float *conv_w, const int32_t *cu_seqlens, int32_t N, int32_t T,
+                             int32_t H, int32_t d, float l2_eps, void *q, void *k, void *v,
+                             int32_t in_dtype, int32_t out_dtype, void *stream) {
+  g_last_error[0] = '\0';
+  if (N < 0 || T < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N, T must be >= 0 and H > 0");
+  if (!head_size_ok(d)) return fail(GDN_ERR_UNSUPPORTED, "%s", "d must be 64 or 128");
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32 or GDN_BF16");
+  if (!(l2_eps >= 0.0f)) return fail(GDN_ERR_INVALID_ARG, "%s", "l2_eps must be >= 0");
+  const int64_t rows = cu_seqlens ? static_cast<int64_t>(T) : static_cast<int64_t>(N) * T;
+  if (rows * H * d >= (int64_t{1} << 40)) return fail(GDN_ERR_INVALID_ARG, "%s", "input too large");
+  if (rows / 64 >= (int64_t{1} << 31)) return fail(GDN_ERR_INVALID_ARG, "%s", "too many rows");
+  if (rows > 0 && (!q_raw || !k_raw || !v_raw || !conv_w || !q || !k || !v))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "null pointer");
+  if (misaligned(q_raw) || misaligned(k_raw) || misaligned(v_raw) || misaligned(conv_w) ||
+      misaligned(q) || misaligned(k) || misaligned(v) || misaligned(cu_seqlens, 4))
+    return fail(GDN_ERR_MISALIGNED, "%s", "tensors need 16-byte alignment, cu_seqlens 4");
+  const size_t nin = static_cast<size_t>(rows) * H * d * esize(in_dtype);
+  const size_t nout = static_cast<size_t>(rows) * H * d * esize(out_dtype);
+  const void *ins[4] = {q_raw, k_raw, v_raw, conv_w};
+  const size_t in_n[4] = {nin, nin, nin, static_cast<size_t>(3) * H * d * 4 * 4};
+  const void *outs[3] = {q, k, v};
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 3; ++j)
+      if (overlap(ins[i], in_n[i], outs[j], nout))
+        return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps an output");
+  if (overlap(q, nout, k, nout) || overlap(q, nout, v, nout) || overlap(k, nout, v, nout))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "outputs overlap");
+  gdn::FrontendArgs a;
+  a.xq = q_raw;
+  a.xk = k_raw;
+  a.xv = v_raw;
+  a.conv_w = conv_w;
+  a.cu_seqlens = cu_seqlens;
+  a.N = N;
+  a.T = T;
+  a.rows = rows;
+  a.H = H;
+  a.d = d;
+  a.eps = l2_eps;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.in_dtype = in_dtype;
+  a.out_dtype = out_dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  if (cu_seqlens == nullptr && T == 0) return GDN_OK;
+  return hip_status(gdn::launch_frontend(a), "gdn_frontend_qkv launch");
+}
+
+GDN_API int gdn_output_gate(const void *y, const void *z, const float *norm_w, float rms_eps,
+                            void *o, int64_t rows, int32_t d, int32_t in_dtype, int32_t out_dtype,
+                            void *stream) {
+  g_last_error[0] = '\0';
+  if (rows < 0) return fail(GDN_ERR_INVALID_ARG, "%s", "rows must be >= 0");
+  if (!head_size_ok(d)) return fail(GDN_ERR_UNSUPPORTED, "%s", "d must be 64 or 128");
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32 or GDN_BF16");
+  if (!(rms_eps >= 0.0f)) return fail(GDN_ERR_INVALID_ARG, "%s", "rms_eps must be >= 0");
+  if (rows / 64 >= (int64_t{1} << 31)) return fail(GDN_ERR_INVALID_ARG, "%s", "too many rows");
+  if (rows > 0 && (!y || !z || !o)) return fail(GDN_ERR_INVALID_ARG, "%s", "null pointer");
+  if (misaligned(y) || misaligned(z) || misaligned(o) || misaligned(norm_w, 4))
+    return fail(GDN_ERR_MISALIGNED, "%s", "y, z, o need 16-byte alignment, norm_w 4");
+  const size_t nin = static_cast<size_t>(rows) * d * esize(in_dtype);
+  const size_t nout = static_cast<size_t>(rows) * d * esize(out_dtype);
+  if (overlap(y, nin, o, nout) || overlap(z, nin, o, nout) ||
+      overlap(norm_w, static_cast<size_t>(d) * 4, o, nout))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps the output");
+  gdn::GateArgs a;
+  a.y = y;
+  a.z = z;
+  a.norm_w = norm_w;
+  a.eps = rms_eps;
+  a.o = o;
+  a.rows = rows;
+  a.d = d;
+  a.in_dtype = in_dtype;
+  a.out_dtype = out_dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_output_gate(a), "gdn_output_gate launch");
+}
+
 }  // extern "C"

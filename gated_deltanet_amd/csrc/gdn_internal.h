@@ -29,7 +29,33 @@ struct ChunkArgs {
   hipStream_t stream;
 };
 
+struct FrontendArgs {
+  const void *xq, *xk, *xv;  // raw projections [rows, H, d]
+  const float *conv_w;       // [3][H*d][4]
+  const int32_t *cu_seqlens; // may be null
+  int N, T;                  // sequences; tokens per sequence when cu_seqlens is null
+  int64_t rows;
+  int H, d;
+  float eps;
+  void *q, *k, *v;
+  int in_dtype, out_dtype;
+  hipStream_t stream;
+};
+
+struct GateArgs {
+  const void *y, *z;  // [rows, d]
+  const float *norm_w;  // [d] or null
+  float eps;
+  void *o;
+  int64_t rows;
+  int d;
+  int in_dtype, out_dtype;
+  hipStream_t stream;
+};
+
 hipError_t launch_decode_step(const DecodeArgs &a);
+hipError_t launch_frontend(const FrontendArgs &a);
+hipError_t launch_output_gate(const GateArgs &a);
 hipError_t launch_chunk_fwd(const ChunkArgs &a);      // dispatches on in_dtype
 hipError_t launch_chunk_fwd_f32(const ChunkArgs &a);  // fp32 inputs
 hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a); // bf16 inputs

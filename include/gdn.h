@@ -114,6 +114,48 @@ GDN_API int gdn_decode_step(const void *q, const void *k, const void *v,
                             int32_t dk, int32_t dv, int32_t in_dtype,
                             int32_t out_dtype, void *stream);
 
+/*
+ * Front end of the mixer (page "NLP——技术报告解读-Qwen3.8-Flash-Next",
+ * section "GDN 参数化细节", first display; the convolution is short and causal
+ * per the pwwt.cn page's Fig. 2 caption): for the three projected streams
+ * x_q, x_k, x_v and each channel c = h*d + i,
+ *     u_t[c] = sum_{j=0..3} w[c][j] * x_{t-3+j}[c]   (no bias; rows before the
+ *              start of the token's sequence count as zero)
+ *     a_t = SiLU(u_t) = u_t / (1 + exp(-u_t))
+ *     q_t = a_t / sqrt(sum_i a_t[i]^2 + l2_eps) over the head's d channels,
+ *     k_t likewise, v_t = a_t (no normalisation).
+ *
+ *   q_raw, k_raw, v_raw  [rows, H, d] in in_dtype.
+ *   conv_w               float32 [3][H*d][4]: q taps, then k, then v; tap 3
+ *                        multiplies the current token, tap 0 the one three
+ *                        rows back.
+ *   cu_seqlens, N, T     as for gdn_chunk_fwd (sequence boundaries).
+ *   q, k, v              outputs [rows, H, d] in out_dtype.
+ * Requires dk == dv == d in {64, 128}. q, k, v, the raw inputs and conv_w
+ * 16-byte aligned; outputs must not overlap inputs.
+ */
+GDN_API int gdn_frontend_qkv(const void *q_raw, const void *k_raw,
+                             const void *v_raw, const float *conv_w,
+                             const int32_t *cu_seqlens, int32_t N, int32_t T,
+                             int32_t H, int32_t d, float l2_eps, void *q,
+                             void *k, void *v, int32_t in_dtype,
+                             int32_t out_dtype, void *stream);
+
+/*
+ * Output gate (same section, third display; the RMSNorm is the zero-centred
+ * one of the pwwt.cn page, section 2.1.1, whose gain is 1 + w): for each row
+ * of d values (one token of one head)
+ *     o = sigmoid(z) * y / sqrt(mean(y^2) + rms_eps) * (1 + norm_w).
+ *
+ *   y, z    [rows, d] in in_dtype (a [tokens, H, d] tensor is rows = tokens*H).
+ *   norm_w  float32 [d], shared by all heads, or NULL for w = 0.
+ *   o       [rows, d] in out_dtype; must not overlap y or z.
+ * d in {64, 128}; y, z, o 16-byte aligned.
+ */
+GDN_API int gdn_output_gate(const void *y, const void *z, const float *norm_w,
+                            float rms_eps, void *o, int64_t rows, int32_t d,
+                            int32_t in_dtype, int32_t out_dtype, void *stream);
+
 /* Human-readable name of a return code (static string, never NULL). */
 GDN_API const char *gdn_status_string(int status);
 

@@ -98,3 +98,25 @@ def test_decode_rejects(lib):
     rc = lib.gdn_decode_step(A, A + 4096, A + 8192, A + 12288, A + 16384, B, B + (1 << 24), 4, 2,
                              128, 100, 1, 1, None)
     assert rc == -2
+
+
+def test_frontend_and_gate_reject(lib):
+    v = ctypes.c_void_p
+    lib.gdn_frontend_qkv.argtypes = [v, v, v, v, v, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_float, v, v, v, ctypes.c_int32,
+                                     ctypes.c_int32, v]
+    lib.gdn_output_gate.argtypes = [v, v, v, ctypes.c_float, v, ctypes.c_int64, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, v]
+    base = [A, A + (1 << 26), A + (2 << 26), A + (3 << 26), None, 1, 64, 2, 128, 1e-6,
+            B, B + (1 << 26), B + (2 << 26), 1, 1, None]
+    bad = list(base); bad[8] = 96
+    assert lib.gdn_frontend_qkv(*bad) == -2
+    bad = list(base); bad[10] = A + 64          # q overlaps q_raw
+    assert lib.gdn_frontend_qkv(*bad) == -1
+    bad = list(base); bad[0] = A + 8            # misaligned
+    assert lib.gdn_frontend_qkv(*bad) == -3
+    bad = list(base); bad[9] = -1.0             # negative eps
+    assert lib.gdn_frontend_qkv(*bad) == -1
+    assert lib.gdn_output_gate(A, A + 4096, None, 1e-6, A + 64, 16, 128, 1, 1, None) == -1
+    assert lib.gdn_output_gate(A, A + 65536, None, 1e-6, B, 16, 100, 1, 1, None) == -2
+    assert lib.gdn_output_gate(None, A, None, 1e-6, B, 16, 128, 1, 1, None) == -1

@@ -214,3 +214,63 @@ def test_decode_matches_prefill():
     yd = torch.stack(yd, 1).reshape(3 * T, 2, 128)
     assert rel_l2(yd, y.cpu().double().numpy()) < 1e-5
     assert rel_l2(Sd, S.cpu().double().numpy()) < 1e-5
+
+
+# ------------------------------------------------------------ front end -----
+@gpu
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_frontend_varlen(d, dtype):
+    g = _lib()
+    lengths = [1, 2, 3, 4, 5, 63, 64, 65, 300, 0, 17]
+    f = gi.frontend_inputs(lengths, 3, d, d, dtype=dtype, seed=61)
+    dev = to_dev(f)
+    q, k, v = g.gdn_frontend_qkv(dev["q_raw"], dev["k_raw"], dev["v_raw"], dev["conv_w"],
+                                 cu_seqlens=dev["cu_seqlens"], l2_eps=1e-6, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    cu = f["cu_seqlens"]
+    H = 3
+    for i, (raw, got, l2) in enumerate(((f["q_raw"], q, True), (f["k_raw"], k, True),
+                                        (f["v_raw"], v, False))):
+        ref = oracle.frontend(raw, f["conv_w"][i], cu_seqlens=cu, l2=l2, eps=1e-6)
+        e = rel_l2(got, ref)
+        print("stream %d rel_l2 %.3e" % (i, e))
+        assert e <= 1e-5, (i, e)  # fp32 arithmetic on exact inputs
+    # bf16 outputs: one rounding on top
+    qb, kb, vb = g.gdn_frontend_qkv(dev["q_raw"], dev["k_raw"], dev["v_raw"], dev["conv_w"],
+                                    cu_seqlens=dev["cu_seqlens"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.frontend(f["q_raw"], f["conv_w"][0], cu_seqlens=cu, l2=True, eps=1e-6)
+    assert rel_l2(qb, ref) <= 4e-3
+
+
+@gpu
+def test_frontend_equal_length_batches():
+    g = _lib()
+    f = gi.frontend_inputs([50, 50, 50], 2, 128, 128, dtype="bf16", seed=62)
+    dev = to_dev(f)
+    q, k, v = g.gdn_frontend_qkv(dev["q_raw"], dev["k_raw"], dev["v_raw"], dev["conv_w"], N=3,
+                                 out_dtype=torch.float32)
+    q2, k2, v2 = g.gdn_frontend_qkv(dev["q_raw"], dev["k_raw"], dev["v_raw"], dev["conv_w"],
+                                    cu_seqlens=dev["cu_seqlens"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(k, k2) and torch.equal(v, v2)
+
+
+@gpu
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("with_w", [False, True])
+def test_output_gate(d, dtype, with_w):
+    g = _lib()
+    rows = 1000
+    y = gi.normal((rows, d), 71, 1).to(gi.torch_dtype(dtype))
+    z = gi.normal((rows, d), 71, 2).to(gi.torch_dtype(dtype))
+    w = gi.normal((d,), 71, 3, std=0.1) if with_w else None
+    o = g.gdn_output_gate(y.cuda(), z.cuda(), None if w is None else w.cuda(), 1e-6,
+                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.output_gate(y, z, w, eps=1e-6)
+    e = rel_l2(o, ref)
+    print("rel_l2 %.3e" % e)
+    assert e <= 1e-5
