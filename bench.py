@@ -130,6 +130,61 @@ def bench_decode(g, n_steps=128, reps=2):
                 tokens_per_s=N / (us_step * 1e-6), bytes_per_step=bytes_step, steps=n_steps)
 
 
+def bench_longctx(g, steps=3, warmup=1):
+    """B=1, H=32, T=65536 prefill from a nonzero S0 (fp32 state)."""
+    w = gi.WORKLOADS[2]
+    inp = gi.workload_inputs(2)
+    dev = torch.device("cuda", 0)
+    d = {k: inp[k].to(dev) for k in ("q", "k", "v", "log_alpha", "beta", "S0")}
+    y = torch.empty(d["v"].shape, dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty_like(d["S0"])
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        g.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"], y=y, S_T=S_T)
+
+    ms = time_launches(step, steps, warmup, stream) / steps
+    tokens = w.B * w.T
+    flops = tokens * w.H * prefill_flops_per_token_head(w.dk, w.dv)
+    nbytes = prefill_bytes(tokens, w.H, w.dk, w.dv, w.B, s0=True)
+    return dict(workload=w.name, ms_per_call=ms, tokens_per_s=tokens / (ms * 1e-3),
+                pct_bf16_mfma_peak=100.0 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                hbm_GBps=nbytes / (ms * 1e-3) / 1e9)
+
+
+def bench_varlen_frontend(g, steps=3, warmup=1):
+    """64 packed sequences (lengths U[512, 8192]), H=16, d=128: front end ->
+    chunked prefill -> output gate, as three kernels (q/k/v in fp16 and y in
+    fp32 between them)."""
+    w = gi.WORKLOADS[4]
+    f = gi.workload_inputs(4)
+    dev = torch.device("cuda", 0)
+    d = {k: v.to(dev) for k, v in f.items() if isinstance(v, torch.Tensor)}
+    rows = int(f["cu_seqlens"][-1])
+    shape = d["q_raw"].shape
+    qkv = tuple(torch.empty(shape, dtype=torch.float16, device=dev) for _ in range(3))
+    y = torch.empty(shape, dtype=torch.float32, device=dev)
+    S_T = torch.empty_like(d["S0"])
+    o = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        q, k, v = g.gdn_frontend_qkv(d["q_raw"], d["k_raw"], d["v_raw"], d["conv_w"],
+                                     cu_seqlens=d["cu_seqlens"], out=qkv,
+                                     out_dtype=torch.float16)
+        g.gdn_chunk_fwd(q, k, v, d["log_alpha"], d["beta"], d["S0"], cu_seqlens=d["cu_seqlens"],
+                        y=y, S_T=S_T, out_dtype=torch.float32)
+        g.gdn_output_gate(y, d["z"], d["norm_w"], 1e-6, out_dtype=torch.bfloat16, o=o)
+
+    ms = time_launches(step, steps, warmup, stream) / steps
+    flops = rows * w.H * prefill_flops_per_token_head(w.dk, w.dv)
+    fused_bytes = rows * w.H * (3 * 128 * 2 + 128 * 2 + 128 * 2 + 8) + 2 * w.n_seqs * w.H * 128 * 128 * 4
+    return dict(workload=w.name, tokens=rows, ms_per_call=ms, tokens_per_s=rows / (ms * 1e-3),
+                pct_bf16_mfma_peak=100.0 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                hbm_GBps_of_fused_bytes=fused_bytes / (ms * 1e-3) / 1e9,
+                kernels="gdn_frontend_qkv + gdn_chunk_fwd + gdn_output_gate")
+
+
 def cpu_baseline(pf, max_seconds=30.0):
     """The fp64 oracle on the host cores, on the same prefill batch: every
     head of as many whole sequences as fit the time budget (starting with
@@ -167,6 +222,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the long-context and varlen front-end workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the GDN mixer shards over (sequence, head) with no "
@@ -215,6 +272,14 @@ def main():
         print("[bench] decode workload 3: 256 x 32 heads, %d steps" % args.decode_steps,
               file=sys.stderr, flush=True)
         rec["decode"] = bench_decode(g, args.decode_steps)
+
+    if not args.no_extra:
+        print("[bench] long-context prefill workload 2: B=1 H=32 T=65536", file=sys.stderr,
+              flush=True)
+        rec["longctx"] = bench_longctx(g)
+        print("[bench] varlen front-end workload 4: 64 sequences, H=16", file=sys.stderr,
+              flush=True)
+        rec["varlen_frontend"] = bench_varlen_frontend(g)
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

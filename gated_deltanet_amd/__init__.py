@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_F32 = 0
 GDN_BF16 = 1
+GDN_F16 = 2
 GDN_OK = 0
 
 _lib = None
@@ -54,7 +55,7 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_frontend_qkv.argtypes = [vp, vp, vp, fp, ip, i32, i32, i32, i32, f32, vp, vp, vp,
                                      i32, i32, vp]
     lib.gdn_frontend_qkv.restype = ctypes.c_int
-    lib.gdn_output_gate.argtypes = [vp, vp, fp, f32, vp, i64, i32, i32, i32, vp]
+    lib.gdn_output_gate.argtypes = [vp, vp, fp, f32, vp, i64, i32, i32, i32, i32, vp]
     lib.gdn_output_gate.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -71,7 +72,9 @@ def _dt(t: torch.dtype) -> int:
         return GDN_BF16
     if t == torch.float32:
         return GDN_F32
-    raise GdnError("unsupported dtype %s (bf16 or fp32)" % t)
+    if t == torch.float16:
+        return GDN_F16
+    raise GdnError("unsupported dtype %s (fp32, bf16 or fp16)" % t)
 
 
 def _p(t):
@@ -200,12 +203,14 @@ def gdn_frontend_qkv(q_raw, k_raw, v_raw, conv_w, cu_seqlens=None, N=None, l2_ep
 
 def gdn_output_gate(y, z, norm_w=None, rms_eps=1e-6, out_dtype=None, o=None):
     """o = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + norm_w) over the last
-    dimension (d in {64, 128}); y and z share a dtype."""
+    dimension (d in {64, 128}); y and z may have different dtypes."""
     lib = load_library()
     in_dtype = y.dtype
     out_dtype = in_dtype if out_dtype is None else out_dtype
     _need(y, "y", in_dtype)
-    _need(z, "z", in_dtype)
+    _need(z, "z", z.dtype)
+    if z.shape != y.shape:
+        raise GdnError("z must have the shape of y")
     if norm_w is not None:
         _need(norm_w, "norm_w", torch.float32)
     d = y.shape[-1]
@@ -213,7 +218,7 @@ def gdn_output_gate(y, z, norm_w=None, rms_eps=1e-6, out_dtype=None, o=None):
     if o is None:
         o = torch.empty(y.shape, dtype=out_dtype, device=y.device)
     rc = lib.gdn_output_gate(_p(y), _p(z), _p(norm_w), float(rms_eps), _p(o), rows, d,
-                             _dt(in_dtype), _dt(out_dtype), _stream(y.device))
+                             _dt(in_dtype), _dt(z.dtype), _dt(out_dtype), _stream(y.device))
     _check(rc, lib, "gdn_output_gate")
     return o
 

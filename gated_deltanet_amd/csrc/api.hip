@@ -22,9 +22,9 @@ bool misaligned(const void *p, uintptr_t a = 16) {
 
 bool head_size_ok(int d) { return d == 64 || d == 128; }
 
-bool dtype_ok(int t) { return t == GDN_F32 || t == GDN_BF16; }
+bool dtype_ok(int t) { return t == GDN_F32 || t == GDN_BF16 || t == GDN_F16; }
 
-size_t esize(int t) { return t == GDN_BF16 ? 2 : 4; }
+size_t esize(int t) { return t == GDN_F32 ? 4 : 2; }
 
 // half-open byte ranges [a, a+na) and [b, b+nb) overlap?
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
@@ -68,7 +68,7 @@ GDN_API int gdn_chunk_fwd(const void *q, const void *k, const void *v, const flo
   if (!head_size_ok(dk) || !head_size_ok(dv))
     return fail(GDN_ERR_UNSUPPORTED, "%s", "dk and dv must be 64 or 128");
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
-    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32 or GDN_BF16");
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32, GDN_BF16 or GDN_F16");
   const int64_t rows = cu_seqlens ? static_cast<int64_t>(T) : static_cast<int64_t>(N) * T;
   if (static_cast<int64_t>(N) * H > (int64_t{1} << 31) / 8)
     return fail(GDN_ERR_INVALID_ARG, "%s", "N * H too large");
@@ -129,7 +129,7 @@ GDN_API int gdn_decode_step(const void *q, const void *k, const void *v, const f
   if (!head_size_ok(dk) || !head_size_ok(dv))
     return fail(GDN_ERR_UNSUPPORTED, "%s", "dk and dv must be 64 or 128");
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
-    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32 or GDN_BF16");
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32, GDN_BF16 or GDN_F16");
   if (static_cast<int64_t>(N) * H >= (int64_t{1} << 31))
     return fail(GDN_ERR_INVALID_ARG, "%s", "N * H too large");
   if (N > 0 && (!q || !k || !v || !log_alpha || !beta || !S || !y))
@@ -176,7 +176,7 @@ GDN_API int gdn_frontend_qkv(const void *q_raw, const void *k_raw, const void *v
   if (N < 0 || T < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N, T must be >= 0 and H > 0");
   if (!head_size_ok(d)) return fail(GDN_ERR_UNSUPPORTED, "%s", "d must be 64 or 128");
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
-    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32 or GDN_BF16");
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32, GDN_BF16 or GDN_F16");
   if (!(l2_eps >= 0.0f)) return fail(GDN_ERR_INVALID_ARG, "%s", "l2_eps must be >= 0");
   const int64_t rows = cu_seqlens ? static_cast<int64_t>(T) : static_cast<int64_t>(N) * T;
   if (rows * H * d >= (int64_t{1} << 40)) return fail(GDN_ERR_INVALID_ARG, "%s", "input too large");
@@ -220,21 +220,23 @@ GDN_API int gdn_frontend_qkv(const void *q_raw, const void *k_raw, const void *v
 }
 
 GDN_API int gdn_output_gate(const void *y, const void *z, const float *norm_w, float rms_eps,
-                            void *o, int64_t rows, int32_t d, int32_t in_dtype, int32_t out_dtype,
-                            void *stream) {
+                            void *o, int64_t rows, int32_t d, int32_t y_dtype, int32_t z_dtype,
+                            int32_t out_dtype, void *stream) {
+  const int32_t in_dtype = y_dtype;
   g_last_error[0] = '\0';
   if (rows < 0) return fail(GDN_ERR_INVALID_ARG, "%s", "rows must be >= 0");
   if (!head_size_ok(d)) return fail(GDN_ERR_UNSUPPORTED, "%s", "d must be 64 or 128");
-  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
-    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32 or GDN_BF16");
+  if (!dtype_ok(in_dtype) || !dtype_ok(z_dtype) || !dtype_ok(out_dtype))
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32, GDN_BF16 or GDN_F16");
   if (!(rms_eps >= 0.0f)) return fail(GDN_ERR_INVALID_ARG, "%s", "rms_eps must be >= 0");
   if (rows / 64 >= (int64_t{1} << 31)) return fail(GDN_ERR_INVALID_ARG, "%s", "too many rows");
   if (rows > 0 && (!y || !z || !o)) return fail(GDN_ERR_INVALID_ARG, "%s", "null pointer");
   if (misaligned(y) || misaligned(z) || misaligned(o) || misaligned(norm_w, 4))
     return fail(GDN_ERR_MISALIGNED, "%s", "y, z, o need 16-byte alignment, norm_w 4");
   const size_t nin = static_cast<size_t>(rows) * d * esize(in_dtype);
+  const size_t nz = static_cast<size_t>(rows) * d * esize(z_dtype);
   const size_t nout = static_cast<size_t>(rows) * d * esize(out_dtype);
-  if (overlap(y, nin, o, nout) || overlap(z, nin, o, nout) ||
+  if (overlap(y, nin, o, nout) || overlap(z, nz, o, nout) ||
       overlap(norm_w, static_cast<size_t>(d) * 4, o, nout))
     return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps the output");
   gdn::GateArgs a;
@@ -246,6 +248,7 @@ GDN_API int gdn_output_gate(const void *y, const void *z, const float *norm_w, f
   a.rows = rows;
   a.d = d;
   a.in_dtype = in_dtype;
+  a.z_dtype = z_dtype;
   a.out_dtype = out_dtype;
   a.stream = static_cast<hipStream_t>(stream);
   return hip_status(gdn::launch_output_gate(a), "gdn_output_gate launch");

@@ -158,18 +158,47 @@ __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(bf16_t *p, float v) {
   *reinterpret_cast<__bf16 *>(p) = (__bf16)v;  // v_cvt_pk_bf16_f32, round to nearest even
 }
+__device__ __forceinline__ void store_out(_Float16 *p, float v) { *p = (_Float16)v; }
+
+// Operations on the raw 16-bit input tiles (K, Q, V) for each input type.
+// bf16 inputs keep bf16 operands for the key-side products (exact inputs;
+// the state operand of K S is rounded to bf16) and have Q converted to fp16
+// by a prep wave for Q S; fp16 inputs use fp16 operands throughout.
+template <typename TIN>
+struct KOps;
+template <>
+struct KOps<bf16_t> {
+  typedef bf16x8 vec;
+  static constexpr bool kConvertQ = true;
+  __device__ static f32x4 mma(const vec &a, const vec &b, f32x4 c) { return mma_bf16(a, b, c); }
+  __device__ static vec pack(const f32x4 &a, const f32x4 &b) { return pack_bf16(a, b); }
+  __device__ static float to_f32(uint16_t bits) { return bf16_to_f32(bits); }
+};
+template <>
+struct KOps<_Float16> {
+  typedef f16x8 vec;
+  static constexpr bool kConvertQ = false;
+  __device__ static f32x4 mma(const vec &a, const vec &b, f32x4 c) { return mma_f16(a, b, c); }
+  __device__ static vec pack(const f32x4 &a, const f32x4 &b) { return pack_f16(a, b); }
+  __device__ static float to_f32(uint16_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, bits));
+  }
+};
+
 template <typename V>
 __device__ __forceinline__ V lds_read16(const char *p) {
   return *reinterpret_cast<const V *>(p);
 }
 
-template <int DK, int NS, typename TOUT>
+template <int DK, int NS, typename TIN, typename TOUT>
 __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
-    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ v,
+    const TIN *__restrict__ q, const TIN *__restrict__ k, const TIN *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
     const float *__restrict__ S0, TOUT *__restrict__ y, float *__restrict__ S_T,
     const int32_t *__restrict__ cu_seqlens, int T, int H, int DV, int n_vt) {
   using L = Lay<DK, NS>;
+  using KO = KOps<TIN>;
+  using kvec = typename KO::vec;
   constexpr int NKB = L::NKB;
   constexpr int NST = L::NST;
   constexpr int DVT = L::DVT;
@@ -308,20 +337,20 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
       reinterpret_cast<float *>(pb + L::BT_OFF)[lane] = G.bt;
       fac0[lane] = G.bt * __builtin_amdgcn_exp2f(G.g2 - G.gm2);  // beta_r a_r
     }
-    bf16x8 kf[kNCT][NKB];
+    kvec kf[kNCT][NKB];
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        kf[rt][kb] = lds_read16<bf16x8>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
     f32x4 gram[3];
 #pragma unroll
     for (int t = 0; t < 3; ++t) gram[t] = zero4();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      gram[0] = mma_bf16(kf[0][kb], kf[0][kb], gram[0]);
-      gram[1] = mma_bf16(kf[1][kb], kf[0][kb], gram[1]);
-      gram[2] = mma_bf16(kf[1][kb], kf[1][kb], gram[2]);
+      gram[0] = KO::mma(kf[0][kb], kf[0][kb], gram[0]);
+      gram[1] = KO::mma(kf[1][kb], kf[0][kb], gram[1]);
+      gram[2] = KO::mma(kf[1][kb], kf[1][kb], gram[2]);
     }
     wait_lds();
     f32x4 rf[kNCT];
@@ -428,12 +457,12 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
   // ---- prep wave 1: P = tril(Q K^T o G), Q -> fp16, Kt^T ------------------
   // 0/1 selector operand for exact transposes on the matrix cores: in lane
   // (lg, lc), slot j is 1 iff lg == lc >> 2 and j == 4u + (lc & 3).
-  bf16x8 sel[2];
+  kvec sel[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      sel[u][j] = (__bf16)((lg == (lc >> 2) && j == 4 * u + (lc & 3)) ? 1.0f : 0.0f);
+      sel[u][j] = (lg == (lc >> 2) && j == 4 * u + (lc & 3)) ? 1.0f : 0.0f;
 
   auto prep1 = [&](int x) {
     char *slot = ring + (x % kRing) * L::SLOT;
@@ -442,37 +471,39 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
     scan_gates(slot, x, fac1, G);
     const float kdec = __builtin_amdgcn_exp2f(G.gC2 - G.g2);
     if (lane < kC) fac1[lane] = __builtin_amdgcn_exp2f(G.g2 - G.gm2);  // a_r
-    bf16x8 kf[kNCT][NKB], qf[kNCT][NKB];
+    kvec kf[kNCT][NKB], qf[kNCT][NKB];
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        kf[rt][kb] = lds_read16<bf16x8>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
-        qf[rt][kb] = lds_read16<bf16x8>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+        qf[rt][kb] = lds_read16<kvec>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
       }
     f32x4 qk[3];
 #pragma unroll
     for (int t = 0; t < 3; ++t) qk[t] = zero4();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      qk[0] = mma_bf16(qf[0][kb], kf[0][kb], qk[0]);
-      qk[1] = mma_bf16(qf[1][kb], kf[0][kb], qk[1]);
-      qk[2] = mma_bf16(qf[1][kb], kf[1][kb], qk[2]);
+      qk[0] = KO::mma(qf[0][kb], kf[0][kb], qk[0]);
+      qk[1] = KO::mma(qf[1][kb], kf[0][kb], qk[1]);
+      qk[2] = KO::mma(qf[1][kb], kf[1][kb], qk[2]);
     }
     // Q in fp16 for the state waves' Q S: D_u = Sel_u x Q^T puts keys
     // 8 lg + 4u + i of token lc in lane (lg, lc), i.e. the A-operand slots;
     // exact, then rounded from bf16 values that fp16 represents exactly.
     // Written back over the raw Q of this slot, which no other wave reads
     // during this chunk step.
+    if constexpr (KO::kConvertQ) {
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const f32x4 d0 = mma_bf16(sel[0], qf[rt][kb], zero4());
-        const f32x4 d1 = mma_bf16(sel[1], qf[rt][kb], zero4());
+        const f32x4 d0 = KO::mma(sel[0], qf[rt][kb], zero4());
+        const f32x4 d1 = KO::mma(sel[1], qf[rt][kb], zero4());
         *reinterpret_cast<f16x8 *>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane) =
             pack_f16(d0, d1);
       }
+    }
     wait_lds();
     f32x4 rf[kNCT];
     float cf[kNCT];
@@ -521,8 +552,8 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
     for (int j = 0; j < 8; ++j) kd[j] = __shfl(kdec, 16 * (j >> 2) + 4 * lg + (j & 3), 64);
 #pragma unroll
     for (int t = 0; t < NST; ++t) {
-      const f32x4 d0 = mma_bf16(kf[0][t >> 1], sel[t & 1], zero4());
-      const f32x4 d1 = mma_bf16(kf[1][t >> 1], sel[t & 1], zero4());
+      const f32x4 d0 = KO::mma(kf[0][t >> 1], sel[t & 1], zero4());
+      const f32x4 d1 = KO::mma(kf[1][t >> 1], sel[t & 1], zero4());
       f16x8 f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -550,11 +581,11 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
     // the state as B operand: bf16 against the raw bf16 keys for X = K S,
     // fp16 against the fp16 queries for Q S (Q S feeds y directly, so it gets
     // the finer rounding; errors in X are largely corrected by the delta rule)
-    bf16x8 sb[NKB];
+    kvec sb[NKB];
     f16x8 sh[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      sb[kb] = pack_bf16(st[2 * kb], st[2 * kb + 1]);
+      sb[kb] = KO::pack(st[2 * kb], st[2 * kb + 1]);
       sh[kb] = pack_f16(st[2 * kb], st[2 * kb + 1]);
     }
     f32x4 X[kNCT], QS[kNCT];
@@ -567,8 +598,8 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int rt = 0; rt < kNCT; ++rt) {
-        const bf16x8 kf = lds_read16<bf16x8>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
-        X[rt] = mma_bf16(kf, sb[kb], X[rt]);
+        const kvec kf = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+        X[rt] = KO::mma(kf, sb[kb], X[rt]);
       }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -579,7 +610,7 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
       }
     const float *gam = reinterpret_cast<const float *>(pb + L::GM_OFF);
     const float *bet = reinterpret_cast<const float *>(pb + L::BT_OFF);
-    const bf16_t *vt_ = reinterpret_cast<const bf16_t *>(slot + L::V_OFF);
+    const uint16_t *vt_ = reinterpret_cast<const uint16_t *>(slot + L::V_OFF);
     f32x4 R[kNCT], G4[kNCT];
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt) {
@@ -587,7 +618,7 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
       const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + 16 * rt + 4 * lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float vv = bf16_to_f32(vt_[(16 * rt + 4 * lg + i) * DVT + slab + lc]);
+        const float vv = KO::to_f32(vt_[(16 * rt + 4 * lg + i) * DVT + slab + lc]);
         R[rt][i] = b4[i] * (vv - G4[rt][i] * X[rt][i]);
       }
     }
@@ -672,15 +703,15 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
   }
 }
 
-template <int DK, int NS, typename TOUT>
+template <int DK, int NS, typename TIN, typename TOUT>
 hipError_t launch_bf16(const ChunkArgs &a) {
   constexpr int DVT = 16 * NS;
   const int n_vt = a.dv / DVT;
   const int64_t blocks = static_cast<int64_t>(a.N) * a.H * n_vt;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, NS, TOUT>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(64 * (NS + 2)), 0, a.stream, static_cast<const bf16_t *>(a.q),
-                     static_cast<const bf16_t *>(a.k), static_cast<const bf16_t *>(a.v),
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, NS, TIN, TOUT>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(64 * (NS + 2)), 0, a.stream, static_cast<const TIN *>(a.q),
+                     static_cast<const TIN *>(a.k), static_cast<const TIN *>(a.v),
                      a.log_alpha, a.beta, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.cu_seqlens,
                      a.T, a.H, a.dv, n_vt);
   return hipGetLastError();
@@ -688,15 +719,26 @@ hipError_t launch_bf16(const ChunkArgs &a) {
 
 }  // namespace
 
+template <typename TIN, typename TOUT>
+static hipError_t launch_16(const ChunkArgs &a) {
+  return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT>(a) : launch_bf16<64, 2, TIN, TOUT>(a);
+}
+
+template <typename TIN>
+static hipError_t launch_16_out(const ChunkArgs &a) {
+  switch (a.out_dtype) {
+    case 1: return launch_16<TIN, bf16_t>(a);
+    case 2: return launch_16<TIN, _Float16>(a);
+    default: return launch_16<TIN, float>(a);
+  }
+}
+
 hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a) {
-  const bool out_bf16 = a.out_dtype == 1;
-  if (a.dk == 128)
-    return out_bf16 ? launch_bf16<128, 2, bf16_t>(a) : launch_bf16<128, 2, float>(a);
-  return out_bf16 ? launch_bf16<64, 2, bf16_t>(a) : launch_bf16<64, 2, float>(a);
+  return a.in_dtype == 2 ? launch_16_out<_Float16>(a) : launch_16_out<bf16_t>(a);
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a) {
-  return a.in_dtype == 1 ? launch_chunk_fwd_bf16(a) : launch_chunk_fwd_f32(a);
+  return a.in_dtype == 0 ? launch_chunk_fwd_f32(a) : launch_chunk_fwd_bf16(a);
 }
 
 }  // namespace gdn

@@ -367,14 +367,18 @@ static hipError_t launch_tile(const ChunkArgs &a) {
   return hipGetLastError();
 }
 
+template <typename TOUT>
+static hipError_t launch_f32_out(const ChunkArgs &a) {
+  if (a.dk == 128) return launch_tile<128, 16, float, TOUT, float>(a);
+  return launch_tile<64, 64, float, TOUT, float>(a);
+}
+
 hipError_t launch_chunk_fwd_f32(const ChunkArgs &a) {
-  const bool out_bf16 = a.out_dtype == 1;
-  if (a.dk == 128) {
-    return out_bf16 ? launch_tile<128, 16, float, bf16_t, float>(a)
-                    : launch_tile<128, 16, float, float, float>(a);
+  switch (a.out_dtype) {
+    case 1: return launch_f32_out<bf16_t>(a);
+    case 2: return launch_f32_out<_Float16>(a);
+    default: return launch_f32_out<float>(a);
   }
-  return out_bf16 ? launch_tile<64, 64, float, bf16_t, float>(a)
-                  : launch_tile<64, 64, float, float, float>(a);
 }
 
 }  // namespace gdn

@@ -144,13 +144,21 @@ static hipError_t launch_d(const DecodeArgs &a) {
   return launch<64, 64, TIN, TOUT>(a);
 }
 
+template <typename TIN>
+static hipError_t launch_d_out(const DecodeArgs &a) {
+  switch (a.out_dtype) {
+    case 1: return launch_d<TIN, bf16_t>(a);
+    case 2: return launch_d<TIN, _Float16>(a);
+    default: return launch_d<TIN, float>(a);
+  }
+}
+
 hipError_t launch_decode_step(const DecodeArgs &a) {
-  const bool in_bf16 = a.in_dtype == 1;
-  const bool out_bf16 = a.out_dtype == 1;
-  if (in_bf16 && out_bf16) return launch_d<bf16_t, bf16_t>(a);
-  if (in_bf16) return launch_d<bf16_t, float>(a);
-  if (out_bf16) return launch_d<float, bf16_t>(a);
-  return launch_d<float, float>(a);
+  switch (a.in_dtype) {
+    case 1: return launch_d_out<bf16_t>(a);
+    case 2: return launch_d_out<_Float16>(a);
+    default: return launch_d_out<float>(a);
+  }
 }
 
 }  // namespace gdn

@@ -50,6 +50,16 @@ struct Vec8<float> {
   }
 };
 template <>
+struct Vec8<_Float16> {
+  __device__ static void load(const _Float16 *p, float *o) { io<_Float16>::load16(p, o); }
+  __device__ static void store(_Float16 *p, const float *v) {
+    f16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (_Float16)v[i];
+    *reinterpret_cast<f16x8 *>(p) = r;
+  }
+};
+template <>
 struct Vec8<bf16_t> {
   __device__ static void load(const bf16_t *p, float *o) { io<bf16_t>::load16(p, o); }
   __device__ static void store(bf16_t *p, const float *v) {
@@ -140,9 +150,9 @@ __global__ __launch_bounds__(256) void frontend_kernel(
   }
 }
 
-template <int D, typename TIN, typename TOUT>
+template <int D, typename TIN, typename TZ, typename TOUT>
 __global__ __launch_bounds__(256) void output_gate_kernel(const TIN *__restrict__ y,
-                                                          const TIN *__restrict__ z,
+                                                          const TZ *__restrict__ z,
                                                           const float *__restrict__ nw, float eps,
                                                           TOUT *__restrict__ o, int64_t nrows) {
   constexpr int G = D / 8;
@@ -158,7 +168,7 @@ __global__ __launch_bounds__(256) void output_gate_kernel(const TIN *__restrict_
     const int64_t rr = live ? r : nrows - 1;
     float yv[8], zv[8];
     Vec8<TIN>::load(y + rr * D + c0, yv);
-    Vec8<TIN>::load(z + rr * D + c0, zv);
+    Vec8<TZ>::load(z + rr * D + c0, zv);
     float ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) ss = fmaf(yv[c], yv[c], ss);
@@ -182,38 +192,51 @@ hipError_t launch_fe(const FrontendArgs &a) {
   return hipGetLastError();
 }
 
-template <int D, typename TIN, typename TOUT>
+template <int D, typename TIN, typename TZ, typename TOUT>
 hipError_t launch_og(const GateArgs &a) {
   const int64_t blocks = (a.rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL((output_gate_kernel<D, TIN, TOUT>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((output_gate_kernel<D, TIN, TZ, TOUT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(256), 0, a.stream, static_cast<const TIN *>(a.y),
-                     static_cast<const TIN *>(a.z), a.norm_w, a.eps, static_cast<TOUT *>(a.o),
+                     static_cast<const TZ *>(a.z), a.norm_w, a.eps, static_cast<TOUT *>(a.o),
                      a.rows);
   return hipGetLastError();
+}
+
+// runtime dtype code (0 f32, 1 bf16, 2 f16) -> type, one template level at a time
+template <typename F>
+hipError_t with_type(int code, F &&f) {
+  switch (code) {
+    case 1: return f(bf16_t{});
+    case 2: return f(_Float16{});
+    default: return f(float{});
+  }
 }
 
 }  // namespace
 
 hipError_t launch_frontend(const FrontendArgs &a) {
   if (a.rows == 0) return hipSuccess;
-  const bool ib = a.in_dtype == 1, ob = a.out_dtype == 1;
-  if (a.d == 128) {
-    if (ib) return ob ? launch_fe<128, bf16_t, bf16_t>(a) : launch_fe<128, bf16_t, float>(a);
-    return ob ? launch_fe<128, float, bf16_t>(a) : launch_fe<128, float, float>(a);
-  }
-  if (ib) return ob ? launch_fe<64, bf16_t, bf16_t>(a) : launch_fe<64, bf16_t, float>(a);
-  return ob ? launch_fe<64, float, bf16_t>(a) : launch_fe<64, float, float>(a);
+  return with_type(a.in_dtype, [&](auto tin) {
+    return with_type(a.out_dtype, [&](auto tout) {
+      using TI = decltype(tin);
+      using TO = decltype(tout);
+      return a.d == 128 ? launch_fe<128, TI, TO>(a) : launch_fe<64, TI, TO>(a);
+    });
+  });
 }
 
 hipError_t launch_output_gate(const GateArgs &a) {
   if (a.rows == 0) return hipSuccess;
-  const bool ib = a.in_dtype == 1, ob = a.out_dtype == 1;
-  if (a.d == 128) {
-    if (ib) return ob ? launch_og<128, bf16_t, bf16_t>(a) : launch_og<128, bf16_t, float>(a);
-    return ob ? launch_og<128, float, bf16_t>(a) : launch_og<128, float, float>(a);
-  }
-  if (ib) return ob ? launch_og<64, bf16_t, bf16_t>(a) : launch_og<64, bf16_t, float>(a);
-  return ob ? launch_og<64, float, bf16_t>(a) : launch_og<64, float, float>(a);
+  return with_type(a.in_dtype, [&](auto ty) {
+    return with_type(a.z_dtype, [&](auto tz) {
+      return with_type(a.out_dtype, [&](auto to) {
+        using TY = decltype(ty);
+        using TZ = decltype(tz);
+        using TO = decltype(to);
+        return a.d == 128 ? launch_og<128, TY, TZ, TO>(a) : launch_og<64, TY, TZ, TO>(a);
+      });
+    });
+  });
 }
 
 }  // namespace gdn

@@ -60,6 +60,18 @@ struct io<bf16_t> {
   __device__ static __forceinline__ bf16_t from_f32(float x) { return f32_to_bf16(x); }
 };
 
+template <>
+struct io<_Float16> {
+  static constexpr int kVec = 8;
+  __device__ static __forceinline__ void load16(const _Float16 *p, float *out) {
+    const f16x8 v = *reinterpret_cast<const f16x8 *>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = static_cast<float>(v[i]);
+  }
+  __device__ static __forceinline__ float to_f32(_Float16 x) { return static_cast<float>(x); }
+  __device__ static __forceinline__ _Float16 from_f32(float x) { return static_cast<_Float16>(x); }
+};
+
 // ---------------------------------------------------------------------------
 // MFMA fragments.
 //

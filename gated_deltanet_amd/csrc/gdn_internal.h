@@ -13,7 +13,7 @@ struct DecodeArgs {
   float *S;
   void *y;
   int N, H, dk, dv;
-  int in_dtype, out_dtype;  // 0 = f32, 1 = bf16
+  int in_dtype, out_dtype;  // 0 = f32, 1 = bf16, 2 = f16
   hipStream_t stream;
 };
 
@@ -49,7 +49,7 @@ struct GateArgs {
   void *o;
   int64_t rows;
   int d;
-  int in_dtype, out_dtype;
+  int in_dtype, z_dtype, out_dtype;
   hipStream_t stream;
 };
 

@@ -41,7 +41,7 @@ class Workload:
     T: int
     dk: int
     dv: int
-    dtype: str  # "f32" | "bf16" for q/k/v
+    dtype: str  # "f32" | "bf16" | "f16" for q/k/v
     s0_std: float  # 0.0 => S0 = zeros (passed as NULL)
     steps: int = 0
     n_seqs: int = 0
@@ -62,7 +62,7 @@ WORKLOADS = {
                 0.02, n_seqs=64, len_lo=512, len_hi=8192),
 }
 
-_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def torch_dtype(name: str) -> torch.dtype:

@@ -29,10 +29,11 @@
  * where rows = N*T for equal-length batches (sequence n owns rows
  * n*T .. n*T+T-1) or the packed total for varlen batches.
  *
- * Supported: dk, dv in {64, 128}; q/k/v dtype GDN_BF16 or GDN_F32; y dtype
- * GDN_BF16 or GDN_F32. With bf16 inputs the matrix products run on fp16
- * MFMA with fp32 accumulation and an fp32 state; with fp32 inputs every
- * product runs on fp32 MFMA. Gates must satisfy log_alpha finite and <= 0,
+ * Supported: dk, dv in {64, 128}; q/k/v and y dtypes GDN_F32, GDN_BF16 or
+ * GDN_F16. With 16-bit inputs the matrix products run on 16-bit MFMA
+ * (bf16 inputs: the key-side products on bf16, the rest on fp16) with fp32
+ * accumulation and an fp32 state; with fp32 inputs every product runs on
+ * fp32 MFMA. Gates must satisfy log_alpha finite and <= 0,
  * 0 <= beta <= 1; outside that domain the kernels still terminate and stay in
  * bounds but the accuracy is not specified. With bf16 inputs the internal
  * fp16 operands assume |v|, |S| and the intermediate errors stay below
@@ -54,6 +55,7 @@ extern "C" {
 enum gdn_dtype_e {
   GDN_F32 = 0,
   GDN_BF16 = 1,
+  GDN_F16 = 2,
 };
 
 /* return codes */
@@ -147,14 +149,16 @@ GDN_API int gdn_frontend_qkv(const void *q_raw, const void *k_raw,
  * of d values (one token of one head)
  *     o = sigmoid(z) * y / sqrt(mean(y^2) + rms_eps) * (1 + norm_w).
  *
- *   y, z    [rows, d] in in_dtype (a [tokens, H, d] tensor is rows = tokens*H).
+ *   y       [rows, d] in y_dtype (a [tokens, H, d] tensor is rows = tokens*H).
+ *   z       [rows, d] in z_dtype.
  *   norm_w  float32 [d], shared by all heads, or NULL for w = 0.
  *   o       [rows, d] in out_dtype; must not overlap y or z.
  * d in {64, 128}; y, z, o 16-byte aligned.
  */
 GDN_API int gdn_output_gate(const void *y, const void *z, const float *norm_w,
                             float rms_eps, void *o, int64_t rows, int32_t d,
-                            int32_t in_dtype, int32_t out_dtype, void *stream);
+                            int32_t y_dtype, int32_t z_dtype, int32_t out_dtype,
+                            void *stream);
 
 /* Human-readable name of a return code (static string, never NULL). */
 GDN_API const char *gdn_status_string(int status);

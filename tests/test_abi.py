@@ -77,6 +77,7 @@ def test_status_strings(lib):
     (dict(dk=96), -2),
     (dict(dv=32), -2),
     (dict(it=7), -2),
+    (dict(ot=3), -2),
     (dict(q=A + 4), -3),
     (dict(ST=A + (1 << 26)), -1),   # S_T overlaps k
     (dict(y=A), -1),                # y overlaps q
@@ -106,7 +107,7 @@ def test_frontend_and_gate_reject(lib):
                                      ctypes.c_int32, ctypes.c_float, v, v, v, ctypes.c_int32,
                                      ctypes.c_int32, v]
     lib.gdn_output_gate.argtypes = [v, v, v, ctypes.c_float, v, ctypes.c_int64, ctypes.c_int32,
-                                    ctypes.c_int32, ctypes.c_int32, v]
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, v]
     base = [A, A + (1 << 26), A + (2 << 26), A + (3 << 26), None, 1, 64, 2, 128, 1e-6,
             B, B + (1 << 26), B + (2 << 26), 1, 1, None]
     bad = list(base); bad[8] = 96
@@ -117,6 +118,7 @@ def test_frontend_and_gate_reject(lib):
     assert lib.gdn_frontend_qkv(*bad) == -3
     bad = list(base); bad[9] = -1.0             # negative eps
     assert lib.gdn_frontend_qkv(*bad) == -1
-    assert lib.gdn_output_gate(A, A + 4096, None, 1e-6, A + 64, 16, 128, 1, 1, None) == -1
-    assert lib.gdn_output_gate(A, A + 65536, None, 1e-6, B, 16, 100, 1, 1, None) == -2
-    assert lib.gdn_output_gate(None, A, None, 1e-6, B, 16, 128, 1, 1, None) == -1
+    assert lib.gdn_output_gate(A, A + 4096, None, 1e-6, A + 64, 16, 128, 1, 1, 1, None) == -1
+    assert lib.gdn_output_gate(A, A + 65536, None, 1e-6, B, 16, 100, 1, 1, 1, None) == -2
+    assert lib.gdn_output_gate(None, A, None, 1e-6, B, 16, 128, 1, 1, 1, None) == -1
+    assert lib.gdn_output_gate(A, A + 65536, None, 1e-6, B, 16, 128, 1, 5, 1, None) == -2

@@ -1,0 +1,141 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times, on (sequence, head) units the oracle recomputes one by one.
+
+Bar: relative L2 error <= 2e-3 on y / o and on the final states (bf16 inputs,
+fp32 state), per sampled unit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import oracle
+from tests.util import rel_l2
+
+gpu = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _lib():
+    import gated_deltanet_amd as g
+    g.load_library()
+    return g
+
+
+def _unit(inp, n, h, T):
+    rows = slice(n * T, (n + 1) * T)
+    return [inp[key][rows, h:h + 1].contiguous() for key in ("q", "k", "v", "log_alpha", "beta")]
+
+
+@gpu
+def test_prefill_B4_H16_T4096_sampled():
+    g = _lib()
+    inp = gi.workload_inputs(1)
+    dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    y, S = g.gdn_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], None,
+                           N=4)  # bf16 y, as timed
+    torch.cuda.synchronize()
+    y, S = y.cpu(), S.cpu()
+    T = 4096
+    for n, h in [(0, 0), (1, 7), (2, 12), (3, 15)]:
+        q, k, v, la, b = _unit(inp, n, h, T)
+        yo, So = oracle.gdn_fwd(q, k, v, la, b, None, col_blocks=8)
+        ey = rel_l2(y[n * T:(n + 1) * T, h], yo[:, 0])
+        es = rel_l2(S[n, h], So[0, 0])
+        print("unit (%d, %d): y %.3e S %.3e" % (n, h, ey, es), flush=True)
+        assert ey <= TOL and es <= TOL
+
+
+@gpu
+def test_prefill_B1_H32_T65536_sampled():
+    g = _lib()
+    inp = gi.workload_inputs(2)
+    dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    y, S = g.gdn_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["S0"])
+    torch.cuda.synchronize()
+    y, S = y.cpu(), S.cpu()
+    T = 65536
+    for h in (0, 31):
+        q, k, v, la, b = _unit(inp, 0, h, T)
+        yo, So = oracle.gdn_fwd(q, k, v, la, b, inp["S0"][:, h:h + 1], col_blocks=16)
+        ey = rel_l2(y[:, h], yo[:, 0])
+        es = rel_l2(S[0, h], So[0, 0])
+        print("head %d: y %.3e S %.3e" % (h, ey, es), flush=True)
+        assert ey <= TOL and es <= TOL
+
+
+@gpu
+def test_decode_N256_H32_sampled():
+    g = _lib()
+    steps = 8
+    inp = gi.workload_inputs(3, steps=steps)
+    S = inp["S0"].cuda()
+    dq, dk_, dv_ = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    dla, db = inp["log_alpha"].cuda(), inp["beta"].cuda()
+    ys = [g.gdn_decode_step(dq[t], dk_[t], dv_[t], dla[t], db[t], S) for t in range(steps)]
+    torch.cuda.synchronize()
+    ys = torch.stack(ys).cpu()
+    Sc = S.cpu()
+    units = [(0, 0), (17, 5), (128, 31), (255, 16), (200, 2)]
+    for n, h in units:
+        Su = inp["S0"][n:n + 1, h:h + 1].double().numpy()
+        yo = []
+        for t in range(steps):
+            args = [inp[key][t, n:n + 1, h:h + 1] for key in ("q", "k", "v", "log_alpha", "beta")]
+            yt, Su = oracle.decode_step(*args, Su)
+            yo.append(yt[0, 0])
+        ey = rel_l2(ys[:, n, h], np.stack(yo))
+        es = rel_l2(Sc[n, h], Su[0, 0])
+        print("unit (%d, %d): y %.3e S %.3e" % (n, h, ey, es), flush=True)
+        assert ey <= TOL and es <= TOL
+
+
+def run_frontend_chain(g, dev, out_dtype=torch.bfloat16):
+    """Front end (fp16 q/k/v) -> chunked prefill (fp32 y) -> output gate."""
+    q, k, v = g.gdn_frontend_qkv(dev["q_raw"], dev["k_raw"], dev["v_raw"], dev["conv_w"],
+                                 cu_seqlens=dev["cu_seqlens"], l2_eps=1e-6,
+                                 out_dtype=torch.float16)
+    y, S = g.gdn_chunk_fwd(q, k, v, dev["log_alpha"], dev["beta"], dev["S0"],
+                           cu_seqlens=dev["cu_seqlens"], out_dtype=torch.float32)
+    o = g.gdn_output_gate(y, dev["z"], dev["norm_w"], 1e-6, out_dtype=out_dtype)
+    return o, S
+
+
+def oracle_frontend_chain(f, n, h):
+    cu = f["cu_seqlens"]
+    s, e = int(cu[n]), int(cu[n + 1])
+    w = f["conv_w"]
+    H = f["H"]
+    d = f["dk"]
+    sl = lambda x: x[s:e, h:h + 1]
+    wsl = lambda i: w[i].reshape(H, d, -1)[h]
+    q = oracle.frontend(sl(f["q_raw"]), wsl(0), l2=True, eps=1e-6)
+    k = oracle.frontend(sl(f["k_raw"]), wsl(1), l2=True, eps=1e-6)
+    v = oracle.frontend(sl(f["v_raw"]), wsl(2), l2=False)
+    y, S = oracle.gdn_fwd(q, k, v, sl(f["log_alpha"]), sl(f["beta"]), f["S0"][n:n + 1, h:h + 1],
+                          col_blocks=8)
+    o = oracle.output_gate(y, sl(f["z"]), f["norm_w"], eps=1e-6)
+    return o[:, 0], S[0, 0]
+
+
+@gpu
+@pytest.mark.parametrize("norm_w_std", [0.0, 0.1])
+def test_varlen_frontend_chain_sampled(norm_w_std):
+    """Front-end workload distributions on 12 sequences (lengths from the
+    workload's U[512, 8192] draw plus edge lengths), all heads on the GPU,
+    sampled (sequence, head) units against the oracle chain."""
+    g = _lib()
+    lengths = gi.seq_lengths(64, 512, 8192, seed=4)[:8].tolist() + [1, 31, 33, 515]
+    f = gi.frontend_inputs(lengths, 16, 128, 128, dtype="bf16", seed=4, norm_w_std=norm_w_std)
+    dev = {k: v.cuda() for k, v in f.items() if isinstance(v, torch.Tensor)}
+    o, S = run_frontend_chain(g, dev)
+    torch.cuda.synchronize()
+    o, S = o.cpu(), S.cpu()
+    cu = f["cu_seqlens"]
+    for n, h in [(0, 0), (3, 9), (7, 15), (8, 4), (10, 1), (11, 13)]:
+        oo, So = oracle_frontend_chain(f, n, h)
+        s, e = int(cu[n]), int(cu[n + 1])
+        eo = rel_l2(o[s:e, h], oo)
+        es = rel_l2(S[n, h], So)
+        print("unit (%d, %d) len %d: o %.3e S %.3e" % (n, h, e - s, eo, es), flush=True)
+        assert eo <= TOL and es <= TOL

@@ -61,8 +61,17 @@ def test_chunk_small(T, d, dtype):
 
 
 @gpu
+@pytest.mark.parametrize("T", [1, 65, 200])
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunk_small_f16(T, d):
+    inp = gi.prefill_inputs(2, 3, T, d, d, "f16", s0_std=0.02, seed=T + d + 5)
+    _check(inp, out_dtype=torch.float32)
+    _check(inp, out_dtype=torch.float16)
+
+
+@gpu
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_chunk_rect_heads(dk, dv, dtype):
     inp = gi.prefill_inputs(1, 2, 130, dk, dv, dtype, s0_std=0.02, seed=dk + 3 * dv)
     _check(inp, out_dtype=torch.float32)
@@ -107,7 +116,7 @@ def test_chunk_gate_extremes(case, dtype):
 
 
 @gpu
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_chunk_varlen(dtype):
     lengths = [1, 2, 63, 64, 65, 1000, 0, 130]
     inp = gi.prefill_inputs(0, 2, 0, 128, 128, dtype, s0_std=0.02, seed=31, lengths=lengths)
@@ -177,7 +186,7 @@ def test_chunk_nan_isolated():
 # ---------------------------------------------------------------- decode ----
 @gpu
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_decode_steps(dk, dv, dtype):
     g = _lib()
     inp = gi.decode_inputs(5, 3, dk, dv, steps=4, dtype=dtype, s0_std=0.02, seed=dk + dv)
@@ -219,7 +228,7 @@ def test_decode_matches_prefill():
 # ------------------------------------------------------------ front end -----
 @gpu
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_frontend_varlen(d, dtype):
     g = _lib()
     lengths = [1, 2, 3, 4, 5, 63, 64, 65, 300, 0, 17]
@@ -242,6 +251,10 @@ def test_frontend_varlen(d, dtype):
     torch.cuda.synchronize()
     ref = oracle.frontend(f["q_raw"], f["conv_w"][0], cu_seqlens=cu, l2=True, eps=1e-6)
     assert rel_l2(qb, ref) <= 4e-3
+    qh, kh, vh = g.gdn_frontend_qkv(dev["q_raw"], dev["k_raw"], dev["v_raw"], dev["conv_w"],
+                                    cu_seqlens=dev["cu_seqlens"], out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert rel_l2(qh, ref) <= 6e-4  # one fp16 rounding
 
 
 @gpu
@@ -259,13 +272,14 @@ def test_frontend_equal_length_batches():
 
 @gpu
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype,zdtype", [("f32", "f32"), ("bf16", "bf16"), ("f16", "bf16"),
+                                          ("f32", "bf16"), ("f16", "f16")])
 @pytest.mark.parametrize("with_w", [False, True])
-def test_output_gate(d, dtype, with_w):
+def test_output_gate(d, dtype, zdtype, with_w):
     g = _lib()
     rows = 1000
     y = gi.normal((rows, d), 71, 1).to(gi.torch_dtype(dtype))
-    z = gi.normal((rows, d), 71, 2).to(gi.torch_dtype(dtype))
+    z = gi.normal((rows, d), 71, 2).to(gi.torch_dtype(zdtype))
     w = gi.normal((d,), 71, 3, std=0.1) if with_w else None
     o = g.gdn_output_gate(y.cuda(), z.cuda(), None if w is None else w.cuda(), 1e-6,
                           out_dtype=torch.float32)

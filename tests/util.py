@@ -18,4 +18,4 @@ def to_dev(d, device="cuda"):
 
 
 # tolerances: relative L2 error against the fp64 oracle
-TOL = {"f32": 1e-5, "bf16": 2e-3}
+TOL = {"f32": 1e-5, "bf16": 2e-3, "f16": 2e-3}
