@@ -224,6 +224,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the long-context and varlen front-end workloads")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 1 GiB device copy (torch copy_), the known-size "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the GDN mixer shards over (sequence, head) with no "
@@ -236,6 +239,17 @@ def main():
     import gated_deltanet_amd as g
     g.load_library()
     torch.cuda.set_device(0)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] calibration copy: %d bytes read, %d bytes written" %
+              (src.numel() * 4, dst.numel() * 4), file=sys.stderr, flush=True)
+        del src, dst
 
     print("[bench] prefill workload 1: B=4 H=16 T=4096 d=128 bf16", file=sys.stderr, flush=True)
     pf = bench_prefill(g, args.steps, args.warmup)

@@ -195,7 +195,7 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
     const TIN *__restrict__ q, const TIN *__restrict__ k, const TIN *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
     const float *__restrict__ S0, TOUT *__restrict__ y, float *__restrict__ S_T,
-    const int32_t *__restrict__ cu_seqlens, int T, int H, int DV, int n_vt) {
+    const int32_t *__restrict__ cu_seqlens, int T, int H, int DV, int n_vt, int n_units) {
   using L = Lay<DK, NS>;
   using KO = KOps<TIN>;
   using kvec = typename KO::vec;
@@ -204,11 +204,17 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
   constexpr int DVT = L::DVT;
   __shared__ __attribute__((aligned(1024))) char smem[L::TOTAL];
 
-  int bid = blockIdx.x;
-  const int vt = bid % n_vt;
-  bid /= n_vt;
-  const int h = bid % H;
-  const int n = bid / H;
+  // Workgroups are dealt to the 8 XCDs round-robin by id. The n_vt column
+  // tiles of one (sequence, head) read the same K, Q and gates, so they are
+  // given ids that agree mod 8: they run on one XCD and share its L2.
+  const int units = n_units;
+  const int grp = blockIdx.x / (8 * n_vt);
+  const int rem = blockIdx.x % (8 * n_vt);
+  const int vt = rem / 8;
+  const int unit = grp * 8 + rem % 8;
+  if (unit >= units) return;
+  const int h = unit % H;
+  const int n = unit / H;
   int64_t bos, len;
   if (cu_seqlens) {
     int64_t a = cu_seqlens[n], b = cu_seqlens[n + 1];
@@ -707,13 +713,14 @@ template <int DK, int NS, typename TIN, typename TOUT>
 hipError_t launch_bf16(const ChunkArgs &a) {
   constexpr int DVT = 16 * NS;
   const int n_vt = a.dv / DVT;
-  const int64_t blocks = static_cast<int64_t>(a.N) * a.H * n_vt;
-  if (blocks == 0) return hipSuccess;
+  const int64_t units = static_cast<int64_t>(a.N) * a.H;
+  const int64_t blocks = (units + 7) / 8 * 8 * n_vt;
+  if (units == 0) return hipSuccess;
   hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, NS, TIN, TOUT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * (NS + 2)), 0, a.stream, static_cast<const TIN *>(a.q),
                      static_cast<const TIN *>(a.k), static_cast<const TIN *>(a.v),
                      a.log_alpha, a.beta, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.cu_seqlens,
-                     a.T, a.H, a.dv, n_vt);
+                     a.T, a.H, a.dv, n_vt, static_cast<int>(units));
   return hipGetLastError();
 }
 
