@@ -54,6 +54,20 @@ def decode_bytes_per_step(N, H, dk, dv, in_b=2, out_b=2):
     return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * in_b + dv * out_b + 8)
 
 
+def measured_traffic(key, source):
+    """HBM bytes per dispatch measured with rocprofv3 counters (profiles/),
+    or None when the kernel source changed since they were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_per_dispatch.json")))[key]
+        src = open(os.path.join(ROOT, "gated_deltanet_amd", "csrc", source), "rb").read()
+    except (OSError, KeyError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != rec.get("source_sha256_16"):
+        return None
+    return rec["bytes"]
+
+
 def rel_l2(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
@@ -127,7 +141,12 @@ def bench_decode(g, n_steps=128, reps=2):
     bytes_step = decode_bytes_per_step(N, H, dk, dv)
     gbs = bytes_step / (us_step * 1e-6) / 1e9
     return dict(workload=w.name, us_per_step=us_step, GBps=gbs, frac_hbm=gbs / HBM_PEAK_GBS,
-                tokens_per_s=N / (us_step * 1e-6), bytes_per_step=bytes_step, steps=n_steps)
+                tokens_per_s=N / (us_step * 1e-6), bytes_per_step=bytes_step, steps=n_steps,
+                roofline=dict(kernel="decode_step_kernel<128,128,bf16,bf16>", bound="hbm",
+                              achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=gbs / HBM_PEAK_GBS,
+                              traffic=measured_traffic("decode_step_kernel_N256_H32_d128",
+                                                       "decode.hip")))
 
 
 def bench_longctx(g, steps=3, warmup=1):
@@ -260,14 +279,8 @@ def main():
     nbytes = prefill_bytes(tokens, H, dk, dv, N)
     achieved_gbs = nbytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "chunk_fwd_prefill_B4_H16_T4096_d128_traffic.json")
-    if os.path.exists(tfile):
-        try:
-            traffic = json.load(open(tfile)).get("bytes_per_launch")
-        except Exception:
-            traffic = None
-    roofline = dict(kernel="chunk_fwd_kernel<128,64,bf16,bf16,f16>", bound="hbm",
+    traffic = measured_traffic("chunk_fwd_bf16_kernel_B4_H16_T4096_d128", "chunk_fwd.hip")
+    roofline = dict(kernel="chunk_fwd_bf16_kernel<128,2,bf16,bf16>", bound="hbm",
                     achieved=achieved_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=achieved_gbs / HBM_PEAK_GBS, traffic=traffic,
                     alg_bytes_per_launch=nbytes, alg_flops_per_launch=flops,
