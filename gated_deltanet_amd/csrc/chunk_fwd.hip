@@ -584,6 +584,39 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
   auto state_step = [&](int x) {
     const char *slot = ring + (x % kRing) * L::SLOT;
     const char *pb = procb + (x & 1) * L::PROC;
+    // every LDS operand of this chunk, issued up front (one wave per SIMD:
+    // nothing else would hide their latency)
+    kvec kf[kNCT][NKB];
+    f16x8 qf[kNCT][NKB], tf[kNCT], pf[kNCT], ktf[NST];
+    f32x4 G4[kNCT], B4[kNCT];
+    uint16_t vraw[kNCT][4];
+    const float *gam = reinterpret_cast<const float *>(pb + L::GM_OFF);
+    const float *bet = reinterpret_cast<const float *>(pb + L::BT_OFF);
+    const uint16_t *vt_ = reinterpret_cast<const uint16_t *>(slot + L::V_OFF);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int rt = 0; rt < kNCT; ++rt)
+        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+#pragma unroll
+    for (int rt = 0; rt < kNCT; ++rt) {
+      G4[rt] = *reinterpret_cast<const f32x4 *>(gam + 16 * rt + 4 * lg);
+      B4[rt] = *reinterpret_cast<const f32x4 *>(bet + 16 * rt + 4 * lg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vraw[rt][i] = vt_[(16 * rt + 4 * lg + i) * DVT + slab + lc];
+      tf[rt] = lds_read16<f16x8>(pb + L::T_OFF + rt * 1024 + 16 * lane);
+    }
+    const float gC = gam[kC - 1];
+#pragma unroll
+    for (int t = 0; t < NST; ++t) ktf[t] = lds_read16<f16x8>(pb + L::KT_OFF + t * 1024 + 16 * lane);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int rt = 0; rt < kNCT; ++rt)
+        qf[rt][kb] = lds_read16<f16x8>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+#pragma unroll
+    for (int rt = 0; rt < kNCT; ++rt) pf[rt] = lds_read16<f16x8>(pb + L::P_OFF + rt * 1024 + 16 * lane);
+
     // the state as B operand: bf16 against the raw bf16 keys for X = K S,
     // fp16 against the fp16 queries for Q S (Q S feeds y directly, so it gets
     // the finer rounding; errors in X are largely corrected by the delta rule)
@@ -594,59 +627,42 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
       sb[kb] = KO::pack(st[2 * kb], st[2 * kb + 1]);
       sh[kb] = pack_f16(st[2 * kb], st[2 * kb + 1]);
     }
-    f32x4 X[kNCT], QS[kNCT];
+    // serial chain: X = K S -> R -> E = T R -> S update
+    f32x4 X[kNCT];
 #pragma unroll
-    for (int rt = 0; rt < kNCT; ++rt) {
-      X[rt] = zero4();
-      QS[rt] = zero4();
-    }
+    for (int rt = 0; rt < kNCT; ++rt) X[rt] = zero4();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int rt = 0; rt < kNCT; ++rt) {
-        const kvec kf = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
-        X[rt] = KO::mma(kf, sb[kb], X[rt]);
-      }
+      for (int rt = 0; rt < kNCT; ++rt) X[rt] = KO::mma(kf[rt][kb], sb[kb], X[rt]);
+    f32x4 QS[kNCT];
+#pragma unroll
+    for (int rt = 0; rt < kNCT; ++rt) QS[rt] = zero4();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int rt = 0; rt < kNCT; ++rt) {
-        const f16x8 qf = lds_read16<f16x8>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
-        QS[rt] = mma_f16(qf, sh[kb], QS[rt]);
-      }
-    const float *gam = reinterpret_cast<const float *>(pb + L::GM_OFF);
-    const float *bet = reinterpret_cast<const float *>(pb + L::BT_OFF);
-    const uint16_t *vt_ = reinterpret_cast<const uint16_t *>(slot + L::V_OFF);
-    f32x4 R[kNCT], G4[kNCT];
+      for (int rt = 0; rt < kNCT; ++rt) QS[rt] = mma_f16(qf[rt][kb], sh[kb], QS[rt]);
+    f32x4 R[kNCT];
 #pragma unroll
-    for (int rt = 0; rt < kNCT; ++rt) {
-      G4[rt] = *reinterpret_cast<const f32x4 *>(gam + 16 * rt + 4 * lg);
-      const f32x4 b4 = *reinterpret_cast<const f32x4 *>(bet + 16 * rt + 4 * lg);
+    for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float vv = KO::to_f32(vt_[(16 * rt + 4 * lg + i) * DVT + slab + lc]);
-        R[rt][i] = b4[i] * (vv - G4[rt][i] * X[rt][i]);
-      }
-    }
+      for (int i = 0; i < 4; ++i)
+        R[rt][i] = B4[rt][i] * (KO::to_f32(vraw[rt][i]) - G4[rt][i] * X[rt][i]);
     const f16x8 rb = pack_f16(R[0], R[1]);
     f32x4 E[kNCT];
 #pragma unroll
-    for (int rt = 0; rt < kNCT; ++rt)
-      E[rt] = mma_f16(lds_read16<f16x8>(pb + L::T_OFF + rt * 1024 + 16 * lane), rb, zero4());
+    for (int rt = 0; rt < kNCT; ++rt) E[rt] = mma_f16(tf[rt], rb, zero4());
     const f16x8 eb = pack_f16(E[0], E[1]);
-    // state update first: it is the serial dependency into the next chunk
-    const float gC = gam[kC - 1];
 #pragma unroll
-    for (int t = 0; t < NST; ++t)
-      st[t] = mma_f16(lds_read16<f16x8>(pb + L::KT_OFF + t * 1024 + 16 * lane), eb, st[t] * gC);
+    for (int t = 0; t < NST; ++t) st[t] = mma_f16(ktf[t], eb, st[t] * gC);
+    // output: Y = gamma o (Q S) + P E
+    f32x4 Yt[kNCT];
+#pragma unroll
+    for (int rt = 0; rt < kNCT; ++rt) Yt[rt] = mma_f16(pf[rt], eb, G4[rt] * QS[rt]);
     const int64_t t0 = bos + static_cast<int64_t>(x) * kC;
     const int valid = static_cast<int>(len - static_cast<int64_t>(x) * kC < kC
                                            ? len - static_cast<int64_t>(x) * kC
                                            : kC);
-    f32x4 Yt[kNCT];
-#pragma unroll
-    for (int rt = 0; rt < kNCT; ++rt)
-      Yt[rt] = mma_f16(lds_read16<f16x8>(pb + L::P_OFF + rt * 1024 + 16 * lane), eb, G4[rt] * QS[rt]);
     TOUT *yp = y + static_cast<size_t>(t0 * H + h) * DV + v0 + slab + lc;
     const size_t rstride = static_cast<size_t>(H) * DV;
     if (valid == kC) {
