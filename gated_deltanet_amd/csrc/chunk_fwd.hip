@@ -1,4 +1,4 @@
-// Chunked parallel prefill of the gated delta rule, bf16 inputs (gfx950).
+// Chunked parallel prefill of the gated delta rule, 16-bit inputs (gfx950).
 //
 // Math (page "NLP——技术报告解读-Qwen3.8-Flash-Next", section "Gated DeltaNet
 // 核心机制", unrolled over a chunk). Inside a chunk of C tokens that starts
@@ -13,24 +13,28 @@
 // (I - beta k k^T) factors. Only exponentials of non-positive numbers occur.
 //
 // Work split. One workgroup owns one (sequence, head, 16*NS-column slice of
-// the state) and walks the sequence's chunks in order. It has NS "state"
-// waves and two "prep" waves:
-//   * the state waves keep their 16-column slab of the fp32 state in
-//     registers for the whole sequence and run the serial part: X = K S
-//     (bf16 MFMA, A operands straight from the raw K tile), Q S (fp16 MFMA on
-//     queries converted to fp16 in place by a prep wave), R, E = T R,
-//     Y = gamma QS + P E and the state update (fp16 MFMA);
-//   * the prep waves run one chunk ahead and produce, for the next chunk,
-//     everything that does not depend on the state: the gate scan, T (Gram
-//     tiles on MFMA, 16x16 diagonal blocks by forward substitution in fp32,
-//     off-diagonal blocks on MFMA), P = tril(Q K^T o G), and Kt^T (the
-//     transpose is done on the matrix cores with a 0/1 selector operand, so
-//     it is exact).
-//   * raw K, Q, V and gate tiles are streamed from HBM into a ring of LDS
-//     slots by direct-to-LDS loads (global_load_lds_dwordx4) issued R-1
-//     chunks ahead, so HBM latency overlaps with compute. One workgroup
-//     barrier per chunk hands a finished chunk from the prep waves to the
-//     state waves.
+// the state) and walks the sequence's chunks in order. Its NS "state" waves
+// keep their 16-column slabs of the fp32 state in registers for the whole
+// sequence and run the serial part: X = K S (bf16 MFMA, A operands straight
+// from the raw K tile), Q S (fp16 MFMA on queries converted to fp16 in
+// place), R, E = T R, Y = gamma QS + P E and the state update (fp16 MFMA).
+// Four "prep" waves produce everything that does not depend on the state,
+// pipelined ahead of the state waves:
+//   * gram    (two chunks ahead): direct-to-LDS loads of K and the gates,
+//             the gate scan (wavefront prefix sum) and its decay factors,
+//             the Gram tiles K K^T on MFMA and A;
+//   * inverse (one chunk ahead): T = (I + A)^{-1}: 16x16 diagonal blocks by
+//             forward substitution in fp32, the off-diagonal block on MFMA;
+//   * qk      (one chunk ahead): direct-to-LDS loads of Q and V,
+//             P = tril(Q K^T o G) computed as K Q^T so that the MFMA result
+//             already sits in P's operand layout, and Q converted to fp16;
+//   * kt      (one chunk ahead): Kt^T, transposed on the matrix cores with a
+//             0/1 selector operand (exact) and scaled per token.
+// The direct-to-LDS loads (buffer_load ... lds) go through a buffer resource
+// that ends at the sequence's last row, so rows past the end read as zeros
+// and no per-row clamping is needed; they are issued three chunk steps before
+// the gram wave needs them, into a ring of LDS slots. One workgroup barrier
+// per chunk step hands finished chunks from stage to stage.
 //
 // Operand layouts in LDS are "fragment-linear": a 16x32 MFMA operand slice is
 // stored as 64 lanes x 16 bytes, lane L's eight values contiguous at 16*L, so
@@ -38,6 +42,8 @@
 // rows land that way straight from HBM, the key dimension inside each
 // 32-slice is visited in the order 8*lg + j for lane group lg and slot j, and
 // the state rows are stored in the matching order (see state_row()).
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -45,11 +51,13 @@ namespace gdn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 32;     // tokens per chunk
 constexpr int kNCT = 2;    // 16-token tiles per chunk
 constexpr int kRing = 6;   // raw-tile ring slots
-constexpr int kDepth = kRing - 1;  // chunks of prefetch issued ahead
+constexpr int kAhead = kRing - 3;  // chunk steps between a load's issue and its first use
+constexpr int kPrep = 4;   // prep waves per workgroup
 
 // LDS layout (bytes) for key size DK and NS state waves.
 template <int DK, int NS>
@@ -57,34 +65,40 @@ struct Lay {
   static constexpr int DVT = 16 * NS;
   static constexpr int NKB = DK / 32;  // 32-deep key slices
   static constexpr int NST = DK / 16;  // 16-row state tiles
-  // ring slot: raw bf16 tiles of one chunk
+  // ring slot: raw 16-bit tiles of one chunk, loaded straight from HBM
   static constexpr int K_OFF = 0;
   static constexpr int Q_OFF = K_OFF + kNCT * NKB * 1024;
   static constexpr int V_OFF = Q_OFF + kNCT * NKB * 1024;
   static constexpr int G_OFF = V_OFF + kC * DVT * 2;  // log_alpha[32], beta[32]
   static constexpr int SLOT = G_OFF + 256;
-  // processed buffer (double-buffered): prep -> state hand-off
-  static constexpr int T_OFF = 0;                      // T, kNCT fragments
-  static constexpr int P_OFF = T_OFF + kNCT * 1024;    // P, kNCT fragments
-  static constexpr int KT_OFF = P_OFF + kNCT * 1024;   // Kt^T, NST fragments
-  static constexpr int GM_OFF = KT_OFF + NST * 1024;   // gamma[32]
-  static constexpr int BT_OFF = GM_OFF + kC * 4;       // beta[32]
-  static constexpr int PROC = BT_OFF + kC * 4;
-  // prep-private fp32 scratch for the UT inverse
-  static constexpr int LDA = kC + 4;  // A^T, row stride (floats)
-  static constexpr int LDT = kC + 1;  // T, row stride (floats)
+  // per-chunk gate values (triple-buffered), 32 floats each:
+  //   G2 running log2 decay, BT beta, GAM gamma = 2^G2, RA 2^(G2 - G2[m]),
+  //   CB 2^(G2[m] - G2), KD 2^(G2[C-1] - G2), BR beta * RA, MISC[0] fast flag
+  static constexpr int GB_G2 = 0, GB_BT = 128, GB_GAM = 256, GB_RA = 384, GB_CB = 512,
+                       GB_KD = 640, GB_BR = 768, GB_MISC = 896;
+  static constexpr int GATE = 1024;
+  // processed operands (double-buffered): T, P, Kt^T fragments
+  static constexpr int T_OFF = 0;
+  static constexpr int P_OFF = T_OFF + kNCT * 1024;
+  static constexpr int KT_OFF = P_OFF + kNCT * 1024;
+  static constexpr int PROC = KT_OFF + NST * 1024;
+  // fp32 A^T (double-buffered) and the inverse wave's scratch for T
+  static constexpr int LDA = kC + 4;  // A^T row stride (floats)
+  static constexpr int LDT = kC + 1;  // T row stride (floats)
+  static constexpr int AMTB = kC * LDA * 4;
   static constexpr int RING = 0;
   static constexpr int PROCB = RING + kRing * SLOT;
-  static constexpr int AMT = PROCB + 2 * PROC;
-  static constexpr int TMP = AMT + kC * LDA * 4;
-  static constexpr int FAC = TMP + kC * LDT * 4;  // decay factors, 2 x 128 floats
-  static constexpr int TOTAL = FAC + 2 * 128 * 4;
-  // direct-to-LDS loads per chunk issued by each prep wave
-  static constexpr int NV = kC * DVT * 2 / 1024;  // V tile, 1 KiB per load
-  static constexpr int LOADS_P0 = kNCT * NKB + 1; // K + gates
-  static constexpr int LOADS_P1 = kNCT * NKB + NV; // Q + V
+  static constexpr int GATEB = PROCB + 2 * PROC;
+  static constexpr int AMT = GATEB + 3 * GATE;
+  static constexpr int TMP = AMT + 2 * AMTB;
+  static constexpr int TOTAL = TMP + kC * LDT * 4;
+  // direct-to-LDS loads per chunk issued by the gram and qk waves
+  static constexpr int NV = kC * DVT * 2 / 1024;    // V tile, 1 KiB per load
+  static constexpr int LOADS_GRAM = kNCT * NKB + 2;  // K, log_alpha, beta
+  static constexpr int LOADS_QK = kNCT * NKB + NV;   // Q, V
   static_assert(kC * DVT * 2 % 1024 == 0, "V tile must be whole KiB");
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(kAhead * LOADS_GRAM < 64 && (kAhead + 1) * LOADS_QK < 64, "vmcnt range");
 };
 
 // state tile t, lane group lg, element i  ->  key index
@@ -98,15 +112,30 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
       (const __attribute__((address_space(3))) char *)(p)));
 }
 
+// Raw buffer resource over [base, base + bytes): loads at or past the end
+// return zeros, stores there are dropped.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = static_cast<int32_t>(static_cast<uint32_t>(a));
+  r[1] = static_cast<int32_t>(static_cast<uint32_t>(a >> 32));  // stride 0
+  r[2] = static_cast<int32_t>(bytes);
+  r[3] = 0x00020000;  // raw dword access
+  return r;
+}
+
 // Direct-to-LDS loads: lane L's data lands at (M0 + 16*L) or (M0 + 4*L).
 // Written in asm so the compiler does not serialise later LDS reads behind
-// them; completion is tracked explicitly with vmcnt waits.
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds)
+// them; completion is tracked explicitly with vmcnt waits. M0 is written one
+// wait state before the load reads it.
+__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               ::"v"(voff), "s"(rsrc), "s"(lds)
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void *gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds)
+__device__ __forceinline__ void dma4(const i32x4 &rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               ::"v"(voff), "s"(rsrc), "s"(lds)
                : "memory", "m0");
 }
 template <int N>
@@ -154,11 +183,19 @@ __device__ __forceinline__ bf16x8 pack_bf16(const f32x4 &a, const f32x4 &b) {
   }
   return r;
 }
-__device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
-__device__ __forceinline__ void store_out(bf16_t *p, float v) {
-  *reinterpret_cast<__bf16 *>(p) = (__bf16)v;  // v_cvt_pk_bf16_f32, round to nearest even
+// y element stores through a buffer resource (rows past its end are dropped)
+template <typename TOUT>
+__device__ __forceinline__ void store_y(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (std::is_same<TOUT, float>::value)
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r,
+                                          static_cast<int>(off), 0, 0);
+  else if constexpr (std::is_same<TOUT, bf16_t>::value)
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), r,
+                                          static_cast<int>(off), 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), r,
+                                          static_cast<int>(off), 0, 0);
 }
-__device__ __forceinline__ void store_out(_Float16 *p, float v) { *p = (_Float16)v; }
 
 // Operations on the raw 16-bit input tiles (K, Q, V) for each input type.
 // bf16 inputs keep bf16 operands for the key-side products (exact inputs;
@@ -191,7 +228,7 @@ __device__ __forceinline__ V lds_read16(const char *p) {
 }
 
 template <int DK, int NS, typename TIN, typename TOUT>
-__global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     const TIN *__restrict__ q, const TIN *__restrict__ k, const TIN *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
     const float *__restrict__ S0, TOUT *__restrict__ y, float *__restrict__ S_T,
@@ -202,6 +239,7 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
   constexpr int NKB = L::NKB;
   constexpr int NST = L::NST;
   constexpr int DVT = L::DVT;
+  constexpr int NTHR = 64 * (NS + kPrep);
   __shared__ __attribute__((aligned(1024))) char smem[L::TOTAL];
 
   // Workgroups are dealt to the 8 XCDs round-robin by id. The n_vt column
@@ -233,65 +271,86 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
   const int lc = lane & 15;
   const int lg = lane >> 4;
   const int v0 = vt * DVT;
+  // roles; wave w runs on SIMD w % 4, so the two helpers that share a SIMD
+  // with a state wave (gram, kt) are the lighter ones
   const bool is_state = wave < NS;
-  const bool is_p0 = wave == NS;  // gates, Gram, UT inverse
-  const int slab = 16 * wave;     // state waves: first column of the slab
+  const bool is_inv = wave == NS;
+  const bool is_qk = wave == NS + 1;
+  const bool is_gram = wave == NS + 2;
+  const bool is_kt = wave == NS + 3;
+  const int slab = 16 * wave;  // state waves: first column of the slab
 
   char *const ring = smem + L::RING;
   char *const procb = smem + L::PROCB;
-  float *const amt = reinterpret_cast<float *>(smem + L::AMT);
+  char *const gateb = smem + L::GATEB;
   float *const tmp = reinterpret_cast<float *>(smem + L::TMP);
-
-  // zero the parts of the hand-off buffers that are never rewritten (upper
-  // blocks of P) and the prep scratch for T (its upper block stays zero)
-  for (int i = threadIdx.x; i < 2 * L::PROC / 4; i += 64 * (NS + 2))
-    reinterpret_cast<float *>(procb)[i] = 0.0f;
-  for (int i = threadIdx.x; i < kC * L::LDT; i += 64 * (NS + 2)) tmp[i] = 0.0f;
-
-  // ---- prep: issue the direct-to-LDS loads of chunk x into its ring slot --
-  // Rows past the end of the sequence are clamped to its last row (in
-  // bounds; their contributions are masked by beta = 0 and the store mask),
-  // so every call issues the same number of loads and the vmcnt arithmetic
-  // below holds even for chunk indices past the end.
-  auto issue_chunk = [&](int x) {
-    char *slot = ring + (x % kRing) * L::SLOT;
-    const int64_t last = bos + len - 1;
-    if (is_p0) {
-#pragma unroll
-      for (int rt = 0; rt < kNCT; ++rt) {
-        int64_t row = bos + static_cast<int64_t>(x) * kC + 16 * rt + lc;
-        row = row > last ? last : row;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          dma16(k + (row * H + h) * DK + 32 * kb + 8 * lg,
-                lds_addr(slot + L::K_OFF + (rt * NKB + kb) * 1024));
-      }
-      int64_t row = bos + static_cast<int64_t>(x) * kC + (lane & 31);
-      row = row > last ? last : row;
-      dma4((lane < 32 ? log_alpha : beta) + row * H + h, lds_addr(slot + L::G_OFF));
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < kNCT; ++rt) {
-        int64_t row = bos + static_cast<int64_t>(x) * kC + 16 * rt + lc;
-        row = row > last ? last : row;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          dma16(q + (row * H + h) * DK + 32 * kb + 8 * lg,
-                lds_addr(slot + L::Q_OFF + (rt * NKB + kb) * 1024));
-      }
-#pragma unroll
-      for (int p = 0; p < L::NV; ++p) {
-        const int qi = 64 * p + lane;
-        const int r = qi / (DVT / 8);
-        const int cc = qi % (DVT / 8);
-        int64_t row = bos + static_cast<int64_t>(x) * kC + r;
-        row = row > last ? last : row;
-        dma16(v + (row * H + h) * DV + v0 + 8 * cc, lds_addr(slot + L::V_OFF + p * 1024));
-      }
-    }
+  auto amt_of = [&](int c) { return reinterpret_cast<float *>(smem + L::AMT + (c & 1) * L::AMTB); };
+  auto gate_of = [&](int c) {
+    return reinterpret_cast<float *>(gateb + (c % 3) * L::GATE);
   };
 
-  // ---- prep: gate scan and decay factors -----------------------------------
+  // Zero all of LDS once: the parts of the operand buffers that are never
+  // written (upper blocks of T and P) must read as zeros, and ring rows that
+  // a chunk past the end of the sequence does not load hold finite values.
+  for (int i = threadIdx.x; i < L::TOTAL / 16; i += NTHR)
+    reinterpret_cast<f32x4 *>(smem)[i] = zero4();
+  wg_barrier();
+
+  // ---- direct-to-LDS loads of chunk c into its ring slot --------------------
+  // The buffer resource of each tensor starts at the chunk's first row and
+  // ends after its last row inside the sequence, so rows past the end read as
+  // zeros; per-lane offsets are fixed for the whole sequence.
+  const int hdk = H * DK;
+  const int hdv = H * DV;
+  auto rows_of = [&](int c) -> int {
+    const int64_t r = len - static_cast<int64_t>(c) * kC;
+    return r <= 0 ? 0 : (r >= kC ? kC : static_cast<int>(r));
+  };
+  auto row0_of = [&](int c) -> int64_t {
+    const int64_t r = static_cast<int64_t>(c) * kC;
+    return bos + (r < len ? r : len);
+  };
+  // per-lane byte offsets of this lane's K/Q and V pieces inside a chunk
+  const uint32_t kq_lane = static_cast<uint32_t>((lc * hdk + h * DK + 8 * lg) * 2);
+  auto v_lane = [&](int p) -> uint32_t {
+    const int qi = 64 * p + lane;
+    const int r = qi / (DVT / 8);
+    const int cc = qi % (DVT / 8);
+    return static_cast<uint32_t>((r * hdv + h * DV + v0 + 8 * cc) * 2);
+  };
+  const uint32_t g_off = static_cast<uint32_t>(((lane & 31) * H + h) * 4);
+
+  auto issue_gram = [&](int c) {
+    char *slot = ring + (c % kRing) * L::SLOT;
+    const int64_t r0 = row0_of(c);
+    const uint32_t rows = static_cast<uint32_t>(rows_of(c));
+    const i32x4 rk = buffer_rsrc(k + r0 * hdk, rows * hdk * 2);
+#pragma unroll
+    for (int rt = 0; rt < kNCT; ++rt)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        dma16(rk, kq_lane + static_cast<uint32_t>(16 * rt * hdk * 2 + 64 * kb), lds_addr(slot + L::K_OFF + (rt * NKB + kb) * 1024));
+    const i32x4 rla = buffer_rsrc(log_alpha + r0 * H, rows * H * 4);
+    const i32x4 rb = buffer_rsrc(beta + r0 * H, rows * H * 4);
+    if (lane < 32) dma4(rla, g_off, lds_addr(slot + L::G_OFF));
+    else dma4(rb, g_off, lds_addr(slot + L::G_OFF));
+  };
+  auto issue_qk = [&](int c) {
+    char *slot = ring + (c % kRing) * L::SLOT;
+    const int64_t r0 = row0_of(c);
+    const uint32_t rows = static_cast<uint32_t>(rows_of(c));
+    const i32x4 rq = buffer_rsrc(q + r0 * hdk, rows * hdk * 2);
+#pragma unroll
+    for (int rt = 0; rt < kNCT; ++rt)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        dma16(rq, kq_lane + static_cast<uint32_t>(16 * rt * hdk * 2 + 64 * kb), lds_addr(slot + L::Q_OFF + (rt * NKB + kb) * 1024));
+    const i32x4 rv = buffer_rsrc(v + r0 * hdv, rows * hdv * 2);
+#pragma unroll
+    for (int p = 0; p < L::NV; ++p) dma16(rv, v_lane(p), lds_addr(slot + L::V_OFF + p * 1024));
+  };
+
+  // ---- gram wave: gate scan, decay factors, Gram tiles, A ------------------
   // Running sums are kept in log2 units (g2 = g / ln 2) so every decay is a
   // single v_exp_f32. Within a chunk the decay G_rc = 2^(g2_r - g2_c) factors
   // as a_r * b_c with a_r = 2^(g2_r - g2_m), b_c = 2^(g2_m - g2_c) around the
@@ -299,49 +358,15 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
   // per row. The factorisation is used only when both factors stay well
   // inside the fp32 range; otherwise (extreme gates) the chunk falls back to
   // one exponential per element. The branch is uniform per chunk.
-  struct Gates {
-    float g2, bt, gC2, gm2;
-    bool fast;
-  };
-  auto scan_gates = [&](const char *slot, int x, float *fac, Gates &G) {
+  auto gram = [&](int c) {
+    const char *slot = ring + (c % kRing) * L::SLOT;
+    float *gt = gate_of(c);
     const float *gl = reinterpret_cast<const float *>(slot + L::G_OFF);
-    const int64_t tok = static_cast<int64_t>(x) * kC + lane;
+    const int64_t tok = static_cast<int64_t>(c) * kC + lane;
     float la = 0.0f, bt = 0.0f;
     if (lane < kC && tok < len) {
       la = gl[lane];
       bt = gl[32 + lane];
-    }
-    float sc = la * 1.4426950408889634f;
-    sc += dpp_shr<1>(sc);
-    sc += dpp_shr<2>(sc);
-    sc += dpp_shr<4>(sc);
-    sc += dpp_shr<8>(sc);
-    const float r15 = readlane(sc, 15);
-    if (lane >= 16) sc += r15;
-    G.g2 = sc;
-    G.bt = bt;
-    G.gC2 = readlane(sc, kC - 1);
-    G.gm2 = r15;
-    const float g0 = readlane(sc, 0);
-    G.fast = (g0 - G.gm2 <= 120.0f) && (G.gm2 - G.gC2 <= 120.0f);
-    if (lane < kC) {
-      fac[64 + lane] = sc;
-      fac[96 + lane] = bt;
-      fac[32 + lane] = __builtin_amdgcn_exp2f(G.gm2 - sc);  // b_c
-    }
-  };
-  // ---- prep wave 0: gates, Gram -> A, T = (I + A)^{-1} ---------------------
-  float *const fac0 = reinterpret_cast<float *>(smem + L::FAC);
-  float *const fac1 = fac0 + 128;
-  auto prep0 = [&](int x) {
-    const char *slot = ring + (x % kRing) * L::SLOT;
-    char *pb = procb + (x & 1) * L::PROC;
-    Gates G;
-    scan_gates(slot, x, fac0, G);
-    if (lane < kC) {
-      reinterpret_cast<float *>(pb + L::GM_OFF)[lane] = __builtin_amdgcn_exp2f(G.g2);
-      reinterpret_cast<float *>(pb + L::BT_OFF)[lane] = G.bt;
-      fac0[lane] = G.bt * __builtin_amdgcn_exp2f(G.g2 - G.gm2);  // beta_r a_r
     }
     kvec kf[kNCT][NKB];
 #pragma unroll
@@ -349,76 +374,268 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
         kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
-    f32x4 gram[3];
+    float sc = la * 1.4426950408889634f;
+    sc += dpp_shr<1>(sc);
+    sc += dpp_shr<2>(sc);
+    sc += dpp_shr<4>(sc);
+    sc += dpp_shr<8>(sc);
+    const float r15 = readlane(sc, 15);
+    if (lane >= 16) sc += r15;
+    const float gC2 = readlane(sc, kC - 1);
+    const float gm2 = r15;
+    const float g0 = readlane(sc, 0);
+    const bool fast = (g0 - gm2 <= 120.0f) && (gm2 - gC2 <= 120.0f);
+    const float ra = __builtin_amdgcn_exp2f(sc - gm2);
+    if (lane < kC) {
+      gt[L::GB_G2 / 4 + lane] = sc;
+      gt[L::GB_BT / 4 + lane] = bt;
+      gt[L::GB_GAM / 4 + lane] = __builtin_amdgcn_exp2f(sc);
+      gt[L::GB_RA / 4 + lane] = ra;
+      gt[L::GB_CB / 4 + lane] = __builtin_amdgcn_exp2f(gm2 - sc);
+      gt[L::GB_KD / 4 + lane] = __builtin_amdgcn_exp2f(gC2 - sc);
+      gt[L::GB_BR / 4 + lane] = bt * ra;
+    }
+    if (lane == 0) gt[L::GB_MISC / 4] = fast ? 1.0f : 0.0f;
+    f32x4 gm[3];
 #pragma unroll
-    for (int t = 0; t < 3; ++t) gram[t] = zero4();
+    for (int t = 0; t < 3; ++t) gm[t] = zero4();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      gram[0] = KO::mma(kf[0][kb], kf[0][kb], gram[0]);
-      gram[1] = KO::mma(kf[1][kb], kf[0][kb], gram[1]);
-      gram[2] = KO::mma(kf[1][kb], kf[1][kb], gram[2]);
+      gm[0] = KO::mma(kf[0][kb], kf[0][kb], gm[0]);
+      gm[1] = KO::mma(kf[1][kb], kf[0][kb], gm[1]);
+      gm[2] = KO::mma(kf[1][kb], kf[1][kb], gm[2]);
     }
-    wait_lds();
-    f32x4 rf[kNCT];
-    float cf[kNCT];
-#pragma unroll
-    for (int rt = 0; rt < kNCT; ++rt) {
-      rf[rt] = *reinterpret_cast<const f32x4 *>(fac0 + 16 * rt + 4 * lg);
-      cf[rt] = fac0[32 + 16 * rt + lc];
-    }
-    // A = strictly_lower(diag(beta) (K K^T o G)), stored transposed in fp32
+    // A = strictly_lower(diag(beta) (K K^T o G)); tile t = (row tile, col tile)
+    // (0,0), (1,0), (1,1); element i of lane (lg, lc) is row 4 lg + i, column lc
     f32x4 av[3];
-    if (G.fast) {
+    if (fast) {
+      f32x4 br[kNCT];
+      float cb[kNCT];
+#pragma unroll
+      for (int rt = 0; rt < kNCT; ++rt) {
+        br[rt] = *reinterpret_cast<const f32x4 *>(gt + L::GB_BR / 4 + 16 * rt + 4 * lg);
+        cb[rt] = gt[L::GB_CB / 4 + 16 * rt + lc];
+      }
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         const int rt = t == 0 ? 0 : 1, ct = t == 2 ? 1 : 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) av[t][i] = rf[rt][i] * cf[ct] * gram[t][i];
+        for (int i = 0; i < 4; ++i) av[t][i] = br[rt][i] * cb[ct] * gm[t][i];
       }
     } else {
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         const int rt = t == 0 ? 0 : 1, ct = t == 2 ? 1 : 0;
-        const f32x4 gr = *reinterpret_cast<const f32x4 *>(fac0 + 64 + 16 * rt + 4 * lg);
-        const f32x4 br = *reinterpret_cast<const f32x4 *>(fac0 + 96 + 16 * rt + 4 * lg);
-        const float gc = fac0[64 + 16 * ct + lc];
+        const f32x4 gr = *reinterpret_cast<const f32x4 *>(gt + L::GB_G2 / 4 + 16 * rt + 4 * lg);
+        const f32x4 bv = *reinterpret_cast<const f32x4 *>(gt + L::GB_BT / 4 + 16 * rt + 4 * lg);
+        const float gc = gt[L::GB_G2 / 4 + 16 * ct + lc];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          av[t][i] = br[i] * __builtin_amdgcn_exp2f(fminf(gr[i] - gc, 0.0f)) * gram[t][i];
+          av[t][i] = bv[i] * __builtin_amdgcn_exp2f(fminf(gr[i] - gc, 0.0f)) * gm[t][i];
       }
     }
+    // stored transposed (A^T row c = column c of A) in fp32
+    float *amt = amt_of(c);
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       const int rt = t == 0 ? 0 : 1, ct = t == 2 ? 1 : 0;
-      const int c = 16 * ct + lc;
+      const int col = 16 * ct + lc;
       f32x4 a;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = (16 * rt + 4 * lg + i > c) ? av[t][i] : 0.0f;
-      *reinterpret_cast<f32x4 *>(amt + c * L::LDA + 16 * rt + 4 * lg) = a;
+      for (int i = 0; i < 4; ++i) a[i] = (16 * rt + 4 * lg + i > col) ? av[t][i] : 0.0f;
+      *reinterpret_cast<f32x4 *>(amt + col * L::LDA + 16 * rt + 4 * lg) = a;
     }
-    wait_lds();
-    // diagonal 16x16 blocks of T by forward substitution, one column per lane
+  };
+
+  // ---- inverse wave: T = (I + A)^{-1} ----------------------------------------
+  auto inverse = [&](int c) {
+    const float *amt = amt_of(c);
+    char *pb = procb + (c & 1) * L::PROC;
+    // Diagonal 16x16 blocks by forward substitution. Each 16-lane row works
+    // on one block (rows 2 and 3 repeat rows 0 and 1); lane lc holds column lc
+    // of T and column lc of A, so A is read from LDS once. Step s subtracts
+    // A[r][s] x_s from x_r for r > s with A[r][s] taken from lane s of the row
+    // by a DPP broadcast (v_fmac_f32_dpp row_newbcast:s). The leading s_nop
+    // of each step gives the two wait states a DPP source needs after a VALU
+    // write.
     {
       const int b = lg & (kNCT - 1);
-      float xv[16];
+      float ac[16], xv[16];
+      const float *acol = amt + (16 * b + lc) * L::LDA + 16 * b;  // A[16b + r][16b + lc]
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 t4 = *reinterpret_cast<const f32x4 *>(acol + 4 * u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ac[4 * u + i] = t4[i];
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) xv[r] = (r == lc) ? 1.0f : 0.0f;
-#pragma unroll
-      for (int sidx = 0; sidx < 15; ++sidx) {
-        const float *arow = amt + (16 * b + sidx) * L::LDA + 16 * b;  // A[16b + r][16b + s]
-        float av[16];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const f32x4 t4 = *reinterpret_cast<const f32x4 *>(arow + 4 * u);
-          av[4 * u] = t4[0];
-          av[4 * u + 1] = t4[1];
-          av[4 * u + 2] = t4[2];
-          av[4 * u + 3] = t4[3];
-        }
-        const float xs = xv[sidx];
-#pragma unroll
-        for (int r = sidx + 1; r < 16; ++r) xv[r] = fmaf(-av[r], xs, xv[r]);
-      }
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%15, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%16, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%17, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %3, -%18, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %4, -%19, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %5, -%20, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %6, -%21, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %7, -%22, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %8, -%23, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %9, -%24, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %10, -%25, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %11, -%26, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %12, -%27, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %13, -%28, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %14, -%29, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]), "+v"(xv[4]), "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[1]), "v"(ac[2]), "v"(ac[3]), "v"(ac[4]), "v"(ac[5]), "v"(ac[6]), "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[0]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%14, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%15, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%16, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %3, -%17, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %4, -%18, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %5, -%19, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %6, -%20, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %7, -%21, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %8, -%22, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %9, -%23, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %10, -%24, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %11, -%25, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %12, -%26, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %13, -%27, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[2]), "+v"(xv[3]), "+v"(xv[4]), "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[2]), "v"(ac[3]), "v"(ac[4]), "v"(ac[5]), "v"(ac[6]), "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[1]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%13, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%14, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%15, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %3, -%16, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %4, -%17, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %5, -%18, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %6, -%19, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %7, -%20, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %8, -%21, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %9, -%22, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %10, -%23, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %11, -%24, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %12, -%25, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[3]), "+v"(xv[4]), "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[3]), "v"(ac[4]), "v"(ac[5]), "v"(ac[6]), "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[2]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%12, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%13, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%14, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %3, -%15, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %4, -%16, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %5, -%17, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %6, -%18, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %7, -%19, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %8, -%20, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %9, -%21, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %10, -%22, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %11, -%23, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[4]), "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[4]), "v"(ac[5]), "v"(ac[6]), "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[3]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%11, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%12, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%13, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %3, -%14, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %4, -%15, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %5, -%16, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %6, -%17, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %7, -%18, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %8, -%19, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %9, -%20, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %10, -%21, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[5]), "v"(ac[6]), "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[4]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%10, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%11, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%12, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %3, -%13, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %4, -%14, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %5, -%15, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %6, -%16, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %7, -%17, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %8, -%18, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %9, -%19, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[6]), "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[6]), "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[5]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%9, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%10, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%11, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %3, -%12, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %4, -%13, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %5, -%14, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %6, -%15, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %7, -%16, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %8, -%17, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[6]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%8, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%9, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%10, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %3, -%11, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %4, -%12, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %5, -%13, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %6, -%14, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %7, -%15, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[7]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%7, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%8, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%9, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %3, -%10, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %4, -%11, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %5, -%12, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %6, -%13, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[8]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%6, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%7, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%8, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %3, -%9, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %4, -%10, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %5, -%11, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[9]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%5, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%6, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%7, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %3, -%8, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %4, -%9, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[10]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%4, %8 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%5, %8 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%6, %8 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %3, -%7, %8 row_newbcast:11 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[11]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%3, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%4, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %2, -%5, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[12]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%2, %4 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+                   "v_fmac_f32_dpp %1, -%3, %4 row_newbcast:13 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[14]), "+v"(xv[15])
+                   : "v"(ac[14]), "v"(ac[15]), "v"(xv[13]));
+      asm volatile("s_nop 1\n\t"
+                   "v_fmac_f32_dpp %0, -%1, %2 row_newbcast:14 row_mask:0xf bank_mask:0xf"
+                   : "+v"(xv[15])
+                   : "v"(ac[15]), "v"(xv[14]));
+
       if (lg < kNCT) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmp[(16 * b + r) * L::LDT + 16 * b + lc] = xv[r];
@@ -460,23 +677,20 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
     }
   };
 
-  // ---- prep wave 1: P = tril(Q K^T o G), Q -> fp16, Kt^T ------------------
   // 0/1 selector operand for exact transposes on the matrix cores: in lane
   // (lg, lc), slot j is 1 iff lg == lc >> 2 and j == 4u + (lc & 3).
-  kvec sel[2];
+  auto selector = [&](int u) {
+    kvec s_;
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      sel[u][j] = (lg == (lc >> 2) && j == 4 * u + (lc & 3)) ? 1.0f : 0.0f;
+    for (int j = 0; j < 8; ++j) s_[j] = (lg == (lc >> 2) && j == 4 * u + (lc & 3)) ? 1.0f : 0.0f;
+    return s_;
+  };
 
-  auto prep1 = [&](int x) {
-    char *slot = ring + (x % kRing) * L::SLOT;
-    char *pb = procb + (x & 1) * L::PROC;
-    Gates G;
-    scan_gates(slot, x, fac1, G);
-    const float kdec = __builtin_amdgcn_exp2f(G.gC2 - G.g2);
-    if (lane < kC) fac1[lane] = __builtin_amdgcn_exp2f(G.g2 - G.gm2);  // a_r
+  // ---- qk wave: P = tril(Q K^T o G), Q -> fp16 -------------------------------
+  auto qkp = [&](int c) {
+    char *slot = ring + (c % kRing) * L::SLOT;
+    char *pb = procb + (c & 1) * L::PROC;
+    const float *gt = gate_of(c);
     kvec kf[kNCT][NKB], qf[kNCT][NKB];
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt)
@@ -485,14 +699,18 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
         kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
         qf[rt][kb] = lds_read16<kvec>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
       }
-    f32x4 qk[3];
+    const bool fast = __builtin_amdgcn_readfirstlane(
+                          __builtin_bit_cast(int, gt[L::GB_MISC / 4])) != 0;
+    // K Q^T: element i of lane (lg, lc) in tile (ct, rt) is P[16 rt + lc][16 ct + 4 lg + i],
+    // i.e. slot i (ct = 0) or 4 + i (ct = 1) of P's operand fragment for row tile rt
+    f32x4 pk[3];  // (ct, rt) = (0, 0), (0, 1), (1, 1)
 #pragma unroll
-    for (int t = 0; t < 3; ++t) qk[t] = zero4();
+    for (int t = 0; t < 3; ++t) pk[t] = zero4();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      qk[0] = KO::mma(qf[0][kb], kf[0][kb], qk[0]);
-      qk[1] = KO::mma(qf[1][kb], kf[0][kb], qk[1]);
-      qk[2] = KO::mma(qf[1][kb], kf[1][kb], qk[2]);
+      pk[0] = KO::mma(kf[0][kb], qf[0][kb], pk[0]);
+      pk[1] = KO::mma(kf[0][kb], qf[1][kb], pk[1]);
+      pk[2] = KO::mma(kf[1][kb], qf[1][kb], pk[2]);
     }
     // Q in fp16 for the state waves' Q S: D_u = Sel_u x Q^T puts keys
     // 8 lg + 4u + i of token lc in lane (lg, lc), i.e. the A-operand slots;
@@ -500,98 +718,98 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
     // Written back over the raw Q of this slot, which no other wave reads
     // during this chunk step.
     if constexpr (KO::kConvertQ) {
+      const kvec sel[2] = {selector(0), selector(1)};
 #pragma unroll
-    for (int rt = 0; rt < kNCT; ++rt)
+      for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const f32x4 d0 = KO::mma(sel[0], qf[rt][kb], zero4());
-        const f32x4 d1 = KO::mma(sel[1], qf[rt][kb], zero4());
-        *reinterpret_cast<f16x8 *>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane) =
-            pack_f16(d0, d1);
-      }
+        for (int kb = 0; kb < NKB; ++kb) {
+          const f32x4 d0 = KO::mma(sel[0], qf[rt][kb], zero4());
+          const f32x4 d1 = KO::mma(sel[1], qf[rt][kb], zero4());
+          *reinterpret_cast<f16x8 *>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane) =
+              pack_f16(d0, d1);
+        }
     }
-    wait_lds();
-    f32x4 rf[kNCT];
-    float cf[kNCT];
-#pragma unroll
-    for (int rt = 0; rt < kNCT; ++rt) {
-      rf[rt] = *reinterpret_cast<const f32x4 *>(fac1 + 16 * rt + 4 * lg);
-      cf[rt] = fac1[32 + 16 * rt + lc];
-    }
-    // P: lower tiles, written straight into fragment-linear positions
     f32x4 pv[3];
-    if (G.fast) {
+    if (fast) {
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
-        const int rt = t == 0 ? 0 : 1, ct = t == 2 ? 1 : 0;
+        const int ct = t == 2 ? 1 : 0, rt = t == 0 ? 0 : 1;
+        const float ar = gt[L::GB_RA / 4 + 16 * rt + lc];
+        const f32x4 cb = *reinterpret_cast<const f32x4 *>(gt + L::GB_CB / 4 + 16 * ct + 4 * lg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[t][i] = rf[rt][i] * cf[ct] * qk[t][i];
+        for (int i = 0; i < 4; ++i) pv[t][i] = ar * cb[i] * pk[t][i];
       }
     } else {
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
-        const int rt = t == 0 ? 0 : 1, ct = t == 2 ? 1 : 0;
-        const f32x4 gr = *reinterpret_cast<const f32x4 *>(fac1 + 64 + 16 * rt + 4 * lg);
-        const float gc = fac1[64 + 16 * ct + lc];
+        const int ct = t == 2 ? 1 : 0, rt = t == 0 ? 0 : 1;
+        const float gr = gt[L::GB_G2 / 4 + 16 * rt + lc];
+        const f32x4 gc = *reinterpret_cast<const f32x4 *>(gt + L::GB_G2 / 4 + 16 * ct + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          pv[t][i] = __builtin_amdgcn_exp2f(fminf(gr[i] - gc, 0.0f)) * qk[t][i];
+          pv[t][i] = __builtin_amdgcn_exp2f(fminf(gr - gc[i], 0.0f)) * pk[t][i];
       }
     }
-    _Float16 *pm = reinterpret_cast<_Float16 *>(pb + L::P_OFF);
+    // causal mask on the diagonal tiles: column 4 lg + i <= row lc
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      const int rt = t == 0 ? 0 : 1, ct = t == 2 ? 1 : 0;
-      const int c = 16 * ct + lc;
-      const int jc = 4 * (ct & 1) + (lc & 3);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i;
-        const int ldst = 16 * (lc >> 2) + 4 * lg + i;  // destination lane
-        pm[(rt * 64 + ldst) * 8 + jc] = (_Float16)(r >= c ? pv[t][i] : 0.0f);
-      }
+    for (int i = 0; i < 4; ++i) {
+      pv[0][i] = (4 * lg + i <= lc) ? pv[0][i] : 0.0f;
+      pv[2][i] = (4 * lg + i <= lc) ? pv[2][i] : 0.0f;
     }
-    // Kt^T: for each state tile, transpose 16 keys x 32 tokens on the matrix
-    // cores and scale token columns by exp(g_C - g_t)
-    float kd[8];
+    *reinterpret_cast<f16x8 *>(pb + L::P_OFF + 16 * lane) = pack_f16(pv[0], zero4());
+    *reinterpret_cast<f16x8 *>(pb + L::P_OFF + 1024 + 16 * lane) = pack_f16(pv[1], pv[2]);
+  };
+
+  // ---- kt wave: Kt^T ---------------------------------------------------------
+  // For each state tile, transpose 16 keys x 32 tokens on the matrix cores
+  // and scale token columns by exp(g_C - g_t).
+  auto ktt = [&](int c) {
+    const char *slot = ring + (c % kRing) * L::SLOT;
+    char *pb = procb + (c & 1) * L::PROC;
+    const float *gt = gate_of(c);
+    kvec kf[kNCT][NKB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kd[j] = __shfl(kdec, 16 * (j >> 2) + 4 * lg + (j & 3), 64);
+    for (int rt = 0; rt < kNCT; ++rt)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+    const kvec sel[2] = {selector(0), selector(1)};
+    // slot j of the A operand <-> token 16 (j >> 2) + 4 lg + (j & 3)
+    const f32x4 kd0 = *reinterpret_cast<const f32x4 *>(gt + L::GB_KD / 4 + 4 * lg);
+    const f32x4 kd1 = *reinterpret_cast<const f32x4 *>(gt + L::GB_KD / 4 + 16 + 4 * lg);
 #pragma unroll
     for (int t = 0; t < NST; ++t) {
       const f32x4 d0 = KO::mma(kf[0][t >> 1], sel[t & 1], zero4());
       const f32x4 d1 = KO::mma(kf[1][t >> 1], sel[t & 1], zero4());
-      f16x8 f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f[j] = (_Float16)(kd[j] * d0[j]);
-        f[4 + j] = (_Float16)(kd[4 + j] * d1[j]);
-      }
-      *reinterpret_cast<f16x8 *>(pb + L::KT_OFF + t * 1024 + 16 * lane) = f;
+      *reinterpret_cast<f16x8 *>(pb + L::KT_OFF + t * 1024 + 16 * lane) =
+          pack_f16(kd0 * d0, kd1 * d1);
     }
   };
 
-  // ---- state waves: registers ---------------------------------------------
+  // ---- state waves -----------------------------------------------------------
   f32x4 st[NST];
   const size_t sbase = static_cast<size_t>(n * H + h) * DK * DV + v0 + slab + lc;
   if (is_state) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         st[t][i] = S0 ? S0[sbase + static_cast<size_t>(state_row(t, lg, i)) * DV] : 0.0f;
   }
+  // byte offset of this lane's first y element inside a chunk's rows
+  const uint32_t y_lane =
+      static_cast<uint32_t>((4 * lg * hdv + h * DV + v0 + slab + lc) * sizeof(TOUT));
 
   auto state_step = [&](int x) {
     const char *slot = ring + (x % kRing) * L::SLOT;
     const char *pb = procb + (x & 1) * L::PROC;
-    // every LDS operand of this chunk, issued up front (one wave per SIMD:
-    // nothing else would hide their latency)
+    const float *gt = gate_of(x);
+    // every LDS operand of this chunk, issued up front
     kvec kf[kNCT][NKB];
     f16x8 qf[kNCT][NKB], tf[kNCT], pf[kNCT], ktf[NST];
     f32x4 G4[kNCT], B4[kNCT];
     uint16_t vraw[kNCT][4];
-    const float *gam = reinterpret_cast<const float *>(pb + L::GM_OFF);
-    const float *bet = reinterpret_cast<const float *>(pb + L::BT_OFF);
     const uint16_t *vt_ = reinterpret_cast<const uint16_t *>(slot + L::V_OFF);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -600,13 +818,13 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
         kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt) {
-      G4[rt] = *reinterpret_cast<const f32x4 *>(gam + 16 * rt + 4 * lg);
-      B4[rt] = *reinterpret_cast<const f32x4 *>(bet + 16 * rt + 4 * lg);
+      G4[rt] = *reinterpret_cast<const f32x4 *>(gt + L::GB_GAM / 4 + 16 * rt + 4 * lg);
+      B4[rt] = *reinterpret_cast<const f32x4 *>(gt + L::GB_BT / 4 + 16 * rt + 4 * lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) vraw[rt][i] = vt_[(16 * rt + 4 * lg + i) * DVT + slab + lc];
       tf[rt] = lds_read16<f16x8>(pb + L::T_OFF + rt * 1024 + 16 * lane);
     }
-    const float gC = gam[kC - 1];
+    const float gC = gt[L::GB_GAM / 4 + kC - 1];
 #pragma unroll
     for (int t = 0; t < NST; ++t) ktf[t] = lds_read16<f16x8>(pb + L::KT_OFF + t * 1024 + 16 * lane);
 #pragma unroll
@@ -627,14 +845,21 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
       sb[kb] = KO::pack(st[2 * kb], st[2 * kb + 1]);
       sh[kb] = pack_f16(st[2 * kb], st[2 * kb + 1]);
     }
-    // serial chain: X = K S -> R -> E = T R -> S update
-    f32x4 X[kNCT];
+    // serial chain: X = K S -> R -> E = T R -> S update. X is summed in two
+    // halves so that no MFMA waits on the one just before it.
+    f32x4 Xa[kNCT], Xb[kNCT];
 #pragma unroll
-    for (int rt = 0; rt < kNCT; ++rt) X[rt] = zero4();
+    for (int rt = 0; rt < kNCT; ++rt) {
+      Xa[rt] = zero4();
+      Xb[rt] = zero4();
+    }
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; kb += 2)
 #pragma unroll
-      for (int rt = 0; rt < kNCT; ++rt) X[rt] = KO::mma(kf[rt][kb], sb[kb], X[rt]);
+      for (int rt = 0; rt < kNCT; ++rt) {
+        Xa[rt] = KO::mma(kf[rt][kb], sb[kb], Xa[rt]);
+        Xb[rt] = KO::mma(kf[rt][kb + 1], sb[kb + 1], Xb[rt]);
+      }
     f32x4 QS[kNCT];
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt) QS[rt] = zero4();
@@ -647,7 +872,8 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
     for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        R[rt][i] = B4[rt][i] * (KO::to_f32(vraw[rt][i]) - G4[rt][i] * X[rt][i]);
+        R[rt][i] = B4[rt][i] * fmaf(-G4[rt][i], Xb[rt][i],
+                                    fmaf(-G4[rt][i], Xa[rt][i], KO::to_f32(vraw[rt][i])));
     const f16x8 rb = pack_f16(R[0], R[1]);
     f32x4 E[kNCT];
 #pragma unroll
@@ -655,66 +881,56 @@ __global__ __launch_bounds__(64 * (NS + 2)) void chunk_fwd_bf16_kernel(
     const f16x8 eb = pack_f16(E[0], E[1]);
 #pragma unroll
     for (int t = 0; t < NST; ++t) st[t] = mma_f16(ktf[t], eb, st[t] * gC);
-    // output: Y = gamma o (Q S) + P E
+    // output: Y = gamma o (Q S) + P E; rows past the end of the sequence fall
+    // outside the buffer resource and are dropped
     f32x4 Yt[kNCT];
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt) Yt[rt] = mma_f16(pf[rt], eb, G4[rt] * QS[rt]);
-    const int64_t t0 = bos + static_cast<int64_t>(x) * kC;
-    const int valid = static_cast<int>(len - static_cast<int64_t>(x) * kC < kC
-                                           ? len - static_cast<int64_t>(x) * kC
-                                           : kC);
-    TOUT *yp = y + static_cast<size_t>(t0 * H + h) * DV + v0 + slab + lc;
-    const size_t rstride = static_cast<size_t>(H) * DV;
-    if (valid == kC) {
+    const uint32_t rows = static_cast<uint32_t>(rows_of(x));
+    const auto ry = __builtin_amdgcn_make_buffer_rsrc(y + row0_of(x) * hdv, 0,
+                                                      static_cast<int>(rows * hdv * sizeof(TOUT)),
+                                                      0x00020000);
 #pragma unroll
-      for (int rt = 0; rt < kNCT; ++rt)
+    for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) store_out(yp + (16 * rt + 4 * lg + i) * rstride, Yt[rt][i]);
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < kNCT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * rt + 4 * lg + i < valid) store_out(yp + (16 * rt + 4 * lg + i) * rstride, Yt[rt][i]);
-    }
+      for (int i = 0; i < 4; ++i) store_y<TOUT>(Yt[rt][i], ry,
+                              y_lane + static_cast<uint32_t>((16 * rt + i) * hdv * sizeof(TOUT)));
   };
 
   // ---- pipeline -------------------------------------------------------------
-  if (!is_state && nc > 0) {
-#pragma unroll 1
-    for (int x = 0; x < kDepth; ++x) issue_chunk(x);
-  }
-  if (!is_state) {
-    // chunk 0 must have landed before the prologue computes it
-    if (is_p0) wait_vmcnt<(kDepth - 1) * L::LOADS_P0>();
-    else wait_vmcnt<(kDepth - 1) * L::LOADS_P1>();
-  }
-  wg_barrier();
+  // Step it (it = -2 .. nc-1): the state waves run chunk it, the gram wave
+  // chunk it + 2, the other prep waves chunk it + 1. The gram and qk waves
+  // issue the loads of chunk it + 2 + kAhead first, so the chunk they need has
+  // kAhead (gram) or kAhead + 1 (qk) younger chunks of loads in flight.
   if (nc > 0) {
-    if (is_p0) prep0(0);
-    else if (!is_state) prep1(0);
-  }
-  if (!is_state) {
-    if (is_p0) wait_vmcnt<(kDepth - 2) * L::LOADS_P0>();
-    else wait_vmcnt<(kDepth - 2) * L::LOADS_P1>();
-  }
-  wg_barrier();
+    if (is_gram) {
 #pragma unroll 1
-  for (int x = 0; x < nc; ++x) {
-    if (is_state) {
-      state_step(x);
-    } else {
-      issue_chunk(x + kDepth);
-      if (x + 1 < nc) {
-        if (is_p0) prep0(x + 1);
-        else prep1(x + 1);
-      }
-      if (is_p0) wait_vmcnt<(kDepth - 2) * L::LOADS_P0>();
-      else wait_vmcnt<(kDepth - 2) * L::LOADS_P1>();
+      for (int c = 0; c < kAhead; ++c) issue_gram(c);
+    } else if (is_qk) {
+#pragma unroll 1
+      for (int c = 0; c < kAhead; ++c) issue_qk(c);
     }
-    wg_barrier();
+#pragma unroll 1
+    for (int it = -2; it < nc; ++it) {
+      if (is_state) {
+        if (it >= 0) state_step(it);
+      } else if (is_gram) {
+        issue_gram(it + 2 + kAhead);
+        wait_vmcnt<kAhead * L::LOADS_GRAM>();
+        if (it + 2 < nc) gram(it + 2);
+      } else if (is_qk) {
+        issue_qk(it + 2 + kAhead);
+        wait_vmcnt<(kAhead + 1) * L::LOADS_QK>();
+        if (it >= -1 && it + 1 < nc) qkp(it + 1);
+      } else if (is_inv) {
+        if (it >= -1 && it + 1 < nc) inverse(it + 1);
+      } else if (is_kt) {
+        if (it >= -1 && it + 1 < nc) ktt(it + 1);
+      }
+      wg_barrier();
+    }
+    if (is_gram || is_qk) wait_vmcnt<0>();  // drain before the workgroup retires
   }
-  if (!is_state) wait_vmcnt<0>();  // drain before the workgroup retires
 
   if (is_state && S_T) {
 #pragma unroll
@@ -733,7 +949,7 @@ hipError_t launch_bf16(const ChunkArgs &a) {
   const int64_t blocks = (units + 7) / 8 * 8 * n_vt;
   if (units == 0) return hipSuccess;
   hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, NS, TIN, TOUT>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(64 * (NS + 2)), 0, a.stream, static_cast<const TIN *>(a.q),
+                     dim3(64 * (NS + kPrep)), 0, a.stream, static_cast<const TIN *>(a.q),
                      static_cast<const TIN *>(a.k), static_cast<const TIN *>(a.v),
                      a.log_alpha, a.beta, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.cu_seqlens,
                      a.T, a.H, a.dv, n_vt, static_cast<int>(units));
