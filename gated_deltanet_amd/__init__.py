@@ -13,6 +13,10 @@ Functions carry the names of the C entry points declared in include/gdn.h:
 * ``gdn_frontend_qkv(q_raw, k_raw, v_raw, conv_w, cu_seqlens=None, N=None,
   l2_eps=1e-6, out_dtype=None)`` -> (q, k, v)
 * ``gdn_output_gate(y, z, norm_w=None, rms_eps=1e-6, out_dtype=None)`` -> o
+* ``gdn_chunk_fwd_fused(q_raw, k_raw, v_raw, conv_w, log_alpha, beta, z,
+  S0=None, norm_w=None, l2_eps=1e-6, rms_eps=1e-6, cu_seqlens=None, N=None,
+  out_dtype=None)`` -> (o, S_T)
+* ``gdn_fused_workspace_size(rows, H, d)`` -> bytes
 """
 from __future__ import annotations
 
@@ -57,6 +61,12 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_frontend_qkv.restype = ctypes.c_int
     lib.gdn_output_gate.argtypes = [vp, vp, fp, f32, vp, i64, i32, i32, i32, i32, vp]
     lib.gdn_output_gate.restype = ctypes.c_int
+    sz = ctypes.c_size_t
+    lib.gdn_fused_workspace_size.argtypes = [i64, i32, i32]
+    lib.gdn_fused_workspace_size.restype = sz
+    lib.gdn_chunk_fwd_fused.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp, f32, f32, vp, fp, ip,
+                                        i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    lib.gdn_chunk_fwd_fused.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -221,6 +231,63 @@ def gdn_output_gate(y, z, norm_w=None, rms_eps=1e-6, out_dtype=None, o=None):
                              _dt(in_dtype), _dt(z.dtype), _dt(out_dtype), _stream(y.device))
     _check(rc, lib, "gdn_output_gate")
     return o
+
+
+def gdn_fused_workspace_size(rows: int, H: int, d: int) -> int:
+    """Workspace bytes gdn_chunk_fwd_fused needs (0 for invalid sizes)."""
+    return int(load_library().gdn_fused_workspace_size(int(rows), int(H), int(d)))
+
+
+def gdn_chunk_fwd_fused(q_raw, k_raw, v_raw, conv_w, log_alpha, beta, z, S0=None, norm_w=None,
+                        l2_eps=1e-6, rms_eps=1e-6, cu_seqlens=None, N=None, out_dtype=None,
+                        o=None, S_T=None, want_state=True, workspace=None):
+    """Front end -> chunked prefill -> output gate in one library call.
+    q_raw, k_raw, v_raw, z [rows, H, d] (one dtype); conv_w fp32 [3, H*d, 4];
+    gates fp32 [rows, H]; S0 fp32 [N, H, d, d] or None; norm_w fp32 [d] or
+    None. Sequence boundaries as in gdn_chunk_fwd. The workspace (fp16 q, k, v
+    and fp32 y) is allocated here unless given. Returns (o, S_T)."""
+    lib = load_library()
+    in_dtype = q_raw.dtype
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    for t, nm in ((q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw"), (z, "z")):
+        _need(t, nm, in_dtype)
+    _need(conv_w, "conv_w", torch.float32)
+    _need(log_alpha, "log_alpha", torch.float32)
+    _need(beta, "beta", torch.float32)
+    H, d = q_raw.shape[-2], q_raw.shape[-1]
+    rows = q_raw.numel() // (H * d)
+    if tuple(conv_w.shape) != (3, H * d, 4):
+        raise GdnError("conv_w must be [3, H*d, 4]")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        N, T = cu_seqlens.numel() - 1, rows
+    else:
+        if N is None:
+            N = S0.shape[0] if S0 is not None else 1
+        if N <= 0 or rows % N:
+            raise GdnError("rows (%d) must be a multiple of N (%d)" % (rows, N))
+        T = rows // N
+    if S0 is not None:
+        _need(S0, "S0", torch.float32)
+        if tuple(S0.shape) != (N, H, d, d):
+            raise GdnError("S0 must be [N, H, d, d] = %s" % ((N, H, d, d),))
+    if norm_w is not None:
+        _need(norm_w, "norm_w", torch.float32)
+    dev = q_raw.device
+    if o is None:
+        o = torch.empty(q_raw.shape, dtype=out_dtype, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
+    need = gdn_fused_workspace_size(rows, H, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib.gdn_chunk_fwd_fused(_p(q_raw), _p(k_raw), _p(v_raw), _p(conv_w), _p(log_alpha),
+                                 _p(beta), _p(S0), _p(z), _p(norm_w), float(l2_eps),
+                                 float(rms_eps), _p(o), _p(S_T), _p(cu_seqlens), N, T, H, d, d,
+                                 _dt(in_dtype), _dt(out_dtype), _p(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc, lib, "gdn_chunk_fwd_fused")
+    return o, S_T
 
 
 def gdn_version() -> int:

@@ -254,4 +254,143 @@ GDN_API int gdn_output_gate(const void *y, const void *z, const float *norm_w, f
   return hip_status(gdn::launch_output_gate(a), "gdn_output_gate launch");
 }
 
+namespace {
+
+size_t pad256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+// byte offsets of the fused call's intermediates inside the workspace
+struct FusedLayout {
+  size_t qkv_bytes, y_bytes, q, k, v, y, total;
+  FusedLayout(int64_t rows, int32_t H, int32_t d) {
+    qkv_bytes = static_cast<size_t>(rows) * H * d * 2;
+    y_bytes = static_cast<size_t>(rows) * H * d * 4;
+    q = 0;
+    k = q + pad256(qkv_bytes);
+    v = k + pad256(qkv_bytes);
+    y = v + pad256(qkv_bytes);
+    total = rows > 0 ? y + pad256(y_bytes) : 0;
+  }
+};
+
+}  // namespace
+
+GDN_API size_t gdn_fused_workspace_size(int64_t rows, int32_t H, int32_t d) {
+  if (rows < 0 || H <= 0 || !head_size_ok(d) || rows * H * d >= (int64_t{1} << 40)) return 0;
+  return FusedLayout(rows, H, d).total;
+}
+
+GDN_API int gdn_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void *v_raw,
+                                const float *conv_w, const float *log_alpha, const float *beta,
+                                const float *S0, const void *z, const float *norm_w,
+                                float l2_eps, float rms_eps, void *o, float *S_T,
+                                const int32_t *cu_seqlens, int32_t N, int32_t T, int32_t H,
+                                int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  g_last_error[0] = '\0';
+  if (N < 0 || T < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N, T must be >= 0 and H > 0");
+  if (dk != dv) return fail(GDN_ERR_UNSUPPORTED, "%s", "the fused prefill needs dk == dv");
+  const int32_t d = dk;
+  if (!head_size_ok(d)) return fail(GDN_ERR_UNSUPPORTED, "%s", "d must be 64 or 128");
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32, GDN_BF16 or GDN_F16");
+  if (!(l2_eps >= 0.0f) || !(rms_eps >= 0.0f))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "l2_eps and rms_eps must be >= 0");
+  const int64_t rows = cu_seqlens ? static_cast<int64_t>(T) : static_cast<int64_t>(N) * T;
+  if (static_cast<int64_t>(N) * H > (int64_t{1} << 31) / 8)
+    return fail(GDN_ERR_INVALID_ARG, "%s", "N * H too large");
+  if (rows * H * d >= (int64_t{1} << 40)) return fail(GDN_ERR_INVALID_ARG, "%s", "input too large");
+  if (rows / 64 >= (int64_t{1} << 31)) return fail(GDN_ERR_INVALID_ARG, "%s", "too many rows");
+  const FusedLayout lay(rows, H, d);
+  if (rows > 0) {
+    if (!q_raw || !k_raw || !v_raw || !conv_w || !log_alpha || !beta || !z || !o)
+      return fail(GDN_ERR_INVALID_ARG, "%s", "null input or output pointer");
+    if (!workspace || workspace_bytes < lay.total)
+      return fail(GDN_ERR_INVALID_ARG, "%s", "workspace missing or smaller than gdn_fused_workspace_size()");
+  }
+  if (misaligned(q_raw) || misaligned(k_raw) || misaligned(v_raw) || misaligned(conv_w) ||
+      misaligned(z) || misaligned(o) || misaligned(S0) || misaligned(S_T) ||
+      misaligned(workspace, 256) || misaligned(log_alpha, 4) || misaligned(beta, 4) ||
+      misaligned(norm_w, 4) || misaligned(cu_seqlens, 4))
+    return fail(GDN_ERR_MISALIGNED, "%s",
+                "tensors need 16-byte alignment, the workspace 256, gates/norm_w/cu_seqlens 4");
+  const size_t nin = static_cast<size_t>(rows) * H * d * esize(in_dtype);
+  const size_t no = static_cast<size_t>(rows) * H * d * esize(out_dtype);
+  const size_t ng = static_cast<size_t>(rows) * H * 4;
+  const size_t ns = static_cast<size_t>(N) * H * d * d * 4;
+  const void *ins[9] = {q_raw, k_raw, v_raw, z, conv_w, log_alpha, beta, norm_w, cu_seqlens};
+  const size_t in_n[9] = {nin, nin, nin, nin, static_cast<size_t>(3) * H * d * 16, ng, ng,
+                          static_cast<size_t>(d) * 4, static_cast<size_t>(N + 1) * 4};
+  for (int i = 0; i < 9; ++i) {
+    if (overlap(ins[i], in_n[i], o, no) || overlap(ins[i], in_n[i], S_T, ns) ||
+        overlap(ins[i], in_n[i], workspace, lay.total))
+      return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps an output or the workspace");
+  }
+  if (overlap(o, no, S_T, ns) || overlap(o, no, workspace, lay.total) ||
+      overlap(S_T, ns, workspace, lay.total))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "o, S_T and the workspace must not overlap");
+  if (S0 && S0 != S_T && overlap(S0, ns, S_T, ns))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "S0 partially overlaps S_T");
+  if (S0 && (overlap(S0, ns, o, no) || overlap(S0, ns, workspace, lay.total)))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "S0 overlaps o or the workspace");
+
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  void *q = ws + lay.q, *k = ws + lay.k, *v = ws + lay.v, *y = ws + lay.y;
+  if (rows > 0) {
+    gdn::FrontendArgs f;
+    f.xq = q_raw;
+    f.xk = k_raw;
+    f.xv = v_raw;
+    f.conv_w = conv_w;
+    f.cu_seqlens = cu_seqlens;
+    f.N = N;
+    f.T = T;
+    f.rows = rows;
+    f.H = H;
+    f.d = d;
+    f.eps = l2_eps;
+    f.q = q;
+    f.k = k;
+    f.v = v;
+    f.in_dtype = in_dtype;
+    f.out_dtype = GDN_F16;
+    f.stream = st;
+    const int rc = hip_status(gdn::launch_frontend(f), "gdn_chunk_fwd_fused front end");
+    if (rc != GDN_OK) return rc;
+  }
+  gdn::ChunkArgs c;
+  c.q = q;
+  c.k = k;
+  c.v = v;
+  c.log_alpha = log_alpha;
+  c.beta = beta;
+  c.S0 = S0;
+  c.y = y;
+  c.S_T = S_T;
+  c.cu_seqlens = cu_seqlens;
+  c.N = N;
+  c.T = T;
+  c.H = H;
+  c.dk = d;
+  c.dv = d;
+  c.in_dtype = GDN_F16;
+  c.out_dtype = GDN_F32;
+  c.stream = st;
+  int rc = hip_status(gdn::launch_chunk_fwd(c), "gdn_chunk_fwd_fused prefill");
+  if (rc != GDN_OK || rows == 0) return rc;
+  gdn::GateArgs g;
+  g.y = y;
+  g.z = z;
+  g.norm_w = norm_w;
+  g.eps = rms_eps;
+  g.o = o;
+  g.rows = rows * H;
+  g.d = d;
+  g.in_dtype = GDN_F32;
+  g.z_dtype = in_dtype;
+  g.out_dtype = out_dtype;
+  g.stream = st;
+  return hip_status(gdn::launch_output_gate(g), "gdn_chunk_fwd_fused output gate");
+}
+
 }  // extern "C"

@@ -276,8 +276,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   const bool is_state = wave < NS;
   const bool is_inv = wave == NS;
   const bool is_qk = wave == NS + 1;
-  const bool is_gram = wave == NS + 2;
-  const bool is_kt = wave == NS + 3;
+  const bool is_gram = wave == NS + 2;  // wave NS + 3: kt
   const int slab = 16 * wave;  // state waves: first column of the slab
 
   char *const ring = smem + L::RING;
@@ -901,35 +900,53 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   // Step it (it = -2 .. nc-1): the state waves run chunk it, the gram wave
   // chunk it + 2, the other prep waves chunk it + 1. The gram and qk waves
   // issue the loads of chunk it + 2 + kAhead first, so the chunk they need has
-  // kAhead (gram) or kAhead + 1 (qk) younger chunks of loads in flight.
+  // kAhead (gram) or kAhead + 1 (qk) younger chunks of loads in flight. Every
+  // role runs its own loop with one barrier per step (nc + 2 in all).
+  auto step_barrier = [&]() { wg_barrier(); };
   if (nc > 0) {
-    if (is_gram) {
+    if (is_state) {
+      step_barrier();
+      step_barrier();
+#pragma unroll 1
+      for (int x = 0; x < nc; ++x) {
+        state_step(x);
+        step_barrier();
+      }
+    } else if (is_gram) {
 #pragma unroll 1
       for (int c = 0; c < kAhead; ++c) issue_gram(c);
-    } else if (is_qk) {
 #pragma unroll 1
-      for (int c = 0; c < kAhead; ++c) issue_qk(c);
-    }
-#pragma unroll 1
-    for (int it = -2; it < nc; ++it) {
-      if (is_state) {
-        if (it >= 0) state_step(it);
-      } else if (is_gram) {
+      for (int it = -2; it < nc; ++it) {
         issue_gram(it + 2 + kAhead);
         wait_vmcnt<kAhead * L::LOADS_GRAM>();
         if (it + 2 < nc) gram(it + 2);
-      } else if (is_qk) {
+        step_barrier();
+      }
+      wait_vmcnt<0>();  // drain before the workgroup retires
+    } else if (is_qk) {
+#pragma unroll 1
+      for (int c = 0; c < kAhead; ++c) issue_qk(c);
+#pragma unroll 1
+      for (int it = -2; it < nc; ++it) {
         issue_qk(it + 2 + kAhead);
         wait_vmcnt<(kAhead + 1) * L::LOADS_QK>();
         if (it >= -1 && it + 1 < nc) qkp(it + 1);
-      } else if (is_inv) {
-        if (it >= -1 && it + 1 < nc) inverse(it + 1);
-      } else if (is_kt) {
-        if (it >= -1 && it + 1 < nc) ktt(it + 1);
+        step_barrier();
       }
-      wg_barrier();
+      wait_vmcnt<0>();
+    } else if (is_inv) {
+#pragma unroll 1
+      for (int it = -2; it < nc; ++it) {
+        if (it >= -1 && it + 1 < nc) inverse(it + 1);
+        step_barrier();
+      }
+    } else {
+#pragma unroll 1
+      for (int it = -2; it < nc; ++it) {
+        if (it >= -1 && it + 1 < nc) ktt(it + 1);
+        step_barrier();
+      }
     }
-    if (is_gram || is_qk) wait_vmcnt<0>();  // drain before the workgroup retires
   }
 
   if (is_state && S_T) {

@@ -160,6 +160,50 @@ GDN_API int gdn_output_gate(const void *y, const void *z, const float *norm_w,
                             int32_t y_dtype, int32_t z_dtype, int32_t out_dtype,
                             void *stream);
 
+/*
+ * Bytes of device workspace gdn_chunk_fwd_fused needs for `rows` packed rows
+ * of H heads of size d (0 if rows == 0): the normalised q, k, v in fp16 and
+ * y in fp32, each padded to 256 bytes. Returns 0 for invalid sizes.
+ */
+GDN_API size_t gdn_fused_workspace_size(int64_t rows, int32_t H, int32_t d);
+
+/*
+ * The whole mixer prefill in one call (page "NLP——技术报告解读-Qwen3.8-
+ * Flash-Next", section "GDN 参数化细节": front end, recurrence, output gate):
+ *     q, k, v = gdn_frontend_qkv(q_raw, k_raw, v_raw, conv_w, l2_eps)
+ *     y, S_T  = gdn_chunk_fwd(q, k, v, log_alpha, beta, S0)
+ *     o       = gdn_output_gate(y, z, norm_w, rms_eps)
+ * enqueued back to back on `stream`. The intermediates live in `workspace`
+ * (device memory, 256-byte aligned, at least
+ * gdn_fused_workspace_size(rows, H, d) bytes, overwritten by the call):
+ * q, k, v are kept in fp16 and y in fp32, so the result equals the three
+ * separate calls made with those intermediate dtypes.
+ *
+ *   q_raw, k_raw, v_raw, z  [rows, H, d] in in_dtype.
+ *   conv_w                  float32 [3][H*d][4] (as gdn_frontend_qkv).
+ *   log_alpha, beta         float32 [rows, H].
+ *   S0, S_T                 float32 [N, H, d, d]; S0 NULL = zeros, S_T NULL =
+ *                           not written (S_T may equal S0).
+ *   norm_w                  float32 [d] or NULL (w = 0).
+ *   o                       [rows, H, d] in out_dtype.
+ *   cu_seqlens, N, T        as for gdn_chunk_fwd.
+ * Requires dk == dv == d in {64, 128}. Inputs must not overlap o, S_T or the
+ * workspace. All arguments are validated before anything is enqueued; a
+ * GDN_ERR_HIP return from a later stage can leave earlier stages' writes in
+ * the workspace (never in o or S_T before the stage that writes them).
+ */
+GDN_API int gdn_chunk_fwd_fused(const void *q_raw, const void *k_raw,
+                                const void *v_raw, const float *conv_w,
+                                const float *log_alpha, const float *beta,
+                                const float *S0, const void *z,
+                                const float *norm_w, float l2_eps,
+                                float rms_eps, void *o, float *S_T,
+                                const int32_t *cu_seqlens, int32_t N,
+                                int32_t T, int32_t H, int32_t dk, int32_t dv,
+                                int32_t in_dtype, int32_t out_dtype,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
 /* Human-readable name of a return code (static string, never NULL). */
 GDN_API const char *gdn_status_string(int status);
 

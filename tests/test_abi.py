@@ -122,3 +122,42 @@ def test_frontend_and_gate_reject(lib):
     assert lib.gdn_output_gate(A, A + 65536, None, 1e-6, B, 16, 100, 1, 1, 1, None) == -2
     assert lib.gdn_output_gate(None, A, None, 1e-6, B, 16, 128, 1, 1, 1, None) == -1
     assert lib.gdn_output_gate(A, A + 65536, None, 1e-6, B, 16, 128, 1, 5, 1, None) == -2
+
+
+def test_fused_rejects(lib):
+    v, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.gdn_fused_workspace_size.argtypes = [ctypes.c_int64, i32, i32]
+    lib.gdn_fused_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_chunk_fwd_fused.argtypes = [v] * 9 + [f32, f32, v, v, v] + [i32] * 7 + [
+        v, ctypes.c_size_t, v]
+    rows, H, d = 64, 2, 128
+    need = lib.gdn_fused_workspace_size(rows, H, d)
+    # fp16 q, k, v and fp32 y, each padded to 256 bytes
+    assert need == 3 * rows * H * d * 2 + rows * H * d * 4
+    assert lib.gdn_fused_workspace_size(0, H, d) == 0
+    assert lib.gdn_fused_workspace_size(rows, H, 96) == 0
+    W = B + (1 << 29)
+    base = [A, A + (1 << 26), A + (2 << 26), A + (3 << 26), A + (4 << 26), A + (5 << 26), None,
+            A + (6 << 26), None, 1e-6, 1e-6, B, B + (1 << 26), None, 1, rows, H, d, d, 1, 1, W,
+            need, None]
+
+    def call(**kw):
+        args = list(base)
+        names = ["qr", "kr", "vr", "w", "la", "b", "S0", "z", "nw", "l2", "rms", "o", "ST", "cu",
+                 "N", "T", "H", "dk", "dv", "it", "ot", "ws", "wsb", "st"]
+        for key, val in kw.items():
+            args[names.index(key)] = val
+        return lib.gdn_chunk_fwd_fused(*args)
+
+    assert call(wsb=need - 1) == -1          # workspace too small
+    assert call(ws=None) == -1               # workspace missing
+    assert call(ws=W + 16) == -3             # workspace not 256-byte aligned
+    assert call(dv=64) == -2                 # dk != dv
+    assert call(dk=96, dv=96) == -2
+    assert call(z=None) == -1
+    assert call(o=A + 64) == -1              # o overlaps q_raw
+    assert call(ws=A) == -1                  # workspace overlaps the inputs
+    assert call(ST=W + 4096) == -1           # S_T inside the workspace
+    assert call(rms=-1.0) == -1
+    assert call(it=9) == -2
+    assert lib.gdn_last_error() != b""

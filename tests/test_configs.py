@@ -139,3 +139,29 @@ def test_varlen_frontend_chain_sampled(norm_w_std):
         es = rel_l2(S[n, h], So)
         print("unit (%d, %d) len %d: o %.3e S %.3e" % (n, h, e - s, eo, es), flush=True)
         assert eo <= TOL and es <= TOL
+
+
+@gpu
+def test_fused_prefill_matches_chain_and_oracle():
+    """gdn_chunk_fwd_fused equals the three separate calls bit for bit (same
+    kernels, same intermediate dtypes) and the oracle chain to the bar."""
+    g = _lib()
+    lengths = gi.seq_lengths(64, 512, 8192, seed=5)[:6].tolist() + [1, 2, 33, 517]
+    f = gi.frontend_inputs(lengths, 16, 128, 128, dtype="bf16", seed=5, norm_w_std=0.1)
+    dev = {k: v.cuda() for k, v in f.items() if isinstance(v, torch.Tensor)}
+    o_chain, S_chain = run_frontend_chain(g, dev)
+    o, S = g.gdn_chunk_fwd_fused(dev["q_raw"], dev["k_raw"], dev["v_raw"], dev["conv_w"],
+                                 dev["log_alpha"], dev["beta"], dev["z"], S0=dev["S0"],
+                                 norm_w=dev["norm_w"], l2_eps=1e-6, rms_eps=1e-6,
+                                 cu_seqlens=dev["cu_seqlens"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_chain) and torch.equal(S, S_chain)
+    o, S = o.cpu(), S.cpu()
+    cu = f["cu_seqlens"]
+    for n, h in [(0, 3), (5, 11), (6, 0), (7, 15), (8, 8), (9, 2)]:
+        oo, So = oracle_frontend_chain(f, n, h)
+        s, e = int(cu[n]), int(cu[n + 1])
+        eo = rel_l2(o[s:e, h], oo)
+        es = rel_l2(S[n, h], So)
+        print("unit (%d, %d) len %d: o %.3e S %.3e" % (n, h, e - s, eo, es), flush=True)
+        assert eo <= TOL and es <= TOL

@@ -288,3 +288,31 @@ def test_output_gate(d, dtype, zdtype, with_w):
     e = rel_l2(o, ref)
     print("rel_l2 %.3e" % e)
     assert e <= 1e-5
+
+
+@gpu
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fused_prefill_small(d, dtype):
+    """gdn_chunk_fwd_fused against the oracle chain (front end -> recurrence
+    -> gate) on every unit of a small varlen batch with edge lengths. The
+    fused call keeps q, k, v in fp16 between its stages, so the bar is the
+    16-bit one (2e-3) whatever the input dtype."""
+    g = _lib()
+    lengths = [1, 2, 31, 33, 100, 0, 65]
+    f = gi.frontend_inputs(lengths, 3, d, d, dtype=dtype, seed=63, norm_w_std=0.1)
+    dev = to_dev(f)
+    o, S = g.gdn_chunk_fwd_fused(dev["q_raw"], dev["k_raw"], dev["v_raw"], dev["conv_w"],
+                                 dev["log_alpha"], dev["beta"], dev["z"], S0=dev["S0"],
+                                 norm_w=dev["norm_w"], cu_seqlens=dev["cu_seqlens"],
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    cu = f["cu_seqlens"]
+    q, k, v = (oracle.frontend(f[key], f["conv_w"][i], cu_seqlens=cu, l2=l2, eps=1e-6)
+               for i, (key, l2) in enumerate((("q_raw", True), ("k_raw", True),
+                                              ("v_raw", False))))
+    y, So = oracle.gdn_fwd(q, k, v, f["log_alpha"], f["beta"], f["S0"], cu_seqlens=cu)
+    oo = oracle.output_gate(y.reshape(-1, d), f["z"].reshape(-1, d), f["norm_w"], eps=1e-6)
+    eo, es = rel_l2(o.reshape(-1, d), oo), rel_l2(S, So)
+    print("rel_l2 o=%.3e S=%.3e" % (eo, es), flush=True)
+    assert eo <= 2e-3 and es <= 2e-3, (eo, es)
