@@ -172,28 +172,25 @@ def bench_longctx(g, steps=3, warmup=1):
 
 
 def bench_varlen_frontend(g, steps=3, warmup=1):
-    """64 packed sequences (lengths U[512, 8192]), H=16, d=128: front end ->
-    chunked prefill -> output gate, as three kernels (q/k/v in fp16 and y in
-    fp32 between them)."""
+    """64 packed sequences (lengths U[512, 8192]), H=16, d=128 through
+    gdn_chunk_fwd_fused: front end -> chunked prefill -> output gate (q/k/v
+    in fp16 and y in fp32 between the stages, in a preallocated workspace)."""
     w = gi.WORKLOADS[4]
     f = gi.workload_inputs(4)
     dev = torch.device("cuda", 0)
     d = {k: v.to(dev) for k, v in f.items() if isinstance(v, torch.Tensor)}
     rows = int(f["cu_seqlens"][-1])
     shape = d["q_raw"].shape
-    qkv = tuple(torch.empty(shape, dtype=torch.float16, device=dev) for _ in range(3))
-    y = torch.empty(shape, dtype=torch.float32, device=dev)
     S_T = torch.empty_like(d["S0"])
     o = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(g.gdn_fused_workspace_size(rows, w.H, w.dk), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        q, k, v = g.gdn_frontend_qkv(d["q_raw"], d["k_raw"], d["v_raw"], d["conv_w"],
-                                     cu_seqlens=d["cu_seqlens"], out=qkv,
-                                     out_dtype=torch.float16)
-        g.gdn_chunk_fwd(q, k, v, d["log_alpha"], d["beta"], d["S0"], cu_seqlens=d["cu_seqlens"],
-                        y=y, S_T=S_T, out_dtype=torch.float32)
-        g.gdn_output_gate(y, d["z"], d["norm_w"], 1e-6, out_dtype=torch.bfloat16, o=o)
+        g.gdn_chunk_fwd_fused(d["q_raw"], d["k_raw"], d["v_raw"], d["conv_w"], d["log_alpha"],
+                              d["beta"], d["z"], S0=d["S0"], norm_w=d["norm_w"],
+                              cu_seqlens=d["cu_seqlens"], out_dtype=torch.bfloat16, o=o,
+                              S_T=S_T, workspace=ws)
 
     ms = time_launches(step, steps, warmup, stream) / steps
     flops = rows * w.H * prefill_flops_per_token_head(w.dk, w.dv)
@@ -201,7 +198,7 @@ def bench_varlen_frontend(g, steps=3, warmup=1):
     return dict(workload=w.name, tokens=rows, ms_per_call=ms, tokens_per_s=rows / (ms * 1e-3),
                 pct_bf16_mfma_peak=100.0 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                 hbm_GBps_of_fused_bytes=fused_bytes / (ms * 1e-3) / 1e9,
-                kernels="gdn_frontend_qkv + gdn_chunk_fwd + gdn_output_gate")
+                entry_point="gdn_chunk_fwd_fused (front end + prefill + gate kernels)")
 
 
 def cpu_baseline(pf, max_seconds=30.0):
