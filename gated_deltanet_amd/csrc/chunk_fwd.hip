@@ -20,21 +20,22 @@
 // place), R, E = T R, Y = gamma QS + P E and the state update (fp16 MFMA).
 // Four "prep" waves produce everything that does not depend on the state,
 // pipelined ahead of the state waves:
-//   * gram    (two chunks ahead): direct-to-LDS loads of K and the gates,
-//             the gate scan (wavefront prefix sum) and its decay factors,
-//             the Gram tiles K K^T on MFMA and A;
+//   * gram    (two chunks ahead): the gate scan (wavefront prefix sum) and
+//             its decay factors, the Gram tiles K K^T on MFMA and A;
 //   * inverse (one chunk ahead): T = (I + A)^{-1}: 16x16 diagonal blocks by
 //             forward substitution in fp32, the off-diagonal block on MFMA;
-//   * qk      (one chunk ahead): direct-to-LDS loads of Q and V,
-//             P = tril(Q K^T o G) computed as K Q^T so that the MFMA result
-//             already sits in P's operand layout, and Q converted to fp16;
+//   * qk      (one chunk ahead): P = tril(Q K^T o G) computed as K Q^T so
+//             that the MFMA result already sits in P's operand layout, and Q
+//             converted to fp16;
 //   * kt      (one chunk ahead): Kt^T, transposed on the matrix cores with a
 //             0/1 selector operand (exact) and scaled per token.
-// The direct-to-LDS loads (buffer_load ... lds) go through a buffer resource
-// that ends at the sequence's last row, so rows past the end read as zeros
-// and no per-row clamping is needed; they are issued three chunk steps before
-// the gram wave needs them, into a ring of LDS slots. One workgroup barrier
-// per chunk step hands finished chunks from stage to stage.
+// Two more waves do nothing but issue the direct-to-LDS loads (buffer_load
+// ... lds) of K and the gates, and of Q and V, into a ring of LDS slots and
+// wait for them: issuing those loads stalls the issuing wave for hundreds of
+// cycles per chunk, which the compute waves no longer pay. The loads go
+// through buffer resources that end at the sequence's last row, so rows past
+// the end read as zeros and no per-row clamping is needed. One workgroup
+// barrier per chunk step hands finished chunks from stage to stage.
 //
 // Operand layouts in LDS are "fragment-linear": a 16x32 MFMA operand slice is
 // stored as 64 lanes x 16 bytes, lane L's eight values contiguous at 16*L, so
@@ -56,8 +57,7 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kC = 32;     // tokens per chunk
 constexpr int kNCT = 2;    // 16-token tiles per chunk
 constexpr int kRing = 6;   // raw-tile ring slots
-constexpr int kAhead = kRing - 3;  // chunk steps between a load's issue and its first use
-constexpr int kPrep = 4;   // prep waves per workgroup
+constexpr int kPrep = 6;   // prep waves per workgroup (four compute, two load)
 
 // LDS layout (bytes) for key size DK and NS state waves.
 template <int DK, int NS>
@@ -98,7 +98,6 @@ struct Lay {
   static constexpr int LOADS_QK = kNCT * NKB + NV;   // Q, V
   static_assert(kC * DVT * 2 % 1024 == 0, "V tile must be whole KiB");
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
-  static_assert(kAhead * LOADS_GRAM < 64 && (kAhead + 1) * LOADS_QK < 64, "vmcnt range");
 };
 
 // state tile t, lane group lg, element i  ->  key index
@@ -277,6 +276,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   const bool is_inv = wave == NS;
   const bool is_qk = wave == NS + 1;
   const bool is_gram = wave == NS + 2;  // wave NS + 3: kt
+  const bool is_ldk = wave == NS + 4;   // loads K and the gates
+  const bool is_ldq = wave == NS + 5;   // loads Q and V
   const int slab = 16 * wave;  // state waves: first column of the slab
 
   char *const ring = smem + L::RING;
@@ -897,14 +898,22 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   };
 
   // ---- pipeline -------------------------------------------------------------
-  // Step it (it = -2 .. nc-1): the state waves run chunk it, the gram wave
-  // chunk it + 2, the other prep waves chunk it + 1. The gram and qk waves
-  // issue the loads of chunk it + 2 + kAhead first, so the chunk they need has
-  // kAhead (gram) or kAhead + 1 (qk) younger chunks of loads in flight. Every
-  // role runs its own loop with one barrier per step (nc + 2 in all).
+  // Step it (it = -3 .. nc-1): the state waves run chunk it, the gram wave
+  // chunk it + 2, the inverse, qk and kt waves chunk it + 1. Two waves only
+  // load: one issues K and the gates of chunk it + 3 + kLdK and then waits
+  // for chunk it + 3 (the gram wave's next chunk); the other issues Q and V
+  // of chunk it + 2 + kLdQ and waits for chunk it + 2 (the qk wave's next
+  // chunk). A chunk's ring slot is reloaded only after the state waves have
+  // finished it. Every role runs its own loop with one barrier per step
+  // (nc + 3 in all).
+  constexpr int kLdK = kRing - 4;
+  constexpr int kLdQ = kRing - 3;
+  static_assert((kLdK + 1) * L::LOADS_GRAM < 64 && (kLdQ + 1) * L::LOADS_QK < 64, "vmcnt range");
   auto step_barrier = [&]() { wg_barrier(); };
+  auto in_range = [&](int c) { return c >= 0 && c < nc; };
   if (nc > 0) {
     if (is_state) {
+      step_barrier();
       step_barrier();
       step_barrier();
 #pragma unroll 1
@@ -912,38 +921,38 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
         state_step(x);
         step_barrier();
       }
-    } else if (is_gram) {
+    } else if (is_ldk) {
 #pragma unroll 1
-      for (int c = 0; c < kAhead; ++c) issue_gram(c);
+      for (int c = 0; c < kLdK; ++c) issue_gram(c);
 #pragma unroll 1
-      for (int it = -2; it < nc; ++it) {
-        issue_gram(it + 2 + kAhead);
-        wait_vmcnt<kAhead * L::LOADS_GRAM>();
-        if (it + 2 < nc) gram(it + 2);
+      for (int it = -3; it < nc; ++it) {
+        issue_gram(it + 3 + kLdK);
+        wait_vmcnt<kLdK * L::LOADS_GRAM>();
         step_barrier();
       }
       wait_vmcnt<0>();  // drain before the workgroup retires
-    } else if (is_qk) {
+    } else if (is_ldq) {
 #pragma unroll 1
-      for (int c = 0; c < kAhead; ++c) issue_qk(c);
+      for (int c = 0; c < kLdQ - 1; ++c) issue_qk(c);
 #pragma unroll 1
-      for (int it = -2; it < nc; ++it) {
-        issue_qk(it + 2 + kAhead);
-        wait_vmcnt<(kAhead + 1) * L::LOADS_QK>();
-        if (it >= -1 && it + 1 < nc) qkp(it + 1);
+      for (int it = -3; it < nc; ++it) {
+        issue_qk(it + 2 + kLdQ);
+        wait_vmcnt<kLdQ * L::LOADS_QK>();
         step_barrier();
       }
       wait_vmcnt<0>();
-    } else if (is_inv) {
-#pragma unroll 1
-      for (int it = -2; it < nc; ++it) {
-        if (it >= -1 && it + 1 < nc) inverse(it + 1);
-        step_barrier();
-      }
     } else {
 #pragma unroll 1
-      for (int it = -2; it < nc; ++it) {
-        if (it >= -1 && it + 1 < nc) ktt(it + 1);
+      for (int it = -3; it < nc; ++it) {
+        if (is_gram) {
+          if (in_range(it + 2)) gram(it + 2);
+        } else if (is_qk) {
+          if (in_range(it + 1)) qkp(it + 1);
+        } else if (is_inv) {
+          if (in_range(it + 1)) inverse(it + 1);
+        } else {
+          if (in_range(it + 1)) ktt(it + 1);
+        }
         step_barrier();
       }
     }
