@@ -180,7 +180,8 @@ GDN_API int gdn_frontend_qkv(const void *q_raw, const void *k_raw, const void *v
   if (!(l2_eps >= 0.0f)) return fail(GDN_ERR_INVALID_ARG, "%s", "l2_eps must be >= 0");
   const int64_t rows = cu_seqlens ? static_cast<int64_t>(T) : static_cast<int64_t>(N) * T;
   if (rows * H * d >= (int64_t{1} << 40)) return fail(GDN_ERR_INVALID_ARG, "%s", "input too large");
-  if (rows / 64 >= (int64_t{1} << 31)) return fail(GDN_ERR_INVALID_ARG, "%s", "too many rows");
+  if ((rows + 63) / 64 * H * 3 >= (int64_t{1} << 31))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "too many rows");
   if (rows > 0 && (!q_raw || !k_raw || !v_raw || !conv_w || !q || !k || !v))
     return fail(GDN_ERR_INVALID_ARG, "%s", "null pointer");
   if (misaligned(q_raw) || misaligned(k_raw) || misaligned(v_raw) || misaligned(conv_w) ||
@@ -299,7 +300,8 @@ GDN_API int gdn_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void
   if (static_cast<int64_t>(N) * H > (int64_t{1} << 31) / 8)
     return fail(GDN_ERR_INVALID_ARG, "%s", "N * H too large");
   if (rows * H * d >= (int64_t{1} << 40)) return fail(GDN_ERR_INVALID_ARG, "%s", "input too large");
-  if (rows / 64 >= (int64_t{1} << 31)) return fail(GDN_ERR_INVALID_ARG, "%s", "too many rows");
+  if ((rows + 63) / 64 * H * 3 >= (int64_t{1} << 31))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "too many rows");
   const FusedLayout lay(rows, H, d);
   if (rows > 0) {
     if (!q_raw || !k_raw || !v_raw || !conv_w || !log_alpha || !beta || !z || !o)

@@ -13,9 +13,11 @@
 //
 // Both are pure HBM streams (~2 flops per byte): one pass over the inputs, one
 // over the outputs. A row of 8*G channels is owned by G consecutive lanes
-// with 16-byte accesses (8 channels each); the per-row reductions are lane
-// shuffles inside those G lanes. The convolution re-reads the three previous
-// rows, which are in cache (the same workgroup reads them as its own rows).
+// with 16-byte accesses (8 channels each); the per-row reductions are DPP
+// lane exchanges inside those G lanes. The front end streams whole rows down a
+// block of tokens and keeps the three previous rows of its channels in
+// registers for the causal taps, so every input byte is read from memory
+// about once.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -23,7 +25,7 @@ namespace gdn {
 namespace {
 
 constexpr int kTaps = 4;
-constexpr int kRowsPerBlock = 64;
+constexpr int kRowsPerBlock = 64;  // output gate rows per workgroup
 
 template <typename T>
 struct Vec8;
@@ -71,45 +73,108 @@ struct Vec8<bf16_t> {
   }
 };
 
-// sum over the G consecutive lanes that own one row (G a power of two <= 16)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// sum over the G consecutive lanes that own one row (G = 8 or 16: a half or a
+// whole 16-lane DPP row): pairs and quads by quad permutes, then quads joined
+// by the half-row and row mirrors; every lane ends with the row's sum
 template <int G>
 __device__ __forceinline__ float row_sum(float v) {
-#pragma unroll
-  for (int off = 1; off < G; off <<= 1) v += __shfl_xor(v, off, 64);
+  static_assert(G == 8 || G == 16, "row width");
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  if constexpr (G == 16) v += dpp<0x140>(v);  // row_mirror
   return v;
 }
 
-// first row of the sequence containing `row` (rows of a packed batch)
-__device__ __forceinline__ int64_t seq_begin(const int32_t *cu, int N, int T, int64_t row) {
-  if (!cu) return (row / T) * T;
-  int lo = 0, hi = N;  // invariant: cu[lo] <= row < cu[hi]
+// 1 / (1 + exp(-x)) with one v_exp_f32 and one v_rcp_f32 (about 1 ulp each);
+// exp overflows to inf for x < -88 and the reciprocal then gives 0
+__device__ __forceinline__ float sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+// index of the sequence containing `row` of a packed batch: the last k with
+// cu[k] <= row (0 if none). Called with a row that is uniform across the
+// workgroup, so the loads go through the scalar cache.
+__device__ __forceinline__ int seq_index(const int32_t *cu, int N, int64_t row) {
+  int lo = 0, hi = N;  // invariant: cu[lo] <= row < cu[hi] (when well formed)
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (cu[mid] <= row) lo = mid;
     else hi = mid;
   }
-  const int64_t b = cu[lo];
-  return b < 0 ? 0 : b;  // malformed offsets must not address before the buffer
+  return lo;
 }
 
-// grid: x = row blocks, y = head, z = stream (0 q, 1 k, 2 v)
+// Eight elements of type T as raw bits in registers (16 bytes for 16-bit
+// types, 32 for fp32).
+template <typename T>
+struct Raw8 {
+  u32x4 v[sizeof(T) / 2];
+};
+template <typename T>
+__device__ __forceinline__ Raw8<T> load_raw8(const T *p) {
+  Raw8<T> r;
+#pragma unroll
+  for (int q = 0; q < static_cast<int>(sizeof(T)) / 2; ++q)
+    r.v[q] = reinterpret_cast<const u32x4 *>(p)[q];
+  return r;
+}
+__device__ __forceinline__ void raw8_to_f32(const Raw8<float> &r, float *o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[i] = __uint_as_float(r.v[0][i]);
+    o[4 + i] = __uint_as_float(r.v[1][i]);
+  }
+}
+__device__ __forceinline__ void raw8_to_f32(const Raw8<bf16_t> &r, float *o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(r.v[0][i] << 16);
+    o[2 * i + 1] = __uint_as_float(r.v[0][i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void raw8_to_f32(const Raw8<_Float16> &r, float *o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(r.v[0][i])));
+    o[2 * i + 1] =
+        static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(r.v[0][i] >> 16)));
+  }
+}
+
+constexpr int kFeRows = 64;   // rows per workgroup, streamed in order
+constexpr int kFeAhead = 8;   // rows of loads in flight per lane
+
+// One workgroup streams kFeRows consecutive rows of one stream (0 q, 1 k,
+// 2 v); its lanes cover (head, 8-channel group) pairs, 256 per workgroup
+// (grid.y covers the rest), so a row is read and written as one contiguous
+// span. The three previous rows of each lane's channels stay in registers
+// and are cleared at every sequence start (uniform bookkeeping).
+// grid: x = stream * row_blocks + row_block, y = slice of the H*D/8 pairs
 template <int D, typename TIN, typename TOUT>
 __global__ __launch_bounds__(256) void frontend_kernel(
     const TIN *__restrict__ xq, const TIN *__restrict__ xk, const TIN *__restrict__ xv,
     const float *__restrict__ conv_w, const int32_t *__restrict__ cu, int N, int T, int64_t rows,
     int H, float eps, TOUT *__restrict__ oq, TOUT *__restrict__ ok, TOUT *__restrict__ ov) {
-  constexpr int G = D / 8;          // lanes per row
-  constexpr int RPP = 256 / G;      // rows per pass
-  const int s = blockIdx.z;
-  const int h = blockIdx.y;
+  constexpr int G = D / 8;  // lanes per (token, head) row
+  const int64_t nrb = (rows + kFeRows - 1) / kFeRows;
+  const int s = static_cast<int>(blockIdx.x / nrb);
+  const int64_t rb = blockIdx.x % nrb;
+  const int hg = blockIdx.y * 256 + threadIdx.x;
+  const bool active = hg < H * G;
+  const int hgc = active ? hg : 0;  // idle lanes shadow pair 0 (in bounds, never stored)
   const TIN *x = s == 0 ? xq : (s == 1 ? xk : xv);
   TOUT *out = s == 0 ? oq : (s == 1 ? ok : ov);
   const bool l2 = s < 2;
-  const int g = threadIdx.x % G;
-  const int c0 = 8 * g;
-  // this lane's taps: 8 channels x 4 taps
+  const int64_t col = static_cast<int64_t>(hgc) * 8;  // = head * D + 8 * group
   float w[8][kTaps];
-  const float *wp = conv_w + (static_cast<size_t>(s) * H * D + static_cast<size_t>(h) * D + c0) * kTaps;
+  const float *wp = conv_w + (static_cast<size_t>(s) * H * D + col) * kTaps;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const f32x4 t4 = *reinterpret_cast<const f32x4 *>(wp + c * kTaps);
@@ -117,36 +182,88 @@ __global__ __launch_bounds__(256) void frontend_kernel(
     for (int j = 0; j < kTaps; ++j) w[c][j] = t4[j];
   }
   const int64_t rstride = static_cast<int64_t>(H) * D;
-  for (int pass = 0; pass < kRowsPerBlock / RPP; ++pass) {
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + pass * RPP + threadIdx.x / G;
-    const bool live = r < rows;
-    const int64_t rr = live ? r : rows - 1;  // keep every lane in the shuffles
-    const int64_t bos = seq_begin(cu, N, T, rr);
-    float u[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) u[c] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kTaps; ++j) {
-      const int64_t src = rr - (kTaps - 1) + j;
-      if (src >= bos) {
-        float xv8[8];
-        Vec8<TIN>::load(x + src * rstride + static_cast<int64_t>(h) * D + c0, xv8);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) u[c] = fmaf(w[c][j], xv8[c], u[c]);
+  const int64_t r_first = rb * kFeRows;
+  const int64_t r_end = r_first + kFeRows < rows ? r_first + kFeRows : rows;
+  // current sequence [bos, next); uniform across the workgroup
+  int k = 0;
+  int64_t bos, next;
+  if (cu) {
+    k = seq_index(cu, N, r_first);
+    bos = cu[k];
+    next = cu[k + 1];
+  } else {
+    bos = (r_first / T) * T;
+    next = bos + T;
+  }
+  auto advance = [&](int64_t row) {  // move [bos, next) to the sequence holding row
+    while (row >= next) {
+      if (cu) {
+        if (k + 1 >= N) {
+          bos = next;
+          next = INT64_MAX;
+          break;
+        }
+        ++k;
+        bos = next;
+        next = cu[k + 1];
+      } else {
+        bos = next;
+        next += T;
       }
     }
-    float a[8], ss = 0.0f;
+  };
+  // the three rows before r_first, zero outside the sequence of r_first
+  float x1[8], x2[8], x3[8];
+  {
+    float* win[3] = {x1, x2, x3};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      a[c] = u[c] / (1.0f + __expf(-u[c]));
-      ss = fmaf(a[c], a[c], ss);
-    }
-    if (l2) {
-      const float scale = rsqrtf(row_sum<G>(ss) + eps);
+    for (int j = 0; j < 3; ++j) {
+      const int64_t row = r_first - 1 - j;
+      if (row >= bos && row >= 0) {
+        raw8_to_f32(load_raw8(x + row * rstride + col), win[j]);
+      } else {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) a[c] *= scale;
+        for (int c = 0; c < 8; ++c) win[j][c] = 0.0f;
+      }
     }
-    if (live) Vec8<TOUT>::store(out + rr * rstride + static_cast<int64_t>(h) * D + c0, a);
+  }
+  Raw8<TIN> buf[kFeAhead];
+#pragma unroll
+  for (int i = 0; i < kFeAhead; ++i)
+    if (r_first + i < r_end) buf[i] = load_raw8(x + (r_first + i) * rstride + col);
+#pragma unroll 1
+  for (int64_t r0 = r_first; r0 < r_end; r0 += kFeAhead) {
+#pragma unroll
+    for (int i = 0; i < kFeAhead; ++i) {
+      const int64_t row = r0 + i;
+      if (row >= r_end) break;
+      float xc[8];
+      raw8_to_f32(buf[i], xc);
+      if (row + kFeAhead < r_end) buf[i] = load_raw8(x + (row + kFeAhead) * rstride + col);
+      if (row >= next) {
+        advance(row);
+        if (row == bos) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) x1[c] = x2[c] = x3[c] = 0.0f;
+        }
+      }
+      float a[8], ss = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float u = w[c][3] * xc[c] + w[c][2] * x1[c] + w[c][1] * x2[c] + w[c][0] * x3[c];
+        a[c] = u * sigmoid(u);
+        ss = fmaf(a[c], a[c], ss);
+        x3[c] = x2[c];
+        x2[c] = x1[c];
+        x1[c] = xc[c];
+      }
+      if (l2) {
+        const float scale = rsqrtf(row_sum<G>(ss) + eps);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a[c] *= scale;
+      }
+      if (active) Vec8<TOUT>::store(out + row * rstride + col, a);
+    }
   }
 }
 
@@ -175,20 +292,20 @@ __global__ __launch_bounds__(256) void output_gate_kernel(const TIN *__restrict_
     const float inv = rsqrtf(row_sum<G>(ss) * (1.0f / D) + eps);
     float ov[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) ov[c] = yv[c] * inv * gain[c] / (1.0f + __expf(-zv[c]));
+    for (int c = 0; c < 8; ++c) ov[c] = yv[c] * inv * gain[c] * sigmoid(zv[c]);
     if (live) Vec8<TOUT>::store(o + rr * D + c0, ov);
   }
 }
 
 template <int D, typename TIN, typename TOUT>
 hipError_t launch_fe(const FrontendArgs &a) {
-  const int64_t blocks = (a.rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  dim3 grid(static_cast<unsigned>(blocks), a.H, 3);
-  hipLaunchKernelGGL((frontend_kernel<D, TIN, TOUT>), grid, dim3(256), 0, a.stream,
-                     static_cast<const TIN *>(a.xq), static_cast<const TIN *>(a.xk),
-                     static_cast<const TIN *>(a.xv), a.conv_w, a.cu_seqlens, a.N, a.T, a.rows, a.H,
-                     a.eps, static_cast<TOUT *>(a.q), static_cast<TOUT *>(a.k),
-                     static_cast<TOUT *>(a.v));
+  const int64_t blocks = (a.rows + kFeRows - 1) / kFeRows * 3;
+  const int slices = (a.H * (D / 8) + 255) / 256;
+  hipLaunchKernelGGL((frontend_kernel<D, TIN, TOUT>), dim3(static_cast<unsigned>(blocks), slices),
+                     dim3(256), 0, a.stream, static_cast<const TIN *>(a.xq),
+                     static_cast<const TIN *>(a.xk), static_cast<const TIN *>(a.xv), a.conv_w,
+                     a.cu_seqlens, a.N, a.T, a.rows, a.H, a.eps, static_cast<TOUT *>(a.q),
+                     static_cast<TOUT *>(a.k), static_cast<TOUT *>(a.v));
   return hipGetLastError();
 }
 
