@@ -20,22 +20,24 @@
 // place), R, E = T R, Y = gamma QS + P E and the state update (fp16 MFMA).
 // Four "prep" waves produce everything that does not depend on the state,
 // pipelined ahead of the state waves:
-//   * gram    (two chunks ahead): the gate scan (wavefront prefix sum) and
-//             its decay factors, the Gram tiles K K^T on MFMA and A;
+//   * gram    (two chunks ahead): the Gram tiles K K^T on MFMA and A;
 //   * inverse (one chunk ahead): T = (I + A)^{-1}: 16x16 diagonal blocks by
 //             forward substitution in fp32, the off-diagonal block on MFMA;
 //   * qk      (one chunk ahead): P = tril(Q K^T o G) computed as K Q^T so
 //             that the MFMA result already sits in P's operand layout, and Q
 //             converted to fp16;
-//   * kt      (one chunk ahead): Kt^T, transposed on the matrix cores with a
-//             0/1 selector operand (exact) and scaled per token.
-// Two more waves do nothing but issue the direct-to-LDS loads (buffer_load
-// ... lds) of K and the gates, and of Q and V, into a ring of LDS slots and
-// wait for them: issuing those loads stalls the issuing wave for hundreds of
-// cycles per chunk, which the compute waves no longer pay. The loads go
-// through buffer resources that end at the sequence's last row, so rows past
-// the end read as zeros and no per-row clamping is needed. One workgroup
-// barrier per chunk step hands finished chunks from stage to stage.
+//   * kt      (one chunk ahead): half of the Kt^T tiles, transposed on the
+//             matrix cores with a 0/1 selector operand (exact) and scaled
+//             per token.
+// Two more waves issue the direct-to-LDS loads (buffer_load ... lds) of K and
+// the gates, and of Q and V, into a ring of LDS slots and wait for them:
+// issuing those loads stalls the issuing wave for hundreds of cycles per
+// chunk, which the compute waves no longer pay. Their spare time goes to the
+// gate scan (wavefront prefix sum) and decay factors of the chunk just
+// loaded, and to the other half of the Kt^T tiles. The loads go through
+// buffer resources that end at the sequence's last row, so rows past the end
+// read as zeros and no per-row clamping is needed. One workgroup barrier per
+// chunk step hands finished chunks from stage to stage.
 //
 // Operand layouts in LDS are "fragment-linear": a 16x32 MFMA operand slice is
 // stored as 64 lanes x 16 bytes, lane L's eight values contiguous at 16*L, so
@@ -71,7 +73,7 @@ struct Lay {
   static constexpr int V_OFF = Q_OFF + kNCT * NKB * 1024;
   static constexpr int G_OFF = V_OFF + kC * DVT * 2;  // log_alpha[32], beta[32]
   static constexpr int SLOT = G_OFF + 256;
-  // per-chunk gate values (triple-buffered), 32 floats each:
+  // per-chunk gate values (four buffers), 32 floats each:
   //   G2 running log2 decay, BT beta, GAM gamma = 2^G2, RA 2^(G2 - G2[m]),
   //   CB 2^(G2[m] - G2), KD 2^(G2[C-1] - G2), BR beta * RA, MISC[0] fast flag
   static constexpr int GB_G2 = 0, GB_BT = 128, GB_GAM = 256, GB_RA = 384, GB_CB = 512,
@@ -84,12 +86,12 @@ struct Lay {
   static constexpr int PROC = KT_OFF + NST * 1024;
   // fp32 A^T (double-buffered) and the inverse wave's scratch for T
   static constexpr int LDA = kC + 4;  // A^T row stride (floats)
-  static constexpr int LDT = kC + 1;  // T row stride (floats)
+  static constexpr int LDT = kC + 4;  // T row stride (floats), rows 16-byte aligned
   static constexpr int AMTB = kC * LDA * 4;
   static constexpr int RING = 0;
   static constexpr int PROCB = RING + kRing * SLOT;
   static constexpr int GATEB = PROCB + 2 * PROC;
-  static constexpr int AMT = GATEB + 3 * GATE;
+  static constexpr int AMT = GATEB + 4 * GATE;
   static constexpr int TMP = AMT + 2 * AMTB;
   static constexpr int TOTAL = TMP + kC * LDT * 4;
   // direct-to-LDS loads per chunk issued by the gram and qk waves
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   float *const tmp = reinterpret_cast<float *>(smem + L::TMP);
   auto amt_of = [&](int c) { return reinterpret_cast<float *>(smem + L::AMT + (c & 1) * L::AMTB); };
   auto gate_of = [&](int c) {
-    return reinterpret_cast<float *>(gateb + (c % 3) * L::GATE);
+    return reinterpret_cast<float *>(gateb + (c & 3) * L::GATE);
   };
 
   // Zero all of LDS once: the parts of the operand buffers that are never
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   // per row. The factorisation is used only when both factors stay well
   // inside the fp32 range; otherwise (extreme gates) the chunk falls back to
   // one exponential per element. The branch is uniform per chunk.
-  auto gram = [&](int c) {
+  auto scan_gates = [&](int c) {
     const char *slot = ring + (c % kRing) * L::SLOT;
     float *gt = gate_of(c);
     const float *gl = reinterpret_cast<const float *>(slot + L::G_OFF);
@@ -368,12 +370,6 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       la = gl[lane];
       bt = gl[32 + lane];
     }
-    kvec kf[kNCT][NKB];
-#pragma unroll
-    for (int rt = 0; rt < kNCT; ++rt)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
     float sc = la * 1.4426950408889634f;
     sc += dpp_shr<1>(sc);
     sc += dpp_shr<2>(sc);
@@ -396,6 +392,18 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       gt[L::GB_BR / 4 + lane] = bt * ra;
     }
     if (lane == 0) gt[L::GB_MISC / 4] = fast ? 1.0f : 0.0f;
+  };
+  auto gram = [&](int c) {
+    const char *slot = ring + (c % kRing) * L::SLOT;
+    const float *gt = gate_of(c);
+    kvec kf[kNCT][NKB];
+#pragma unroll
+    for (int rt = 0; rt < kNCT; ++rt)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+    const bool fast = __builtin_amdgcn_readfirstlane(
+                          __builtin_bit_cast(int, gt[L::GB_MISC / 4])) != 0;
     f32x4 gm[3];
 #pragma unroll
     for (int t = 0; t < 3; ++t) gm[t] = zero4();
@@ -654,9 +662,10 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       }
       const f32x4 M = mma_f16(a, bb, zero4());
       f16x8 t11, mb;
+      const f32x4 t11r = *reinterpret_cast<const f32x4 *>(tmp + (16 + lc) * L::LDT + 16 + 4 * lg);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        t11[j] = (_Float16)tmp[(16 + lc) * L::LDT + 16 + 4 * lg + j];
+        t11[j] = (_Float16)t11r[j];  // T_11[lc][4 lg + j]
         mb[j] = (_Float16)M[j];
         t11[4 + j] = (_Float16)0.0f;
         mb[4 + j] = (_Float16)0.0f;
@@ -669,11 +678,10 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     // T in fragment-linear fp16: row 16 mt + lc, slot j <-> token 16(j>>2) + 4 lg + (j&3)
 #pragma unroll
     for (int mt = 0; mt < kNCT; ++mt) {
-      f16x8 f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        f[j] = (_Float16)tmp[(16 * mt + lc) * L::LDT + 16 * (j >> 2) + 4 * lg + (j & 3)];
-      *reinterpret_cast<f16x8 *>(pb + L::T_OFF + mt * 1024 + 16 * lane) = f;
+      const float *trow = tmp + (16 * mt + lc) * L::LDT + 4 * lg;
+      const f32x4 lo = *reinterpret_cast<const f32x4 *>(trow);
+      const f32x4 hi = *reinterpret_cast<const f32x4 *>(trow + 16);
+      *reinterpret_cast<f16x8 *>(pb + L::T_OFF + mt * 1024 + 16 * lane) = pack_f16(lo, hi);
     }
   };
 
@@ -763,22 +771,23 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   // ---- kt wave: Kt^T ---------------------------------------------------------
   // For each state tile, transpose 16 keys x 32 tokens on the matrix cores
   // and scale token columns by exp(g_C - g_t).
-  auto ktt = [&](int c) {
+  auto ktt = [&](int c, int half) {
     const char *slot = ring + (c % kRing) * L::SLOT;
     char *pb = procb + (c & 1) * L::PROC;
     const float *gt = gate_of(c);
-    kvec kf[kNCT][NKB];
+    kvec kf[kNCT][NKB];  // only the key slices of this half's state tiles are read
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = half * (NKB / 2); kb < (half + 1) * (NKB / 2); ++kb)
         kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
     const kvec sel[2] = {selector(0), selector(1)};
     // slot j of the A operand <-> token 16 (j >> 2) + 4 lg + (j & 3)
     const f32x4 kd0 = *reinterpret_cast<const f32x4 *>(gt + L::GB_KD / 4 + 4 * lg);
     const f32x4 kd1 = *reinterpret_cast<const f32x4 *>(gt + L::GB_KD / 4 + 16 + 4 * lg);
 #pragma unroll
-    for (int t = 0; t < NST; ++t) {
+    for (int tt = 0; tt < NST / 2; ++tt) {
+      const int t = half * (NST / 2) + tt;
       const f32x4 d0 = KO::mma(kf[0][t >> 1], sel[t & 1], zero4());
       const f32x4 d1 = KO::mma(kf[1][t >> 1], sel[t & 1], zero4());
       *reinterpret_cast<f16x8 *>(pb + L::KT_OFF + t * 1024 + 16 * lane) =
@@ -899,10 +908,11 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
 
   // ---- pipeline -------------------------------------------------------------
   // Step it (it = -3 .. nc-1): the state waves run chunk it, the gram wave
-  // chunk it + 2, the inverse, qk and kt waves chunk it + 1. Two waves only
-  // load: one issues K and the gates of chunk it + 3 + kLdK and then waits
-  // for chunk it + 3 (the gram wave's next chunk); the other issues Q and V
-  // of chunk it + 2 + kLdQ and waits for chunk it + 2 (the qk wave's next
+  // chunk it + 2, the inverse, qk and kt waves chunk it + 1. The two load
+  // waves: one issues K and the gates of chunk it + 3 + kLdK, waits for chunk
+  // it + 3 (the gram wave's next chunk) and runs that chunk's gate scan; the
+  // other issues Q and V of chunk it + 2 + kLdQ, builds half of the Kt^T
+  // tiles of chunk it + 1 and waits for chunk it + 2 (the qk wave's next
   // chunk). A chunk's ring slot is reloaded only after the state waves have
   // finished it. Every role runs its own loop with one barrier per step
   // (nc + 3 in all).
@@ -928,6 +938,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       for (int it = -3; it < nc; ++it) {
         issue_gram(it + 3 + kLdK);
         wait_vmcnt<kLdK * L::LOADS_GRAM>();
+        if (in_range(it + 3)) scan_gates(it + 3);
         step_barrier();
       }
       wait_vmcnt<0>();  // drain before the workgroup retires
@@ -937,6 +948,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
 #pragma unroll 1
       for (int it = -3; it < nc; ++it) {
         issue_qk(it + 2 + kLdQ);
+        if (in_range(it + 1)) ktt(it + 1, 1);
         wait_vmcnt<kLdQ * L::LOADS_QK>();
         step_barrier();
       }
@@ -951,7 +963,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
         } else if (is_inv) {
           if (in_range(it + 1)) inverse(it + 1);
         } else {
-          if (in_range(it + 1)) ktt(it + 1);
+          if (in_range(it + 1)) ktt(it + 1, 0);
         }
         step_barrier();
       }
