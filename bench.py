@@ -174,7 +174,7 @@ def bench_longctx(g, steps=3, warmup=1):
 def bench_varlen_frontend(g, steps=3, warmup=1):
     """64 packed sequences (lengths U[512, 8192]), H=16, d=128 through
     gdn_chunk_fwd_fused: front end -> chunked prefill -> output gate (q/k/v
-    in fp16 and y in fp32 between the stages, in a preallocated workspace)."""
+    and y in fp16 between the stages, in a preallocated workspace)."""
     w = gi.WORKLOADS[4]
     f = gi.workload_inputs(4)
     dev = torch.device("cuda", 0)

@@ -245,7 +245,7 @@ def gdn_chunk_fwd_fused(q_raw, k_raw, v_raw, conv_w, log_alpha, beta, z, S0=None
     q_raw, k_raw, v_raw, z [rows, H, d] (one dtype); conv_w fp32 [3, H*d, 4];
     gates fp32 [rows, H]; S0 fp32 [N, H, d, d] or None; norm_w fp32 [d] or
     None. Sequence boundaries as in gdn_chunk_fwd. The workspace (fp16 q, k, v
-    and fp32 y) is allocated here unless given. Returns (o, S_T)."""
+    and y) is allocated here unless given. Returns (o, S_T)."""
     lib = load_library()
     in_dtype = q_raw.dtype
     out_dtype = in_dtype if out_dtype is None else out_dtype

@@ -264,7 +264,7 @@ struct FusedLayout {
   size_t qkv_bytes, y_bytes, q, k, v, y, total;
   FusedLayout(int64_t rows, int32_t H, int32_t d) {
     qkv_bytes = static_cast<size_t>(rows) * H * d * 2;
-    y_bytes = static_cast<size_t>(rows) * H * d * 4;
+    y_bytes = static_cast<size_t>(rows) * H * d * 2;
     q = 0;
     k = q + pad256(qkv_bytes);
     v = k + pad256(qkv_bytes);
@@ -376,7 +376,7 @@ GDN_API int gdn_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void
   c.dk = d;
   c.dv = d;
   c.in_dtype = GDN_F16;
-  c.out_dtype = GDN_F32;
+  c.out_dtype = GDN_F16;
   c.stream = st;
   int rc = hip_status(gdn::launch_chunk_fwd(c), "gdn_chunk_fwd_fused prefill");
   if (rc != GDN_OK || rows == 0) return rc;
@@ -388,7 +388,7 @@ GDN_API int gdn_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void
   g.o = o;
   g.rows = rows * H;
   g.d = d;
-  g.in_dtype = GDN_F32;
+  g.in_dtype = GDN_F16;
   g.z_dtype = in_dtype;
   g.out_dtype = out_dtype;
   g.stream = st;

@@ -162,8 +162,8 @@ GDN_API int gdn_output_gate(const void *y, const void *z, const float *norm_w,
 
 /*
  * Bytes of device workspace gdn_chunk_fwd_fused needs for `rows` packed rows
- * of H heads of size d (0 if rows == 0): the normalised q, k, v in fp16 and
- * y in fp32, each padded to 256 bytes. Returns 0 for invalid sizes.
+ * of H heads of size d (0 if rows == 0): the normalised q, k, v and y in
+ * fp16, each padded to 256 bytes. Returns 0 for invalid sizes.
  */
 GDN_API size_t gdn_fused_workspace_size(int64_t rows, int32_t H, int32_t d);
 
@@ -176,8 +176,8 @@ GDN_API size_t gdn_fused_workspace_size(int64_t rows, int32_t H, int32_t d);
  * enqueued back to back on `stream`. The intermediates live in `workspace`
  * (device memory, 256-byte aligned, at least
  * gdn_fused_workspace_size(rows, H, d) bytes, overwritten by the call):
- * q, k, v are kept in fp16 and y in fp32, so the result equals the three
- * separate calls made with those intermediate dtypes.
+ * q, k, v and y are kept in fp16, so the result equals the three separate
+ * calls made with those intermediate dtypes.
  *
  *   q_raw, k_raw, v_raw, z  [rows, H, d] in in_dtype.
  *   conv_w                  float32 [3][H*d][4] (as gdn_frontend_qkv).

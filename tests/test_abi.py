@@ -132,8 +132,8 @@ def test_fused_rejects(lib):
         v, ctypes.c_size_t, v]
     rows, H, d = 64, 2, 128
     need = lib.gdn_fused_workspace_size(rows, H, d)
-    # fp16 q, k, v and fp32 y, each padded to 256 bytes
-    assert need == 3 * rows * H * d * 2 + rows * H * d * 4
+    # fp16 q, k, v and y, each padded to 256 bytes
+    assert need == 4 * rows * H * d * 2
     assert lib.gdn_fused_workspace_size(0, H, d) == 0
     assert lib.gdn_fused_workspace_size(rows, H, 96) == 0
     W = B + (1 << 29)

@@ -91,12 +91,12 @@ def test_decode_N256_H32_sampled():
 
 
 def run_frontend_chain(g, dev, out_dtype=torch.bfloat16):
-    """Front end (fp16 q/k/v) -> chunked prefill (fp32 y) -> output gate."""
+    """Front end (fp16 q/k/v) -> chunked prefill (fp16 y) -> output gate."""
     q, k, v = g.gdn_frontend_qkv(dev["q_raw"], dev["k_raw"], dev["v_raw"], dev["conv_w"],
                                  cu_seqlens=dev["cu_seqlens"], l2_eps=1e-6,
                                  out_dtype=torch.float16)
     y, S = g.gdn_chunk_fwd(q, k, v, dev["log_alpha"], dev["beta"], dev["S0"],
-                           cu_seqlens=dev["cu_seqlens"], out_dtype=torch.float32)
+                           cu_seqlens=dev["cu_seqlens"], out_dtype=torch.float16)
     o = g.gdn_output_gate(y, dev["z"], dev["norm_w"], 1e-6, out_dtype=out_dtype)
     return o, S
 

@@ -296,7 +296,7 @@ def test_output_gate(d, dtype, zdtype, with_w):
 def test_fused_prefill_small(d, dtype):
     """gdn_chunk_fwd_fused against the oracle chain (front end -> recurrence
     -> gate) on every unit of a small varlen batch with edge lengths. The
-    fused call keeps q, k, v in fp16 between its stages, so the bar is the
+    fused call keeps q, k, v and y in fp16 between its stages, so the bar is the
     16-bit one (2e-3) whatever the input dtype."""
     g = _lib()
     lengths = [1, 2, 31, 33, 100, 0, 65]
