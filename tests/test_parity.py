@@ -93,7 +93,7 @@ def test_workload_tiny_fwd():
 
 @gpu
 @pytest.mark.parametrize("case", ["no_decay", "strong_decay", "beta0", "beta1", "repeated_keys",
-                                  "near_parallel"])
+                                  "near_parallel", "large_v", "banded_decay"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_chunk_gate_extremes(case, dtype):
     inp = gi.prefill_inputs(1, 2, 150, 128, 128, dtype, s0_std=0.02, seed=21)
@@ -112,6 +112,15 @@ def test_chunk_gate_extremes(case, dtype):
         noise = gi.normal(inp["k"].shape, 77, 1) * 1e-2
         kk = base + noise
         inp["k"] = (kk / kk.norm(dim=-1, keepdim=True)).to(inp["k"].dtype)
+    elif case == "large_v":
+        # |v| ~ 64: y and the state reach the hundreds, well inside fp16
+        inp["v"] = (inp["v"].float() * 64.0).to(inp["v"].dtype)
+    elif case == "banded_decay":
+        # bands of 40 tokens alternate between no decay and log alpha = -12:
+        # stretches whose decay spans exceed the fp32 range of a factorised
+        # decay sit next to stretches with none
+        band = (torch.arange(inp["log_alpha"].shape[0]) // 40) % 2 == 1
+        inp["log_alpha"][band] = -12.0
     _check(inp, out_dtype=torch.float32)
 
 
