@@ -74,6 +74,9 @@ def _bind(path):
     lib.oracle_output_gate.argtypes = [dp, dp, dp, ctypes.c_double, dp,
                                        ctypes.c_int64, i, i]
     lib.oracle_output_gate.restype = i
+    lib.oracle_gates_from_raw.argtypes = [dp, dp, dp, dp, dp, dp,
+                                          ctypes.c_int64, i]
+    lib.oracle_gates_from_raw.restype = i
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i
     return lib
@@ -225,3 +228,24 @@ def output_gate(y, z, w=None, eps=1e-6, nthreads=0):
                                 rows, d, int(nthreads))
     assert rc == 0
     return o
+
+
+def gates_from_raw(a, b, A, b_alpha=None):
+    """Gates from raw per-head pre-activations a, b [..., H]:
+    log_alpha = -exp(A) * softplus(a + b_alpha), beta = sigmoid(b).
+    Returns (log_alpha, beta) as float64 arrays of a's shape."""
+    lib = _load()
+    a = _f64(a)
+    b = _f64(b)
+    A = _f64(A)
+    b_alpha = _f64(b_alpha)
+    H = a.shape[-1]
+    assert b.shape == a.shape and A.shape == (H,)
+    assert b_alpha is None or b_alpha.shape == (H,)
+    rows = a.size // H if H else 0
+    la = np.zeros_like(a)
+    bt = np.zeros_like(a)
+    rc = lib.oracle_gates_from_raw(_ptr(a), _ptr(b), _ptr(A), _ptr(b_alpha),
+                                   _ptr(la), _ptr(bt), rows, H)
+    assert rc == 0
+    return la, bt

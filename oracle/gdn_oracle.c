@@ -26,6 +26,10 @@
  *   Output gate (same section, third display; zero-centred RMSNorm from the
  *   pwwt.cn page, section 2.1.1): o = sigmoid(z) * RMSNorm(y) with gain 1 + w.
  *
+ *   Gates from raw pre-activations (same section, second display):
+ *   beta_t = sigmoid(b_t), alpha_t = exp[-exp(A) softplus(a_t + b_alpha)],
+ *   i.e. log alpha_t = -exp(A) * softplus(a_t + b_alpha), per head.
+ *
  * Layouts (row-major, token-major):
  *   q, k        [sum_T, H, dk]
  *   v, y, z, o  [sum_T, H, dv]
@@ -232,6 +236,26 @@ int oracle_output_gate(const double *y, const double *z, const double *w,
       const double gate = 1.0 / (1.0 + exp(-zr[i]));
       const double gain = 1.0 + (w ? w[i] : 0.0);
       o[r * d + i] = gate * yr[i] * inv * gain;
+    }
+  }
+  return 0;
+}
+
+/* Gates from raw pre-activations a, b [rows, H] with per-head A [H] and
+ * b_alpha [H] (may be NULL: zero):
+ *   log_alpha = -exp(A_h) * softplus(a + b_alpha_h),  beta = 1 / (1 + exp(-b)),
+ * softplus(x) = log(1 + exp(x)) evaluated as max(x, 0) + log1p(exp(-|x|)). */
+int oracle_gates_from_raw(const double *a, const double *b, const double *A,
+                          const double *b_alpha, double *log_alpha,
+                          double *beta, int64_t rows, int H) {
+  if (rows < 0 || H <= 0) return -1;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int h = 0; h < H; ++h) {
+      const int64_t i = r * H + h;
+      const double x = a[i] + (b_alpha ? b_alpha[h] : 0.0);
+      const double sp = (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+      log_alpha[i] = -exp(A[h]) * sp;
+      beta[i] = 1.0 / (1.0 + exp(-b[i]));
     }
   }
   return 0;

@@ -293,3 +293,42 @@ def test_output_gate_against_torch_rms_norm():
     # w = 0, sigmoid saturated, eps = 0: rows have unit RMS
     o2 = oracle.output_gate(y, np.full_like(z, 50.0), None, eps=0.0)
     assert np.max(np.abs(np.sqrt((o2 ** 2).mean(-1)) - 1)) < 1e-14
+
+
+# Gates from raw pre-activations -----------------------------------------------
+# log alpha = -exp(A) softplus(a + b_alpha), beta = sigmoid(b): page
+# "NLP——技术报告解读-Qwen3.8-Flash-Next", section "GDN 参数化细节".
+def test_gates_from_raw_against_torch_and_identities():
+    rng = np.random.default_rng(23)
+    H = 5
+    a = rng.standard_normal((40, H)) * 6
+    b = rng.standard_normal((40, H)) * 6
+    A = rng.uniform(-3, 1, size=H)
+    ba = rng.standard_normal(H)
+    la, bt = oracle.gates_from_raw(a, b, A, ba)
+    ref_la = -torch.exp(torch.tensor(A)) * torch.nn.functional.softplus(
+        torch.tensor(a) + torch.tensor(ba))
+    assert np.max(np.abs(la - ref_la.numpy())) < 1e-13
+    assert np.max(np.abs(bt - torch.sigmoid(torch.tensor(b)).numpy())) < 1e-15
+    # softplus(x) - softplus(-x) = x and sigmoid(x) + sigmoid(-x) = 1
+    la_m, bt_m = oracle.gates_from_raw(-a, -b, A, None)
+    la_p, _ = oracle.gates_from_raw(a, b, A, None)
+    assert np.max(np.abs((la_p - la_m) + np.exp(A) * a)) < 1e-12
+    _, bt_p = oracle.gates_from_raw(a, b, A, None)
+    assert np.max(np.abs(bt_p + bt_m - 1)) < 1e-15
+    # the bias is a shift of a
+    la_s, _ = oracle.gates_from_raw(a + ba, b, A, None)
+    assert np.max(np.abs(la_s - la)) < 1e-13
+    # at zero: softplus(0) = ln 2, sigmoid(0) = 1/2
+    z = np.zeros((3, H))
+    la0, bt0 = oracle.gates_from_raw(z, z, A, None)
+    assert np.max(np.abs(la0 + np.exp(A) * np.log(2.0))) < 1e-15
+    assert np.all(bt0 == 0.5)
+    # decay strictly in (0, 1) away from saturation; asymptotes
+    assert np.all(la < 0) and np.all(bt > 0) and np.all(bt < 1)
+    big = np.full((1, H), 60.0)
+    la_big, bt_big = oracle.gates_from_raw(big, big, np.zeros(H), None)
+    assert np.allclose(la_big, -60.0, rtol=0, atol=1e-13) and np.all(bt_big == 1.0)
+    la_neg, bt_neg = oracle.gates_from_raw(-big, -big, np.zeros(H), None)
+    assert np.allclose(la_neg, -np.exp(-60.0), rtol=1e-12, atol=0)
+    assert np.allclose(bt_neg, np.exp(-60.0), rtol=1e-12, atol=0)

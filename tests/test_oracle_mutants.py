@@ -39,6 +39,15 @@ MUTANTS = [
      "const double gain = (w ? w[i] : 1.0);"),
     ("gate sign", "const double gate = 1.0 / (1.0 + exp(-zr[i]));",
      "const double gate = 1.0 / (1.0 + exp(zr[i]));"),
+    ("softplus without its linear part",
+     "const double sp = (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));",
+     "const double sp = log1p(exp(-fabs(x)));"),
+    ("decay bias dropped", "const double x = a[i] + (b_alpha ? b_alpha[h] : 0.0);",
+     "const double x = a[i];"),
+    ("decay scale A without exp", "log_alpha[i] = -exp(A[h]) * sp;",
+     "log_alpha[i] = -A[h] * sp;"),
+    ("beta sigmoid sign", "beta[i] = 1.0 / (1.0 + exp(-b[i]));",
+     "beta[i] = 1.0 / (1.0 + exp(b[i]));"),
 ]
 
 PIN_FUNCS = [
@@ -55,6 +64,7 @@ PIN_FUNCS = [
     pins.test_conv_impulse_response_tap_order,
     pins.test_l2norm_gives_unit_rows_and_matches_twin,
     pins.test_output_gate_against_torch_rms_norm,
+    pins.test_gates_from_raw_against_torch_and_identities,
 ]
 
 
