@@ -74,10 +74,22 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
+WARM_SECONDS = 0.5
+
+
 def time_launches(fn, steps, warmup, stream):
+    """Events around `steps` back-to-back calls of fn on `stream`, after
+    `warmup` untimed calls and, beyond those, untimed calls until the GPU
+    has been busy for WARM_SECONDS (its clocks ramp up over the first few
+    hundred milliseconds of load)."""
+    t0 = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < WARM_SECONDS:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -117,6 +129,37 @@ def bench_prefill(g, steps, warmup, copies=3):
     torch.cuda.synchronize()
     return dict(inp=inp, ms_step=ms_step, tokens=tokens, N=N, H=H, T=T, dk=dk, dv=dv,
                 y=y.float().cpu(), S_T=S_T.cpu())
+
+
+def bench_prefill_gated(g, steps, warmup, copies=3):
+    """The prefill workload through gdn_chunk_fwd_gated: raw gate
+    pre-activations (a, b, A, b_alpha) turned into gates inside the kernel."""
+    w = gi.WORKLOADS[1]
+    inp = gi.workload_inputs(1)
+    N, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    tokens = N * T
+    dev = torch.device("cuda", 0)
+    a, b, A, b_alpha = gi.raw_gates(tokens, H, seed=11)
+    sets = []
+    for _ in range(copies):
+        d = {k: inp[k].to(dev) for k in ("q", "k", "v")}
+        d.update(a=a.to(dev), b=b.to(dev))
+        sets.append(d)
+    A, b_alpha = A.to(dev), b_alpha.to(dev)
+    y = torch.empty((tokens, H, dv), dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    it = [0]
+
+    def step():
+        d = sets[it[0] % copies]
+        it[0] += 1
+        g.gdn_chunk_fwd_gated(d["q"], d["k"], d["v"], d["a"], d["b"], A, b_alpha, None, y=y,
+                              S_T=S_T, N=N)
+
+    ms = time_launches(step, steps, warmup, stream) / steps
+    return dict(workload=w.name, entry_point="gdn_chunk_fwd_gated", ms_per_call=ms,
+                tokens_per_s=tokens / (ms * 1e-3))
 
 
 def bench_decode(g, n_steps=128, reps=2):
@@ -240,6 +283,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the long-context and varlen front-end workloads")
+    ap.add_argument("--warm-seconds", type=float, default=0.5,
+                    help="untimed GPU load before each timed region, beyond --warmup steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (torch copy_), the known-size "
                          "reference for scaling HBM byte counters")
@@ -252,6 +297,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    global WARM_SECONDS
+    WARM_SECONDS = max(0.0, args.warm_seconds)
     import gated_deltanet_amd as g
     g.load_library()
     torch.cuda.set_device(0)
@@ -298,6 +345,9 @@ def main():
         rec["decode"] = bench_decode(g, args.decode_steps)
 
     if not args.no_extra:
+        print("[bench] prefill workload 1 with raw gates", file=sys.stderr, flush=True)
+        rec["prefill_gated"] = bench_prefill_gated(g, args.steps, args.warmup)
+        rec["prefill_gated"]["ms_vs_plain"] = rec["prefill_gated"]["ms_per_call"] / ms
         print("[bench] long-context prefill workload 2: B=1 H=32 T=65536", file=sys.stderr,
               flush=True)
         rec["longctx"] = bench_longctx(g)

@@ -67,6 +67,12 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_chunk_fwd_fused.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp, f32, f32, vp, fp, ip,
                                         i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.gdn_chunk_fwd_fused.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_gated.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, ip, i32, i32,
+                                        i32, i32, i32, i32, i32, vp]
+    lib.gdn_chunk_fwd_gated.restype = ctypes.c_int
+    lib.gdn_decode_step_gated.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, ip, i32, vp, i32, i32,
+                                          i32, i32, i32, i32, vp]
+    lib.gdn_decode_step_gated.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -110,21 +116,9 @@ def _need(t, name, dtype=None):
         raise GdnError("%s must be %s" % (name, dtype))
 
 
-def gdn_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, out_dtype=None,
-                  S_T=None, y=None, want_state=True, N=None):
-    """Chunked prefill. q, k [rows, H, dk]; v [rows, H, dv] (bf16 or fp32);
-    log_alpha, beta fp32 [rows, H]; S0 fp32 [N, H, dk, dv] or None; cu_seqlens
-    int32 [N+1] (device) or None. Without cu_seqlens the rows hold N
-    equal-length sequences back to back: N is taken from a 4-D q [N, T, H, dk],
-    else from the argument N, else from S0, else 1. Returns (y, S_T) with y
-    shaped like v."""
-    lib = load_library()
-    in_dtype = q.dtype
-    out_dtype = in_dtype if out_dtype is None else out_dtype
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, nm, in_dtype)
-    _need(log_alpha, "log_alpha", torch.float32)
-    _need(beta, "beta", torch.float32)
+def _prefill_shape(q, v, S0, cu_seqlens, N):
+    """(N, T, H, dk, dv) of a prefill call; T is the per-sequence length, or
+    the total row count when cu_seqlens is given."""
     dk, dv = q.shape[-1], v.shape[-1]
     H = q.shape[-2]
     if cu_seqlens is not None:
@@ -144,6 +138,30 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, out_dtype=
         _need(S0, "S0", torch.float32)
         if tuple(S0.shape) != (N, H, dk, dv):
             raise GdnError("S0 must be [N, H, dk, dv] = %s" % ((N, H, dk, dv),))
+    return N, T, H, dk, dv
+
+
+def _prefill_checked(q, k, v, g1, g2, names):
+    in_dtype = q.dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, in_dtype)
+    _need(g1, names[0], torch.float32)
+    _need(g2, names[1], torch.float32)
+    return in_dtype
+
+
+def gdn_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, out_dtype=None,
+                  S_T=None, y=None, want_state=True, N=None):
+    """Chunked prefill. q, k [rows, H, dk]; v [rows, H, dv] (bf16 or fp32);
+    log_alpha, beta fp32 [rows, H]; S0 fp32 [N, H, dk, dv] or None; cu_seqlens
+    int32 [N+1] (device) or None. Without cu_seqlens the rows hold N
+    equal-length sequences back to back: N is taken from a 4-D q [N, T, H, dk],
+    else from the argument N, else from S0, else 1. Returns (y, S_T) with y
+    shaped like v."""
+    lib = load_library()
+    in_dtype = _prefill_checked(q, k, v, log_alpha, beta, ("log_alpha", "beta"))
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    N, T, H, dk, dv = _prefill_shape(q, v, S0, cu_seqlens, N)
     if y is None:
         y = torch.empty(v.shape, dtype=out_dtype, device=v.device)
     if S_T is None and want_state:
@@ -152,6 +170,38 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, out_dtype=
                            _p(cu_seqlens), N, T, H, dk, dv, _dt(in_dtype), _dt(out_dtype),
                            _stream(v.device))
     _check(rc, lib, "gdn_chunk_fwd")
+    return y, S_T
+
+
+def _head_params(A, b_alpha, H):
+    _need(A, "A", torch.float32)
+    if A.numel() != H:
+        raise GdnError("A must hold one value per head (%d)" % H)
+    if b_alpha is not None:
+        _need(b_alpha, "b_alpha", torch.float32)
+        if b_alpha.numel() != H:
+            raise GdnError("b_alpha must hold one value per head (%d)" % H)
+
+
+def gdn_chunk_fwd_gated(q, k, v, a, b, A, b_alpha=None, S0=None, cu_seqlens=None,
+                        out_dtype=None, S_T=None, y=None, want_state=True, N=None):
+    """Chunked prefill with the gates computed in-kernel from raw fp32
+    pre-activations a, b [rows, H] and per-head A, b_alpha [H]:
+    log alpha = -exp(A) softplus(a + b_alpha), beta = sigmoid(b). Otherwise
+    as gdn_chunk_fwd."""
+    lib = load_library()
+    in_dtype = _prefill_checked(q, k, v, a, b, ("a", "b"))
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    N, T, H, dk, dv = _prefill_shape(q, v, S0, cu_seqlens, N)
+    _head_params(A, b_alpha, H)
+    if y is None:
+        y = torch.empty(v.shape, dtype=out_dtype, device=v.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=v.device)
+    rc = lib.gdn_chunk_fwd_gated(_p(q), _p(k), _p(v), _p(a), _p(b), _p(A), _p(b_alpha), _p(S0),
+                                 _p(y), _p(S_T), _p(cu_seqlens), N, T, H, dk, dv, _dt(in_dtype),
+                                 _dt(out_dtype), _stream(v.device))
+    _check(rc, lib, "gdn_chunk_fwd_gated")
     return y, S_T
 
 
@@ -173,6 +223,43 @@ def gdn_decode_step(q, k, v, log_alpha, beta, S, out_dtype=None, y=None):
     rc = lib.gdn_decode_step(_p(q), _p(k), _p(v), _p(log_alpha), _p(beta), _p(S), _p(y), N, H,
                              dk, dv, _dt(in_dtype), _dt(out_dtype), _stream(v.device))
     _check(rc, lib, "gdn_decode_step")
+    return y
+
+
+def gdn_decode_step_gated(q, k, v, a, b, A, S, b_alpha=None, state_idx=None, out_dtype=None,
+                          y=None):
+    """One decode token per (sequence, head) with the gates computed in-kernel
+    from raw fp32 pre-activations a, b [N, H] and per-head A, b_alpha [H].
+    S is [N, H, dk, dv], or with state_idx (int32 [N]) a pool
+    [n_slots, H, dk, dv] of which sequence n updates slot state_idx[n]; an
+    out-of-range slot leaves the pool untouched and gives y = 0."""
+    lib = load_library()
+    in_dtype = q.dtype
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, in_dtype)
+    _need(a, "a", torch.float32)
+    _need(b, "b", torch.float32)
+    _need(S, "S", torch.float32)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _head_params(A, b_alpha, H)
+    n_slots = 0
+    if state_idx is not None:
+        _need(state_idx, "state_idx", torch.int32)
+        if state_idx.numel() != N:
+            raise GdnError("state_idx must hold one slot per sequence (%d)" % N)
+        n_slots = S.shape[0]
+    elif S.shape[0] != N:
+        raise GdnError("S must be [N, H, dk, dv]")
+    if tuple(S.shape[1:]) != (H, dk, dv):
+        raise GdnError("S must be [slots, H, dk, dv] with H, dk, dv = %s" % ((H, dk, dv),))
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=out_dtype, device=v.device)
+    rc = lib.gdn_decode_step_gated(_p(q), _p(k), _p(v), _p(a), _p(b), _p(A), _p(b_alpha), _p(S),
+                                   _p(state_idx), n_slots, _p(y), N, H, dk, dv, _dt(in_dtype),
+                                   _dt(out_dtype), _stream(v.device))
+    _check(rc, lib, "gdn_decode_step_gated")
     return y
 
 

@@ -58,11 +58,17 @@ GDN_API const char *gdn_last_error(void) { return g_last_error; }
 
 GDN_API int gdn_version(void) { return 100; }
 
-GDN_API int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
-                          const float *beta, const float *S0, void *y, float *S_T,
-                          const int32_t *cu_seqlens, int32_t N, int32_t T, int32_t H,
-                          int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype,
-                          void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by gdn_chunk_fwd (A == null: gates given as log alpha and beta) and
+// gdn_chunk_fwd_gated (raw pre-activations plus per-head A and b_alpha).
+int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                   const float *beta, const float *A, const float *b_alpha, const float *S0,
+                   void *y, float *S_T, const int32_t *cu_seqlens, int32_t N, int32_t T,
+                   int32_t H, int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype,
+                   void *stream, const char *name) {
   g_last_error[0] = '\0';
   if (N < 0 || T < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N, T must be >= 0 and H > 0");
   if (!head_size_ok(dk) || !head_size_ok(dv))
@@ -98,6 +104,14 @@ GDN_API int gdn_chunk_fwd(const void *q, const void *k, const void *v, const flo
   if (S0 && S0 != S_T && overlap(S0, ns, S_T, ns))
     return fail(GDN_ERR_INVALID_ARG, "%s", "S0 partially overlaps S_T");
   if (S0 && overlap(S0, ns, y, ny)) return fail(GDN_ERR_INVALID_ARG, "%s", "S0 overlaps y");
+  if (A) {
+    if (misaligned(A, 4) || misaligned(b_alpha, 4))
+      return fail(GDN_ERR_MISALIGNED, "%s", "A and b_alpha need 4-byte alignment");
+    const size_t nh = static_cast<size_t>(H) * 4;
+    if (overlap(A, nh, y, ny) || overlap(A, nh, S_T, ns) || overlap(b_alpha, nh, y, ny) ||
+        overlap(b_alpha, nh, S_T, ns))
+      return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps an output");
+  }
 
   gdn::ChunkArgs a;
   a.q = q;
@@ -105,6 +119,8 @@ GDN_API int gdn_chunk_fwd(const void *q, const void *k, const void *v, const flo
   a.v = v;
   a.log_alpha = log_alpha;
   a.beta = beta;
+  a.A = A;
+  a.b_alpha = A ? b_alpha : nullptr;
   a.S0 = S0;
   a.y = y;
   a.S_T = S_T;
@@ -117,13 +133,17 @@ GDN_API int gdn_chunk_fwd(const void *q, const void *k, const void *v, const flo
   a.in_dtype = in_dtype;
   a.out_dtype = out_dtype;
   a.stream = static_cast<hipStream_t>(stream);
-  return hip_status(gdn::launch_chunk_fwd(a), "gdn_chunk_fwd launch");
+  char where[64];
+  snprintf(where, sizeof(where), "%s launch", name);
+  return hip_status(gdn::launch_chunk_fwd(a), where);
 }
 
-GDN_API int gdn_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
-                            const float *beta, float *S, void *y, int32_t N, int32_t H,
-                            int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype,
-                            void *stream) {
+// Shared by gdn_decode_step (A and state_idx null) and gdn_decode_step_gated.
+int decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                const float *beta, const float *A, const float *b_alpha, float *S,
+                const int32_t *state_idx, int32_t n_slots, void *y, int32_t N, int32_t H,
+                int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype, void *stream,
+                const char *name) {
   g_last_error[0] = '\0';
   if (N < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N must be >= 0 and H > 0");
   if (!head_size_ok(dk) || !head_size_ok(dv))
@@ -132,19 +152,25 @@ GDN_API int gdn_decode_step(const void *q, const void *k, const void *v, const f
     return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32, GDN_BF16 or GDN_F16");
   if (static_cast<int64_t>(N) * H >= (int64_t{1} << 31))
     return fail(GDN_ERR_INVALID_ARG, "%s", "N * H too large");
-  if (N > 0 && (!q || !k || !v || !log_alpha || !beta || !S || !y))
+  if (state_idx && n_slots < 0) return fail(GDN_ERR_INVALID_ARG, "%s", "n_slots must be >= 0");
+  if (state_idx && static_cast<int64_t>(n_slots) * H >= (int64_t{1} << 31))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "n_slots * H too large");
+  const int64_t slots = state_idx ? n_slots : N;
+  if (N > 0 && (!q || !k || !v || !log_alpha || !beta || !y || (slots > 0 && !S)))
     return fail(GDN_ERR_INVALID_ARG, "%s", "null pointer");
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(y) || misaligned(S) ||
-      misaligned(log_alpha, 4) || misaligned(beta, 4))
-    return fail(GDN_ERR_MISALIGNED, "%s", "q, k, v, y, S need 16-byte alignment, the gates 4");
+      misaligned(log_alpha, 4) || misaligned(beta, 4) || misaligned(A, 4) ||
+      misaligned(b_alpha, 4) || misaligned(state_idx, 4))
+    return fail(GDN_ERR_MISALIGNED, "%s", "q, k, v, y, S need 16-byte alignment, the rest 4");
   const size_t in_b = esize(in_dtype);
   const size_t units = static_cast<size_t>(N) * H;
-  const size_t ns = units * dk * dv * 4;
+  const size_t ns = static_cast<size_t>(slots) * H * dk * dv * 4;
   const size_t ny = units * dv * esize(out_dtype);
-  const void *ins[5] = {q, k, v, log_alpha, beta};
-  const size_t in_n[5] = {units * dk * in_b, units * dk * in_b, units * dv * in_b, units * 4,
-                          units * 4};
-  for (int i = 0; i < 5; ++i) {
+  const size_t nh = static_cast<size_t>(H) * 4;
+  const void *ins[8] = {q, k, v, log_alpha, beta, A, A ? b_alpha : nullptr, state_idx};
+  const size_t in_n[8] = {units * dk * in_b, units * dk * in_b, units * dv * in_b, units * 4,
+                          units * 4, nh, nh, static_cast<size_t>(N) * 4};
+  for (int i = 0; i < 8; ++i) {
     if (overlap(ins[i], in_n[i], S, ns) || overlap(ins[i], in_n[i], y, ny))
       return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps an output");
   }
@@ -156,7 +182,11 @@ GDN_API int gdn_decode_step(const void *q, const void *k, const void *v, const f
   a.v = v;
   a.log_alpha = log_alpha;
   a.beta = beta;
+  a.A = A;
+  a.b_alpha = A ? b_alpha : nullptr;
   a.S = S;
+  a.state_idx = state_idx;
+  a.n_slots = state_idx ? n_slots : N;
   a.y = y;
   a.N = N;
   a.H = H;
@@ -165,7 +195,52 @@ GDN_API int gdn_decode_step(const void *q, const void *k, const void *v, const f
   a.in_dtype = in_dtype;
   a.out_dtype = out_dtype;
   a.stream = static_cast<hipStream_t>(stream);
-  return hip_status(gdn::launch_decode_step(a), "gdn_decode_step launch");
+  char where[64];
+  snprintf(where, sizeof(where), "%s launch", name);
+  return hip_status(gdn::launch_decode_step(a), where);
+}
+
+}  // namespace
+
+extern "C" {
+
+GDN_API int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const float *beta, const float *S0, void *y, float *S_T,
+                          const int32_t *cu_seqlens, int32_t N, int32_t T, int32_t H,
+                          int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype,
+                          void *stream) {
+  return chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, nullptr, S0, y, S_T, cu_seqlens, N,
+                        T, H, dk, dv, in_dtype, out_dtype, stream, "gdn_chunk_fwd");
+}
+
+GDN_API int gdn_chunk_fwd_gated(const void *q, const void *k, const void *v, const float *a,
+                                const float *b, const float *A, const float *b_alpha,
+                                const float *S0, void *y, float *S_T, const int32_t *cu_seqlens,
+                                int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                                int32_t in_dtype, int32_t out_dtype, void *stream) {
+  g_last_error[0] = '\0';
+  if (H > 0 && !A) return fail(GDN_ERR_INVALID_ARG, "%s", "A is required");
+  return chunk_fwd_impl(q, k, v, a, b, A, b_alpha, S0, y, S_T, cu_seqlens, N, T, H, dk, dv,
+                        in_dtype, out_dtype, stream, "gdn_chunk_fwd_gated");
+}
+
+GDN_API int gdn_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                            const float *beta, float *S, void *y, int32_t N, int32_t H,
+                            int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype,
+                            void *stream) {
+  return decode_impl(q, k, v, log_alpha, beta, nullptr, nullptr, S, nullptr, 0, y, N, H, dk, dv,
+                     in_dtype, out_dtype, stream, "gdn_decode_step");
+}
+
+GDN_API int gdn_decode_step_gated(const void *q, const void *k, const void *v, const float *a,
+                                  const float *b, const float *A, const float *b_alpha,
+                                  float *S, const int32_t *state_idx, int32_t n_slots, void *y,
+                                  int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                  int32_t in_dtype, int32_t out_dtype, void *stream) {
+  g_last_error[0] = '\0';
+  if (H > 0 && !A) return fail(GDN_ERR_INVALID_ARG, "%s", "A is required");
+  return decode_impl(q, k, v, a, b, A, b_alpha, S, state_idx, n_slots, y, N, H, dk, dv,
+                     in_dtype, out_dtype, stream, "gdn_decode_step_gated");
 }
 
 GDN_API int gdn_frontend_qkv(const void *q_raw, const void *k_raw, const void *v_raw,

@@ -232,6 +232,7 @@ template <int DK, int NS, typename TIN, typename TOUT>
 __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     const TIN *__restrict__ q, const TIN *__restrict__ k, const TIN *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
+    const float *__restrict__ gA, const float *__restrict__ gbias,
     const float *__restrict__ S0, TOUT *__restrict__ y, float *__restrict__ S_T,
     const int32_t *__restrict__ cu_seqlens, int T, int H, int DV, int n_vt, int n_units) {
   using L = Lay<DK, NS>;
@@ -360,6 +361,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   // per row. The factorisation is used only when both factors stay well
   // inside the fp32 range; otherwise (extreme gates) the chunk falls back to
   // one exponential per element. The branch is uniform per chunk.
+  const RawGate gate = RawGate::load(gA, gbias, h);
   auto scan_gates = [&](int c) {
     const char *slot = ring + (c % kRing) * L::SLOT;
     float *gt = gate_of(c);
@@ -369,6 +371,10 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     if (lane < kC && tok < len) {
       la = gl[lane];
       bt = gl[32 + lane];
+      if (gate.raw()) {
+        la = gate.log_alpha(la);
+        bt = RawGate::beta(bt);
+      }
     }
     float sc = la * 1.4426950408889634f;
     sc += dpp_shr<1>(sc);
@@ -989,7 +995,7 @@ hipError_t launch_bf16(const ChunkArgs &a) {
   hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, NS, TIN, TOUT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * (NS + kPrep)), 0, a.stream, static_cast<const TIN *>(a.q),
                      static_cast<const TIN *>(a.k), static_cast<const TIN *>(a.v),
-                     a.log_alpha, a.beta, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.cu_seqlens,
+                     a.log_alpha, a.beta, a.A, a.b_alpha, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.cu_seqlens,
                      a.T, a.H, a.dv, n_vt, static_cast<int>(units));
   return hipGetLastError();
 }

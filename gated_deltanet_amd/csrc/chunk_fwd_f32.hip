@@ -49,6 +49,7 @@ template <int DK, int DVT, typename TIN, typename TOUT, typename MT>
 __global__ __launch_bounds__(64 * (DVT / 16)) void chunk_fwd_f32_kernel(
     const TIN *__restrict__ q, const TIN *__restrict__ k, const TIN *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
+    const float *__restrict__ gA, const float *__restrict__ gbias,
     const float *__restrict__ S0, TOUT *__restrict__ y, float *__restrict__ S_T,
     const int32_t *__restrict__ cu_seqlens, int T, int H, int DV, int n_vt) {
   constexpr int C = kChunkF32;
@@ -112,6 +113,7 @@ __global__ __launch_bounds__(64 * (DVT / 16)) void chunk_fwd_f32_kernel(
     for (int i = 0; i < 4; ++i)
       st[it][i] = S0 ? S0[sbase + static_cast<size_t>(16 * it + 4 * lg + i) * DV] : 0.0f;
 
+  const RawGate gate = RawGate::load(gA, gbias, h);
   const int nchunks = static_cast<int>((len + C - 1) / C);
   for (int c = 0; c < nchunks; ++c) {
     const int64_t t0 = bos + static_cast<int64_t>(c) * C;
@@ -124,6 +126,10 @@ __global__ __launch_bounds__(64 * (DVT / 16)) void chunk_fwd_f32_kernel(
     if (lane < valid) {
       la = log_alpha[(t0 + lane) * H + h];
       bt = beta[(t0 + lane) * H + h];
+      if (gate.raw()) {
+        la = gate.log_alpha(la);
+        bt = RawGate::beta(bt);
+      }
     }
     float g = la;
 #pragma unroll
@@ -362,7 +368,7 @@ static hipError_t launch_tile(const ChunkArgs &a) {
   hipLaunchKernelGGL((chunk_fwd_f32_kernel<DK, DVT, TIN, TOUT, MT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * (DVT / 16)), 0, a.stream, static_cast<const TIN *>(a.q),
                      static_cast<const TIN *>(a.k), static_cast<const TIN *>(a.v), a.log_alpha,
-                     a.beta, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.cu_seqlens, a.T, a.H, a.dv,
+                     a.beta, a.A, a.b_alpha, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.cu_seqlens, a.T, a.H, a.dv,
                      n_vt);
   return hipGetLastError();
 }

@@ -13,6 +13,11 @@
 // keeps DK*DV/256 state values in registers (16-byte accesses, 4 adjacent
 // columns), so the read-modify-write never round-trips through LDS; only the
 // per-column partial dot products are reduced across row groups.
+//
+// Gates arrive either as log alpha and beta or as raw pre-activations that
+// are turned into gates here (RawGate). For serving, the states may live in
+// a pool of slots: sequence n then updates slot state_idx[n], and a sequence
+// whose slot is out of range leaves the pool untouched and gets y = 0.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -21,8 +26,9 @@ namespace gdn {
 template <int DK, int DV, typename TIN, typename TOUT>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const TIN *__restrict__ q, const TIN *__restrict__ k, const TIN *__restrict__ v,
-    const float *__restrict__ log_alpha, const float *__restrict__ beta, float *__restrict__ S,
-    TOUT *__restrict__ y, int H) {
+    const float *__restrict__ log_alpha, const float *__restrict__ beta,
+    const float *__restrict__ gA, const float *__restrict__ gbias, float *__restrict__ S,
+    const int32_t *__restrict__ state_idx, int n_slots, TOUT *__restrict__ y, int H) {
   constexpr int NT = 256;
   constexpr int CG = DV / 4;   // column groups of 4 adjacent columns
   constexpr int RG = NT / CG;  // row groups
@@ -41,7 +47,19 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   const int rg = tid / CG;
   const int wave = tid / 64;
 
-  float *Su = S + static_cast<size_t>(unit) * DK * DV;
+  int64_t slot_unit = unit;
+  if (state_idx) {
+    const int n = unit / H;
+    const int slot = state_idx[n];
+    if (slot < 0 || slot >= n_slots) {
+      // padding entry: no state to update; y = 0
+      const size_t y_off = static_cast<size_t>(unit) * DV;
+      for (int j = tid; j < DV; j += NT) y[y_off + j] = io<TOUT>::from_f32(0.0f);
+      return;
+    }
+    slot_unit = static_cast<int64_t>(slot) * H + (unit - n * H);
+  }
+  float *Su = S + static_cast<size_t>(slot_unit) * DK * DV;
 
   // issue every state load first: they are the whole cost of the kernel
   f32x4 s[RPT];
@@ -56,8 +74,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     sq[i] = io<TIN>::to_f32(q[qk_off + i]);
     sk[i] = io<TIN>::to_f32(k[qk_off + i]);
   }
-  const float alpha = __expf(log_alpha[unit]);
-  const float b = beta[unit];
+  const RawGate rg_h = RawGate::load(gA, gbias, unit % H);
+  float la = log_alpha[unit];
+  float b = beta[unit];
+  if (rg_h.raw()) {
+    la = rg_h.log_alpha(la);
+    b = RawGate::beta(b);
+  }
+  const float alpha = __expf(la);
   __syncthreads();
 
   // partial dot products over this thread's rows: s_j.k, s_j.q (4 columns)
@@ -131,8 +155,8 @@ static hipError_t launch(const DecodeArgs &a) {
   if (units == 0) return hipSuccess;
   hipLaunchKernelGGL((decode_step_kernel<DK, DV, TIN, TOUT>), dim3(units), dim3(256), 0,
                      a.stream, static_cast<const TIN *>(a.q), static_cast<const TIN *>(a.k),
-                     static_cast<const TIN *>(a.v), a.log_alpha, a.beta, a.S,
-                     static_cast<TOUT *>(a.y), a.H);
+                     static_cast<const TIN *>(a.v), a.log_alpha, a.beta, a.A, a.b_alpha, a.S,
+                     a.state_idx, a.n_slots, static_cast<TOUT *>(a.y), a.H);
   return hipGetLastError();
 }
 

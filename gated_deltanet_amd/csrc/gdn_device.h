@@ -249,4 +249,30 @@ __device__ __forceinline__ f32x4 zero4() {
   return z;
 }
 
+// Gates from raw per-head pre-activations (page "NLP——技术报告解读-
+// Qwen3.8-Flash-Next", section "GDN 参数化细节"): the decay gate is
+// alpha = exp(-exp(A) softplus(a + b_alpha)) and the write gate is
+// beta = sigmoid(b). RawGate holds exp(A) and b_alpha of one head; scale = 0
+// marks gates that arrive already as log alpha and beta.
+struct RawGate {
+  float scale;  // exp(A_h), or 0 when the gates are not raw
+  float bias;   // b_alpha of the head
+
+  __device__ static __forceinline__ RawGate load(const float *A, const float *b_alpha, int h) {
+    RawGate g{0.0f, 0.0f};
+    if (A) {
+      g.scale = expf(A[h]);
+      if (b_alpha) g.bias = b_alpha[h];
+    }
+    return g;
+  }
+  __device__ __forceinline__ bool raw() const { return scale != 0.0f; }
+  // softplus(x) = max(x, 0) + log(1 + exp(-|x|)), accurate at both ends
+  __device__ __forceinline__ float log_alpha(float a) const {
+    const float x = a + bias;
+    return -scale * (fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))));
+  }
+  __device__ static __forceinline__ float beta(float b) { return 1.0f / (1.0f + expf(-b)); }
+};
+
 }  // namespace gdn

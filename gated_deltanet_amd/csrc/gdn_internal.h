@@ -7,10 +7,18 @@
 
 namespace gdn {
 
+// Gate inputs: when A is null, log_alpha and beta hold log alpha and beta;
+// otherwise they hold the raw pre-activations a and b, turned into gates
+// in-kernel with the per-head A and b_alpha (b_alpha may be null: zero).
 struct DecodeArgs {
   const void *q, *k, *v;
   const float *log_alpha, *beta;
+  const float *A = nullptr, *b_alpha = nullptr;
   float *S;
+  // state slots: null = S holds [N, H, dk, dv]; otherwise sequence n uses
+  // slot state_idx[n] of a pool of n_slots states (out of range: skipped)
+  const int32_t *state_idx = nullptr;
+  int n_slots = 0;
   void *y;
   int N, H, dk, dv;
   int in_dtype, out_dtype;  // 0 = f32, 1 = bf16, 2 = f16
@@ -20,6 +28,7 @@ struct DecodeArgs {
 struct ChunkArgs {
   const void *q, *k, *v;
   const float *log_alpha, *beta;
+  const float *A = nullptr, *b_alpha = nullptr;
   const float *S0;  // may be null (zeros)
   void *y;
   float *S_T;       // may be null

@@ -15,6 +15,8 @@ Distributions (the five workloads the library is measured on):
   log_alpha = -exp(A_h) * softplus(x), beta = sigmoid(N(0, 1)); this is the
   gate parameterisation of the page "NLP——技术报告解读-Qwen3.8-Flash-Next",
   section "GDN 参数化细节", with the projections replaced by random draws;
+* raw gate inputs (for the in-kernel gate path): the same a = x and b = n
+  draws with the same A_h, plus a per-head bias b_alpha ~ N(0, 0.5);
 * states S0 ~ N(0, std) with std the second parameter;
 * front-end workload: raw projections ~ N(0, 1) bf16, depthwise conv weights
   ~ N(0, 0.5) float32 [3][H*d][4], z ~ N(0, 1) bf16, sequence lengths drawn
@@ -108,6 +110,17 @@ def gates(rows, H, seed, A=None, tid_x=91, tid_b=92):
     log_alpha = -torch.exp(A)[None, :] * torch.nn.functional.softplus(x)
     beta = torch.sigmoid(normal((rows, H), seed, tid_b))
     return log_alpha.contiguous(), beta.contiguous()
+
+
+def raw_gates(rows, H, seed, bias_std=0.5, tid_x=91, tid_b=92, tid_bias=93):
+    """Raw gate pre-activations for the in-kernel gate path: a, b ~ N(0, 1)
+    [rows, H] (the same draws as ``gates``), per head A ~ U(-4, 0) and
+    b_alpha ~ N(0, bias_std). Returns float32 (a, b, A, b_alpha)."""
+    a = normal((rows, H), seed, tid_x)
+    b = normal((rows, H), seed, tid_b)
+    A = head_log_decay_scale(H, seed)
+    b_alpha = normal((H,), seed, tid_bias, std=bias_std)
+    return a.contiguous(), b.contiguous(), A, b_alpha
 
 
 def seq_lengths(n, lo, hi, seed, tensor_id=80) -> torch.Tensor:

@@ -117,6 +117,57 @@ GDN_API int gdn_decode_step(const void *q, const void *k, const void *v,
                             int32_t out_dtype, void *stream);
 
 /*
+ * Gates from raw pre-activations (page "NLP——技术报告解读-Qwen3.8-Flash-Next",
+ * section "GDN 参数化细节", gate display): with per-head parameters A and
+ * b_alpha, the gates of a token-head with pre-activations a (decay) and b
+ * (write) are
+ *     log alpha = -exp(A_h) * softplus(a + b_alpha_h),   beta = sigmoid(b).
+ * The two calls below take a and b in place of log_alpha and beta and
+ * compute the gates inside the kernels, in fp32, so no separate elementwise
+ * pass over the gates is needed.
+ *
+ *   a, b       float32 [rows, H] (prefill) or [N, H] (decode), raw
+ *              pre-activations; any finite values.
+ *   A          float32 [H], required (log of the per-head decay rate).
+ *   b_alpha    float32 [H], or NULL for zeros.
+ * All three are 4-byte aligned inputs and must not overlap an output.
+ */
+
+/* Chunked prefill with raw gates; every other argument as gdn_chunk_fwd. */
+GDN_API int gdn_chunk_fwd_gated(const void *q, const void *k, const void *v,
+                                const float *a, const float *b, const float *A,
+                                const float *b_alpha, const float *S0, void *y,
+                                float *S_T, const int32_t *cu_seqlens,
+                                int32_t N, int32_t T, int32_t H, int32_t dk,
+                                int32_t dv, int32_t in_dtype,
+                                int32_t out_dtype, void *stream);
+
+/*
+ * Decode step with raw gates and, for serving, an optional pool of state
+ * slots (the fixed-size state per sequence of the same section makes a slot
+ * pool the natural cache).
+ *
+ *   S          float32 state(s), updated in place. With state_idx NULL, S is
+ *              [N, H, dk, dv] as in gdn_decode_step and n_slots is ignored.
+ *              Otherwise S is a pool [n_slots, H, dk, dv].
+ *   state_idx  int32 [N] device array or NULL: sequence n reads and writes
+ *              slot state_idx[n]. A slot outside [0, n_slots) marks a
+ *              padding entry: the pool is left untouched and y[n] = 0. Two
+ *              sequences must not name the same slot (their updates would
+ *              race; the result is unspecified but stays in bounds).
+ *   n_slots    number of states in the pool (>= 0) when state_idx is given.
+ * Every other argument as gdn_decode_step.
+ */
+GDN_API int gdn_decode_step_gated(const void *q, const void *k, const void *v,
+                                  const float *a, const float *b,
+                                  const float *A, const float *b_alpha,
+                                  float *S, const int32_t *state_idx,
+                                  int32_t n_slots, void *y, int32_t N,
+                                  int32_t H, int32_t dk, int32_t dv,
+                                  int32_t in_dtype, int32_t out_dtype,
+                                  void *stream);
+
+/*
  * Front end of the mixer (page "NLP——技术报告解读-Qwen3.8-Flash-Next",
  * section "GDN 参数化细节", first display; the convolution is short and causal
  * per the pwwt.cn page's Fig. 2 caption): for the three projected streams

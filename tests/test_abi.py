@@ -161,3 +161,42 @@ def test_fused_rejects(lib):
     assert call(rms=-1.0) == -1
     assert call(it=9) == -2
     assert lib.gdn_last_error() != b""
+
+
+def test_gated_entry_points_reject(lib):
+    v, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.gdn_chunk_fwd_gated.argtypes = [v] * 11 + [i32] * 7 + [v]
+    lib.gdn_decode_step_gated.argtypes = [v] * 9 + [i32] + [v] + [i32] * 6 + [v]
+
+    def chunk(**kw):
+        a = dict(q=A, k=A + (1 << 26), v=A + (2 << 26), a=A + (3 << 26), b=A + (4 << 26),
+                 Ah=A + (5 << 26), ba=A + (5 << 26) + 256, S0=None, y=B, ST=B + (1 << 28),
+                 cu=None, N=1, T=64, H=2, dk=128, dv=128, it=1, ot=1)
+        a.update(kw)
+        return lib.gdn_chunk_fwd_gated(a["q"], a["k"], a["v"], a["a"], a["b"], a["Ah"], a["ba"],
+                                       a["S0"], a["y"], a["ST"], a["cu"], a["N"], a["T"], a["H"],
+                                       a["dk"], a["dv"], a["it"], a["ot"], None)
+
+    assert chunk(Ah=None) == -1            # A is required
+    assert chunk(Ah=A + (5 << 26) + 2) == -3
+    assert chunk(ba=B + 16) == -1          # b_alpha overlaps y
+    assert chunk(Ah=B + (1 << 28)) == -1   # A overlaps S_T
+    assert chunk(dk=96) == -2
+    assert lib.gdn_last_error() != b""
+
+    def dec(**kw):
+        a = dict(q=A, k=A + 4096, v=A + 8192, a=A + 12288, b=A + 16384, Ah=A + 20480,
+                 ba=None, S=B, idx=A + 24576, ns=8, y=B + (1 << 26), N=4, H=2, dk=128, dv=128)
+        a.update(kw)
+        return lib.gdn_decode_step_gated(a["q"], a["k"], a["v"], a["a"], a["b"], a["Ah"], a["ba"],
+                                         a["S"], a["idx"], a["ns"], a["y"], a["N"], a["H"],
+                                         a["dk"], a["dv"], 1, 1, None)
+
+    assert dec(Ah=None) == -1
+    assert dec(ns=-1) == -1
+    assert dec(idx=B + 64) == -1            # state_idx overlaps the pool
+    assert dec(idx=A + 24578) == -3
+    assert dec(S=None) == -1                # a pool of 8 slots needs S
+    # y past the first N states but inside the 8-slot pool (1 MiB)
+    assert dec(y=B + (768 << 10)) == -1
+    assert dec(dv=100) == -2

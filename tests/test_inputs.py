@@ -31,3 +31,18 @@ def test_decode_inputs_shapes():
     d = gi.decode_inputs(4, 2, 8, 8, steps=3, seed=3)
     assert d["q"].shape == (3, 4, 2, 8) and d["log_alpha"].shape == (3, 4, 2)
     assert d["S0"].shape == (4, 2, 8, 8)
+
+
+def test_raw_gates_are_the_draws_behind_gates():
+    """With b_alpha = 0 the oracle's gate map applied to the raw draws gives
+    the gates that ``gates`` produces (up to its float32 rounding)."""
+    import numpy as np
+
+    import oracle
+
+    la, bt = gi.gates(50, 4, seed=9)
+    a, b, A, b_alpha = gi.raw_gates(50, 4, seed=9)
+    assert b_alpha.shape == (4,) and float(b_alpha.abs().max()) > 0
+    la_o, bt_o = oracle.gates_from_raw(a, b, A, None)
+    assert np.max(np.abs(la.double().numpy() - la_o)) < 1e-5 * max(1.0, np.abs(la_o).max())
+    assert np.max(np.abs(bt.double().numpy() - bt_o)) < 1e-6

@@ -325,3 +325,90 @@ def test_fused_prefill_small(d, dtype):
     eo, es = rel_l2(o.reshape(-1, d), oo), rel_l2(S, So)
     print("rel_l2 o=%.3e S=%.3e" % (eo, es), flush=True)
     assert eo <= 2e-3 and es <= 2e-3, (eo, es)
+
+
+# ------------------------------------------------- gates from raw inputs -----
+def _raw_case(lengths, H, d, dtype, seed):
+    inp = gi.prefill_inputs(len(lengths), H, 0, d, d, dtype, s0_std=0.02, seed=seed,
+                            lengths=lengths)
+    rows = inp["q"].shape[0]
+    a, b, A, b_alpha = gi.raw_gates(rows, H, seed + 1)
+    return inp, a, b, A, b_alpha
+
+
+@gpu
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_chunk_gated(d, dtype, with_bias):
+    g = _lib()
+    lengths = [1, 33, 100, 0, 65]
+    inp, a, b, A, b_alpha = _raw_case(lengths, 3, d, dtype, seed=60 + d)
+    if not with_bias:
+        b_alpha = None
+    dv_ = to_dev(inp)
+    bias_dev = None if b_alpha is None else b_alpha.cuda()
+    y, S = g.gdn_chunk_fwd_gated(dv_["q"], dv_["k"], dv_["v"], a.cuda(), b.cuda(), A.cuda(),
+                                 bias_dev, dv_["S0"], cu_seqlens=dv_["cu_seqlens"],
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    la, bt = oracle.gates_from_raw(a, b, A, b_alpha)
+    yo, So = oracle.gdn_fwd(inp["q"], inp["k"], inp["v"], la, bt, inp["S0"],
+                            cu_seqlens=inp["cu_seqlens"], N=inp["N"])
+    ey, es = rel_l2(_flat(inp, y), yo), rel_l2(S, So)
+    print("gated rel_l2 y=%.3e S=%.3e" % (ey, es), flush=True)
+    assert ey <= TOL[dtype] and es <= TOL[dtype], (ey, es)
+
+
+@gpu
+def test_chunk_gated_matches_precomputed_gates():
+    """The in-kernel gate map and gates precomputed in fp32 by torch drive
+    the same recurrence: the two outputs agree to fp32 rounding."""
+    g = _lib()
+    inp, a, b, A, b_alpha = _raw_case([300, 77], 4, 128, "bf16", seed=70)
+    d = to_dev(inp)
+    la = (-torch.exp(A)[None, :] * torch.nn.functional.softplus(a + b_alpha[None, :])).contiguous()
+    bt = torch.sigmoid(b).contiguous()
+    y1, S1 = g.gdn_chunk_fwd(d["q"], d["k"], d["v"], la.cuda(), bt.cuda(), d["S0"],
+                             cu_seqlens=d["cu_seqlens"], out_dtype=torch.float32)
+    y2, S2 = g.gdn_chunk_fwd_gated(d["q"], d["k"], d["v"], a.cuda(), b.cuda(), A.cuda(),
+                                   b_alpha.cuda(), d["S0"], cu_seqlens=d["cu_seqlens"],
+                                   out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert rel_l2(y2, y1.cpu().double().numpy()) < 1e-4
+    assert rel_l2(S2, S1.cpu().double().numpy()) < 1e-4
+
+
+@gpu
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_gated_state_slots(dtype):
+    """Raw gates plus a slot pool: sequences update their own slots, padding
+    entries leave the pool alone and get y = 0."""
+    g = _lib()
+    N, H, d, n_slots = 6, 3, 128, 9
+    idx = torch.tensor([4, -1, 0, 8, 9, 2], dtype=torch.int32)  # 9 is out of range
+    inp = gi.decode_inputs(N, H, d, d, steps=3, dtype=dtype, s0_std=0.02, seed=81)
+    pool = gi.normal((n_slots, H, d, d), 82, 1, std=0.02)
+    S = pool.clone().cuda()
+    S_or = pool.double().numpy().copy()
+    a, b, A, b_alpha = gi.raw_gates(3 * N, H, 83)
+    a, b = a.reshape(3, N, H), b.reshape(3, N, H)
+    live = [n for n in range(N) if 0 <= int(idx[n]) < n_slots]
+    for t in range(3):
+        q, k, v = (inp[nm][t].contiguous() for nm in ("q", "k", "v"))
+        y = g.gdn_decode_step_gated(q.cuda(), k.cuda(), v.cuda(), a[t].contiguous().cuda(),
+                                    b[t].contiguous().cuda(), A.cuda(), S, b_alpha=b_alpha.cuda(),
+                                    state_idx=idx.cuda(), out_dtype=torch.float32)
+        la, bt = oracle.gates_from_raw(a[t], b[t], A, b_alpha)
+        sl = [int(idx[n]) for n in live]
+        yo, Sn = oracle.decode_step(q[live], k[live], v[live], la[live], bt[live], S_or[sl])
+        S_or[sl] = Sn
+        torch.cuda.synchronize()
+        yc = y.cpu()
+        assert rel_l2(yc[live], yo) <= TOL[dtype]
+        for n in range(N):
+            if n not in live:
+                assert torch.all(yc[n] == 0)
+    untouched = [s for s in range(n_slots) if s not in [int(idx[n]) for n in live]]
+    assert torch.equal(S.cpu()[untouched], pool[untouched])
+    assert rel_l2(S, S_or) <= TOL[dtype]
