@@ -192,6 +192,31 @@ def bench_decode(g, n_steps=128, reps=2):
                                                        "decode.hip")))
 
 
+def bench_decode_multi(g, n_tok=4, calls=32):
+    """The decode workload (256 sequences x 32 heads, 128x128 states) with
+    n_tok tokens per sequence in each call (a speculative verify step of
+    next_n = 4); the state is read and written once per call."""
+    w = gi.WORKLOADS[3]
+    N, H, dk, dv = w.B, w.H, w.dk, w.dv
+    dev = torch.device("cuda", 0)
+    inp = gi.workload_inputs(3, steps=n_tok)
+    tm = {nm: inp[nm].transpose(0, 1).contiguous().to(dev)
+          for nm in ("q", "k", "v", "log_alpha", "beta")}
+    S = inp["S0"].to(dev)
+    y = torch.empty((N, n_tok, H, dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        g.gdn_decode_multi(tm["q"], tm["k"], tm["v"], tm["log_alpha"], tm["beta"], S, y=y)
+
+    us = time_launches(call, calls, 2, stream) * 1e3 / calls
+    nbytes = N * H * (2 * dk * dv * 4 + n_tok * ((2 * dk + 2 * dv) * 2 + 8))
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return dict(workload=w.name, entry_point="gdn_decode_multi", n_tok=n_tok, us_per_call=us,
+                tokens_per_s=N * n_tok / (us * 1e-6), GBps=gbs, frac_hbm=gbs / HBM_PEAK_GBS,
+                bytes_per_call=nbytes)
+
+
 def bench_longctx(g, steps=3, warmup=1):
     """B=1, H=32, T=65536 prefill from a nonzero S0 (fp32 state)."""
     w = gi.WORKLOADS[2]
@@ -343,6 +368,8 @@ def main():
         print("[bench] decode workload 3: 256 x 32 heads, %d steps" % args.decode_steps,
               file=sys.stderr, flush=True)
         rec["decode"] = bench_decode(g, args.decode_steps)
+        print("[bench] decode workload 3 with 4 tokens per call", file=sys.stderr, flush=True)
+        rec["decode_multi"] = bench_decode_multi(g)
 
     if not args.no_extra:
         print("[bench] prefill workload 1 with raw gates", file=sys.stderr, flush=True)

@@ -73,6 +73,9 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_decode_step_gated.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, ip, i32, vp, i32, i32,
                                           i32, i32, i32, i32, vp]
     lib.gdn_decode_step_gated.restype = ctypes.c_int
+    lib.gdn_decode_multi.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, ip, i32, vp, i32, i32, i32,
+                                     i32, i32, i32, i32, vp]
+    lib.gdn_decode_multi.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -260,6 +263,49 @@ def gdn_decode_step_gated(q, k, v, a, b, A, S, b_alpha=None, state_idx=None, out
                                    _p(state_idx), n_slots, _p(y), N, H, dk, dv, _dt(in_dtype),
                                    _dt(out_dtype), _stream(v.device))
     _check(rc, lib, "gdn_decode_step_gated")
+    return y
+
+
+def gdn_decode_multi(q, k, v, g_a, g_b, S, A=None, b_alpha=None, state_idx=None,
+                     out_dtype=None, y=None):
+    """n_tok decode tokens per sequence in one pass over the state.
+    q, k [N, n_tok, H, dk]; v [N, n_tok, H, dv]; g_a, g_b fp32 [N, n_tok, H]
+    (log_alpha and beta, or raw a and b when A [H] is given). S is
+    [N, H, dk, dv] (updated in place), or with state_idx (int32
+    [N, 1 + n_tok]: start slot, then the slot receiving the state after each
+    token) a pool [n_slots, H, dk, dv]. Returns y [N, n_tok, H, dv]."""
+    lib = load_library()
+    in_dtype = q.dtype
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, in_dtype)
+    _need(g_a, "g_a", torch.float32)
+    _need(g_b, "g_b", torch.float32)
+    _need(S, "S", torch.float32)
+    if q.dim() != 4:
+        raise GdnError("q must be [N, n_tok, H, dk]")
+    N, n_tok, H, dk = q.shape
+    dv = v.shape[-1]
+    if A is not None:
+        _head_params(A, b_alpha, H)
+    elif b_alpha is not None:
+        raise GdnError("b_alpha needs A")
+    n_slots = 0
+    if state_idx is not None:
+        _need(state_idx, "state_idx", torch.int32)
+        if tuple(state_idx.shape) != (N, 1 + n_tok):
+            raise GdnError("state_idx must be [N, 1 + n_tok]")
+        n_slots = S.shape[0]
+    elif S.shape[0] != N:
+        raise GdnError("S must be [N, H, dk, dv]")
+    if tuple(S.shape[1:]) != (H, dk, dv):
+        raise GdnError("S must be [slots, H, dk, dv] with H, dk, dv = %s" % ((H, dk, dv),))
+    if y is None:
+        y = torch.empty((N, n_tok, H, dv), dtype=out_dtype, device=v.device)
+    rc = lib.gdn_decode_multi(_p(q), _p(k), _p(v), _p(g_a), _p(g_b), _p(A), _p(b_alpha), _p(S),
+                              _p(state_idx), n_slots, _p(y), N, n_tok, H, dk, dv, _dt(in_dtype),
+                              _dt(out_dtype), _stream(v.device))
+    _check(rc, lib, "gdn_decode_multi")
     return y
 
 

@@ -138,20 +138,25 @@ int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log
   return hip_status(gdn::launch_chunk_fwd(a), where);
 }
 
-// Shared by gdn_decode_step (A and state_idx null) and gdn_decode_step_gated.
+// Shared by every decode entry point. state_idx (may be null) is an int32
+// table [N, idx_cols]: column 0 is the slot each sequence reads; with
+// idx_cols = 1 + n_tok, column 1 + j is the slot the state after token j is
+// written to; with idx_cols = 1 the final state goes back to the read slot.
 int decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                 const float *beta, const float *A, const float *b_alpha, float *S,
-                const int32_t *state_idx, int32_t n_slots, void *y, int32_t N, int32_t H,
-                int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype, void *stream,
-                const char *name) {
+                const int32_t *state_idx, int32_t idx_cols, int32_t n_slots, void *y, int32_t N,
+                int32_t n_tok, int32_t H, int32_t dk, int32_t dv, int32_t in_dtype,
+                int32_t out_dtype, void *stream, const char *name) {
   g_last_error[0] = '\0';
   if (N < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N must be >= 0 and H > 0");
+  if (n_tok < 1 || n_tok > gdn::kDecodeMaxTok)
+    return fail(GDN_ERR_INVALID_ARG, "%s", "n_tok must be in [1, 8]");
   if (!head_size_ok(dk) || !head_size_ok(dv))
     return fail(GDN_ERR_UNSUPPORTED, "%s", "dk and dv must be 64 or 128");
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
     return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32, GDN_BF16 or GDN_F16");
-  if (static_cast<int64_t>(N) * H >= (int64_t{1} << 31))
-    return fail(GDN_ERR_INVALID_ARG, "%s", "N * H too large");
+  if (static_cast<int64_t>(N) * H * n_tok >= (int64_t{1} << 31))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "N * H * n_tok too large");
   if (state_idx && n_slots < 0) return fail(GDN_ERR_INVALID_ARG, "%s", "n_slots must be >= 0");
   if (state_idx && static_cast<int64_t>(n_slots) * H >= (int64_t{1} << 31))
     return fail(GDN_ERR_INVALID_ARG, "%s", "n_slots * H too large");
@@ -163,13 +168,13 @@ int decode_impl(const void *q, const void *k, const void *v, const float *log_al
       misaligned(b_alpha, 4) || misaligned(state_idx, 4))
     return fail(GDN_ERR_MISALIGNED, "%s", "q, k, v, y, S need 16-byte alignment, the rest 4");
   const size_t in_b = esize(in_dtype);
-  const size_t units = static_cast<size_t>(N) * H;
+  const size_t rows = static_cast<size_t>(N) * n_tok * H;
   const size_t ns = static_cast<size_t>(slots) * H * dk * dv * 4;
-  const size_t ny = units * dv * esize(out_dtype);
+  const size_t ny = rows * dv * esize(out_dtype);
   const size_t nh = static_cast<size_t>(H) * 4;
   const void *ins[8] = {q, k, v, log_alpha, beta, A, A ? b_alpha : nullptr, state_idx};
-  const size_t in_n[8] = {units * dk * in_b, units * dk * in_b, units * dv * in_b, units * 4,
-                          units * 4, nh, nh, static_cast<size_t>(N) * 4};
+  const size_t in_n[8] = {rows * dk * in_b, rows * dk * in_b, rows * dv * in_b, rows * 4,
+                          rows * 4, nh, nh, static_cast<size_t>(N) * idx_cols * 4};
   for (int i = 0; i < 8; ++i) {
     if (overlap(ins[i], in_n[i], S, ns) || overlap(ins[i], in_n[i], y, ny))
       return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps an output");
@@ -185,10 +190,14 @@ int decode_impl(const void *q, const void *k, const void *v, const float *log_al
   a.A = A;
   a.b_alpha = A ? b_alpha : nullptr;
   a.S = S;
-  a.state_idx = state_idx;
-  a.n_slots = state_idx ? n_slots : N;
+  a.read_idx = state_idx;
+  a.r_stride = idx_cols;
+  a.write_idx = (state_idx && idx_cols > 1) ? state_idx + 1 : nullptr;
+  a.w_stride = idx_cols;
+  a.n_slots = static_cast<int>(slots);
   a.y = y;
   a.N = N;
+  a.n_tok = n_tok;
   a.H = H;
   a.dk = dk;
   a.dv = dv;
@@ -228,8 +237,8 @@ GDN_API int gdn_decode_step(const void *q, const void *k, const void *v, const f
                             const float *beta, float *S, void *y, int32_t N, int32_t H,
                             int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype,
                             void *stream) {
-  return decode_impl(q, k, v, log_alpha, beta, nullptr, nullptr, S, nullptr, 0, y, N, H, dk, dv,
-                     in_dtype, out_dtype, stream, "gdn_decode_step");
+  return decode_impl(q, k, v, log_alpha, beta, nullptr, nullptr, S, nullptr, 1, 0, y, N, 1, H,
+                     dk, dv, in_dtype, out_dtype, stream, "gdn_decode_step");
 }
 
 GDN_API int gdn_decode_step_gated(const void *q, const void *k, const void *v, const float *a,
@@ -239,8 +248,17 @@ GDN_API int gdn_decode_step_gated(const void *q, const void *k, const void *v, c
                                   int32_t in_dtype, int32_t out_dtype, void *stream) {
   g_last_error[0] = '\0';
   if (H > 0 && !A) return fail(GDN_ERR_INVALID_ARG, "%s", "A is required");
-  return decode_impl(q, k, v, a, b, A, b_alpha, S, state_idx, n_slots, y, N, H, dk, dv,
+  return decode_impl(q, k, v, a, b, A, b_alpha, S, state_idx, 1, n_slots, y, N, 1, H, dk, dv,
                      in_dtype, out_dtype, stream, "gdn_decode_step_gated");
+}
+
+GDN_API int gdn_decode_multi(const void *q, const void *k, const void *v, const float *g_a,
+                             const float *g_b, const float *A, const float *b_alpha, float *S,
+                             const int32_t *state_idx, int32_t n_slots, void *y, int32_t N,
+                             int32_t n_tok, int32_t H, int32_t dk, int32_t dv, int32_t in_dtype,
+                             int32_t out_dtype, void *stream) {
+  return decode_impl(q, k, v, g_a, g_b, A, b_alpha, S, state_idx, 1 + n_tok, n_slots, y, N,
+                     n_tok, H, dk, dv, in_dtype, out_dtype, stream, "gdn_decode_multi");
 }
 
 GDN_API int gdn_frontend_qkv(const void *q_raw, const void *k_raw, const void *v_raw,

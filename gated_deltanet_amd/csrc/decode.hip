@@ -1,34 +1,40 @@
-// Single-token decode step of the gated delta rule (gfx950).
+// Decode steps of the gated delta rule (gfx950).
 //
-// One token per (sequence, head) updates the fixed-size fp32 state in place
-// (page "NLP——技术报告解读-Qwen3.8-Flash-Next", section "Gated DeltaNet 核心机制"):
+// Each token updates the fixed-size fp32 state of its (sequence, head) in
+// place (page "NLP——技术报告解读-Qwen3.8-Flash-Next", section "Gated DeltaNet
+// 核心机制"):
 //     S~ = alpha S;  e = v - S~^T k;  S = S~ + beta k e^T;  y = S^T q.
 // Per column j of S this needs the two dot products s_j.k and s_j.q over the
 // key dimension, so
 //     e_j = v_j - alpha (s_j.k),    y_j = alpha (s_j.q) + beta (k.q) e_j,
 //     s_j <- alpha s_j + beta e_j k.
-// The step is a pure HBM stream: the state (64 KiB per (sequence, head) at
-// dk = dv = 128) is read once and written once; everything else is ~1% of
-// the bytes. One 256-thread workgroup owns one (sequence, head): each thread
-// keeps DK*DV/256 state values in registers (16-byte accesses, 4 adjacent
-// columns), so the read-modify-write never round-trips through LDS; only the
-// per-column partial dot products are reduced across row groups.
+// A call applies n_tok (1..kDecodeMaxTok) consecutive tokens per (sequence,
+// head), e.g. a speculative-decoding verify step. The work is a pure HBM
+// stream: the state (64 KiB per (sequence, head) at dk = dv = 128) is read
+// once and written once per call, however many tokens it applies; the token
+// inputs are ~1% of the bytes. One 256-thread workgroup owns one (sequence,
+// head): each thread keeps DK*DV/256 state values in registers (16-byte
+// accesses, 4 adjacent columns), so the state never round-trips through LDS
+// between tokens; only the per-column partial dot products are reduced
+// across row groups, one barrier per token.
 //
 // Gates arrive either as log alpha and beta or as raw pre-activations that
 // are turned into gates here (RawGate). For serving, the states may live in
-// a pool of slots: sequence n then updates slot state_idx[n], and a sequence
-// whose slot is out of range leaves the pool untouched and gets y = 0.
+// a pool of slots (see DecodeArgs): a sequence reads one slot, and writes
+// its final state back there or, for speculative verification, the state
+// after each token into a slot of its own.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
 template <int DK, int DV, typename TIN, typename TOUT>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+__global__ __launch_bounds__(256) void decode_kernel(
     const TIN *__restrict__ q, const TIN *__restrict__ k, const TIN *__restrict__ v,
-    const float *__restrict__ log_alpha, const float *__restrict__ beta,
-    const float *__restrict__ gA, const float *__restrict__ gbias, float *__restrict__ S,
-    const int32_t *__restrict__ state_idx, int n_slots, TOUT *__restrict__ y, int H) {
+    const float *__restrict__ ga, const float *__restrict__ gb, const float *__restrict__ gA,
+    const float *__restrict__ gbias, float *__restrict__ S, const int32_t *__restrict__ read_idx,
+    int r_stride, const int32_t *__restrict__ write_idx, int w_stride, int n_slots,
+    TOUT *__restrict__ y, int H, int n_tok) {
   constexpr int NT = 256;
   constexpr int CG = DV / 4;   // column groups of 4 adjacent columns
   constexpr int RG = NT / CG;  // row groups
@@ -37,126 +43,176 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   constexpr int NWAVE = NT / 64;
   static_assert(DK % RG == 0 && RG_PER_WAVE >= 1, "shape");
 
-  __shared__ float sq[DK];
-  __shared__ float sk[DK];
-  __shared__ float red[NWAVE][CG][9];
+  __shared__ float sq[kDecodeMaxTok][DK];
+  __shared__ float sk[kDecodeMaxTok][DK];
+  __shared__ float sv[kDecodeMaxTok][DV];
+  __shared__ float s_alpha[kDecodeMaxTok], s_beta[kDecodeMaxTok];
+  __shared__ float red[2][NWAVE][CG][9];
 
   const int unit = blockIdx.x;  // n * H + h
+  const int n = unit / H;
+  const int h = unit - n * H;
   const int tid = threadIdx.x;
   const int cg = tid % CG;
   const int rg = tid / CG;
   const int wave = tid / 64;
 
-  int64_t slot_unit = unit;
-  if (state_idx) {
-    const int n = unit / H;
-    const int slot = state_idx[n];
+  int slot = n;
+  if (read_idx) {
+    slot = read_idx[static_cast<int64_t>(n) * r_stride];
     if (slot < 0 || slot >= n_slots) {
       // padding entry: no state to update; y = 0
-      const size_t y_off = static_cast<size_t>(unit) * DV;
-      for (int j = tid; j < DV; j += NT) y[y_off + j] = io<TOUT>::from_f32(0.0f);
+      for (int idx = tid; idx < n_tok * DV; idx += NT) {
+        const size_t row = static_cast<size_t>(n) * n_tok + idx / DV;
+        y[(row * H + h) * DV + idx % DV] = io<TOUT>::from_f32(0.0f);
+      }
       return;
     }
-    slot_unit = static_cast<int64_t>(slot) * H + (unit - n * H);
   }
-  float *Su = S + static_cast<size_t>(slot_unit) * DK * DV;
+  // State accesses go through a buffer resource per (slot, head): one lane
+  // offset register and a scalar offset per row step, instead of a 64-bit
+  // address per access. aux = 2 marks them non-temporal (streamed once).
+  auto state_rsrc = [&](int64_t sl) {
+    return __builtin_amdgcn_make_buffer_rsrc(S + (static_cast<size_t>(sl) * H + h) * DK * DV, 0,
+                                             DK * DV * 4, 0x00020000);
+  };
+  const int s_lane = (rg * DV + 4 * cg) * 4;
+  constexpr int kRowStep = RG * DV * 4;
+  const auto Sr = state_rsrc(slot);
 
   // issue every state load first: they are the whole cost of the kernel
   f32x4 s[RPT];
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int i = rg + RG * m;
-    s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Su + i * DV + 4 * cg));
-  }
+  for (int m = 0; m < RPT; ++m)
+    s[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(Sr, s_lane,
+                                                                           m * kRowStep, 2));
 
-  const size_t qk_off = static_cast<size_t>(unit) * DK;
-  for (int i = tid; i < DK; i += NT) {
-    sq[i] = io<TIN>::to_f32(q[qk_off + i]);
-    sk[i] = io<TIN>::to_f32(k[qk_off + i]);
+  // every token's q, k, v and gates into LDS, one 16-byte load per thread
+  // and tensor. All loads are issued before the first one is waited for,
+  // so their latencies overlap the state's. Nothing here branches (a branch
+  // would make the compiler wait inside it): lanes past the last piece are
+  // clamped to it and store the same values again.
+  constexpr int VEC = io<TIN>::kVec;
+  static_assert(kDecodeMaxTok * DK / VEC <= NT && kDecodeMaxTok * DV / VEC <= NT, "lanes");
+  const size_t row0 = static_cast<size_t>(n) * n_tok;
+  const int pk = min(tid, n_tok * (DK / VEC) - 1);  // piece of q / k
+  const int pv = min(tid, n_tok * (DV / VEC) - 1);  // piece of v
+  const int jk = pk / (DK / VEC), ck = (pk % (DK / VEC)) * VEC;
+  const int jv = pv / (DV / VEC), cv = (pv % (DV / VEC)) * VEC;
+  float qf[VEC], kf[VEC], vf[VEC];
+  io<TIN>::load16(q + ((row0 + jk) * H + h) * DK + ck, qf);
+  io<TIN>::load16(k + ((row0 + jk) * H + h) * DK + ck, kf);
+  io<TIN>::load16(v + ((row0 + jv) * H + h) * DV + cv, vf);
+  const int gj = min(tid, n_tok - 1);
+  const size_t gi = (row0 + gj) * H + h;
+  float la = ga[gi];
+  float bt = gb[gi];
+  const RawGate gate = RawGate::load(gA, gbias, h);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    sq[jk][ck + e] = qf[e];
+    sk[jk][ck + e] = kf[e];
+    sv[jv][cv + e] = vf[e];
   }
-  const RawGate rg_h = RawGate::load(gA, gbias, unit % H);
-  float la = log_alpha[unit];
-  float b = beta[unit];
-  if (rg_h.raw()) {
-    la = rg_h.log_alpha(la);
-    b = RawGate::beta(b);
+  if (gate.raw()) {
+    la = gate.log_alpha(la);
+    bt = RawGate::beta(bt);
   }
-  const float alpha = __expf(la);
+  s_alpha[gj] = __expf(la);
+  s_beta[gj] = bt;
   __syncthreads();
 
-  // partial dot products over this thread's rows: s_j.k, s_j.q (4 columns)
-  // and k.q (the same for every column group)
-  float p[9];
+  auto token = [&](const int j) __attribute__((always_inline)) {
+    // partial dot products over this thread's rows: s_j.k, s_j.q (4 columns)
+    // and k.q (the same for every column group)
+    float p[9];
 #pragma unroll
-  for (int c = 0; c < 9; ++c) p[c] = 0.0f;
+    for (int c = 0; c < 9; ++c) p[c] = 0.0f;
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int i = rg + RG * m;
-    const float ki = sk[i];
-    const float qi = sq[i];
+    for (int m = 0; m < RPT; ++m) {
+      const int i = rg + RG * m;
+      const float ki = sk[j][i];
+      const float qi = sq[j][i];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      p[c] = fmaf(s[m][c], ki, p[c]);
-      p[4 + c] = fmaf(s[m][c], qi, p[4 + c]);
+      for (int c = 0; c < 4; ++c) {
+        p[c] = fmaf(s[m][c], ki, p[c]);
+        p[4 + c] = fmaf(s[m][c], qi, p[4 + c]);
+      }
+      p[8] = fmaf(ki, qi, p[8]);
     }
-    p[8] = fmaf(ki, qi, p[8]);
-  }
-  // reduce over the row groups inside the wave (lanes that differ by CG)
+    // reduce over the row groups inside the wave (lanes that differ by CG)
 #pragma unroll
-  for (int off = CG; off < 64; off <<= 1) {
+    for (int off = CG; off < 64; off <<= 1) {
 #pragma unroll
-    for (int c = 0; c < 9; ++c) p[c] += __shfl_xor(p[c], off, 64);
-  }
-  if ((tid % 64) < CG) {
+      for (int c = 0; c < 9; ++c) p[c] += __shfl_xor(p[c], off, 64);
+    }
+    // red is double-buffered by token parity: buffer j & 1 was last read
+    // before the previous token's barrier, which every thread has passed
+    if ((tid % 64) < CG) {
 #pragma unroll
-    for (int c = 0; c < 9; ++c) red[wave][cg][c] = p[c];
-  }
-  __syncthreads();
-  float tot[9];
+      for (int c = 0; c < 9; ++c) red[j & 1][wave][cg][c] = p[c];
+    }
+    __syncthreads();
+    float tot[9];
 #pragma unroll
-  for (int c = 0; c < 9; ++c) {
-    float acc = 0.0f;
+    for (int c = 0; c < 9; ++c) {
+      float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NWAVE; ++w) acc += red[w][cg][c];
-    tot[c] = acc;
-  }
+      for (int w = 0; w < NWAVE; ++w) acc += red[j & 1][w][cg][c];
+      tot[c] = acc;
+    }
 
-  const size_t v_off = static_cast<size_t>(unit) * DV + 4 * cg;
-  float e[4];
+    const float alpha = s_alpha[j];
+    const float b = s_beta[j];
+    float e[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float vj = io<TIN>::to_f32(v[v_off + c]);
-    e[c] = vj - alpha * tot[c];
-  }
-  if (rg == 0) {
+    for (int c = 0; c < 4; ++c) e[c] = sv[j][4 * cg + c] - alpha * tot[c];
+    if (rg == 0) {
+      // the 4 adjacent outputs of this column group in one store
+      struct alignas(4 * sizeof(TOUT)) Y4 { TOUT v[4]; } yv;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float yj = alpha * tot[4 + c] + b * tot[8] * e[c];
-      y[v_off + c] = io<TOUT>::from_f32(yj);
+      for (int c = 0; c < 4; ++c) yv.v[c] = io<TOUT>::from_f32(alpha * tot[4 + c] + b * tot[8] * e[c]);
+      *reinterpret_cast<Y4 *>(y + ((row0 + j) * H + h) * DV + 4 * cg) = yv;
     }
-  }
-  float be[4];
+    float be[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) be[c] = b * e[c];
+    for (int c = 0; c < 4; ++c) be[c] = b * e[c];
+    // where the state after this token goes, if anywhere; each row is
+    // stored as soon as it is updated, so the stores drain while the rest
+    // of the update still runs
+    bool store = !write_idx && j == n_tok - 1;
+    int dst = slot;
+    if (write_idx) {
+      dst = write_idx[static_cast<int64_t>(n) * w_stride + j];
+      store = dst >= 0 && dst < n_slots;
+    }
+    const auto Sw = state_rsrc(store ? dst : slot);
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int i = rg + RG * m;
-    const float ki = sk[i];
-    f32x4 o;
+    for (int m = 0; m < RPT; ++m) {
+      const float ki = sk[j][rg + RG * m];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) o[c] = fmaf(alpha, s[m][c], be[c] * ki);
-    __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(Su + i * DV + 4 * cg));
-  }
+      for (int c = 0; c < 4; ++c) s[m][c] = fmaf(alpha, s[m][c], be[c] * ki);
+      if (store)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), Sw, s_lane,
+                                               m * kRowStep, 2);
+    }
+  };
+  // token 0 is peeled off the loop: entering the loop with the freshly
+  // loaded state made the compiler copy all of it into separate
+  // loop-carried registers, which costs occupancy
+  token(0);
+  for (int j = 1; j < n_tok; ++j) token(j);
 }
 
 template <int DK, int DV, typename TIN, typename TOUT>
 static hipError_t launch(const DecodeArgs &a) {
   const int units = a.N * a.H;
-  if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_step_kernel<DK, DV, TIN, TOUT>), dim3(units), dim3(256), 0,
-                     a.stream, static_cast<const TIN *>(a.q), static_cast<const TIN *>(a.k),
+  if (units == 0 || a.n_tok <= 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_kernel<DK, DV, TIN, TOUT>), dim3(units), dim3(256), 0, a.stream,
+                     static_cast<const TIN *>(a.q), static_cast<const TIN *>(a.k),
                      static_cast<const TIN *>(a.v), a.log_alpha, a.beta, a.A, a.b_alpha, a.S,
-                     a.state_idx, a.n_slots, static_cast<TOUT *>(a.y), a.H);
+                     a.read_idx, a.r_stride, a.write_idx, a.w_stride, a.n_slots,
+                     static_cast<TOUT *>(a.y), a.H, a.n_tok);
   return hipGetLastError();
 }
 
@@ -178,6 +234,7 @@ static hipError_t launch_d_out(const DecodeArgs &a) {
 }
 
 hipError_t launch_decode_step(const DecodeArgs &a) {
+  if (a.n_tok < 1 || a.n_tok > kDecodeMaxTok) return hipErrorInvalidValue;
   switch (a.in_dtype) {
     case 1: return launch_d_out<bf16_t>(a);
     case 2: return launch_d_out<_Float16>(a);

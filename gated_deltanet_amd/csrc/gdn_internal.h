@@ -10,20 +10,33 @@ namespace gdn {
 // Gate inputs: when A is null, log_alpha and beta hold log alpha and beta;
 // otherwise they hold the raw pre-activations a and b, turned into gates
 // in-kernel with the per-head A and b_alpha (b_alpha may be null: zero).
+//
+// Decode: n_tok tokens per (sequence, head), applied in order. Token inputs
+// are [N, n_tok, H, d]. State slots: sequence n reads slot
+// read_idx[n * r_stride] (read_idx null: slot n). write_idx null: the final
+// state goes back to the slot it came from; otherwise the state after token
+// j goes to slot write_idx[n * w_stride + j] when that is in [0, n_slots)
+// and is not written elsewhere. A read slot outside [0, n_slots) marks a
+// padding entry: nothing is written but y = 0.
 struct DecodeArgs {
   const void *q, *k, *v;
   const float *log_alpha, *beta;
   const float *A = nullptr, *b_alpha = nullptr;
   float *S;
-  // state slots: null = S holds [N, H, dk, dv]; otherwise sequence n uses
-  // slot state_idx[n] of a pool of n_slots states (out of range: skipped)
-  const int32_t *state_idx = nullptr;
+  const int32_t *read_idx = nullptr;
+  int r_stride = 1;
+  const int32_t *write_idx = nullptr;
+  int w_stride = 1;
   int n_slots = 0;
   void *y;
   int N, H, dk, dv;
+  int n_tok = 1;
   int in_dtype, out_dtype;  // 0 = f32, 1 = bf16, 2 = f16
   hipStream_t stream;
 };
+
+// most tokens one decode call applies per (sequence, head)
+constexpr int kDecodeMaxTok = 8;
 
 struct ChunkArgs {
   const void *q, *k, *v;

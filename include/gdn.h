@@ -168,6 +168,41 @@ GDN_API int gdn_decode_step_gated(const void *q, const void *k, const void *v,
                                   void *stream);
 
 /*
+ * Multi-token decode: applies n_tok consecutive tokens (1 <= n_tok <= 8) of
+ * every sequence to its state in one pass over the state, e.g. the verify
+ * step of speculative decoding with several drafted tokens. The result
+ * equals n_tok calls of gdn_decode_step; the state is read and written once
+ * instead of n_tok times.
+ *
+ *   q, k       [N, n_tok, H, dk]; v, y [N, n_tok, H, dv] (token-major within
+ *              each sequence).
+ *   g_a, g_b   float32 [N, n_tok, H]: log_alpha and beta when A is NULL,
+ *              otherwise the raw pre-activations a and b of the gate map
+ *              above (A [H], b_alpha [H] or NULL).
+ *   S          float32 states, updated in place.
+ *   state_idx  NULL: S is [N, H, dk, dv] and each sequence's final state is
+ *              written back in place (n_slots ignored). Otherwise an int32
+ *              device table [N, 1 + n_tok] over a pool S [n_slots, H, dk,
+ *              dv]: column 0 is the slot the sequence starts from, column
+ *              1 + j the slot that receives the state after token j (a value
+ *              outside [0, n_slots) skips that write). Writing each
+ *              intermediate state lets a caller roll back to any accepted
+ *              prefix. A start slot outside [0, n_slots) marks a padding
+ *              entry: nothing is written and its y rows are zero. Slots
+ *              written by one sequence must not be read or written by
+ *              another in the same call.
+ * Alignment and aliasing rules as gdn_decode_step; the index table is
+ * 4-byte aligned.
+ */
+GDN_API int gdn_decode_multi(const void *q, const void *k, const void *v,
+                             const float *g_a, const float *g_b,
+                             const float *A, const float *b_alpha, float *S,
+                             const int32_t *state_idx, int32_t n_slots,
+                             void *y, int32_t N, int32_t n_tok, int32_t H,
+                             int32_t dk, int32_t dv, int32_t in_dtype,
+                             int32_t out_dtype, void *stream);
+
+/*
  * Front end of the mixer (page "NLP——技术报告解读-Qwen3.8-Flash-Next",
  * section "GDN 参数化细节", first display; the convolution is short and causal
  * per the pwwt.cn page's Fig. 2 caption): for the three projected streams

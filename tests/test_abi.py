@@ -200,3 +200,26 @@ def test_gated_entry_points_reject(lib):
     # y past the first N states but inside the 8-slot pool (1 MiB)
     assert dec(y=B + (768 << 10)) == -1
     assert dec(dv=100) == -2
+
+
+def test_decode_multi_rejects(lib):
+    v, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.gdn_decode_multi.argtypes = [v] * 9 + [i32] + [v] + [i32] * 7 + [v]
+
+    def dec(**kw):
+        a = dict(q=A, k=A + (1 << 20), v=A + (2 << 20), a=A + (3 << 20), b=A + (4 << 20),
+                 Ah=None, ba=None, S=B, idx=None, ns=0, y=B + (1 << 26), N=4, nt=4, H=2, dk=128,
+                 dv=128)
+        a.update(kw)
+        return lib.gdn_decode_multi(a["q"], a["k"], a["v"], a["a"], a["b"], a["Ah"], a["ba"],
+                                    a["S"], a["idx"], a["ns"], a["y"], a["N"], a["nt"], a["H"],
+                                    a["dk"], a["dv"], 1, 1, None)
+
+    assert dec(nt=0) == -1
+    assert dec(nt=9) == -1
+    assert dec(y=B + 4096) == -1            # y overlaps the states
+    # y rows of 4 tokens: 4*4*2*128*2 bytes = 8 KiB; q at y + 4 KiB overlaps
+    assert dec(q=B + (1 << 26) + 4096) == -1
+    # the index table [N, 1 + n_tok] = 80 bytes must not overlap the pool
+    assert dec(idx=B + 64, ns=4) == -1
+    assert dec(dk=32) == -2

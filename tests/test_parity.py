@@ -412,3 +412,96 @@ def test_decode_gated_state_slots(dtype):
     untouched = [s for s in range(n_slots) if s not in [int(idx[n]) for n in live]]
     assert torch.equal(S.cpu()[untouched], pool[untouched])
     assert rel_l2(S, S_or) <= TOL[dtype]
+
+
+# ------------------------------------------------- multi-token decode -----
+def _multi_inputs(N, H, dk, dv, n_tok, dtype, seed):
+    inp = gi.decode_inputs(N, H, dk, dv, steps=n_tok, dtype=dtype, s0_std=0.02, seed=seed)
+    tm = {nm: inp[nm].transpose(0, 1).contiguous() for nm in ("q", "k", "v", "log_alpha",
+                                                                "beta")}
+    return inp, tm  # inp: [n_tok, N, ...] per step; tm: [N, n_tok, ...]
+
+
+@gpu
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 128), (128, 128)])
+@pytest.mark.parametrize("n_tok", [1, 2, 4, 8])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_multi_matches_steps_and_oracle(dk, dv, n_tok, dtype):
+    """n_tok tokens in one call equal n_tok single-token calls bit for bit
+    (the same arithmetic in the same order) and the oracle to the bar."""
+    g = _lib()
+    N, H = 5, 3
+    inp, tm = _multi_inputs(N, H, dk, dv, n_tok, dtype, seed=dk + dv + n_tok)
+    S1 = inp["S0"].clone().cuda()
+    y1 = g.gdn_decode_multi(*(tm[nm].cuda() for nm in ("q", "k", "v", "log_alpha", "beta")), S1,
+                            out_dtype=torch.float32)
+    S2 = inp["S0"].clone().cuda()
+    y2 = [g.gdn_decode_step(*(inp[nm][t].contiguous().cuda() for nm in
+                              ("q", "k", "v", "log_alpha", "beta")), S2, out_dtype=torch.float32)
+          for t in range(n_tok)]
+    torch.cuda.synchronize()
+    assert torch.equal(y1, torch.stack(y2, 1))
+    assert torch.equal(S1, S2)
+    S_or = inp["S0"].double().numpy()
+    yo = []
+    for t in range(n_tok):
+        y_t, S_or = oracle.decode_step(*(inp[nm][t] for nm in ("q", "k", "v", "log_alpha",
+                                                                "beta")), S_or)
+        yo.append(y_t)
+    assert rel_l2(y1, np.stack(yo, 1)) <= TOL[dtype]
+    assert rel_l2(S1, S_or) <= TOL[dtype]
+
+
+@gpu
+@pytest.mark.parametrize("raw", [False, True])
+def test_decode_multi_slots_and_rollback_states(raw):
+    """Slot table [N, 1 + n_tok]: each sequence starts from its slot and
+    leaves the state after chosen tokens in chosen slots (for rolling back to
+    an accepted prefix); padding entries write nothing and get y = 0."""
+    g = _lib()
+    N, H, d, n_tok, n_slots = 4, 2, 128, 4, 20
+    inp, tm = _multi_inputs(N, H, d, d, n_tok, "bf16", seed=91)
+    pool = gi.normal((n_slots, H, d, d), 92, 1, std=0.02)
+    table = torch.tensor([[3, 10, 11, 12, 3],     # every intermediate, final back in place
+                          [-1, 13, 14, 15, 16],   # padding: nothing written
+                          [7, -1, -1, -1, 17],    # only the final state, elsewhere
+                          [0, 18, -1, 19, -1]],   # two intermediates, final dropped
+                         dtype=torch.int32)
+    if raw:
+        a, b, A, b_alpha = gi.raw_gates(N * n_tok, H, 93)
+        ga, gb = a.reshape(N, n_tok, H), b.reshape(N, n_tok, H)
+        la_o, bt_o = oracle.gates_from_raw(a, b, A, b_alpha)
+        la_o, bt_o = la_o.reshape(N, n_tok, H), bt_o.reshape(N, n_tok, H)
+        kw = dict(A=A.cuda(), b_alpha=b_alpha.cuda())
+    else:
+        ga, gb = tm["log_alpha"], tm["beta"]
+        la_o, bt_o = ga.double().numpy(), gb.double().numpy()
+        kw = {}
+    S = pool.clone().cuda()
+    y = g.gdn_decode_multi(tm["q"].cuda(), tm["k"].cuda(), tm["v"].cuda(), ga.contiguous().cuda(),
+                           gb.contiguous().cuda(), S, state_idx=table.cuda(),
+                           out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    Sc, yc = S.cpu(), y.cpu()
+    expect = pool.double().numpy().copy()
+    written = set()
+    for n in range(N):
+        start = int(table[n, 0])
+        if not 0 <= start < n_slots:
+            assert torch.all(yc[n] == 0)
+            continue
+        st = pool[start].double().numpy()[None]
+        for t in range(n_tok):
+            y_t, st = oracle.decode_step(tm["q"][n, t][None], tm["k"][n, t][None],
+                                         tm["v"][n, t][None], la_o[n, t][None], bt_o[n, t][None],
+                                         st)
+            assert rel_l2(yc[n, t][None], y_t) <= 2e-3
+            w = int(table[n, 1 + t])
+            if 0 <= w < n_slots:
+                expect[w] = st[0]
+                written.add(w)
+    for sl in range(n_slots):
+        if sl in written:
+            assert rel_l2(Sc[sl], expect[sl]) <= 2e-3, sl
+        else:
+            assert torch.equal(Sc[sl], pool[sl]), sl
