@@ -217,6 +217,30 @@ def bench_decode_multi(g, n_tok=4, calls=32):
                 bytes_per_call=nbytes)
 
 
+def bench_decode_fused(g, n_tok=4, calls=32):
+    """The decode workload through gdn_decode_fused: front end with the
+    convolution cache, n_tok recurrence steps and the output gate in one
+    kernel, from raw projections to o."""
+    w = gi.WORKLOADS[3]
+    N, H, d = w.B, w.H, w.dk
+    dev = torch.device("cuda", 0)
+    f = gi.decode_fused_inputs(N, n_tok, H, d, "bf16", seed=12)
+    t = {k: v.to(dev) for k, v in f.items() if isinstance(v, torch.Tensor)}
+    o = torch.empty((N, n_tok, H, d), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        g.gdn_decode_fused(t["q_raw"], t["k_raw"], t["v_raw"], t["conv_w"], t["conv_state"],
+                           t["log_alpha"], t["beta"], t["S0"], t["z"], norm_w=t["norm_w"], o=o)
+
+    us = time_launches(call, calls, 2, stream) * 1e3 / calls
+    nbytes = N * H * (2 * d * d * 4 + 2 * 9 * d * 2 + n_tok * (5 * d * 2 + 8))
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return dict(workload=w.name, entry_point="gdn_decode_fused", n_tok=n_tok, us_per_call=us,
+                tokens_per_s=N * n_tok / (us * 1e-6), GBps=gbs, frac_hbm=gbs / HBM_PEAK_GBS,
+                bytes_per_call=nbytes)
+
+
 def bench_longctx(g, steps=3, warmup=1):
     """B=1, H=32, T=65536 prefill from a nonzero S0 (fp32 state)."""
     w = gi.WORKLOADS[2]
@@ -370,6 +394,8 @@ def main():
         rec["decode"] = bench_decode(g, args.decode_steps)
         print("[bench] decode workload 3 with 4 tokens per call", file=sys.stderr, flush=True)
         rec["decode_multi"] = bench_decode_multi(g)
+        print("[bench] fused serving decode, 4 tokens per call", file=sys.stderr, flush=True)
+        rec["decode_fused"] = bench_decode_fused(g)
 
     if not args.no_extra:
         print("[bench] prefill workload 1 with raw gates", file=sys.stderr, flush=True)

@@ -76,6 +76,9 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_decode_multi.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, ip, i32, vp, i32, i32, i32,
                                      i32, i32, i32, i32, vp]
     lib.gdn_decode_multi.restype = ctypes.c_int
+    lib.gdn_decode_fused.argtypes = [vp, vp, vp, fp, vp, fp, fp, fp, fp, fp, ip, i32, vp, fp, f32,
+                                     f32, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.gdn_decode_fused.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -307,6 +310,56 @@ def gdn_decode_multi(q, k, v, g_a, g_b, S, A=None, b_alpha=None, state_idx=None,
                               _dt(out_dtype), _stream(v.device))
     _check(rc, lib, "gdn_decode_multi")
     return y
+
+
+def gdn_decode_fused(q_raw, k_raw, v_raw, conv_w, conv_state, g_a, g_b, S, z, A=None,
+                     b_alpha=None, state_idx=None, norm_w=None, l2_eps=1e-6, rms_eps=1e-6,
+                     out_dtype=None, o=None):
+    """Serving decode of the whole mixer: front end with a convolution cache,
+    n_tok recurrence steps and the output gate in one kernel.
+    q_raw, k_raw, v_raw, z [N, n_tok, H, d]; conv_w fp32 [3, H*d, 4];
+    conv_state [slots, H, 3, 3, d] in the input dtype (the three previous raw
+    rows of q, k, v, oldest first) and S fp32 [slots, H, d, d], both updated
+    in place (slots = N without state_idx); g_a, g_b fp32 [N, n_tok, H] (log
+    alpha and beta, or raw a and b when A is given); state_idx int32
+    [N, 1 + n_tok] as for gdn_decode_multi. Returns o [N, n_tok, H, d]."""
+    lib = load_library()
+    in_dtype = q_raw.dtype
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    for t, nm in ((q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw"), (z, "z"),
+                  (conv_state, "conv_state")):
+        _need(t, nm, in_dtype)
+    _need(conv_w, "conv_w", torch.float32)
+    _need(g_a, "g_a", torch.float32)
+    _need(g_b, "g_b", torch.float32)
+    _need(S, "S", torch.float32)
+    if q_raw.dim() != 4:
+        raise GdnError("q_raw must be [N, n_tok, H, d]")
+    N, n_tok, H, d = q_raw.shape
+    if A is not None:
+        _head_params(A, b_alpha, H)
+    elif b_alpha is not None:
+        raise GdnError("b_alpha needs A")
+    if norm_w is not None:
+        _need(norm_w, "norm_w", torch.float32)
+    n_slots = 0
+    if state_idx is not None:
+        _need(state_idx, "state_idx", torch.int32)
+        if tuple(state_idx.shape) != (N, 1 + n_tok):
+            raise GdnError("state_idx must be [N, 1 + n_tok]")
+        n_slots = S.shape[0]
+    elif S.shape[0] != N:
+        raise GdnError("S must be [N, H, d, d]")
+    if tuple(S.shape[1:]) != (H, d, d) or tuple(conv_state.shape) != (S.shape[0], H, 3, 3, d):
+        raise GdnError("S must be [slots, H, d, d] and conv_state [slots, H, 3, 3, d]")
+    if o is None:
+        o = torch.empty((N, n_tok, H, d), dtype=out_dtype, device=q_raw.device)
+    rc = lib.gdn_decode_fused(_p(q_raw), _p(k_raw), _p(v_raw), _p(conv_w), _p(conv_state),
+                              _p(g_a), _p(g_b), _p(A), _p(b_alpha), _p(S), _p(state_idx), n_slots,
+                              _p(z), _p(norm_w), float(l2_eps), float(rms_eps), _p(o), N, n_tok,
+                              H, d, _dt(in_dtype), _dt(out_dtype), _stream(q_raw.device))
+    _check(rc, lib, "gdn_decode_fused")
+    return o
 
 
 def gdn_frontend_qkv(q_raw, k_raw, v_raw, conv_w, cu_seqlens=None, N=None, l2_eps=1e-6,

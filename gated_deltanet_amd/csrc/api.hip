@@ -142,11 +142,21 @@ int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log
 // table [N, idx_cols]: column 0 is the slot each sequence reads; with
 // idx_cols = 1 + n_tok, column 1 + j is the slot the state after token j is
 // written to; with idx_cols = 1 the final state goes back to the read slot.
+// front end and output gate of the fused decode
+struct DecodeFusion {
+  const float *conv_w;
+  void *conv_state;
+  const void *z;
+  const float *norm_w;
+  float l2_eps, rms_eps;
+};
+
 int decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                 const float *beta, const float *A, const float *b_alpha, float *S,
                 const int32_t *state_idx, int32_t idx_cols, int32_t n_slots, void *y, int32_t N,
                 int32_t n_tok, int32_t H, int32_t dk, int32_t dv, int32_t in_dtype,
-                int32_t out_dtype, void *stream, const char *name) {
+                int32_t out_dtype, void *stream, const char *name,
+                const DecodeFusion *fx = nullptr) {
   g_last_error[0] = '\0';
   if (N < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N must be >= 0 and H > 0");
   if (n_tok < 1 || n_tok > gdn::kDecodeMaxTok)
@@ -180,6 +190,30 @@ int decode_impl(const void *q, const void *k, const void *v, const float *log_al
       return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps an output");
   }
   if (overlap(S, ns, y, ny)) return fail(GDN_ERR_INVALID_ARG, "%s", "S overlaps y");
+  if (fx) {
+    if (dk != dv) return fail(GDN_ERR_UNSUPPORTED, "%s", "the fused decode needs dk == dv");
+    if (!(fx->l2_eps >= 0.0f) || !(fx->rms_eps >= 0.0f))
+      return fail(GDN_ERR_INVALID_ARG, "%s", "l2_eps and rms_eps must be >= 0");
+    if (N > 0 && (!fx->conv_w || !fx->z || (slots > 0 && !fx->conv_state)))
+      return fail(GDN_ERR_INVALID_ARG, "%s", "null pointer");
+    if (misaligned(fx->conv_w) || misaligned(fx->z) || misaligned(fx->conv_state) ||
+        misaligned(fx->norm_w, 4))
+      return fail(GDN_ERR_MISALIGNED, "%s",
+                  "conv_w, z and conv_state need 16-byte alignment, norm_w 4");
+    const size_t ncs = static_cast<size_t>(slots) * H * 9 * dk * in_b;
+    const size_t nw = static_cast<size_t>(3) * H * dk * 4 * 4;
+    const void *fin[3] = {fx->conv_w, fx->z, fx->norm_w};
+    const size_t fin_n[3] = {nw, rows * dv * in_b, static_cast<size_t>(dv) * 4};
+    for (int i = 0; i < 3; ++i)
+      if (overlap(fin[i], fin_n[i], S, ns) || overlap(fin[i], fin_n[i], y, ny) ||
+          overlap(fin[i], fin_n[i], fx->conv_state, ncs))
+        return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps an output");
+    for (int i = 0; i < 8; ++i)
+      if (overlap(ins[i], in_n[i], fx->conv_state, ncs))
+        return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps conv_state");
+    if (overlap(fx->conv_state, ncs, S, ns) || overlap(fx->conv_state, ncs, y, ny))
+      return fail(GDN_ERR_INVALID_ARG, "%s", "conv_state overlaps an output");
+  }
 
   gdn::DecodeArgs a;
   a.q = q;
@@ -204,9 +238,17 @@ int decode_impl(const void *q, const void *k, const void *v, const float *log_al
   a.in_dtype = in_dtype;
   a.out_dtype = out_dtype;
   a.stream = static_cast<hipStream_t>(stream);
+  if (fx) {
+    a.conv_w = fx->conv_w;
+    a.conv_state = fx->conv_state;
+    a.z = fx->z;
+    a.norm_w = fx->norm_w;
+    a.l2_eps = fx->l2_eps;
+    a.rms_eps = fx->rms_eps;
+  }
   char where[64];
   snprintf(where, sizeof(where), "%s launch", name);
-  return hip_status(gdn::launch_decode_step(a), where);
+  return hip_status(fx ? gdn::launch_decode_fused(a) : gdn::launch_decode_step(a), where);
 }
 
 }  // namespace
@@ -250,6 +292,18 @@ GDN_API int gdn_decode_step_gated(const void *q, const void *k, const void *v, c
   if (H > 0 && !A) return fail(GDN_ERR_INVALID_ARG, "%s", "A is required");
   return decode_impl(q, k, v, a, b, A, b_alpha, S, state_idx, 1, n_slots, y, N, 1, H, dk, dv,
                      in_dtype, out_dtype, stream, "gdn_decode_step_gated");
+}
+
+GDN_API int gdn_decode_fused(const void *q_raw, const void *k_raw, const void *v_raw,
+                             const float *conv_w, void *conv_state, const float *g_a,
+                             const float *g_b, const float *A, const float *b_alpha, float *S,
+                             const int32_t *state_idx, int32_t n_slots, const void *z,
+                             const float *norm_w, float l2_eps, float rms_eps, void *o,
+                             int32_t N, int32_t n_tok, int32_t H, int32_t d, int32_t in_dtype,
+                             int32_t out_dtype, void *stream) {
+  const DecodeFusion fx{conv_w, conv_state, z, norm_w, l2_eps, rms_eps};
+  return decode_impl(q_raw, k_raw, v_raw, g_a, g_b, A, b_alpha, S, state_idx, 1 + n_tok, n_slots,
+                     o, N, n_tok, H, d, d, in_dtype, out_dtype, stream, "gdn_decode_fused", &fx);
 }
 
 GDN_API int gdn_decode_multi(const void *q, const void *k, const void *v, const float *g_a,

@@ -23,18 +23,57 @@
 // a pool of slots (see DecodeArgs): a sequence reads one slot, and writes
 // its final state back there or, for speculative verification, the state
 // after each token into a slot of its own.
+//
+// The fused variant also runs the mixer's front end and output gate (page
+// "NLP——技术报告解读-Qwen3.8-Flash-Next", section "GDN 参数化细节"): it takes
+// the raw projections, applies the short causal convolution with the three
+// previous raw rows kept per slot (conv_state), SiLU, and the L2 norm of q
+// and k, and writes o = sigmoid(z) * RMSNorm(y) * (1 + w) instead of y. That
+// work is per (sequence, head) and small; it adds the raw rows, z and the
+// conv cache (~3% of the bytes at d = 128) to the stream.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-template <int DK, int DV, typename TIN, typename TOUT>
-__global__ __launch_bounds__(256) void decode_kernel(
-    const TIN *__restrict__ q, const TIN *__restrict__ k, const TIN *__restrict__ v,
-    const float *__restrict__ ga, const float *__restrict__ gb, const float *__restrict__ gA,
-    const float *__restrict__ gbias, float *__restrict__ S, const int32_t *__restrict__ read_idx,
-    int r_stride, const int32_t *__restrict__ write_idx, int w_stride, int n_slots,
-    TOUT *__restrict__ y, int H, int n_tok) {
+// four consecutive elements of a 16- or 32-bit type as floats, and back
+template <typename T>
+__device__ __forceinline__ void load4(const T *p, float *o) {
+  if constexpr (sizeof(T) == 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = v[i];
+  } else {
+    struct alignas(8) R { T v[4]; } r = *reinterpret_cast<const R *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = io<T>::to_f32(r.v[i]);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store4(T *p, const float *v) {
+  struct alignas(4 * sizeof(T)) R { T v[4]; } r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.v[i] = io<T>::from_f32(v[i]);
+  *reinterpret_cast<R *>(p) = r;
+}
+
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+template <int DK, int DV, typename TIN, typename TOUT, bool FUSED>
+__global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
+  const TIN *__restrict__ q = static_cast<const TIN *>(a.q);
+  const TIN *__restrict__ k = static_cast<const TIN *>(a.k);
+  const TIN *__restrict__ v = static_cast<const TIN *>(a.v);
+  const float *__restrict__ ga = a.log_alpha;
+  const float *__restrict__ gb = a.beta;
+  float *__restrict__ S = a.S;
+  const int32_t *__restrict__ read_idx = a.read_idx;
+  const int32_t *__restrict__ write_idx = a.write_idx;
+  const int r_stride = a.r_stride, w_stride = a.w_stride, n_slots = a.n_slots;
+  TOUT *__restrict__ y = static_cast<TOUT *>(a.y);
+  const int H = a.H, n_tok = a.n_tok;
   constexpr int NT = 256;
   constexpr int CG = DV / 4;   // column groups of 4 adjacent columns
   constexpr int RG = NT / CG;  // row groups
@@ -42,12 +81,14 @@ __global__ __launch_bounds__(256) void decode_kernel(
   constexpr int RG_PER_WAVE = 64 / CG;
   constexpr int NWAVE = NT / 64;
   static_assert(DK % RG == 0 && RG_PER_WAVE >= 1, "shape");
+  static_assert(!FUSED || DK == DV, "the fused front end needs dk == dv");
 
   __shared__ float sq[kDecodeMaxTok][DK];
   __shared__ float sk[kDecodeMaxTok][DK];
   __shared__ float sv[kDecodeMaxTok][DV];
   __shared__ float s_alpha[kDecodeMaxTok], s_beta[kDecodeMaxTok];
   __shared__ float red[2][NWAVE][CG][9];
+  __shared__ float sz[FUSED ? kDecodeMaxTok : 1][DV];
 
   const int unit = blockIdx.x;  // n * H + h
   const int n = unit / H;
@@ -61,7 +102,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
   if (read_idx) {
     slot = read_idx[static_cast<int64_t>(n) * r_stride];
     if (slot < 0 || slot >= n_slots) {
-      // padding entry: no state to update; y = 0
+      // padding entry: no state to update; y (or o) = 0
       for (int idx = tid; idx < n_tok * DV; idx += NT) {
         const size_t row = static_cast<size_t>(n) * n_tok + idx / DV;
         y[(row * H + h) * DV + idx % DV] = io<TOUT>::from_f32(0.0f);
@@ -80,18 +121,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
   constexpr int kRowStep = RG * DV * 4;
   const auto Sr = state_rsrc(slot);
 
-  // issue every state load first: they are the whole cost of the kernel
-  f32x4 s[RPT];
-#pragma unroll
-  for (int m = 0; m < RPT; ++m)
-    s[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(Sr, s_lane,
-                                                                           m * kRowStep, 2));
-
-  // every token's q, k, v and gates into LDS, one 16-byte load per thread
-  // and tensor. All loads are issued before the first one is waited for,
-  // so their latencies overlap the state's. Nothing here branches (a branch
-  // would make the compiler wait inside it): lanes past the last piece are
-  // clamped to it and store the same values again.
+  // Token inputs go to LDS, one 16-byte load per thread and tensor; with
+  // the front end fused these are the raw rows (and z). Nothing here
+  // branches (a branch would make the compiler wait inside it): lanes past
+  // the last piece are clamped to it and store the same values again.
   constexpr int VEC = io<TIN>::kVec;
   static_assert(kDecodeMaxTok * DK / VEC <= NT && kDecodeMaxTok * DV / VEC <= NT, "lanes");
   const size_t row0 = static_cast<size_t>(n) * n_tok;
@@ -99,20 +132,59 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const int pv = min(tid, n_tok * (DV / VEC) - 1);  // piece of v
   const int jk = pk / (DK / VEC), ck = (pk % (DK / VEC)) * VEC;
   const int jv = pv / (DV / VEC), cv = (pv % (DV / VEC)) * VEC;
-  float qf[VEC], kf[VEC], vf[VEC];
+  float qf[VEC], kf[VEC], vf[VEC], zf[VEC];
+  f32x4 s[RPT];
+  auto load_state = [&]() {
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+      s[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(Sr, s_lane,
+                                                                             m * kRowStep, 2));
+  };
+  // Without the front end the state loads go first: they are the whole
+  // cost of the kernel. With it, the small loads the front end needs go
+  // first, so that waiting for them leaves the state loads in flight.
+  if constexpr (!FUSED) load_state();
   io<TIN>::load16(q + ((row0 + jk) * H + h) * DK + ck, qf);
   io<TIN>::load16(k + ((row0 + jk) * H + h) * DK + ck, kf);
   io<TIN>::load16(v + ((row0 + jv) * H + h) * DV + cv, vf);
+  if constexpr (FUSED)
+    io<TIN>::load16(static_cast<const TIN *>(a.z) + ((row0 + jv) * H + h) * DV + cv, zf);
   const int gj = min(tid, n_tok - 1);
   const size_t gi = (row0 + gj) * H + h;
   float la = ga[gi];
   float bt = gb[gi];
-  const RawGate gate = RawGate::load(gA, gbias, h);
+  const RawGate gate = RawGate::load(a.A, a.b_alpha, h);
+
+  // front-end lanes: lane f < 3 * FG owns 4 channels of one stream
+  // (q, k, v); lanes past them repeat the last one
+  constexpr int FG = DK / 4;
+  const int fj = min(tid, 3 * FG - 1);
+  const int fs = fj / FG;
+  const int fc = (fj % FG) * 4;
+  float fw[4][4], hist[3][4], nw[4];
+  TIN *cstate = nullptr;
+  if constexpr (FUSED) {
+    const float *wp = a.conv_w + ((static_cast<size_t>(fs) * H + h) * DK + fc) * 4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 w4 = *reinterpret_cast<const f32x4 *>(wp + 4 * c);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) fw[c][t] = w4[t];
+    }
+    cstate = static_cast<TIN *>(a.conv_state);
+    const TIN *hp = cstate + ((static_cast<size_t>(slot) * H + h) * 3 + fs) * 3 * DK + fc;
+#pragma unroll
+    for (int r = 0; r < 3; ++r) load4(hp + r * DK, hist[r]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) nw[c] = 1.0f + (a.norm_w ? a.norm_w[4 * cg + c] : 0.0f);
+    load_state();
+  }
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     sq[jk][ck + e] = qf[e];
     sk[jk][ck + e] = kf[e];
     sv[jv][cv + e] = vf[e];
+    if constexpr (FUSED) sz[jv][cv + e] = zf[e];
   }
   if (gate.raw()) {
     la = gate.log_alpha(la);
@@ -121,6 +193,53 @@ __global__ __launch_bounds__(256) void decode_kernel(
   s_alpha[gj] = __expf(la);
   s_beta[gj] = bt;
   __syncthreads();
+
+  if constexpr (FUSED) {
+    // Front end, token by token, in place in sq / sk / sv: each lane owns
+    // its 4 channels in every row, so nobody else reads or writes them.
+    // hist keeps the three previous raw rows, oldest first.
+    if (wave * 64 < 3 * FG) {
+      float *const row_base = fs == 0 ? &sq[0][0] : (fs == 1 ? &sk[0][0] : &sv[0][0]);
+      for (int j = 0; j < n_tok; ++j) {
+        float *const rp = row_base + j * DK + fc;
+        float x[4], u[4], ss = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x[c] = rp[c];
+          const float acc = fw[c][0] * hist[0][c] + fw[c][1] * hist[1][c] +
+                            fw[c][2] * hist[2][c] + fw[c][3] * x[c];
+          u[c] = acc * sigmoid_fast(acc);
+          ss = fmaf(u[c], u[c], ss);
+        }
+        // sum of squares over the stream's FG lanes (aligned lane groups)
+#pragma unroll
+        for (int off = 1; off < FG; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        const float scale = fs < 2 ? rsqrtf(ss + a.l2_eps) : 1.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          rp[c] = u[c] * scale;
+          hist[0][c] = hist[1][c];
+          hist[1][c] = hist[2][c];
+          hist[2][c] = x[c];
+        }
+        // the convolution history after token j goes wherever the state
+        // after token j goes
+        int dst = -1;
+        if (write_idx) {
+          const int ws = write_idx[static_cast<int64_t>(n) * w_stride + j];
+          if (ws >= 0 && ws < n_slots) dst = ws;
+        } else if (j == n_tok - 1) {
+          dst = slot;
+        }
+        if (dst >= 0 && tid < 3 * FG) {
+          TIN *hp = cstate + ((static_cast<size_t>(dst) * H + h) * 3 + fs) * 3 * DK + fc;
+#pragma unroll
+          for (int r = 0; r < 3; ++r) store4(hp + r * DK, hist[r]);
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   auto token = [&](const int j) __attribute__((always_inline)) {
     // partial dot products over this thread's rows: s_j.k, s_j.q (4 columns)
@@ -169,10 +288,23 @@ __global__ __launch_bounds__(256) void decode_kernel(
     for (int c = 0; c < 4; ++c) e[c] = sv[j][4 * cg + c] - alpha * tot[c];
     if (rg == 0) {
       // the 4 adjacent outputs of this column group in one store
-      struct alignas(4 * sizeof(TOUT)) Y4 { TOUT v[4]; } yv;
+      float yv[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) yv.v[c] = io<TOUT>::from_f32(alpha * tot[4 + c] + b * tot[8] * e[c]);
-      *reinterpret_cast<Y4 *>(y + ((row0 + j) * H + h) * DV + 4 * cg) = yv;
+      for (int c = 0; c < 4; ++c) yv[c] = alpha * tot[4 + c] + b * tot[8] * e[c];
+      if constexpr (FUSED) {
+        // output gate: RMS over the row's DV values, held by the CG lanes
+        // with rg == 0 (an aligned lane group)
+        float ss = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ss = fmaf(yv[c], yv[c], ss);
+#pragma unroll
+        for (int off = 1; off < CG; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        const float inv = rsqrtf(ss * (1.0f / DV) + a.rms_eps);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          yv[c] = yv[c] * inv * nw[c] * sigmoid_fast(sz[j][4 * cg + c]);
+      }
+      store4(y + ((row0 + j) * H + h) * DV + 4 * cg, yv);
     }
     float be[4];
 #pragma unroll
@@ -204,42 +336,51 @@ __global__ __launch_bounds__(256) void decode_kernel(
   for (int j = 1; j < n_tok; ++j) token(j);
 }
 
-template <int DK, int DV, typename TIN, typename TOUT>
+template <int DK, int DV, typename TIN, typename TOUT, bool FUSED>
 static hipError_t launch(const DecodeArgs &a) {
   const int units = a.N * a.H;
   if (units == 0 || a.n_tok <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_kernel<DK, DV, TIN, TOUT>), dim3(units), dim3(256), 0, a.stream,
-                     static_cast<const TIN *>(a.q), static_cast<const TIN *>(a.k),
-                     static_cast<const TIN *>(a.v), a.log_alpha, a.beta, a.A, a.b_alpha, a.S,
-                     a.read_idx, a.r_stride, a.write_idx, a.w_stride, a.n_slots,
-                     static_cast<TOUT *>(a.y), a.H, a.n_tok);
+  hipLaunchKernelGGL((decode_kernel<DK, DV, TIN, TOUT, FUSED>), dim3(units), dim3(256), 0,
+                     a.stream, a);
   return hipGetLastError();
 }
 
-template <typename TIN, typename TOUT>
+template <typename TIN, typename TOUT, bool FUSED>
 static hipError_t launch_d(const DecodeArgs &a) {
-  if (a.dk == 128 && a.dv == 128) return launch<128, 128, TIN, TOUT>(a);
-  if (a.dk == 128 && a.dv == 64) return launch<128, 64, TIN, TOUT>(a);
-  if (a.dk == 64 && a.dv == 128) return launch<64, 128, TIN, TOUT>(a);
-  return launch<64, 64, TIN, TOUT>(a);
+  if constexpr (FUSED) {
+    return a.dk == 128 ? launch<128, 128, TIN, TOUT, true>(a) : launch<64, 64, TIN, TOUT, true>(a);
+  } else {
+    if (a.dk == 128 && a.dv == 128) return launch<128, 128, TIN, TOUT, false>(a);
+    if (a.dk == 128 && a.dv == 64) return launch<128, 64, TIN, TOUT, false>(a);
+    if (a.dk == 64 && a.dv == 128) return launch<64, 128, TIN, TOUT, false>(a);
+    return launch<64, 64, TIN, TOUT, false>(a);
+  }
 }
 
-template <typename TIN>
+template <typename TIN, bool FUSED>
 static hipError_t launch_d_out(const DecodeArgs &a) {
   switch (a.out_dtype) {
-    case 1: return launch_d<TIN, bf16_t>(a);
-    case 2: return launch_d<TIN, _Float16>(a);
-    default: return launch_d<TIN, float>(a);
+    case 1: return launch_d<TIN, bf16_t, FUSED>(a);
+    case 2: return launch_d<TIN, _Float16, FUSED>(a);
+    default: return launch_d<TIN, float, FUSED>(a);
   }
 }
 
-hipError_t launch_decode_step(const DecodeArgs &a) {
+template <bool FUSED>
+static hipError_t launch_in(const DecodeArgs &a) {
   if (a.n_tok < 1 || a.n_tok > kDecodeMaxTok) return hipErrorInvalidValue;
   switch (a.in_dtype) {
-    case 1: return launch_d_out<bf16_t>(a);
-    case 2: return launch_d_out<_Float16>(a);
-    default: return launch_d_out<float>(a);
+    case 1: return launch_d_out<bf16_t, FUSED>(a);
+    case 2: return launch_d_out<_Float16, FUSED>(a);
+    default: return launch_d_out<float, FUSED>(a);
   }
+}
+
+hipError_t launch_decode_step(const DecodeArgs &a) { return launch_in<false>(a); }
+
+hipError_t launch_decode_fused(const DecodeArgs &a) {
+  if (a.dk != a.dv) return hipErrorInvalidValue;
+  return launch_in<true>(a);
 }
 
 }  // namespace gdn

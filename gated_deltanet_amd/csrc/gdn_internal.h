@@ -33,6 +33,16 @@ struct DecodeArgs {
   int n_tok = 1;
   int in_dtype, out_dtype;  // 0 = f32, 1 = bf16, 2 = f16
   hipStream_t stream;
+  // Fused decode only (front end and output gate in the same kernel): q, k,
+  // v are then the raw projections, y receives o, and conv_state holds per
+  // slot and head the three previous raw rows of each stream,
+  // [slots, H, 3 (q, k, v), 3 (oldest first), d] in in_dtype, read from the
+  // start slot and written wherever the state is.
+  const float *conv_w = nullptr;  // [3][H*d][4]
+  void *conv_state = nullptr;
+  const void *z = nullptr;        // [N, n_tok, H, d] in in_dtype
+  const float *norm_w = nullptr;  // [d] or null
+  float l2_eps = 0.0f, rms_eps = 0.0f;
 };
 
 // most tokens one decode call applies per (sequence, head)
@@ -76,6 +86,7 @@ struct GateArgs {
 };
 
 hipError_t launch_decode_step(const DecodeArgs &a);
+hipError_t launch_decode_fused(const DecodeArgs &a);  // dk == dv
 hipError_t launch_frontend(const FrontendArgs &a);
 hipError_t launch_output_gate(const GateArgs &a);
 hipError_t launch_chunk_fwd(const ChunkArgs &a);      // dispatches on in_dtype

@@ -209,6 +209,29 @@ def frontend_inputs(lengths, H, dk, dv, dtype="bf16", s0_std=0.02, seed=4, conv_
                 dtype=dtype)
 
 
+def decode_fused_inputs(N, n_tok, H, d, dtype="bf16", s0_std=0.02, seed=5, conv_std=0.5,
+                        norm_w_std=0.1):
+    """Inputs for the fused serving decode: raw projections q_raw, k_raw,
+    v_raw and z [N, n_tok, H, d] (N(0,1), ``dtype``), conv_w float32
+    [3, H*d, 4], a convolution cache conv_state [N, H, 3, 3, d] holding three
+    earlier raw rows per stream (N(0,1), ``dtype``), gates float32
+    [N, n_tok, H], S0 float32 [N, H, d, d] and norm_w float32 [d]."""
+    tdt = _DT[dtype]
+    q_raw = normal((N, n_tok, H, d), seed, 31).to(tdt)
+    k_raw = normal((N, n_tok, H, d), seed, 32).to(tdt)
+    v_raw = normal((N, n_tok, H, d), seed, 33).to(tdt)
+    z = normal((N, n_tok, H, d), seed, 34).to(tdt)
+    conv_w = normal((3, H * d, 4), seed, 35, std=conv_std)
+    conv_state = normal((N, H, 3, 3, d), seed, 36).to(tdt)
+    la, b = gates(N * n_tok, H, seed)
+    S0 = normal((N, H, d, d), seed, 37, std=s0_std)
+    norm_w = normal((d,), seed, 38, std=norm_w_std)
+    return dict(q_raw=q_raw, k_raw=k_raw, v_raw=v_raw, z=z, conv_w=conv_w,
+                conv_state=conv_state, log_alpha=la.reshape(N, n_tok, H).contiguous(),
+                beta=b.reshape(N, n_tok, H).contiguous(), S0=S0, norm_w=norm_w, N=N,
+                n_tok=n_tok, H=H, d=d, dtype=dtype)
+
+
 def workload_inputs(wid: int, seed: Optional[int] = None, **kw):
     """Inputs of workload ``wid`` (0..4), seeded by ``seed`` (default: wid)."""
     w = WORKLOADS[wid]

@@ -290,6 +290,44 @@ GDN_API int gdn_chunk_fwd_fused(const void *q_raw, const void *k_raw,
                                 void *workspace, size_t workspace_bytes,
                                 void *stream);
 
+/*
+ * Serving decode of the whole mixer in one kernel (page "NLP——技术报告解读-
+ * Qwen3.8-Flash-Next", section "GDN 参数化细节": front end, recurrence,
+ * output gate), n_tok tokens per sequence as gdn_decode_multi:
+ *     q, k, v = front end of q_raw, k_raw, v_raw with the cached history
+ *     y       = the recurrence of gdn_decode_multi
+ *     o       = sigmoid(z) * y / sqrt(mean(y^2) + rms_eps) * (1 + norm_w)
+ * The front end is that of gdn_frontend_qkv (short causal convolution with
+ * conv_w, SiLU, L2 norm of q and k with l2_eps), with the convolution's
+ * three previous rows taken from conv_state instead of zeros; the
+ * intermediates stay in fp32 inside the kernel.
+ *
+ *   q_raw, k_raw, v_raw, z   [N, n_tok, H, d] in in_dtype (raw projections).
+ *   conv_w       float32 [3][H*d][4] (as gdn_frontend_qkv).
+ *   conv_state   in_dtype [slots, H, 3, 3, d]: per slot and head, for q, k
+ *                and v in turn, the three raw rows before the call's first
+ *                token, oldest first (zeros for a fresh sequence). Read from
+ *                the start slot; the rows before the next token are written
+ *                wherever the state is written (see state_idx of
+ *                gdn_decode_multi).
+ *   g_a, g_b, A, b_alpha, S, state_idx, n_slots   as gdn_decode_multi.
+ *   norm_w       float32 [d] or NULL (w = 0).
+ *   o            [N, n_tok, H, d] in out_dtype.
+ * Requires dk == dv == d in {64, 128}. q_raw, k_raw, v_raw, z, conv_w,
+ * conv_state, S and o are 16-byte aligned; the rest 4-byte aligned. Inputs
+ * must not overlap S, conv_state or o.
+ */
+GDN_API int gdn_decode_fused(const void *q_raw, const void *k_raw,
+                             const void *v_raw, const float *conv_w,
+                             void *conv_state, const float *g_a,
+                             const float *g_b, const float *A,
+                             const float *b_alpha, float *S,
+                             const int32_t *state_idx, int32_t n_slots,
+                             const void *z, const float *norm_w, float l2_eps,
+                             float rms_eps, void *o, int32_t N, int32_t n_tok,
+                             int32_t H, int32_t d, int32_t in_dtype,
+                             int32_t out_dtype, void *stream);
+
 /* Human-readable name of a return code (static string, never NULL). */
 GDN_API const char *gdn_status_string(int status);
 

@@ -223,3 +223,28 @@ def test_decode_multi_rejects(lib):
     # the index table [N, 1 + n_tok] = 80 bytes must not overlap the pool
     assert dec(idx=B + 64, ns=4) == -1
     assert dec(dk=32) == -2
+
+
+def test_decode_fused_rejects(lib):
+    v, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.gdn_decode_fused.argtypes = ([v] * 11 + [i32] + [v, v, f32, f32, v] + [i32] * 6 + [v])
+
+    def dec(**kw):
+        a = dict(q=A, k=A + (1 << 20), v=A + (2 << 20), w=A + (3 << 20), cs=B + (1 << 28),
+                 ga=A + (4 << 20), gb=A + (5 << 20), Ah=None, ba=None, S=B, idx=None, ns=0,
+                 z=A + (6 << 20), nw=None, l2=1e-6, rms=1e-6, o=B + (1 << 26), N=4, nt=2, H=2,
+                 d=128)
+        a.update(kw)
+        return lib.gdn_decode_fused(a["q"], a["k"], a["v"], a["w"], a["cs"], a["ga"], a["gb"],
+                                    a["Ah"], a["ba"], a["S"], a["idx"], a["ns"], a["z"], a["nw"],
+                                    a["l2"], a["rms"], a["o"], a["N"], a["nt"], a["H"], a["d"], 1,
+                                    1, None)
+
+    assert dec(d=96) == -2
+    assert dec(l2=-1.0) == -1
+    assert dec(w=None) == -1
+    assert dec(z=None) == -1
+    assert dec(cs=None) == -1
+    assert dec(cs=B + 4096) == -1           # conv_state overlaps S
+    assert dec(cs=A + (6 << 20)) == -1      # conv_state overlaps z
+    assert dec(cs=B + (1 << 28) + 8) == -3

@@ -505,3 +505,106 @@ def test_decode_multi_slots_and_rollback_states(raw):
             assert rel_l2(Sc[sl], expect[sl]) <= 2e-3, sl
         else:
             assert torch.equal(Sc[sl], pool[sl]), sl
+
+
+# ------------------------------------------------------- fused decode -----
+def _fused_decode_reference(f, hist, S0, la, bt, l2_eps=1e-6, rms_eps=1e-6):
+    """The fp64 oracle chain for one fused decode call: the front end over
+    [three history rows, the call's raw rows] of each sequence (the outputs
+    of the history rows are dropped), n_tok oracle decode steps, then the
+    output gate. hist [N, H, 3, 3, d]; returns (o [N, n_tok, H, d], S)."""
+    N, n_tok, H, d = f["q_raw"].shape
+    L = 3 + n_tok
+    cu = np.arange(N + 1, dtype=np.int32) * L
+    proc = []
+    for s, nm in enumerate(("q_raw", "k_raw", "v_raw")):
+        h_s = np.asarray(hist, dtype=np.float64)[:, :, s].transpose(0, 2, 1, 3)  # [N, 3, H, d]
+        x = np.concatenate([h_s, f[nm].double().numpy()], axis=1).reshape(N * L, H, d)
+        out = oracle.frontend(x, f["conv_w"][s], cu_seqlens=cu, l2=s < 2, eps=l2_eps)
+        proc.append(out.reshape(N, L, H, d)[:, 3:])
+    S = np.asarray(S0, dtype=np.float64)
+    ys = []
+    for t in range(n_tok):
+        y_t, S = oracle.decode_step(proc[0][:, t], proc[1][:, t], proc[2][:, t], la[:, t],
+                                    bt[:, t], S)
+        ys.append(y_t)
+    y = np.stack(ys, 1)
+    o = oracle.output_gate(y, f["z"], f["norm_w"], eps=rms_eps)
+    return o, S
+
+
+@gpu
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n_tok", [1, 4])
+def test_decode_fused(d, dtype, n_tok):
+    g = _lib()
+    f = gi.decode_fused_inputs(5, n_tok, 3, d, dtype, seed=d + n_tok)
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in f.items()}
+    cs = dev["conv_state"].clone()
+    S = dev["S0"].clone()
+    o = g.gdn_decode_fused(dev["q_raw"], dev["k_raw"], dev["v_raw"], dev["conv_w"], cs,
+                           dev["log_alpha"], dev["beta"], S, dev["z"], norm_w=dev["norm_w"],
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _fused_decode_reference(f, f["conv_state"].double().numpy(), f["S0"],
+                                           f["log_alpha"].double().numpy(),
+                                           f["beta"].double().numpy())
+    eo, es = rel_l2(o, o_ref), rel_l2(S, S_ref)
+    print("fused decode rel_l2 o=%.3e S=%.3e" % (eo, es), flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+    # the new convolution history is the last three raw rows, bit for bit
+    rows = torch.cat([f["conv_state"].permute(0, 2, 3, 1, 4)[:, :, :, :, :],
+                      torch.stack([f["q_raw"], f["k_raw"], f["v_raw"]], 1)], 2)  # [N,3,3+n,H,d]
+    want = rows[:, :, -3:].permute(0, 3, 1, 2, 4).contiguous()  # [N, H, 3, 3, d]
+    assert torch.equal(cs.cpu(), want)
+
+
+@gpu
+def test_decode_fused_slots_match_unfused_chain():
+    """With a slot table, the fused decode leaves the same states in the same
+    slots as the oracle chain, the conv cache follows the state, and padding
+    entries write nothing."""
+    g = _lib()
+    N, n_tok, H, d, n_slots = 3, 3, 2, 128, 12
+    f = gi.decode_fused_inputs(N, n_tok, H, d, "bf16", seed=77)
+    pool_S = gi.normal((n_slots, H, d, d), 78, 1, std=0.02)
+    pool_c = gi.normal((n_slots, H, 3, 3, d), 78, 2).to(torch.bfloat16)
+    table = torch.tensor([[5, 6, 7, 5], [-1, 8, 9, 10], [2, -1, -1, 11]], dtype=torch.int32)
+    a, b, A, b_alpha = gi.raw_gates(N * n_tok, H, 79)
+    ga, gb = a.reshape(N, n_tok, H).contiguous(), b.reshape(N, n_tok, H).contiguous()
+    S, cs = pool_S.clone().cuda(), pool_c.clone().cuda()
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in f.items()}
+    o = g.gdn_decode_fused(dev["q_raw"], dev["k_raw"], dev["v_raw"], dev["conv_w"], cs,
+                           ga.cuda(), gb.cuda(), S, dev["z"], A=A.cuda(), b_alpha=b_alpha.cuda(),
+                           state_idx=table.cuda(), norm_w=dev["norm_w"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    la, bt = oracle.gates_from_raw(a, b, A, b_alpha)
+    la, bt = la.reshape(N, n_tok, H), bt.reshape(N, n_tok, H)
+    Sc, cc, oc = S.cpu(), cs.cpu(), o.cpu()
+    touched = set()
+    for n in range(N):
+        start = int(table[n, 0])
+        if start < 0:
+            assert torch.all(oc[n] == 0)
+            continue
+        fn = {k: (v[n:n + 1] if isinstance(v, torch.Tensor) and k in
+                  ("q_raw", "k_raw", "v_raw", "z") else v) for k, v in f.items()}
+        raw_rows = torch.stack([f["q_raw"][n], f["k_raw"][n], f["v_raw"][n]], 0)  # [3,n_tok,H,d]
+        for t in range(n_tok):
+            w = int(table[n, 1 + t])
+            if w < 0:
+                continue
+            sub = {k: (v[:, :t + 1].contiguous() if k in ("q_raw", "k_raw", "v_raw", "z") else v)
+                   for k, v in fn.items()}
+            o_ref, S_ref = _fused_decode_reference(sub, pool_c[start:start + 1].double().numpy(),
+                                                   pool_S[start:start + 1], la[n:n + 1, :t + 1],
+                                                   bt[n:n + 1, :t + 1])
+            assert rel_l2(Sc[w:w + 1], S_ref) <= 2e-3
+            assert rel_l2(oc[n:n + 1, :t + 1], o_ref) <= 2e-3
+            hist = torch.cat([pool_c[start].permute(1, 2, 0, 3), raw_rows[:, :t + 1]], 1)
+            assert torch.equal(cc[w], hist[:, -3:].permute(2, 0, 1, 3))
+            touched.add(w)
+    for sl in range(n_slots):
+        if sl not in touched:
+            assert torch.equal(Sc[sl], pool_S[sl]) and torch.equal(cc[sl], pool_c[sl]), sl
