@@ -185,10 +185,10 @@ def bench_decode(g, n_steps=128, reps=2):
     gbs = bytes_step / (us_step * 1e-6) / 1e9
     return dict(workload=w.name, us_per_step=us_step, GBps=gbs, frac_hbm=gbs / HBM_PEAK_GBS,
                 tokens_per_s=N / (us_step * 1e-6), bytes_per_step=bytes_step, steps=n_steps,
-                roofline=dict(kernel="decode_step_kernel<128,128,bf16,bf16>", bound="hbm",
+                roofline=dict(kernel="decode_kernel<128,128,bf16,bf16,unfused> (n_tok = 1)", bound="hbm",
                               achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                               frac=gbs / HBM_PEAK_GBS,
-                              traffic=measured_traffic("decode_step_kernel_N256_H32_d128",
+                              traffic=measured_traffic("decode_kernel_N256_H32_d128",
                                                        "decode.hip")))
 
 
@@ -332,6 +332,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the long-context and varlen front-end workloads")
+    ap.add_argument("--no-serving", action="store_true",
+                    help="skip the multi-token and fused serving decode workloads")
     ap.add_argument("--warm-seconds", type=float, default=0.5,
                     help="untimed GPU load before each timed region, beyond --warmup steps")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -392,6 +394,7 @@ def main():
         print("[bench] decode workload 3: 256 x 32 heads, %d steps" % args.decode_steps,
               file=sys.stderr, flush=True)
         rec["decode"] = bench_decode(g, args.decode_steps)
+    if not args.no_decode and not args.no_serving:
         print("[bench] decode workload 3 with 4 tokens per call", file=sys.stderr, flush=True)
         rec["decode_multi"] = bench_decode_multi(g)
         print("[bench] fused serving decode, 4 tokens per call", file=sys.stderr, flush=True)
