@@ -74,6 +74,9 @@ def _bind(path):
     lib.oracle_output_gate.argtypes = [dp, dp, dp, ctypes.c_double, dp,
                                        ctypes.c_int64, i, i]
     lib.oracle_output_gate.restype = i
+    lib.oracle_gdn_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ip, i, i, i, i, i,
+                                   dp, dp, dp, dp, dp, dp, i]
+    lib.oracle_gdn_bwd.restype = i
     lib.oracle_gates_from_raw.argtypes = [dp, dp, dp, dp, dp, dp,
                                           ctypes.c_int64, i]
     lib.oracle_gates_from_raw.restype = i
@@ -249,3 +252,34 @@ def gates_from_raw(a, b, A, b_alpha=None):
                                    _ptr(la), _ptr(bt), rows, H)
     assert rc == 0
     return la, bt
+
+
+def gdn_bwd(q, k, v, log_alpha, beta, S0, dy, dS_T=None, cu_seqlens=None, N=None, nthreads=0):
+    """Gradients of L = <dy, y> + <dS_T, S_T> of the forward recurrence with
+    respect to (q, k, v, log_alpha, beta, S0). Shapes as gdn_fwd; returns
+    float64 arrays (dq, dk, dv, dlog_alpha, dbeta, dS0) with dS0 of shape
+    [N, H, dk, dv]."""
+    lib = _load()
+    q, k, v, la, b, dy = (_f64(x) for x in (q, k, v, log_alpha, beta, dy))
+    S0 = _f64(S0)
+    dS_T = _f64(dS_T)
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    cu = _cu(cu_seqlens)
+    total = q.size // (H * dk)
+    if cu is not None:
+        N = cu.size - 1
+        T = 0
+    else:
+        if N is None:
+            N = S0.shape[0] if S0 is not None else 1
+        T = total // N if N else 0
+        assert N * T == total
+    dq, dk_, dv_ = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dla, db = np.zeros_like(la), np.zeros_like(b)
+    dS0 = np.zeros((N, H, dk, dv))
+    rc = lib.oracle_gdn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(b), _ptr(S0), _ptr(dy),
+                            _ptr(dS_T), _ptr(cu, ctypes.c_int32), N, T, H, dk, dv, _ptr(dq),
+                            _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(db), _ptr(dS0), int(nthreads))
+    assert rc == 0
+    return dq, dk_, dv_, dla, db, dS0

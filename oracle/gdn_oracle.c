@@ -26,6 +26,16 @@
  *   Output gate (same section, third display; zero-centred RMSNorm from the
  *   pwwt.cn page, section 2.1.1): o = sigmoid(z) * RMSNorm(y) with gain 1 + w.
  *
+ *   Backward (gradients of the recurrence above; the pages report backward
+ *   kernels but print no formula, so this is reverse-mode differentiation of
+ *   the erase-write form written out by hand, token by token, from the last
+ *   token to the first). With S~ = alpha S_{t-1}, e = v - S~^T k:
+ *     dq_t = S_t dy_t,              dS += q dy^T,
+ *     dbeta = k^T dS e,             de = beta dS^T k,
+ *     dk = beta dS e - S~ de,       dv = de,
+ *     dS~ = dS - k de^T,            dlog_alpha = alpha <S_{t-1}, dS~>,
+ *     dS <- alpha dS~  (the gradient of S_{t-1}); dS0 is dS after token 1.
+ *
  *   Gates from raw pre-activations (same section, second display):
  *   beta_t = sigmoid(b_t), alpha_t = exp[-exp(A) softplus(a_t + b_alpha)],
  *   i.e. log alpha_t = -exp(A) * softplus(a_t + b_alpha), per head.
@@ -239,6 +249,127 @@ int oracle_output_gate(const double *y, const double *z, const double *w,
     }
   }
   return 0;
+}
+
+/* Gradients of L = <dy, y> + <dS_T, S_T> with respect to q, k, v,
+ * log_alpha, beta and S0 (dS_T and S0 may be NULL: zeros). Layouts as the
+ * forward; the outputs dq, dk, dv, dlog_alpha, dbeta, dS0 have the shapes of
+ * q, k, v, log_alpha, beta and S0 ([N, H, dk, dv]). Every state S_t of a
+ * (sequence, head) is kept in memory for the backward sweep. */
+int oracle_gdn_bwd(const double *q, const double *k, const double *v,
+                   const double *log_alpha, const double *beta,
+                   const double *S0, const double *dy, const double *dS_T,
+                   const int32_t *cu_seqlens, int N, int T, int H, int dk,
+                   int dv, double *dq, double *dk_out, double *dv_out,
+                   double *dlog_alpha, double *dbeta, double *dS0,
+                   int nthreads) {
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+  const size_t state = (size_t)dk * dv;
+  const int64_t units = (int64_t)N * H;
+  int status = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int64_t nh = 0; nh < units; ++nh) {
+    const int h = (int)(nh % H);
+    const int n = (int)(nh / H);
+    const int64_t t0 = seq_start(cu_seqlens, n, T);
+    const int64_t len = seq_len(cu_seqlens, n, T);
+    double *hist = (double *)malloc(sizeof(double) * state * (size_t)(len + 1));
+    double *dS = (double *)malloc(sizeof(double) * state);
+    double *St = (double *)malloc(sizeof(double) * state);
+    double *e = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *de = (double *)malloc(sizeof(double) * (size_t)dv);
+    if (!hist || !dS || !St || !e || !de) {
+      free(hist); free(dS); free(St); free(e); free(de);
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      status = -2;
+      continue;
+    }
+    /* forward sweep: hist[t] = S_t (S_0 = the initial state) */
+    if (S0) memcpy(hist, S0 + nh * state, sizeof(double) * state);
+    else memset(hist, 0, sizeof(double) * state);
+    for (int64_t t = 0; t < len; ++t) {
+      const int64_t row = (t0 + t) * H + h;
+      const double a = exp(log_alpha[row]);
+      const double b = beta[row];
+      const double *kt = k + row * dk;
+      const double *vt = v + row * dv;
+      const double *Sp = hist + (size_t)t * state;
+      double *Sn = hist + (size_t)(t + 1) * state;
+      for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += a * Sp[i * dv + j] * kt[i];
+        e[j] = vt[j] - acc;
+      }
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) Sn[i * dv + j] = a * Sp[i * dv + j] + b * kt[i] * e[j];
+    }
+    /* backward sweep */
+    if (dS_T) memcpy(dS, dS_T + nh * state, sizeof(double) * state);
+    else memset(dS, 0, sizeof(double) * state);
+    for (int64_t t = len - 1; t >= 0; --t) {
+      const int64_t row = (t0 + t) * H + h;
+      const double a = exp(log_alpha[row]);
+      const double b = beta[row];
+      const double *qt = q + row * dk;
+      const double *kt = k + row * dk;
+      const double *vt = v + row * dv;
+      const double *dyt = dy + row * dv;
+      const double *Sp = hist + (size_t)t * state;
+      const double *Sn = hist + (size_t)(t + 1) * state;
+      /* recompute the error against the decayed state */
+      for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += a * Sp[i * dv + j] * kt[i];
+        e[j] = vt[j] - acc;
+      }
+      /* y_t = S_t^T q_t */
+      for (int i = 0; i < dk; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < dv; ++j) acc += Sn[i * dv + j] * dyt[j];
+        dq[row * dk + i] = acc;
+      }
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) dS[i * dv + j] += qt[i] * dyt[j];
+      /* S_t = S~ + beta k e^T */
+      double db = 0.0;
+      for (int i = 0; i < dk; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < dv; ++j) acc += dS[i * dv + j] * e[j];
+        db += kt[i] * acc;
+        dk_out[row * dk + i] = b * acc; /* the S~ de part follows below */
+      }
+      dbeta[row] = db;
+      for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += dS[i * dv + j] * kt[i];
+        de[j] = b * acc;
+        dv_out[row * dv + j] = de[j];
+      }
+      /* e = v - S~^T k */
+      for (int i = 0; i < dk; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < dv; ++j) acc += a * Sp[i * dv + j] * de[j];
+        dk_out[row * dk + i] -= acc;
+      }
+      /* S~ = alpha S_{t-1} */
+      double dalpha = 0.0;
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) {
+          const double dSt = dS[i * dv + j] - kt[i] * de[j];
+          dalpha += Sp[i * dv + j] * dSt;
+          dS[i * dv + j] = a * dSt;
+        }
+      dlog_alpha[row] = a * dalpha;
+    }
+    memcpy(dS0 + nh * state, dS, sizeof(double) * state);
+    free(hist); free(dS); free(St); free(e); free(de);
+  }
+  return status;
 }
 
 /* Gates from raw pre-activations a, b [rows, H] with per-head A [H] and

@@ -48,6 +48,16 @@ MUTANTS = [
      "log_alpha[i] = -A[h] * sp;"),
     ("beta sigmoid sign", "beta[i] = 1.0 / (1.0 + exp(-b[i]));",
      "beta[i] = 1.0 / (1.0 + exp(b[i]));"),
+    ("bwd: dk without the read-back term", "dk_out[row * dk + i] -= acc;",
+     "dk_out[row * dk + i] -= 0.0 * acc;"),
+    ("bwd: state gradient not decayed", "dS[i * dv + j] = a * dSt;", "dS[i * dv + j] = dSt;"),
+    ("bwd: dq from the previous state", "for (int j = 0; j < dv; ++j) acc += Sn[i * dv + j] * dyt[j];",
+     "for (int j = 0; j < dv; ++j) acc += Sp[i * dv + j] * dyt[j];"),
+    ("bwd: erase term missing", "const double dSt = dS[i * dv + j] - kt[i] * de[j];",
+     "const double dSt = dS[i * dv + j];"),
+    ("bwd: dbeta sign", "dbeta[row] = db;", "dbeta[row] = -db;"),
+    ("bwd: dlog_alpha without alpha", "dlog_alpha[row] = a * dalpha;", "dlog_alpha[row] = dalpha;"),
+    ("bwd: dv without beta", "de[j] = b * acc;", "de[j] = acc;"),
 ]
 
 PIN_FUNCS = [
@@ -65,6 +75,7 @@ PIN_FUNCS = [
     pins.test_l2norm_gives_unit_rows_and_matches_twin,
     pins.test_output_gate_against_torch_rms_norm,
     pins.test_gates_from_raw_against_torch_and_identities,
+    pins.test_bwd_matches_finite_differences,
 ]
 
 
