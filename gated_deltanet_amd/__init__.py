@@ -79,6 +79,11 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_decode_fused.argtypes = [vp, vp, vp, fp, vp, fp, fp, fp, fp, fp, ip, i32, vp, fp, f32,
                                      f32, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.gdn_decode_fused.restype = ctypes.c_int
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [i64, i32, i32, i32, i32]
+    lib.gdn_chunk_bwd_workspace_size.restype = sz
+    lib.gdn_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, ip, i32, i32, i32, i32, i32,
+                                  vp, vp, vp, fp, fp, fp, i32, i32, vp, sz, vp]
+    lib.gdn_chunk_bwd.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -177,6 +182,44 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, out_dtype=
                            _stream(v.device))
     _check(rc, lib, "gdn_chunk_fwd")
     return y, S_T
+
+
+def gdn_chunk_bwd_workspace_size(rows: int, N: int, H: int, dk: int, dv: int) -> int:
+    return int(load_library().gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv))
+
+
+def gdn_chunk_bwd(q, k, v, log_alpha, beta, dy, S0=None, dS_T=None, cu_seqlens=None, N=None,
+                  grad_dtype=None, workspace=None, want_dS0=True):
+    """Gradients of <dy, y> + <dS_T, S_T> of gdn_chunk_fwd with respect to
+    (q, k, v, log_alpha, beta, S0). Shapes as gdn_chunk_fwd; dy like v in
+    grad_dtype (default: dy's dtype). Returns (dq, dk, dv, dlog_alpha, dbeta,
+    dS0) with dS0 None unless want_dS0."""
+    lib = load_library()
+    in_dtype = _prefill_checked(q, k, v, log_alpha, beta, ("log_alpha", "beta"))
+    grad_dtype = dy.dtype if grad_dtype is None else grad_dtype
+    _need(dy, "dy", grad_dtype)
+    N, T, H, dk, dv = _prefill_shape(q, v, S0, cu_seqlens, N)
+    if dS_T is not None:
+        _need(dS_T, "dS_T", torch.float32)
+        if tuple(dS_T.shape) != (N, H, dk, dv):
+            raise GdnError("dS_T must be [N, H, dk, dv]")
+    rows = q.numel() // (H * dk)
+    need = gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dev = q.device
+    dq = torch.empty(q.shape, dtype=grad_dtype, device=dev)
+    dk_ = torch.empty(k.shape, dtype=grad_dtype, device=dev)
+    dv_ = torch.empty(v.shape, dtype=grad_dtype, device=dev)
+    dla = torch.empty(log_alpha.shape, dtype=torch.float32, device=dev)
+    db = torch.empty(beta.shape, dtype=torch.float32, device=dev)
+    dS0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
+    rc = lib.gdn_chunk_bwd(_p(q), _p(k), _p(v), _p(log_alpha), _p(beta), _p(S0), _p(dy), _p(dS_T),
+                           _p(cu_seqlens), N, T, H, dk, dv, _p(dq), _p(dk_), _p(dv_), _p(dla),
+                           _p(db), _p(dS0), _dt(in_dtype), _dt(grad_dtype), _p(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc, lib, "gdn_chunk_bwd")
+    return dq, dk_, dv_, dla, db, dS0
 
 
 def _head_params(A, b_alpha, H):

@@ -542,4 +542,93 @@ GDN_API int gdn_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void
   return hip_status(gdn::launch_output_gate(g), "gdn_chunk_fwd_fused output gate");
 }
 
+GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t rows, int32_t N, int32_t H, int32_t dk,
+                                            int32_t dv) {
+  if (rows < 0 || N < 0 || H <= 0 || !head_size_ok(dk) || !head_size_ok(dv) ||
+      rows * H * (dk > dv ? dk : dv) >= (int64_t{1} << 40))
+    return 0;
+  return gdn::chunk_bwd_workspace_size(rows, N, H, dk, dv);
+}
+
+GDN_API int gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const float *beta, const float *S0, const void *dy, const float *dS_T,
+                          const int32_t *cu_seqlens, int32_t N, int32_t T, int32_t H, int32_t dk,
+                          int32_t dv, void *dq, void *dk_out, void *dv_out, float *dlog_alpha,
+                          float *dbeta, float *dS0, int32_t in_dtype, int32_t grad_dtype,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  g_last_error[0] = '\0';
+  if (N < 0 || T < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N, T must be >= 0 and H > 0");
+  if (!head_size_ok(dk) || !head_size_ok(dv))
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dk and dv must be 64 or 128");
+  if (!dtype_ok(in_dtype) || !dtype_ok(grad_dtype))
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32, GDN_BF16 or GDN_F16");
+  const int64_t rows = cu_seqlens ? static_cast<int64_t>(T) : static_cast<int64_t>(N) * T;
+  if (static_cast<int64_t>(N) * H > (int64_t{1} << 31) / 8)
+    return fail(GDN_ERR_INVALID_ARG, "%s", "N * H too large");
+  if (rows * H * (dk > dv ? dk : dv) >= (int64_t{1} << 40))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "input too large");
+  const size_t need = gdn::chunk_bwd_workspace_size(rows, N, H, dk, dv);
+  if (N > 0 && (!workspace || workspace_bytes < need))
+    return fail(GDN_ERR_INVALID_ARG, "%s",
+                "workspace missing or smaller than gdn_chunk_bwd_workspace_size()");
+  const bool any_rows = rows > 0;
+  if (any_rows && (!q || !k || !v || !log_alpha || !beta || !dy || !dq || !dk_out || !dv_out ||
+                   !dlog_alpha || !dbeta))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "null input or output pointer");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(dy) || misaligned(S0) ||
+      misaligned(dS_T) || misaligned(dq) || misaligned(dk_out) || misaligned(dv_out) ||
+      misaligned(dS0) || misaligned(workspace, 256) || misaligned(log_alpha, 4) ||
+      misaligned(beta, 4) || misaligned(dlog_alpha, 4) || misaligned(dbeta, 4) ||
+      misaligned(cu_seqlens, 4))
+    return fail(GDN_ERR_MISALIGNED, "%s",
+                "tensors need 16-byte alignment, the workspace 256, gates and cu_seqlens 4");
+  const size_t in_b = esize(in_dtype), g_b = esize(grad_dtype);
+  const size_t nqk = static_cast<size_t>(rows) * H * dk, nv = static_cast<size_t>(rows) * H * dv;
+  const size_t ng = static_cast<size_t>(rows) * H * 4;
+  const size_t ns = static_cast<size_t>(N) * H * dk * dv * 4;
+  const void *ins[9] = {q, k, v, log_alpha, beta, S0, dy, dS_T, cu_seqlens};
+  const size_t in_n[9] = {nqk * in_b, nqk * in_b, nv * in_b, ng, ng, ns, nv * g_b, ns,
+                          static_cast<size_t>(N + 1) * 4};
+  const void *outs[7] = {dq, dk_out, dv_out, dlog_alpha, dbeta, dS0, workspace};
+  const size_t out_n[7] = {nqk * g_b, nqk * g_b, nv * g_b, ng, ng, ns, N > 0 ? need : 0};
+  for (int i = 0; i < 9; ++i)
+    for (int j = 0; j < 7; ++j)
+      if (overlap(ins[i], in_n[i], outs[j], out_n[j]))
+        return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps an output or the workspace");
+  for (int i = 0; i < 7; ++i)
+    for (int j = i + 1; j < 7; ++j)
+      if (overlap(outs[i], out_n[i], outs[j], out_n[j]))
+        return fail(GDN_ERR_INVALID_ARG, "%s", "outputs overlap");
+
+  gdn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_alpha = log_alpha;
+  a.beta = beta;
+  a.S0 = S0;
+  a.dy = dy;
+  a.dS_T = dS_T;
+  a.cu_seqlens = cu_seqlens;
+  a.N = N;
+  a.T = T;
+  a.H = H;
+  a.dk_size = dk;
+  a.dv_size = dv;
+  a.rows = rows;
+  a.dq = dq;
+  a.dk = dk_out;
+  a.dv = dv_out;
+  a.dlog_alpha = dlog_alpha;
+  a.dbeta = dbeta;
+  a.dS0 = dS0;
+  a.ws_states = static_cast<float *>(workspace);
+  a.ws_part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                        gdn::chunk_bwd_states_bytes(rows, N, H, dk, dv));
+  a.in_dtype = in_dtype;
+  a.grad_dtype = grad_dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_chunk_bwd(a), "gdn_chunk_bwd launch");
+}
+
 }  // extern "C"

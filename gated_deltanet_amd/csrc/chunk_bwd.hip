@@ -1,0 +1,741 @@
+// Chunked backward pass of the gated delta rule (gfx950).
+//
+// Gradients of L = <dy, y> + <dS_T, S_T> with respect to q, k, v, log alpha,
+// beta and S0 for the recurrence of the page "NLP——技术报告解读-Qwen3.8-Flash-
+// Next", section "Gated DeltaNet 核心机制" (the pages report backward kernels
+// but print no formula; these are the derivatives of the chunk equations the
+// forward evaluates). Per chunk of C tokens starting from state S, with g the
+// in-chunk running sum of log alpha, gamma = e^g, G_ri = e^(g_r - g_i),
+// A = strictly_lower(diag(beta)(K K^T o G)), T = (I + A)^-1, X = K S,
+// R = diag(beta)(V - gamma o X), E = T R, P = tril(Q K^T o G),
+// Kt_r = e^(g_C - g_r) k_r and dS' the gradient of the chunk-end state:
+//     dE = Kt dS' + P^T dY,   dR = T^T dE,   dA = -strictly_lower(dR E^T),
+//     dP = tril(dY E^T),      dV = diag(beta) dR,   dX = -diag(beta gamma) dR,
+//     dQ = diag(gamma) dY S^T + (dP o G) K,
+//     dK = diag(e^(g_C - g)) E dS'^T + (dP o G)^T Q + dX S^T + (N + N^T) K,
+//          N = diag(beta)(dA o G),
+//     dS = gamma_C dS' + (diag(gamma) Q)^T dY + K^T dX   (to the chunk before),
+// and the gradient of g gathers every decay factor (gamma, G, Kt, gamma_C);
+// d log alpha is its reverse running sum inside the chunk.
+//
+// The dS recurrence is separable by columns of the state, so one workgroup
+// owns one (sequence, head, 32-column tile of S). It first sweeps forward
+// over the chunks to rebuild the tile's chunk-start states (written to a
+// workspace), then sweeps backward. dV and dS0 belong to the tile's columns
+// and are written directly; dq, dk, dbeta and dlog alpha sum over all
+// columns, so each tile writes its partial sums and a second kernel adds the
+// tiles in a fixed order (no atomics: results are deterministic).
+//
+// Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32) with
+// operands staged in LDS; the work is split into phases separated by
+// workgroup barriers, each phase's 16x16 output tiles dealt round-robin to
+// the four waves.
+#include <type_traits>
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kC = 32;     // chunk length
+constexpr int kDVT = 32;   // state columns per workgroup
+constexpr int kNT = 256;   // threads
+constexpr int kNW = 4;     // waves
+constexpr int kLDV = kDVT + 4;
+constexpr int kLDC = kC + 4;
+
+// 16x16 output tile (rows m0.., cols n0..) of a product with contraction
+// length K (a multiple of 32). "row" operands are row-major with the
+// contraction index contiguous; "col" operands are row-major with the
+// contraction index as the row.
+__device__ __forceinline__ void mm_rr(f32x4 &acc, const float *A, int lda, const float *B, int ldb,
+                                      int m0, int n0, int K, int lc, int lg) {
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    Frag<float> fa, fb;
+    fa.load_row(A, lda, m0 + lc, k0, lg);
+    fb.load_row(B, ldb, n0 + lc, k0, lg);
+    mma(acc, fa, fb);
+  }
+}
+__device__ __forceinline__ void mm_rc(f32x4 &acc, const float *A, int lda, const float *B, int ldb,
+                                      int m0, int n0, int K, int lc, int lg) {
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    Frag<float> fa, fb;
+    fa.load_row(A, lda, m0 + lc, k0, lg);
+    fb.load_col(B, ldb, n0 + lc, k0, lg);
+    mma(acc, fa, fb);
+  }
+}
+__device__ __forceinline__ void mm_cc(f32x4 &acc, const float *A, int lda, const float *B, int ldb,
+                                      int m0, int n0, int K, int lc, int lg) {
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    Frag<float> fa, fb;
+    fa.load_col(A, lda, m0 + lc, k0, lg);
+    fb.load_col(B, ldb, n0 + lc, k0, lg);
+    mma(acc, fa, fb);
+  }
+}
+
+// sum over the 16 lanes of a row of the wave (lanes with the same lane / 16)
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+template <int DK, typename TIN, typename TG>
+__global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
+  constexpr int C = kC, DVT = kDVT, LDV = kLDV, LDC = kLDC;
+  constexpr int LDK = DK + 4;
+  constexpr int NKT = DK / 16;  // 16-row tiles of the state
+  constexpr int VEC = io<TIN>::kVec;
+
+  __shared__ __attribute__((aligned(16))) float Ks[C * LDK];
+  __shared__ __attribute__((aligned(16))) float Qs[C * LDK];
+  __shared__ __attribute__((aligned(16))) float Vs[C * LDV];
+  __shared__ __attribute__((aligned(16))) float dYs[C * LDV];
+  __shared__ __attribute__((aligned(16))) float Ss[DK * LDV];
+  __shared__ __attribute__((aligned(16))) float dSs[DK * LDV];
+  __shared__ __attribute__((aligned(16))) float Xs[C * LDV];
+  __shared__ __attribute__((aligned(16))) float Rs[C * LDV];
+  __shared__ __attribute__((aligned(16))) float Es[C * LDV];
+  __shared__ __attribute__((aligned(16))) float dEs[C * LDV];
+  __shared__ __attribute__((aligned(16))) float dRs[C * LDV];
+  __shared__ __attribute__((aligned(16))) float dXs[C * LDV];
+  __shared__ __attribute__((aligned(16))) float Am[C * LDC];   // A, strictly lower
+  __shared__ __attribute__((aligned(16))) float Tm[C * LDC];   // (I + A)^-1
+  __shared__ __attribute__((aligned(16))) float Pm[C * LDC];   // tril(Q K^T o G)
+  __shared__ __attribute__((aligned(16))) float KGm[C * LDC];  // tril(K K^T o G)
+  __shared__ __attribute__((aligned(16))) float dAm[C * LDC];
+  __shared__ __attribute__((aligned(16))) float Nm[C * LDC];   // diag(beta)(dA o G)
+  __shared__ __attribute__((aligned(16))) float dPm[C * LDC];
+  __shared__ __attribute__((aligned(16))) float dPGm[C * LDC];  // dP o G
+  __shared__ float s_g[C], s_gam[C], s_beta[C], s_kdec[C];
+  __shared__ float s_qsdy[2][C], s_dbu[2][C], s_dgx[2][C], s_cr[NKT][C];
+  __shared__ float s_dg[C], s_db[C], s_red[kNW];
+
+  const TIN *__restrict__ q = static_cast<const TIN *>(a.q);
+  const TIN *__restrict__ k = static_cast<const TIN *>(a.k);
+  const TIN *__restrict__ v = static_cast<const TIN *>(a.v);
+  const TG *__restrict__ dy = static_cast<const TG *>(a.dy);
+  TG *__restrict__ dv_out = static_cast<TG *>(a.dv);
+  const int H = a.H, DV = a.dv_size;
+  const int n_vt = DV / DVT;
+
+  // the n_vt column tiles of one (sequence, head) get ids that agree mod 8:
+  // they run on one XCD and share its L2 for the K, Q and gate reads
+  const int units = a.N * H;
+  const int grp = blockIdx.x / (8 * n_vt);
+  const int rem = blockIdx.x % (8 * n_vt);
+  const int vt = rem / 8;
+  const int unit = grp * 8 + rem % 8;
+  if (unit >= units) return;
+  const int h = unit % H;
+  const int n = unit / H;
+  int64_t bos, len;
+  if (a.cu_seqlens) {
+    int64_t s0 = a.cu_seqlens[n], s1 = a.cu_seqlens[n + 1];
+    s0 = s0 < 0 ? 0 : (s0 > a.T ? a.T : s0);
+    s1 = s1 < s0 ? s0 : (s1 > a.T ? a.T : s1);
+    bos = s0;
+    len = s1 - s0;
+  } else {
+    bos = static_cast<int64_t>(n) * a.T;
+    len = a.T;
+  }
+  const int nc = static_cast<int>((len + C - 1) / C);
+  // chunk-state slots of this sequence: floor(bos / C) + n + c never
+  // collide between sequences and stay below rows / C + N
+  const int64_t slot0 = bos / C + n;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lc = lane & 15;
+  const int lg = lane >> 4;
+  const int v0 = vt * DVT;
+  const size_t state_sz = static_cast<size_t>(DK) * DV;
+  float *const ws_states = a.ws_states;
+  const size_t part_stride = static_cast<size_t>(a.rows) * H;  // per tile, in rows*H
+
+  auto state_tile = [&](int c) {
+    return ws_states + (static_cast<size_t>(slot0 + c) * H + h) * state_sz + v0;
+  };
+
+  // ---- staging helpers ------------------------------------------------
+  auto rows_valid = [&](int c) -> int {
+    const int64_t r = len - static_cast<int64_t>(c) * C;
+    return r >= C ? C : static_cast<int>(r);
+  };
+  auto load_rows_k = [&](float *dst, const TIN *src, int64_t t0, int valid) {
+    constexpr int PER_ROW = DK / VEC;
+    for (int idx = tid; idx < C * PER_ROW; idx += kNT) {
+      const int r = idx / PER_ROW, d0 = (idx % PER_ROW) * VEC;
+      float x[VEC];
+      if (r < valid) {
+        io<TIN>::load16(src + ((t0 + r) * H + h) * DK + d0, x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dst[r * LDK + d0 + e] = x[e];
+    }
+  };
+  auto load_rows_v = [&](float *dst, const auto *src, int64_t t0, int valid) {
+    using T = typename std::remove_cv<typename std::remove_pointer<decltype(src)>::type>::type;
+    constexpr int V = io<T>::kVec;
+    constexpr int PER_ROW = DVT / V;
+    for (int idx = tid; idx < C * PER_ROW; idx += kNT) {
+      const int r = idx / PER_ROW, d0 = (idx % PER_ROW) * V;
+      float x[V];
+      if (r < valid) {
+        io<T>::load16(src + ((t0 + r) * H + h) * DV + v0 + d0, x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) x[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) dst[r * LDV + d0 + e] = x[e];
+    }
+  };
+  // gates of chunk c: wave 0 scans the log decays (rows past the end: 0)
+  auto scan_gates = [&](int64_t t0, int valid) {
+    if (wave == 0) {
+      float la = 0.0f, bt = 0.0f;
+      if (lane < valid) {
+        la = a.log_alpha[(t0 + lane) * H + h];
+        bt = a.beta[(t0 + lane) * H + h];
+      }
+      float g = la;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const float o = __shfl_up(g, off, 64);
+        if (lane >= off) g += o;
+      }
+      const float gC = __shfl(g, C - 1, 64);
+      if (lane < C) {
+        s_g[lane] = g;
+        s_gam[lane] = __expf(g);
+        s_beta[lane] = bt;
+        s_kdec[lane] = __expf(gC - g);
+      }
+    }
+  };
+  auto decay = [&](int r, int i) { return __expf(fminf(s_g[r] - s_g[i], 0.0f)); };
+  // the 3 lower 16x16 tiles of a 32x32 matrix: (0,0), (1,0), (1,1)
+  auto low_tile = [](int t, int &rt, int &ct) {
+    rt = t >= 1 ? 1 : 0;
+    ct = t == 2 ? 1 : 0;
+  };
+  // T = (I + A)^-1 for C = 32 by wave 0: 16x16 diagonal blocks by forward
+  // substitution (lane (lg < 2, lc) solves column lc of block lg), then
+  // T10 = -T11 (A10 T00) on the matrix cores
+  auto invert = [&]() {
+    if (wave != 0) return;
+    if (lg < 2) {
+      const int b0 = 16 * lg;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc = (r == lc) ? 1.0f : 0.0f;
+#pragma unroll
+        for (int i = 0; i < r; ++i) acc = fmaf(-Am[(b0 + r) * LDC + b0 + i], x[i], acc);
+        x[r] = acc;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDC + b0 + lc] = x[r];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDC + (16 - b0) + lc] = 0.0f;
+    }
+    // M = A10 T00 (16x16, contraction 16: the upper half of the slice is 0)
+    f32x4 M = zero4();
+    {
+      Frag<float> fa, fb;
+      fa.load_row_lo(Am, LDC, 16 + lc, 0, lg);
+      fb.load_col_lo(Tm, LDC, lc, 0, lg);
+      mma(M, fa, fb);
+    }
+    f32x4 T10 = zero4();
+    {
+      Frag<float> fa, fb;
+      fa.load_row_lo(Tm, LDC, 16 + lc, 16, lg);
+      fb.from_acc_lo(M);
+      mma(T10, fa, fb);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Tm[(16 + 4 * lg + i) * LDC + lc] = -T10[i];
+  };
+
+  // ======================= forward sweep: chunk-start states =============
+  // Ss holds the tile of the running state
+  for (int idx = tid; idx < DK * DVT; idx += kNT) {
+    const int r = idx / DVT, cc = idx % DVT;
+    Ss[r * LDV + cc] = a.S0 ? a.S0[static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc] : 0.0f;
+  }
+  __syncthreads();
+  for (int c = 0; c < nc; ++c) {
+    const int64_t t0 = bos + static_cast<int64_t>(c) * C;
+    const int valid = rows_valid(c);
+    {
+      float *dst = state_tile(c);
+      for (int idx = tid; idx < DK * DVT / 4; idx += kNT) {
+        const int r = idx / (DVT / 4), c4 = (idx % (DVT / 4)) * 4;
+        *reinterpret_cast<f32x4 *>(dst + static_cast<size_t>(r) * DV + c4) =
+            *reinterpret_cast<const f32x4 *>(Ss + r * LDV + c4);
+      }
+    }
+    load_rows_k(Ks, k, t0, valid);
+    load_rows_v(Vs, v, t0, valid);
+    scan_gates(t0, valid);
+    __syncthreads();
+    // A (3 tiles) and X = K S (4 tiles)
+    for (int t = wave; t < 7; t += kNW) {
+      f32x4 acc = zero4();
+      if (t < 3) {
+        int rt, ct;
+        low_tile(t, rt, ct);
+        mm_rr(acc, Ks, LDK, Ks, LDK, 16 * rt, 16 * ct, DK, lc, lg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * lg + i, col = 16 * ct + lc;
+          Am[r * LDC + col] = r > col ? s_beta[r] * decay(r, col) * acc[i] : 0.0f;
+        }
+        if (rt == 1 && ct == 0) {  // the upper tile of A is zero
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Am[(4 * lg + i) * LDC + 16 + lc] = 0.0f;
+        }
+      } else {
+        const int rt = (t - 3) >> 1, nt = (t - 3) & 1;
+        mm_rc(acc, Ks, LDK, Ss, LDV, 16 * rt, 16 * nt, DK, lc, lg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Xs[(16 * rt + 4 * lg + i) * LDV + 16 * nt + lc] = acc[i];
+      }
+    }
+    __syncthreads();
+    invert();
+    // R = beta (V - gamma X), all threads
+    for (int idx = tid; idx < C * DVT; idx += kNT) {
+      const int r = idx / DVT, cc = idx % DVT;
+      Rs[r * LDV + cc] = s_beta[r] * (Vs[r * LDV + cc] - s_gam[r] * Xs[r * LDV + cc]);
+    }
+    __syncthreads();
+    // kdec o E, E = T R (4 tiles)
+    for (int t = wave; t < 4; t += kNW) {
+      const int rt = t >> 1, nt = t & 1;
+      f32x4 acc = zero4();
+      mm_rc(acc, Tm, LDC, Rs, LDV, 16 * rt, 16 * nt, C, lc, lg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i;
+        Es[r * LDV + 16 * nt + lc] = s_kdec[r] * acc[i];
+      }
+    }
+    __syncthreads();
+    // S <- gamma_C S + K^T (kdec o E)  (NKT x 2 tiles, contraction over C)
+    const float gamC = s_gam[C - 1];
+    for (int t = wave; t < NKT * 2; t += kNW) {
+      const int mt = t >> 1, nt = t & 1;
+      f32x4 acc = zero4();
+      mm_cc(acc, Ks, LDK, Es, LDV, 16 * mt, 16 * nt, C, lc, lg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float *p = Ss + (16 * mt + 4 * lg + i) * LDV + 16 * nt + lc;
+        *p = gamC * *p + acc[i];
+      }
+    }
+    __syncthreads();
+  }
+
+  // ======================= backward sweep ================================
+  for (int idx = tid; idx < DK * DVT; idx += kNT) {
+    const int r = idx / DVT, cc = idx % DVT;
+    dSs[r * LDV + cc] =
+        a.dS_T ? a.dS_T[static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc] : 0.0f;
+  }
+  for (int c = nc - 1; c >= 0; --c) {
+    const int64_t t0 = bos + static_cast<int64_t>(c) * C;
+    const int valid = rows_valid(c);
+    {
+      const float *src = state_tile(c);
+      for (int idx = tid; idx < DK * DVT / 4; idx += kNT) {
+        const int r = idx / (DVT / 4), c4 = (idx % (DVT / 4)) * 4;
+        *reinterpret_cast<f32x4 *>(Ss + r * LDV + c4) =
+            *reinterpret_cast<const f32x4 *>(src + static_cast<size_t>(r) * DV + c4);
+      }
+    }
+    load_rows_k(Ks, k, t0, valid);
+    load_rows_k(Qs, q, t0, valid);
+    load_rows_v(Vs, v, t0, valid);
+    load_rows_v(dYs, dy, t0, valid);
+    scan_gates(t0, valid);
+    __syncthreads();
+
+    // ---- P1: A, K K^T o G, P (3 tiles each); X, Q S, Kt dS' (4 each) ----
+    for (int t = wave; t < 18; t += kNW) {
+      f32x4 acc = zero4();
+      if (t < 6) {
+        int rt, ct;
+        low_tile(t % 3, rt, ct);
+        const bool gram = t < 3;
+        mm_rr(acc, gram ? Ks : Qs, LDK, Ks, LDK, 16 * rt, 16 * ct, DK, lc, lg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * lg + i, col = 16 * ct + lc;
+          const float gv = r >= col ? decay(r, col) * acc[i] : 0.0f;
+          if (gram) {
+            KGm[r * LDC + col] = gv;
+            Am[r * LDC + col] = r > col ? s_beta[r] * gv : 0.0f;
+          } else {
+            Pm[r * LDC + col] = gv;
+          }
+        }
+        if (rt == 1 && ct == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int o = (4 * lg + i) * LDC + 16 + lc;
+            if (gram) {
+              KGm[o] = 0.0f;
+              Am[o] = 0.0f;
+            } else {
+              Pm[o] = 0.0f;
+            }
+          }
+        }
+      } else {
+        const int kind = (t - 6) / 4;  // 0: X, 1: Q S, 2: Kt dS'
+        const int rt = ((t - 6) % 4) >> 1, nt = (t - 6) & 1;
+        mm_rc(acc, kind == 1 ? Qs : Ks, LDK, kind == 2 ? dSs : Ss, LDV, 16 * rt, 16 * nt, DK,
+              lc, lg);
+        if (kind == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Xs[(16 * rt + 4 * lg + i) * LDV + 16 * nt + lc] = acc[i];
+        } else if (kind == 1) {
+          // gamma_r (Q S)_r . dY_r, summed over this tile's 16 columns
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rt + 4 * lg + i;
+            const float s = sum16(s_gam[r] * acc[i] * dYs[r * LDV + 16 * nt + lc]);
+            if (lc == 0) s_qsdy[nt][r] = s;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rt + 4 * lg + i;
+            dEs[r * LDV + 16 * nt + lc] = s_kdec[r] * acc[i];
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- P2: T; R = beta (V - gamma X) --------------------------------
+    invert();
+    for (int idx = tid; idx < C * DVT; idx += kNT) {
+      const int r = idx / DVT, cc = idx % DVT;
+      Rs[r * LDV + cc] = s_beta[r] * (Vs[r * LDV + cc] - s_gam[r] * Xs[r * LDV + cc]);
+    }
+    __syncthreads();
+
+    // ---- P3: E = T R; dE += P^T dY -------------------------------------
+    for (int t = wave; t < 8; t += kNW) {
+      const int rt = (t & 3) >> 1, nt = t & 1;
+      f32x4 acc = zero4();
+      if (t < 4) {
+        mm_rc(acc, Tm, LDC, Rs, LDV, 16 * rt, 16 * nt, C, lc, lg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Es[(16 * rt + 4 * lg + i) * LDV + 16 * nt + lc] = acc[i];
+      } else {
+        mm_cc(acc, Pm, LDC, dYs, LDV, 16 * rt, 16 * nt, C, lc, lg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dEs[(16 * rt + 4 * lg + i) * LDV + 16 * nt + lc] += acc[i];
+      }
+    }
+    __syncthreads();
+
+    // ---- P4: dR = T^T dE; dV, dX and their row sums ---------------------
+    for (int t = wave; t < 4; t += kNW) {
+      const int rt = t >> 1, nt = t & 1;
+      f32x4 acc = zero4();
+      mm_cc(acc, Tm, LDC, dEs, LDV, 16 * rt, 16 * nt, C, lc, lg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i, cc = 16 * nt + lc;
+        const float dr = acc[i];
+        dRs[r * LDV + cc] = dr;
+        const float bg = s_beta[r] * s_gam[r];
+        const float x = Xs[r * LDV + cc];
+        dXs[r * LDV + cc] = -bg * dr;
+        if (r < valid)
+          dv_out[((t0 + r) * H + h) * DV + v0 + cc] = io<TG>::from_f32(s_beta[r] * dr);
+        const float su = sum16(dr * (Vs[r * LDV + cc] - s_gam[r] * x));
+        const float sx = sum16(-bg * dr * x);
+        if (lc == 0) {
+          s_dbu[nt][r] = su;
+          s_dgx[nt][r] = sx;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- P5: dA = -strictly_lower(dR E^T), dP = tril(dY E^T) ------------
+    for (int t = wave; t < 6; t += kNW) {
+      int rt, ct;
+      low_tile(t % 3, rt, ct);
+      const bool isA = t < 3;
+      f32x4 acc = zero4();
+      mm_rr(acc, isA ? dRs : dYs, LDV, Es, LDV, 16 * rt, 16 * ct, DVT, lc, lg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i, col = 16 * ct + lc;
+        if (isA) {
+          const float d = r > col ? -acc[i] : 0.0f;
+          dAm[r * LDC + col] = d;
+          Nm[r * LDC + col] = r > col ? s_beta[r] * d * decay(r, col) : 0.0f;
+        } else {
+          const float d = r >= col ? acc[i] : 0.0f;
+          dPm[r * LDC + col] = d;
+          dPGm[r * LDC + col] = r >= col ? d * decay(r, col) : 0.0f;
+        }
+      }
+      if (rt == 1 && ct == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int o = (4 * lg + i) * LDC + 16 + lc;
+          if (isA) {
+            dAm[o] = 0.0f;
+            Nm[o] = 0.0f;
+          } else {
+            dPm[o] = 0.0f;
+            dPGm[o] = 0.0f;
+          }
+        }
+      }
+    }
+    // gamma_C <S, dS'> over the tile (every thread, then per wave)
+    {
+      float acc = 0.0f;
+      for (int idx = tid; idx < DK * DVT; idx += kNT) {
+        const int r = idx / DVT, cc = idx % DVT;
+        acc = fmaf(Ss[r * LDV + cc], dSs[r * LDV + cc], acc);
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
+      if (lane == 0) s_red[wave] = acc;
+    }
+    __syncthreads();
+
+    // ---- P6: partial dQ and dK (2 x NKT tiles each) ---------------------
+    for (int t = wave; t < 4 * NKT; t += kNW) {
+      const bool isQ = t < 2 * NKT;
+      const int tt = t % (2 * NKT);
+      const int rt = tt / NKT, kt = tt % NKT;
+      f32x4 acc = zero4();
+      if (isQ) {
+        // diag(gamma) dY S^T + (dP o G) K
+        mm_rr(acc, dYs, LDV, Ss, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] *= s_gam[16 * rt + 4 * lg + i];
+        mm_rc(acc, dPGm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
+      } else {
+        // diag(kdec) E dS'^T + (dP o G)^T Q + dX S^T + (N + N^T) K
+        mm_rr(acc, Es, LDV, dSs, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * lg + i;
+          acc[i] *= s_kdec[r];
+          const float cr = sum16(acc[i] * Ks[r * LDK + 16 * kt + lc]);
+          if (lc == 0) s_cr[kt][r] = cr;
+        }
+        mm_cc(acc, dPGm, LDC, Qs, LDK, 16 * rt, 16 * kt, C, lc, lg);
+        mm_rr(acc, dXs, LDV, Ss, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
+        mm_rc(acc, Nm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
+        mm_cc(acc, Nm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
+      }
+      float *dst = a.ws_part + ((static_cast<size_t>(isQ ? 0 : 1) * n_vt + vt) * part_stride) * DK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i;
+        if (r < valid) dst[((t0 + r) * H + h) * DK + 16 * kt + lc] = acc[i];
+      }
+    }
+    // Row work for dbeta and d log alpha: lane r < 32 of wave 0 owns row r
+    // (it reads dA, A, dP, P and row r of KG, then reuses row r of KG).
+    // The decay factors G_ri = e^(g_r - g_i) contribute W_ri = dP_ri P_ri +
+    // dA_ri A_ri to d g_r and -W_ri to d g_i; summed into d log alpha_s =
+    // sum_{r >= s} d g_r, every W_ri with both indices >= s cancels, leaving
+    // sum_{r >= s} sum_{i < s} W_ri. That sum is formed directly (row prefix
+    // M_rs = sum_{i < s} W_ri, stored over row r of KG) instead of adding
+    // and subtracting terms that cancel, which loses everything in fp32 when
+    // the true gradient is tiny (strong decay).
+    if (wave == 0 && lane < C) {
+      const int r = lane;
+      float db = s_dbu[0][r] + s_dbu[1][r];
+      s_dg[r] = s_qsdy[0][r] + s_qsdy[1][r] + s_dgx[0][r] + s_dgx[1][r];
+      float pre = 0.0f;
+      for (int i = 0; i < C; ++i) {
+        const int o = r * LDC + i;
+        db = fmaf(dAm[o], KGm[o], db);
+        KGm[o] = pre;  // M_ri: the prefix before column i
+        if (i < r) pre += dPm[o] * Pm[o] + dAm[o] * Am[o];
+      }
+      s_db[r] = db;
+    }
+    __syncthreads();
+
+    // ---- P7: dS <- gamma_C dS' + (diag(gamma) Q)^T dY + K^T dX; gates -----
+    const float gamC = s_gam[C - 1];
+    for (int t = wave; t < NKT * 2; t += kNW) {
+      const int mt = t >> 1, nt = t & 1;
+      f32x4 acc = zero4();
+      // (diag(gamma) Q)^T dY: gamma folded into the B operand (rows of dY)
+      for (int k0 = 0; k0 < C; k0 += 32) {
+        Frag<float> fa, fb;
+        fa.load_col(Qs, LDK, 16 * mt + lc, k0, lg);
+        fb.load_col(dYs, LDV, 16 * nt + lc, k0, lg);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          fb.v[j] *= s_gam[k0 + 4 * lg + j];
+          fb.v[4 + j] *= s_gam[k0 + 16 + 4 * lg + j];
+        }
+        mma(acc, fa, fb);
+      }
+      mm_cc(acc, Ks, LDK, dXs, LDV, 16 * mt, 16 * nt, C, lc, lg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float *p = dSs + (16 * mt + 4 * lg + i) * LDV + 16 * nt + lc;
+        *p = gamC * *p + acc[i];
+      }
+    }
+    if (wave == 0 && lane < C) {
+      // d log alpha_s = sum_{r >= s} (gamma and X terms of d g_r)
+      //               + sum_{r >= s} M_rs                  (decays G)
+      //               + sum_{r < s} cr_r                   (Kt: e^(g_C - g_r))
+      //               + gamma_C <S, dS'>                   (gamma_C)
+      // The Kt terms enter d g_r with - and d g_C with +; the exclusive
+      // prefix is what survives, again without forming the cancelling pair.
+      const int r = lane;
+      float rs = s_dg[r];
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const float o = __shfl_down(rs, off, 64);
+        if (r + off < C) rs += o;
+      }
+      float cr = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) cr += s_cr[kt][r];
+      float inc = cr;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const float o = __shfl_up(inc, off, 64);
+        if (r >= off) inc += o;
+      }
+      const float ex = __shfl_up(inc, 1, 64);  // the previous lane's inclusive sum
+      rs += r > 0 ? ex : 0.0f;
+      for (int i = r; i < C; ++i) rs += KGm[i * LDC + r];
+      rs += gamC * (s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+      if (r < valid) {
+        float *dst = a.ws_part + static_cast<size_t>(2) * n_vt * part_stride * DK;
+        dst[(static_cast<size_t>(vt) * 2) * part_stride + (t0 + r) * H + h] = s_db[r];
+        dst[(static_cast<size_t>(vt) * 2 + 1) * part_stride + (t0 + r) * H + h] = rs;
+      }
+    }
+    __syncthreads();
+  }
+  // dS0 for this tile
+  if (a.dS0) {
+    for (int idx = tid; idx < DK * DVT; idx += kNT) {
+      const int r = idx / DVT, cc = idx % DVT;
+      a.dS0[static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc] = dSs[r * LDV + cc];
+    }
+  }
+}
+
+// Sum of the column tiles' partial dq, dk (C x dk rows) and dbeta, dlog
+// alpha, in tile order.
+template <int DK, typename TG>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
+  const int n_vt = a.dv_size / kDVT;
+  const size_t part_stride = static_cast<size_t>(a.rows) * a.H;
+  const size_t total_k = part_stride * DK;
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < total_k) {
+    float sq = 0.0f, sk = 0.0f;
+    for (int t = 0; t < n_vt; ++t) {
+      sq += a.ws_part[(static_cast<size_t>(0) * n_vt + t) * total_k + i];
+      sk += a.ws_part[(static_cast<size_t>(1) * n_vt + t) * total_k + i];
+    }
+    static_cast<TG *>(a.dq)[i] = io<TG>::from_f32(sq);
+    static_cast<TG *>(a.dk)[i] = io<TG>::from_f32(sk);
+  }
+  if (i < part_stride) {
+    const float *g = a.ws_part + static_cast<size_t>(2) * n_vt * total_k;
+    float sb = 0.0f, sl = 0.0f;
+    for (int t = 0; t < n_vt; ++t) {
+      sb += g[(static_cast<size_t>(t) * 2) * part_stride + i];
+      sl += g[(static_cast<size_t>(t) * 2 + 1) * part_stride + i];
+    }
+    a.dbeta[i] = sb;
+    a.dlog_alpha[i] = sl;
+  }
+}
+
+template <int DK, typename TIN, typename TG>
+hipError_t launch_bwd_t(const BwdArgs &a) {
+  const int n_vt = a.dv_size / kDVT;
+  const int64_t units = static_cast<int64_t>(a.N) * a.H;
+  if (units > 0) {
+    const int64_t blocks = (units + 7) / 8 * 8 * n_vt;
+    hipLaunchKernelGGL((chunk_bwd_kernel<DK, TIN, TG>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kNT), 0, a.stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const size_t total = static_cast<size_t>(a.rows) * a.H * DK;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_reduce_kernel<DK, TG>), dim3(static_cast<unsigned>((total + 255) / 256)),
+                     dim3(256), 0, a.stream, a);
+  return hipGetLastError();
+}
+
+template <typename TIN, typename TG>
+hipError_t launch_bwd_d(const BwdArgs &a) {
+  return a.dk_size == 128 ? launch_bwd_t<128, TIN, TG>(a) : launch_bwd_t<64, TIN, TG>(a);
+}
+
+template <typename TIN>
+hipError_t launch_bwd_g(const BwdArgs &a) {
+  switch (a.grad_dtype) {
+    case 1: return launch_bwd_d<TIN, bf16_t>(a);
+    case 2: return launch_bwd_d<TIN, _Float16>(a);
+    default: return launch_bwd_d<TIN, float>(a);
+  }
+}
+
+}  // namespace
+
+// Workspace: the chunk-start states (one slot per chunk, floor(bos / C) + n
+// + c for chunk c of sequence n), then the column tiles' partial sums.
+size_t chunk_bwd_states_bytes(int64_t rows, int N, int H, int dk, int dv) {
+  const size_t slots = static_cast<size_t>(rows / kC + N);
+  const size_t states = slots * H * dk * dv * sizeof(float);
+  return (states + 255) / 256 * 256;
+}
+
+size_t chunk_bwd_workspace_size(int64_t rows, int N, int H, int dk, int dv) {
+  if (rows < 0 || N < 0 || H <= 0) return 0;
+  const size_t n_vt = static_cast<size_t>(dv / kDVT);
+  const size_t parts = n_vt * static_cast<size_t>(rows) * H * (2 * dk + 2) * sizeof(float);
+  return chunk_bwd_states_bytes(rows, N, H, dk, dv) + (parts + 255) / 256 * 256;
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs &a) {
+  switch (a.in_dtype) {
+    case 1: return launch_bwd_g<bf16_t>(a);
+    case 2: return launch_bwd_g<_Float16>(a);
+    default: return launch_bwd_g<float>(a);
+  }
+}
+
+}  // namespace gdn

@@ -85,7 +85,28 @@ struct GateArgs {
   hipStream_t stream;
 };
 
+// Chunked backward pass: gradients of <dy, y> + <dS_T, S_T>.
+struct BwdArgs {
+  const void *q, *k, *v;          // in_dtype
+  const float *log_alpha, *beta;
+  const float *S0;                // may be null (zeros)
+  const void *dy;                 // grad_dtype, [rows, H, dv]
+  const float *dS_T;              // may be null (zeros)
+  const int32_t *cu_seqlens;      // may be null
+  int N, T, H, dk_size, dv_size;
+  int64_t rows;
+  void *dq, *dk, *dv;             // grad_dtype
+  float *dlog_alpha, *dbeta;      // [rows, H]
+  float *dS0;                     // may be null
+  float *ws_states, *ws_part;     // workspace (see chunk_bwd_workspace_size)
+  int in_dtype, grad_dtype;
+  hipStream_t stream;
+};
+
 hipError_t launch_decode_step(const DecodeArgs &a);
+hipError_t launch_chunk_bwd(const BwdArgs &a);
+size_t chunk_bwd_workspace_size(int64_t rows, int N, int H, int dk, int dv);
+size_t chunk_bwd_states_bytes(int64_t rows, int N, int H, int dk, int dv);
 hipError_t launch_decode_fused(const DecodeArgs &a);  // dk == dv
 hipError_t launch_frontend(const FrontendArgs &a);
 hipError_t launch_output_gate(const GateArgs &a);

@@ -328,6 +328,45 @@ GDN_API int gdn_decode_fused(const void *q_raw, const void *k_raw,
                              int32_t H, int32_t d, int32_t in_dtype,
                              int32_t out_dtype, void *stream);
 
+/*
+ * Backward pass of the chunked prefill: the gradients of
+ *     L = <dy, y> + <dS_T, S_T>
+ * (y and S_T as gdn_chunk_fwd computes them from the same inputs) with
+ * respect to q, k, v, log_alpha, beta and S0. The pages report backward
+ * kernels for this mixer (page "NLP——技术报告解读-Qwen3.8-Flash-Next",
+ * section "Gated DeltaNet 核心机制" for the recurrence; the pwwt.cn page,
+ * section 2.1.1, "内核效率", for the kernels); these are the derivatives of
+ * that recurrence, computed chunk by chunk.
+ *
+ *   q, k, v, log_alpha, beta, S0, cu_seqlens, N, T, H, dk, dv
+ *                 the forward's inputs, as gdn_chunk_fwd (S0 NULL = zeros).
+ *   dy            [rows, H, dv] in grad_dtype: gradient of y.
+ *   dS_T          float32 [N, H, dk, dv] or NULL (zeros): gradient of S_T.
+ *   dq, dk_out    [rows, H, dk] in grad_dtype; dv_out [rows, H, dv].
+ *   dlog_alpha, dbeta   float32 [rows, H].
+ *   dS0           float32 [N, H, dk, dv] or NULL (not written).
+ *   workspace     device memory, 256-byte aligned, at least
+ *                 gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv) bytes,
+ *                 overwritten (it holds the state at every chunk start and
+ *                 per-column-tile partial sums).
+ * The states are recomputed from S0 (the forward's outputs are not needed).
+ * Every product runs in fp32. Rows must be covered by the sequences
+ * (cu_seqlens[N] = rows). Inputs must not overlap outputs or the workspace.
+ * Tensors are 16-byte aligned, the gates and cu_seqlens 4-byte aligned.
+ * Results are deterministic (partial sums are added in a fixed order).
+ */
+GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t rows, int32_t N, int32_t H,
+                                            int32_t dk, int32_t dv);
+GDN_API int gdn_chunk_bwd(const void *q, const void *k, const void *v,
+                          const float *log_alpha, const float *beta,
+                          const float *S0, const void *dy, const float *dS_T,
+                          const int32_t *cu_seqlens, int32_t N, int32_t T,
+                          int32_t H, int32_t dk, int32_t dv, void *dq,
+                          void *dk_out, void *dv_out, float *dlog_alpha,
+                          float *dbeta, float *dS0, int32_t in_dtype,
+                          int32_t grad_dtype, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a return code (static string, never NULL). */
 GDN_API const char *gdn_status_string(int status);
 

@@ -248,3 +248,35 @@ def test_decode_fused_rejects(lib):
     assert dec(cs=B + 4096) == -1           # conv_state overlaps S
     assert dec(cs=A + (6 << 20)) == -1      # conv_state overlaps z
     assert dec(cs=B + (1 << 28) + 8) == -3
+
+
+def test_chunk_bwd_rejects(lib):
+    v, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int64, i32, i32, i32, i32]
+    lib.gdn_chunk_bwd_workspace_size.restype = sz
+    lib.gdn_chunk_bwd.argtypes = [v] * 9 + [i32] * 5 + [v] * 6 + [i32, i32, v, sz, v]
+    need = lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 128, 128)
+    # states: (64/32 + 1) slots x 2 heads x 64 KiB; partials: 4 tiles x 64 x 2 x 258 x 4 B
+    assert need == 3 * 2 * 65536 + 4 * 64 * 2 * 258 * 4
+    assert lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 96, 128) == 0
+
+    def bwd(**kw):
+        a = dict(q=A, k=A + (1 << 26), v=A + (2 << 26), la=A + (3 << 26), b=A + (4 << 26),
+                 S0=None, dy=A + (5 << 26), dST=None, cu=None, N=1, T=64, H=2, dk=128, dv=128,
+                 dq=B, dko=B + (1 << 24), dvo=B + (2 << 24), dla=B + (3 << 24), db=B + (4 << 24),
+                 dS0=None, it=1, gt=1, ws=B + (1 << 28), wsb=need)
+        a.update(kw)
+        return lib.gdn_chunk_bwd(a["q"], a["k"], a["v"], a["la"], a["b"], a["S0"], a["dy"],
+                                 a["dST"], a["cu"], a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                                 a["dq"], a["dko"], a["dvo"], a["dla"], a["db"], a["dS0"], a["it"],
+                                 a["gt"], a["ws"], a["wsb"], None)
+
+    assert bwd(wsb=need - 1) == -1
+    assert bwd(ws=None) == -1
+    assert bwd(ws=B + (1 << 28) + 16) == -3
+    assert bwd(dq=None) == -1
+    assert bwd(dk=96) == -2
+    assert bwd(gt=5) == -2
+    assert bwd(dq=A) == -1                  # dq overlaps q
+    assert bwd(dko=B + 64) == -1            # dk overlaps dq
+    assert bwd(ws=B) == -1                  # workspace overlaps dq

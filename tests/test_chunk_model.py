@@ -44,3 +44,25 @@ def test_blocked_inverse_equals_dense():
         A = np.tril(rng.uniform(-1, 1, (C, C)), -1)
         T = chunk_model.unit_lower_inverse_blocked(A)
         assert np.abs(T @ (np.eye(C) + A) - np.eye(C)).max() < 1e-9
+
+
+@pytest.mark.parametrize("T,C", [(1, 64), (37, 64), (64, 16), (70, 32), (130, 64), (45, 1)])
+def test_chunk_bwd_model_equals_oracle(T, C):
+    import oracle
+    rng = np.random.default_rng(T * 7 + C)
+    dk, dv = 6, 5
+    q = rng.standard_normal((T, dk))
+    k = rng.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((T, dv))
+    la = -np.exp(rng.uniform(-3, 0.5, T))
+    b = rng.uniform(0, 1, T)
+    S0 = rng.standard_normal((dk, dv))
+    dy = rng.standard_normal((T, dv))
+    dST = rng.standard_normal((dk, dv))
+    got = chunk_model.chunk_bwd(q, k, v, la, b, S0, dy, dST, C=C)
+    ref = oracle.gdn_bwd(q[:, None], k[:, None], v[:, None], la[:, None], b[:, None],
+                         S0[None, None], dy[:, None], dST[None, None], N=1)
+    ref = [ref[0][:, 0], ref[1][:, 0], ref[2][:, 0], ref[3][:, 0], ref[4][:, 0], ref[5][0, 0]]
+    for gm, gr in zip(got, ref):
+        assert np.max(np.abs(gm - gr)) < 1e-9 * max(1.0, np.abs(gr).max())

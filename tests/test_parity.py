@@ -608,3 +608,81 @@ def test_decode_fused_slots_match_unfused_chain():
     for sl in range(n_slots):
         if sl not in touched:
             assert torch.equal(Sc[sl], pool_S[sl]) and torch.equal(cc[sl], pool_c[sl]), sl
+
+
+# ------------------------------------------------------------- backward -----
+def _bwd_inputs(lengths, H, dk, dv, dtype, seed, s0=True, dst=True):
+    inp = gi.prefill_inputs(len(lengths), H, 0, dk, dv, dtype, s0_std=0.02 if s0 else 0.0,
+                            seed=seed, lengths=lengths)
+    rows = inp["q"].shape[0]
+    dy = gi.normal((rows, H, dv), seed, 40)
+    dST = gi.normal((len(lengths), H, dk, dv), seed, 41) if dst else None
+    return inp, dy, dST
+
+
+def _check_bwd(inp, dy, dST, grad_dtype=torch.float32, tol=None):
+    g = _lib()
+    d = to_dev(inp)
+    dyd = dy.to(grad_dtype).cuda()
+    grads = g.gdn_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], dyd, S0=d["S0"],
+                            dS_T=None if dST is None else dST.cuda(),
+                            cu_seqlens=d["cu_seqlens"], N=d["N"], grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    ref = oracle.gdn_bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"],
+                         dyd.cpu(), dST, cu_seqlens=inp["cu_seqlens"], N=inp["N"])
+    tol = TOL[inp["dtype"]] if tol is None else tol
+    names = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0")
+    errs = {}
+    for nm, got, want in zip(names, grads, ref):
+        errs[nm] = rel_l2(got, want)
+    print("bwd rel_l2 " + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
+    for nm, e in errs.items():
+        assert np.isfinite(e) and e <= tol, (nm, e)
+    return grads
+
+
+@gpu
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_bwd_varlen(d, dtype):
+    inp, dy, dST = _bwd_inputs([1, 31, 32, 33, 100, 0, 65], 2, d, d, dtype, seed=100 + d)
+    _check_bwd(inp, dy, dST, tol=1e-5)
+
+
+@gpu
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+def test_chunk_bwd_rect_heads_no_state(dk, dv):
+    inp, dy, _ = _bwd_inputs([70, 9], 3, dk, dv, "f32", seed=dk + 2 * dv, s0=False, dst=False)
+    _check_bwd(inp, dy, None, tol=1e-5)
+
+
+@gpu
+def test_chunk_bwd_equal_length_bf16_grads_and_deterministic():
+    g = _lib()
+    inp = gi.prefill_inputs(2, 4, 200, 128, 128, "bf16", s0_std=0.02, seed=110)
+    dy = gi.normal((400, 4, 128), 110, 40)
+    inp2 = dict(inp)
+    grads = _check_bwd(inp2, dy, None, grad_dtype=torch.bfloat16, tol=2e-3)
+    d = to_dev(inp)
+    again = g.gdn_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                            dy.to(torch.bfloat16).cuda(), S0=d["S0"], N=2,
+                            grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(grads, again):
+        assert torch.equal(a_, b_)
+
+
+@gpu
+@pytest.mark.parametrize("case", ["no_decay", "strong_decay", "beta0", "beta1"])
+def test_chunk_bwd_gate_extremes(case):
+    inp, dy, dST = _bwd_inputs([90, 40], 2, 64, 64, "f32", seed=120)
+    rows = inp["q"].shape[0]
+    if case == "no_decay":
+        inp["log_alpha"] = torch.zeros(rows, 2)
+    elif case == "strong_decay":
+        inp["log_alpha"] = torch.full((rows, 2), -30.0)
+    elif case == "beta0":
+        inp["beta"] = torch.zeros(rows, 2)
+    else:
+        inp["beta"] = torch.ones(rows, 2)
+    _check_bwd(inp, dy, dST, tol=1e-5)
