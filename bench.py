@@ -162,6 +162,30 @@ def bench_prefill_gated(g, steps, warmup, copies=3):
                 tokens_per_s=tokens / (ms * 1e-3))
 
 
+def bench_backward(g, steps=5, warmup=1):
+    """gdn_chunk_bwd on the prefill workload (B=4 H=16 T=4096 d=128, bf16
+    q/k/v, bf16 dy and gradients, no S0, no dS_T): one call rebuilds the
+    chunk states and runs the reverse sweep plus the tile reduction."""
+    w = gi.WORKLOADS[1]
+    inp = gi.workload_inputs(1)
+    N, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    tokens = N * T
+    dev = torch.device("cuda", 0)
+    d = {k: inp[k].to(dev) for k in ("q", "k", "v", "log_alpha", "beta")}
+    dy = gi.normal((tokens, H, dv), 13, 40).to(torch.bfloat16).to(dev)
+    ws = torch.empty(g.gdn_chunk_bwd_workspace_size(tokens, N, H, dk, dv), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        g.gdn_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], dy, N=N, workspace=ws,
+                        want_dS0=False)
+
+    ms = time_launches(step, steps, warmup, stream) / steps
+    return dict(workload=w.name, entry_point="gdn_chunk_bwd", ms_per_call=ms,
+                tokens_per_s=tokens / (ms * 1e-3), workspace_MB=ws.numel() / 1e6)
+
+
 def bench_decode(g, n_steps=128, reps=2):
     w = gi.WORKLOADS[3]
     N, H, dk, dv = w.B, w.H, w.dk, w.dv
@@ -404,6 +428,9 @@ def main():
         print("[bench] prefill workload 1 with raw gates", file=sys.stderr, flush=True)
         rec["prefill_gated"] = bench_prefill_gated(g, args.steps, args.warmup)
         rec["prefill_gated"]["ms_vs_plain"] = rec["prefill_gated"]["ms_per_call"] / ms
+        print("[bench] backward on prefill workload 1", file=sys.stderr, flush=True)
+        rec["backward"] = bench_backward(g)
+        rec["backward"]["ms_vs_forward"] = rec["backward"]["ms_per_call"] / ms
         print("[bench] long-context prefill workload 2: B=1 H=32 T=65536", file=sys.stderr,
               flush=True)
         rec["longctx"] = bench_longctx(g)

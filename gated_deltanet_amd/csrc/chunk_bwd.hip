@@ -48,40 +48,78 @@ constexpr int kLDC = kC + 4;
 // 16x16 output tile (rows m0.., cols n0..) of a product with contraction
 // length K (a multiple of 32). "row" operands are row-major with the
 // contraction index contiguous; "col" operands are row-major with the
-// contraction index as the row.
+// contraction index as the row. Each fp32 fragment pair is 8 MFMAs; they
+// go to four independent accumulators (summed at the end) so a wave does
+// not wait on one long dependent chain.
+struct Acc4 {
+  f32x4 a[4];
+  __device__ __forceinline__ Acc4() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = zero4();
+  }
+  __device__ __forceinline__ void mma(const Frag<float> &x, const Frag<float> &y) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      a[j & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.v[j], y.v[j], a[j & 3], 0, 0, 0);
+  }
+  __device__ __forceinline__ void add_to(f32x4 &acc) const {
+    acc += (a[0] + a[1]) + (a[2] + a[3]);
+  }
+};
 __device__ __forceinline__ void mm_rr(f32x4 &acc, const float *A, int lda, const float *B, int ldb,
                                       int m0, int n0, int K, int lc, int lg) {
+  Acc4 s;
   for (int k0 = 0; k0 < K; k0 += 32) {
     Frag<float> fa, fb;
     fa.load_row(A, lda, m0 + lc, k0, lg);
     fb.load_row(B, ldb, n0 + lc, k0, lg);
-    mma(acc, fa, fb);
+    s.mma(fa, fb);
   }
+  s.add_to(acc);
 }
 __device__ __forceinline__ void mm_rc(f32x4 &acc, const float *A, int lda, const float *B, int ldb,
                                       int m0, int n0, int K, int lc, int lg) {
+  Acc4 s;
   for (int k0 = 0; k0 < K; k0 += 32) {
     Frag<float> fa, fb;
     fa.load_row(A, lda, m0 + lc, k0, lg);
     fb.load_col(B, ldb, n0 + lc, k0, lg);
-    mma(acc, fa, fb);
+    s.mma(fa, fb);
   }
+  s.add_to(acc);
 }
 __device__ __forceinline__ void mm_cc(f32x4 &acc, const float *A, int lda, const float *B, int ldb,
                                       int m0, int n0, int K, int lc, int lg) {
+  Acc4 s;
   for (int k0 = 0; k0 < K; k0 += 32) {
     Frag<float> fa, fb;
     fa.load_col(A, lda, m0 + lc, k0, lg);
     fb.load_col(B, ldb, n0 + lc, k0, lg);
-    mma(acc, fa, fb);
+    s.mma(fa, fb);
   }
+  s.add_to(acc);
 }
 
 // sum over the 16 lanes of a row of the wave (lanes with the same lane / 16)
-__device__ __forceinline__ float sum16(float x) {
+__device__ __forceinline__ float sum16(float x) { return row_sum<16>(x); }
+
+// 16 raw bytes of a 32- or 16-bit element type as floats
+template <typename T>
+__device__ __forceinline__ void raw16_to_f32(const u32x4 r, float *x) {
+  if constexpr (sizeof(T) == 4) {
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
-  return x;
+    for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(r[i]);
+  } else if constexpr (std::is_same<T, bf16_t>::value) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(r[i] << 16);
+      x[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
+  } else {
+    const f16x8 hv = __builtin_bit_cast(f16x8, r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = static_cast<float>(hv[i]);
+  }
 }
 
 template <int DK, typename TIN, typename TG>
@@ -168,47 +206,116 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     const int64_t r = len - static_cast<int64_t>(c) * C;
     return r >= C ? C : static_cast<int>(r);
   };
-  auto load_rows_k = [&](float *dst, const TIN *src, int64_t t0, int valid) {
-    constexpr int PER_ROW = DK / VEC;
-    for (int idx = tid; idx < C * PER_ROW; idx += kNT) {
-      const int r = idx / PER_ROW, d0 = (idx % PER_ROW) * VEC;
+  // Chunk inputs are fetched into registers one chunk ahead (raw 16-byte
+  // pieces, zeros past the sequence end) and staged into LDS at the start of
+  // the chunk, so their HBM latency hides behind the previous chunk's work.
+  constexpr int VG = io<TG>::kVec;
+  constexpr int KI = C * DK / VEC / kNT;                  // K / Q pieces per thread
+  constexpr int VI = (C * DVT / VEC + kNT - 1) / kNT;     // V pieces per thread
+  constexpr int GI = (C * DVT / VG + kNT - 1) / kNT;      // dY pieces per thread
+  constexpr int SI = DK * DVT / 4 / kNT;                  // state f32x4 per thread
+  static_assert(KI * VEC * kNT == C * DK && SI * 4 * kNT == DK * DVT, "staging shape");
+  struct Pre {
+    u32x4 k[KI], q[KI], v[VI], dy[GI];
+    f32x4 s[SI];
+    float la, bt;
+  };
+  const u32x4 zero_raw = {0u, 0u, 0u, 0u};
+  auto fetch = [&](Pre &p, int c, bool with_q, bool with_dy, bool with_state) {
+    const int64_t t0 = bos + static_cast<int64_t>(c) * C;
+    const int valid = rows_valid(c);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int idx = tid + kNT * i;
+      const int r = idx / (DK / VEC), d0 = (idx % (DK / VEC)) * VEC;
+      const size_t off = ((t0 + r) * H + h) * DK + d0;
+      p.k[i] = r < valid ? *reinterpret_cast<const u32x4 *>(k + off) : zero_raw;
+      if (with_q) p.q[i] = r < valid ? *reinterpret_cast<const u32x4 *>(q + off) : zero_raw;
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int idx = tid + kNT * i;
+      const int r = idx / (DVT / VEC), d0 = (idx % (DVT / VEC)) * VEC;
+      p.v[i] = (idx < C * DVT / VEC && r < valid)
+                   ? *reinterpret_cast<const u32x4 *>(v + ((t0 + r) * H + h) * DV + v0 + d0)
+                   : zero_raw;
+    }
+    if (with_dy) {
+#pragma unroll
+      for (int i = 0; i < GI; ++i) {
+        const int idx = tid + kNT * i;
+        const int r = idx / (DVT / VG), d0 = (idx % (DVT / VG)) * VG;
+        p.dy[i] = (idx < C * DVT / VG && r < valid)
+                      ? *reinterpret_cast<const u32x4 *>(dy + ((t0 + r) * H + h) * DV + v0 + d0)
+                      : zero_raw;
+      }
+    }
+    if (with_state) {
+      const float *src = state_tile(c);
+#pragma unroll
+      for (int i = 0; i < SI; ++i) {
+        const int idx = tid + kNT * i;
+        const int r = idx / (DVT / 4), c4 = (idx % (DVT / 4)) * 4;
+        p.s[i] = *reinterpret_cast<const f32x4 *>(src + static_cast<size_t>(r) * DV + c4);
+      }
+    }
+    p.la = 0.0f;
+    p.bt = 0.0f;
+    if (wave == 0 && lane < valid) {
+      p.la = a.log_alpha[(t0 + lane) * H + h];
+      p.bt = a.beta[(t0 + lane) * H + h];
+    }
+  };
+  auto stage = [&](const Pre &p, bool with_q, bool with_dy, bool with_state) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int idx = tid + kNT * i;
+      const int r = idx / (DK / VEC), d0 = (idx % (DK / VEC)) * VEC;
       float x[VEC];
-      if (r < valid) {
-        io<TIN>::load16(src + ((t0 + r) * H + h) * DK + d0, x);
-      } else {
+      raw16_to_f32<TIN>(p.k[i], x);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) x[e] = 0.0f;
+      for (int e = 0; e < VEC; ++e) Ks[r * LDK + d0 + e] = x[e];
+      if (with_q) {
+        raw16_to_f32<TIN>(p.q[i], x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) Qs[r * LDK + d0 + e] = x[e];
       }
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) dst[r * LDK + d0 + e] = x[e];
     }
-  };
-  auto load_rows_v = [&](float *dst, const auto *src, int64_t t0, int valid) {
-    using T = typename std::remove_cv<typename std::remove_pointer<decltype(src)>::type>::type;
-    constexpr int V = io<T>::kVec;
-    constexpr int PER_ROW = DVT / V;
-    for (int idx = tid; idx < C * PER_ROW; idx += kNT) {
-      const int r = idx / PER_ROW, d0 = (idx % PER_ROW) * V;
-      float x[V];
-      if (r < valid) {
-        io<T>::load16(src + ((t0 + r) * H + h) * DV + v0 + d0, x);
-      } else {
 #pragma unroll
-        for (int e = 0; e < V; ++e) x[e] = 0.0f;
+    for (int i = 0; i < VI; ++i) {
+      const int idx = tid + kNT * i;
+      if (idx < C * DVT / VEC) {
+        const int r = idx / (DVT / VEC), d0 = (idx % (DVT / VEC)) * VEC;
+        float x[VEC];
+        raw16_to_f32<TIN>(p.v[i], x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) Vs[r * LDV + d0 + e] = x[e];
       }
-#pragma unroll
-      for (int e = 0; e < V; ++e) dst[r * LDV + d0 + e] = x[e];
     }
-  };
-  // gates of chunk c: wave 0 scans the log decays (rows past the end: 0)
-  auto scan_gates = [&](int64_t t0, int valid) {
+    if (with_dy) {
+#pragma unroll
+      for (int i = 0; i < GI; ++i) {
+        const int idx = tid + kNT * i;
+        if (idx < C * DVT / VG) {
+          const int r = idx / (DVT / VG), d0 = (idx % (DVT / VG)) * VG;
+          float x[VG];
+          raw16_to_f32<TG>(p.dy[i], x);
+#pragma unroll
+          for (int e = 0; e < VG; ++e) dYs[r * LDV + d0 + e] = x[e];
+        }
+      }
+    }
+    if (with_state) {
+#pragma unroll
+      for (int i = 0; i < SI; ++i) {
+        const int idx = tid + kNT * i;
+        const int r = idx / (DVT / 4), c4 = (idx % (DVT / 4)) * 4;
+        *reinterpret_cast<f32x4 *>(Ss + r * LDV + c4) = p.s[i];
+      }
+    }
+    // gates: wave 0 scans the chunk's log decays (rows past the end: 0)
     if (wave == 0) {
-      float la = 0.0f, bt = 0.0f;
-      if (lane < valid) {
-        la = a.log_alpha[(t0 + lane) * H + h];
-        bt = a.beta[(t0 + lane) * H + h];
-      }
-      float g = la;
+      float g = p.la;
 #pragma unroll
       for (int off = 1; off < 32; off <<= 1) {
         const float o = __shfl_up(g, off, 64);
@@ -218,7 +325,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       if (lane < C) {
         s_g[lane] = g;
         s_gam[lane] = __expf(g);
-        s_beta[lane] = bt;
+        s_beta[lane] = p.bt;
         s_kdec[lane] = __expf(gC - g);
       }
     }
@@ -274,10 +381,10 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     const int r = idx / DVT, cc = idx % DVT;
     Ss[r * LDV + cc] = a.S0 ? a.S0[static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc] : 0.0f;
   }
+  Pre pf;
+  if (nc > 0) fetch(pf, 0, false, false, false);
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
-    const int64_t t0 = bos + static_cast<int64_t>(c) * C;
-    const int valid = rows_valid(c);
     {
       float *dst = state_tile(c);
       for (int idx = tid; idx < DK * DVT / 4; idx += kNT) {
@@ -286,9 +393,8 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
             *reinterpret_cast<const f32x4 *>(Ss + r * LDV + c4);
       }
     }
-    load_rows_k(Ks, k, t0, valid);
-    load_rows_v(Vs, v, t0, valid);
-    scan_gates(t0, valid);
+    stage(pf, false, false, false);
+    if (c + 1 < nc) fetch(pf, c + 1, false, false, false);
     __syncthreads();
     // A (3 tiles) and X = K S (4 tiles)
     for (int t = wave; t < 7; t += kNW) {
@@ -354,22 +460,12 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     dSs[r * LDV + cc] =
         a.dS_T ? a.dS_T[static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc] : 0.0f;
   }
+  if (nc > 0) fetch(pf, nc - 1, true, true, true);
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t t0 = bos + static_cast<int64_t>(c) * C;
     const int valid = rows_valid(c);
-    {
-      const float *src = state_tile(c);
-      for (int idx = tid; idx < DK * DVT / 4; idx += kNT) {
-        const int r = idx / (DVT / 4), c4 = (idx % (DVT / 4)) * 4;
-        *reinterpret_cast<f32x4 *>(Ss + r * LDV + c4) =
-            *reinterpret_cast<const f32x4 *>(src + static_cast<size_t>(r) * DV + c4);
-      }
-    }
-    load_rows_k(Ks, k, t0, valid);
-    load_rows_k(Qs, q, t0, valid);
-    load_rows_v(Vs, v, t0, valid);
-    load_rows_v(dYs, dy, t0, valid);
-    scan_gates(t0, valid);
+    stage(pf, true, true, true);
+    if (c > 0) fetch(pf, c - 1, true, true, true);
     __syncthreads();
 
     // ---- P1: A, K K^T o G, P (3 tiles each); X, Q S, Kt dS' (4 each) ----
@@ -590,16 +686,18 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       const int mt = t >> 1, nt = t & 1;
       f32x4 acc = zero4();
       // (diag(gamma) Q)^T dY: gamma folded into the B operand (rows of dY)
-      for (int k0 = 0; k0 < C; k0 += 32) {
+      {
+        Acc4 sacc;
         Frag<float> fa, fb;
-        fa.load_col(Qs, LDK, 16 * mt + lc, k0, lg);
-        fb.load_col(dYs, LDV, 16 * nt + lc, k0, lg);
+        fa.load_col(Qs, LDK, 16 * mt + lc, 0, lg);
+        fb.load_col(dYs, LDV, 16 * nt + lc, 0, lg);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          fb.v[j] *= s_gam[k0 + 4 * lg + j];
-          fb.v[4 + j] *= s_gam[k0 + 16 + 4 * lg + j];
+          fb.v[j] *= s_gam[4 * lg + j];
+          fb.v[4 + j] *= s_gam[16 + 4 * lg + j];
         }
-        mma(acc, fa, fb);
+        sacc.mma(fa, fb);
+        sacc.add_to(acc);
       }
       mm_cc(acc, Ks, LDK, dXs, LDV, 16 * mt, 16 * nt, C, lc, lg);
 #pragma unroll

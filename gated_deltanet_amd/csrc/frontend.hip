@@ -73,25 +73,6 @@ struct Vec8<bf16_t> {
   }
 };
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-
-// sum over the G consecutive lanes that own one row (G = 8 or 16: a half or a
-// whole 16-lane DPP row): pairs and quads by quad permutes, then quads joined
-// by the half-row and row mirrors; every lane ends with the row's sum
-template <int G>
-__device__ __forceinline__ float row_sum(float v) {
-  static_assert(G == 8 || G == 16, "row width");
-  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp<0x141>(v);  // row_half_mirror
-  if constexpr (G == 16) v += dpp<0x140>(v);  // row_mirror
-  return v;
-}
-
 // 1 / (1 + exp(-x)) with one v_exp_f32 and one v_rcp_f32 (about 1 ulp each);
 // exp overflows to inf for x < -88 and the reciprocal then gives 0
 __device__ __forceinline__ float sigmoid(float x) {

@@ -249,6 +249,25 @@ __device__ __forceinline__ f32x4 zero4() {
   return z;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// sum over the G consecutive lanes that own one row (G = 8 or 16: a half or a
+// whole 16-lane DPP row): pairs and quads by quad permutes, then quads joined
+// by the half-row and row mirrors; every lane ends with the row's sum
+template <int G>
+__device__ __forceinline__ float row_sum(float v) {
+  static_assert(G == 8 || G == 16, "row width");
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  if constexpr (G == 16) v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
 // Gates from raw per-head pre-activations (page "NLP——技术报告解读-
 // Qwen3.8-Flash-Next", section "GDN 参数化细节"): the decay gate is
 // alpha = exp(-exp(A) softplus(a + b_alpha)) and the write gate is
