@@ -77,6 +77,9 @@ def _bind(path):
     lib.oracle_gdn_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ip, i, i, i, i, i,
                                    dp, dp, dp, dp, dp, dp, i]
     lib.oracle_gdn_bwd.restype = i
+    lib.oracle_gates_from_raw_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                              ctypes.c_int64, i]
+    lib.oracle_gates_from_raw_bwd.restype = i
     lib.oracle_gates_from_raw.argtypes = [dp, dp, dp, dp, dp, dp,
                                           ctypes.c_int64, i]
     lib.oracle_gates_from_raw.restype = i
@@ -283,3 +286,19 @@ def gdn_bwd(q, k, v, log_alpha, beta, S0, dy, dS_T=None, cu_seqlens=None, N=None
                             _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(db), _ptr(dS0), int(nthreads))
     assert rc == 0
     return dq, dk_, dv_, dla, db, dS0
+
+
+def gates_from_raw_bwd(a, b, A, b_alpha, dlog_alpha, dbeta):
+    """Chain rule through gates_from_raw: returns (da, db, dA, db_alpha) with
+    dA, db_alpha summed over all rows, one value per head."""
+    lib = _load()
+    a, b, A, dla, dbt = (_f64(x) for x in (a, b, A, dlog_alpha, dbeta))
+    b_alpha = _f64(b_alpha)
+    H = a.shape[-1]
+    rows = a.size // H
+    da, db = np.zeros_like(a), np.zeros_like(a)
+    dA, dba = np.zeros(H), np.zeros(H)
+    rc = lib.oracle_gates_from_raw_bwd(_ptr(a), _ptr(b), _ptr(A), _ptr(b_alpha), _ptr(dla),
+                                       _ptr(dbt), _ptr(da), _ptr(db), _ptr(dA), _ptr(dba), rows, H)
+    assert rc == 0
+    return da, db, dA, dba

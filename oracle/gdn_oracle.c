@@ -392,6 +392,38 @@ int oracle_gates_from_raw(const double *a, const double *b, const double *A,
   return 0;
 }
 
+/* Gradients through the gate map above: given dlog_alpha and dbeta [rows,
+ * H], returns da, db [rows, H] and the per-head sums dA, db_alpha [H]:
+ *   d a       = dlog_alpha * (-exp(A_h) * sigmoid(a + b_alpha_h))
+ *   d b       = dbeta * beta (1 - beta),   beta = sigmoid(b)
+ *   d A_h     = sum over rows of dlog_alpha * log_alpha
+ *   d b_alpha = sum over rows of d a. */
+int oracle_gates_from_raw_bwd(const double *a, const double *b, const double *A,
+                              const double *b_alpha, const double *dlog_alpha,
+                              const double *dbeta, double *da, double *db,
+                              double *dA, double *db_alpha, int64_t rows, int H) {
+  if (rows < 0 || H <= 0) return -1;
+  for (int h = 0; h < H; ++h) {
+    dA[h] = 0.0;
+    db_alpha[h] = 0.0;
+  }
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int h = 0; h < H; ++h) {
+      const int64_t i = r * H + h;
+      const double x = a[i] + (b_alpha ? b_alpha[h] : 0.0);
+      const double sig = 1.0 / (1.0 + exp(-x));
+      const double sp = (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+      const double la = -exp(A[h]) * sp;
+      da[i] = dlog_alpha[i] * (-exp(A[h]) * sig);
+      const double bt = 1.0 / (1.0 + exp(-b[i]));
+      db[i] = dbeta[i] * bt * (1.0 - bt);
+      dA[h] += dlog_alpha[i] * la;
+      db_alpha[h] += da[i];
+    }
+  }
+  return 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -405,3 +405,33 @@ def test_bwd_zero_write_gate():
     assert np.max(np.abs(dS0[0, 0] - want)) < 1e-12
     for t in range(9):
         assert np.max(np.abs(dq[t, 0] - np.exp(g[t]) * S0[0, 0] @ dy[t, 0])) < 1e-12
+
+
+def test_gates_from_raw_bwd_matches_finite_differences():
+    """Central differences of <dla, log alpha> + <dbeta, beta> through the
+    oracle's gate map, for every a, b, A and b_alpha."""
+    rng = np.random.default_rng(34)
+    H = 3
+    a = rng.standard_normal((6, H)) * 3
+    b = rng.standard_normal((6, H)) * 3
+    A = rng.uniform(-2, 1, H)
+    ba = rng.standard_normal(H)
+    dla = rng.standard_normal((6, H))
+    dbt = rng.standard_normal((6, H))
+    da, db, dA, dba = oracle.gates_from_raw_bwd(a, b, A, ba, dla, dbt)
+
+    def loss(x):
+        la, bt = oracle.gates_from_raw(*x)
+        return float(np.sum(dla * la) + np.sum(dbt * bt))
+
+    base = [a, b, A, ba]
+    h = 1e-6
+    for which, g in enumerate((da, db, dA, dba)):
+        fd = np.zeros_like(base[which])
+        for idx in np.ndindex(fd.shape):
+            p_ = [x.copy() for x in base]
+            m_ = [x.copy() for x in base]
+            p_[which][idx] += h
+            m_[which][idx] -= h
+            fd[idx] = (loss(p_) - loss(m_)) / (2 * h)
+        assert np.max(np.abs(fd - g)) < 1e-7 * max(1.0, np.abs(fd).max()), which

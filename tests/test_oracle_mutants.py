@@ -58,6 +58,9 @@ MUTANTS = [
     ("bwd: dbeta sign", "dbeta[row] = db;", "dbeta[row] = -db;"),
     ("bwd: dlog_alpha without alpha", "dlog_alpha[row] = a * dalpha;", "dlog_alpha[row] = dalpha;"),
     ("bwd: dv without beta", "de[j] = b * acc;", "de[j] = acc;"),
+    ("gate bwd: softplus slope as beta", "da[i] = dlog_alpha[i] * (-exp(A[h]) * sig);",
+     "da[i] = dlog_alpha[i] * (-exp(A[h]) * (1.0 - sig));"),
+    ("gate bwd: dA without log_alpha", "dA[h] += dlog_alpha[i] * la;", "dA[h] += dlog_alpha[i];"),
 ]
 
 PIN_FUNCS = [
@@ -76,6 +79,7 @@ PIN_FUNCS = [
     pins.test_output_gate_against_torch_rms_norm,
     pins.test_gates_from_raw_against_torch_and_identities,
     pins.test_bwd_matches_finite_differences,
+    pins.test_gates_from_raw_bwd_matches_finite_differences,
 ]
 
 
