@@ -84,6 +84,10 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, ip, i32, i32, i32, i32, i32,
                                   vp, vp, vp, fp, fp, fp, i32, i32, vp, sz, vp]
     lib.gdn_chunk_bwd.restype = ctypes.c_int
+    lib.gdn_chunk_bwd_gated.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, ip, i32, i32, i32,
+                                        i32, i32, vp, vp, vp, fp, fp, fp, fp, fp, i32, i32, vp,
+                                        sz, vp]
+    lib.gdn_chunk_bwd_gated.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -220,6 +224,40 @@ def gdn_chunk_bwd(q, k, v, log_alpha, beta, dy, S0=None, dS_T=None, cu_seqlens=N
                            workspace.numel() * workspace.element_size(), _stream(dev))
     _check(rc, lib, "gdn_chunk_bwd")
     return dq, dk_, dv_, dla, db, dS0
+
+
+def gdn_chunk_bwd_gated(q, k, v, a, b, A, dy, b_alpha=None, S0=None, dS_T=None,
+                        cu_seqlens=None, N=None, grad_dtype=None, workspace=None, want_dS0=True):
+    """gdn_chunk_bwd for the raw-gate prefill (gdn_chunk_fwd_gated): returns
+    (dq, dk, dv, da, db, dA, db_alpha, dS0)."""
+    lib = load_library()
+    in_dtype = _prefill_checked(q, k, v, a, b, ("a", "b"))
+    grad_dtype = dy.dtype if grad_dtype is None else grad_dtype
+    _need(dy, "dy", grad_dtype)
+    N, T, H, dk, dv = _prefill_shape(q, v, S0, cu_seqlens, N)
+    _head_params(A, b_alpha, H)
+    if dS_T is not None:
+        _need(dS_T, "dS_T", torch.float32)
+    rows = q.numel() // (H * dk)
+    need = gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dev = q.device
+    dq = torch.empty(q.shape, dtype=grad_dtype, device=dev)
+    dk_ = torch.empty(k.shape, dtype=grad_dtype, device=dev)
+    dv_ = torch.empty(v.shape, dtype=grad_dtype, device=dev)
+    da = torch.empty(a.shape, dtype=torch.float32, device=dev)
+    db = torch.empty(b.shape, dtype=torch.float32, device=dev)
+    dA = torch.empty(H, dtype=torch.float32, device=dev)
+    dba = torch.empty(H, dtype=torch.float32, device=dev)
+    dS0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
+    rc = lib.gdn_chunk_bwd_gated(_p(q), _p(k), _p(v), _p(a), _p(b), _p(A), _p(b_alpha), _p(S0),
+                                 _p(dy), _p(dS_T), _p(cu_seqlens), N, T, H, dk, dv, _p(dq),
+                                 _p(dk_), _p(dv_), _p(da), _p(db), _p(dA), _p(dba), _p(dS0),
+                                 _dt(in_dtype), _dt(grad_dtype), _p(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc, lib, "gdn_chunk_bwd_gated")
+    return dq, dk_, dv_, da, db, dA, dba, dS0
 
 
 def _head_params(A, b_alpha, H):

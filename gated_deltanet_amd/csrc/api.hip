@@ -550,13 +550,17 @@ GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t rows, int32_t N, int32_t H, 
   return gdn::chunk_bwd_workspace_size(rows, N, H, dk, dv);
 }
 
-GDN_API int gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
-                          const float *beta, const float *S0, const void *dy, const float *dS_T,
-                          const int32_t *cu_seqlens, int32_t N, int32_t T, int32_t H, int32_t dk,
-                          int32_t dv, void *dq, void *dk_out, void *dv_out, float *dlog_alpha,
-                          float *dbeta, float *dS0, int32_t in_dtype, int32_t grad_dtype,
-                          void *workspace, size_t workspace_bytes, void *stream) {
-  g_last_error[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+int chunk_bwd_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                   const float *beta, const float *A, const float *b_alpha, const float *S0,
+                   const void *dy, const float *dS_T, const int32_t *cu_seqlens, int32_t N,
+                   int32_t T, int32_t H, int32_t dk, int32_t dv, void *dq, void *dk_out,
+                   void *dv_out, float *dlog_alpha, float *dbeta, float *dA, float *db_alpha,
+                   float *dS0, int32_t in_dtype, int32_t grad_dtype, void *workspace,
+                   size_t workspace_bytes, void *stream, const char *name) {
   if (N < 0 || T < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N, T must be >= 0 and H > 0");
   if (!head_size_ok(dk) || !head_size_ok(dv))
     return fail(GDN_ERR_UNSUPPORTED, "%s", "dk and dv must be 64 or 128");
@@ -599,6 +603,26 @@ GDN_API int gdn_chunk_bwd(const void *q, const void *k, const void *v, const flo
     for (int j = i + 1; j < 7; ++j)
       if (overlap(outs[i], out_n[i], outs[j], out_n[j]))
         return fail(GDN_ERR_INVALID_ARG, "%s", "outputs overlap");
+  if (A) {
+    if (!dA || !db_alpha) return fail(GDN_ERR_INVALID_ARG, "%s", "dA and db_alpha are required");
+    if (misaligned(A, 4) || misaligned(b_alpha, 4) || misaligned(dA, 4) ||
+        misaligned(db_alpha, 4))
+      return fail(GDN_ERR_MISALIGNED, "%s", "A, b_alpha, dA, db_alpha need 4-byte alignment");
+    const size_t nh = static_cast<size_t>(H) * 4;
+    const void *hin[2] = {A, b_alpha};
+    const void *hout[2] = {dA, db_alpha};
+    for (int i = 0; i < 2; ++i) {
+      for (int j = 0; j < 7; ++j)
+        if (overlap(hin[i], nh, outs[j], out_n[j]) || overlap(hout[i], nh, outs[j], out_n[j]))
+          return fail(GDN_ERR_INVALID_ARG, "%s", "per-head gate arguments overlap an output");
+      for (int j = 0; j < 9; ++j)
+        if (overlap(hout[i], nh, ins[j], in_n[j]))
+          return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps dA or db_alpha");
+      for (int j = 0; j < 2; ++j)
+        if (overlap(hout[i], nh, hin[j], nh) || (i != j && overlap(hout[i], nh, hout[j], nh)))
+          return fail(GDN_ERR_INVALID_ARG, "%s", "per-head gate arguments overlap");
+    }
+  }
 
   gdn::BwdArgs a;
   a.q = q;
@@ -625,10 +649,48 @@ GDN_API int gdn_chunk_bwd(const void *q, const void *k, const void *v, const flo
   a.ws_states = static_cast<float *>(workspace);
   a.ws_part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                         gdn::chunk_bwd_states_bytes(rows, N, H, dk, dv));
+  a.A = A;
+  a.b_alpha = A ? b_alpha : nullptr;
+  a.dA = dA;
+  a.db_alpha = db_alpha;
   a.in_dtype = in_dtype;
   a.grad_dtype = grad_dtype;
   a.stream = static_cast<hipStream_t>(stream);
-  return hip_status(gdn::launch_chunk_bwd(a), "gdn_chunk_bwd launch");
+  char where[64];
+  snprintf(where, sizeof(where), "%s launch", name);
+  return hip_status(gdn::launch_chunk_bwd(a), where);
+}
+
+}  // namespace
+
+extern "C" {
+
+GDN_API int gdn_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const float *beta, const float *S0, const void *dy, const float *dS_T,
+                          const int32_t *cu_seqlens, int32_t N, int32_t T, int32_t H, int32_t dk,
+                          int32_t dv, void *dq, void *dk_out, void *dv_out, float *dlog_alpha,
+                          float *dbeta, float *dS0, int32_t in_dtype, int32_t grad_dtype,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  g_last_error[0] = '\0';
+  return chunk_bwd_impl(q, k, v, log_alpha, beta, nullptr, nullptr, S0, dy, dS_T, cu_seqlens, N,
+                        T, H, dk, dv, dq, dk_out, dv_out, dlog_alpha, dbeta, nullptr, nullptr,
+                        dS0, in_dtype, grad_dtype, workspace, workspace_bytes, stream,
+                        "gdn_chunk_bwd");
+}
+
+GDN_API int gdn_chunk_bwd_gated(const void *q, const void *k, const void *v, const float *a,
+                                const float *b, const float *A, const float *b_alpha,
+                                const float *S0, const void *dy, const float *dS_T,
+                                const int32_t *cu_seqlens, int32_t N, int32_t T, int32_t H,
+                                int32_t dk, int32_t dv, void *dq, void *dk_out, void *dv_out,
+                                float *da, float *db, float *dA, float *db_alpha, float *dS0,
+                                int32_t in_dtype, int32_t grad_dtype, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  g_last_error[0] = '\0';
+  if (H > 0 && !A) return fail(GDN_ERR_INVALID_ARG, "%s", "A is required");
+  return chunk_bwd_impl(q, k, v, a, b, A, b_alpha, S0, dy, dS_T, cu_seqlens, N, T, H, dk, dv, dq,
+                        dk_out, dv_out, da, db, dA, db_alpha, dS0, in_dtype, grad_dtype,
+                        workspace, workspace_bytes, stream, "gdn_chunk_bwd_gated");
 }
 
 }  // extern "C"

@@ -197,6 +197,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   float *const ws_states = a.ws_states;
   const size_t part_stride = static_cast<size_t>(a.rows) * H;  // per tile, in rows*H
 
+  const RawGate gate = RawGate::load(a.A, a.b_alpha, h);
   auto state_tile = [&](int c) {
     return ws_states + (static_cast<size_t>(slot0 + c) * H + h) * state_sz + v0;
   };
@@ -264,6 +265,10 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     if (wave == 0 && lane < valid) {
       p.la = a.log_alpha[(t0 + lane) * H + h];
       p.bt = a.beta[(t0 + lane) * H + h];
+      if (gate.raw()) {
+        p.la = gate.log_alpha(p.la);
+        p.bt = RawGate::beta(p.bt);
+      }
     }
   };
   auto stage = [&](const Pre &p, bool with_q, bool with_dy, bool with_state) {
@@ -768,14 +773,59 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
     static_cast<TG *>(a.dk)[i] = io<TG>::from_f32(sk);
   }
   if (i < part_stride) {
-    const float *g = a.ws_part + static_cast<size_t>(2) * n_vt * total_k;
+    float *g = a.ws_part + static_cast<size_t>(2) * n_vt * total_k;
     float sb = 0.0f, sl = 0.0f;
     for (int t = 0; t < n_vt; ++t) {
       sb += g[(static_cast<size_t>(t) * 2) * part_stride + i];
       sl += g[(static_cast<size_t>(t) * 2 + 1) * part_stride + i];
     }
-    a.dbeta[i] = sb;
-    a.dlog_alpha[i] = sl;
+    if (a.A) {
+      // chain rule through log alpha = -e^A softplus(a + b_alpha) and
+      // beta = sigmoid(b); the per-row terms of dA and db_alpha go over
+      // tile 0's partials (this thread has read them) for the head sums
+      const int h = static_cast<int>(i % a.H);
+      const RawGate gate = RawGate::load(a.A, a.b_alpha, h);
+      const float x = a.log_alpha[i] + gate.bias;
+      const float sig = 1.0f / (1.0f + expf(-x));
+      const float da = sl * (-gate.scale * sig);
+      const float bt = RawGate::beta(a.beta[i]);
+      a.dbeta[i] = sb * bt * (1.0f - bt);
+      a.dlog_alpha[i] = da;
+      g[i] = sl * gate.log_alpha(a.log_alpha[i]);
+      g[part_stride + i] = da;
+    } else {
+      a.dbeta[i] = sb;
+      a.dlog_alpha[i] = sl;
+    }
+  }
+}
+
+// Per-head sums over rows of the raw-gate terms (dA and db_alpha): one
+// workgroup per head, each thread sums rows in order, then a fixed tree.
+__global__ __launch_bounds__(256) void head_sum_kernel(const BwdArgs a) {
+  const int h = blockIdx.x;
+  const int n_vt = a.dv_size / kDVT;
+  const size_t part_stride = static_cast<size_t>(a.rows) * a.H;
+  const float *g = a.ws_part + static_cast<size_t>(2) * n_vt * part_stride * a.dk_size;
+  float s0 = 0.0f, s1 = 0.0f;
+  for (int64_t r = threadIdx.x; r < a.rows; r += 256) {
+    s0 += g[r * a.H + h];
+    s1 += g[part_stride + r * a.H + h];
+  }
+  __shared__ float red[2][256];
+  red[0][threadIdx.x] = s0;
+  red[1][threadIdx.x] = s1;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + w];
+      red[1][threadIdx.x] += red[1][threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    a.dA[h] = red[0][0];
+    a.db_alpha[h] = red[1][0];
   }
 }
 
@@ -791,9 +841,13 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
     if (e != hipSuccess) return e;
   }
   const size_t total = static_cast<size_t>(a.rows) * a.H * DK;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_reduce_kernel<DK, TG>), dim3(static_cast<unsigned>((total + 255) / 256)),
-                     dim3(256), 0, a.stream, a);
+  if (total > 0) {
+    hipLaunchKernelGGL((bwd_reduce_kernel<DK, TG>),
+                       dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, a.stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.A) hipLaunchKernelGGL(head_sum_kernel, dim3(a.H), dim3(256), 0, a.stream, a);
   return hipGetLastError();
 }
 

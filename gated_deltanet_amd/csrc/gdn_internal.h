@@ -99,6 +99,10 @@ struct BwdArgs {
   float *dlog_alpha, *dbeta;      // [rows, H]
   float *dS0;                     // may be null
   float *ws_states, *ws_part;     // workspace (see chunk_bwd_workspace_size)
+  // raw gates: log_alpha / beta then hold a / b, dlog_alpha / dbeta receive
+  // da / db, and dA, db_alpha [H] the per-head sums
+  const float *A = nullptr, *b_alpha = nullptr;
+  float *dA = nullptr, *db_alpha = nullptr;
   int in_dtype, grad_dtype;
   hipStream_t stream;
 };

@@ -367,6 +367,26 @@ GDN_API int gdn_chunk_bwd(const void *q, const void *k, const void *v,
                           int32_t grad_dtype, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/*
+ * Backward pass with the gates given as raw pre-activations (as
+ * gdn_chunk_fwd_gated): a, b [rows, H] replace log_alpha and beta, A [H]
+ * (required) and b_alpha [H] (or NULL) are the per-head parameters, and the
+ * gate gradients come back through the gate map: da, db [rows, H] float32
+ * and dA, db_alpha [H] float32 (sums over all rows; written even when
+ * b_alpha is NULL). Every other argument as gdn_chunk_bwd.
+ */
+GDN_API int gdn_chunk_bwd_gated(const void *q, const void *k, const void *v,
+                                const float *a, const float *b, const float *A,
+                                const float *b_alpha, const float *S0,
+                                const void *dy, const float *dS_T,
+                                const int32_t *cu_seqlens, int32_t N, int32_t T,
+                                int32_t H, int32_t dk, int32_t dv, void *dq,
+                                void *dk_out, void *dv_out, float *da, float *db,
+                                float *dA, float *db_alpha, float *dS0,
+                                int32_t in_dtype, int32_t grad_dtype,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
 /* Human-readable name of a return code (static string, never NULL). */
 GDN_API const char *gdn_status_string(int status);
 

@@ -686,3 +686,32 @@ def test_chunk_bwd_gate_extremes(case):
     else:
         inp["beta"] = torch.ones(rows, 2)
     _check_bwd(inp, dy, dST, tol=1e-5)
+
+
+@gpu
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_chunk_bwd_gated(with_bias):
+    """Backward through the in-kernel gate map against the oracle chain:
+    backward recurrence, then the gate map's chain rule."""
+    g = _lib()
+    inp, dy, dST = _bwd_inputs([70, 33, 1], 2, 64, 64, "bf16", seed=130)
+    rows = inp["q"].shape[0]
+    a, b, A, b_alpha = gi.raw_gates(rows, 2, 131)
+    if not with_bias:
+        b_alpha = None
+    d = to_dev(inp)
+    out = g.gdn_chunk_bwd_gated(d["q"], d["k"], d["v"], a.cuda(), b.cuda(), A.cuda(), dy.cuda(),
+                                b_alpha=None if b_alpha is None else b_alpha.cuda(), S0=d["S0"],
+                                dS_T=dST.cuda(), cu_seqlens=d["cu_seqlens"])
+    torch.cuda.synchronize()
+    la, bt = oracle.gates_from_raw(a, b, A, b_alpha)
+    dq, dk, dv, dla, dbt, dS0 = oracle.gdn_bwd(inp["q"], inp["k"], inp["v"], la, bt, inp["S0"],
+                                               dy, dST, cu_seqlens=inp["cu_seqlens"],
+                                               N=inp["N"])
+    da, db, dA, dba = oracle.gates_from_raw_bwd(a, b, A, b_alpha, dla, dbt)
+    want = (dq, dk, dv, da, db, dA, dba, dS0)
+    names = ("dq", "dk", "dv", "da", "db", "dA", "db_alpha", "dS0")
+    for nm, got, w in zip(names, out, want):
+        e = rel_l2(got, w)
+        print(nm, "%.2e" % e, flush=True)
+        assert e <= 1e-5, (nm, e)
