@@ -88,6 +88,9 @@ def load_library(path: str = LIB_PATH):
                                         i32, i32, vp, vp, vp, fp, fp, fp, fp, fp, i32, i32, vp,
                                         sz, vp]
     lib.gdn_chunk_bwd_gated.restype = ctypes.c_int
+    lib.gdn_conv_state_from_prefill.argtypes = [vp, vp, vp, ip, i32, i32, i32, i32, ip, i32, vp,
+                                                i32, vp]
+    lib.gdn_conv_state_from_prefill.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -258,6 +261,41 @@ def gdn_chunk_bwd_gated(q, k, v, a, b, A, dy, b_alpha=None, S0=None, dS_T=None,
                                  workspace.numel() * workspace.element_size(), _stream(dev))
     _check(rc, lib, "gdn_chunk_bwd_gated")
     return dq, dk_, dv_, da, db, dA, dba, dS0
+
+
+def gdn_conv_state_from_prefill(q_raw, k_raw, v_raw, cu_seqlens=None, N=None, slot_idx=None,
+                                conv_state=None, n_slots=None):
+    """Convolution cache [slots, H, 3, 3, d] for gdn_decode_fused from a
+    prefill batch's raw projections [rows, H, d]: the last three raw rows of
+    each sequence, oldest first, zero-padded. Written into conv_state (or a
+    new tensor of N slots, or n_slots with slot_idx) and returned."""
+    lib = load_library()
+    dt = q_raw.dtype
+    for t, nm in ((q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw")):
+        _need(t, nm, dt)
+    H, d = q_raw.shape[-2], q_raw.shape[-1]
+    rows = q_raw.numel() // (H * d)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+        T = rows
+    else:
+        N = 1 if N is None else int(N)
+        if N <= 0 or rows % N:
+            raise GdnError("rows must be a multiple of N")
+        T = rows // N
+    if slot_idx is not None:
+        _need(slot_idx, "slot_idx", torch.int32)
+    if conv_state is None:
+        slots = N if slot_idx is None else int(n_slots)
+        conv_state = torch.zeros((slots, H, 3, 3, d), dtype=dt, device=q_raw.device)
+    _need(conv_state, "conv_state", dt)
+    slots = conv_state.shape[0]
+    rc = lib.gdn_conv_state_from_prefill(_p(q_raw), _p(k_raw), _p(v_raw), _p(cu_seqlens), N, T,
+                                         H, d, _p(slot_idx), slots, _p(conv_state), _dt(dt),
+                                         _stream(q_raw.device))
+    _check(rc, lib, "gdn_conv_state_from_prefill")
+    return conv_state
 
 
 def _head_params(A, b_alpha, H):

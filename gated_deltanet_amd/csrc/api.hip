@@ -693,4 +693,47 @@ GDN_API int gdn_chunk_bwd_gated(const void *q, const void *k, const void *v, con
                         workspace, workspace_bytes, stream, "gdn_chunk_bwd_gated");
 }
 
+GDN_API int gdn_conv_state_from_prefill(const void *q_raw, const void *k_raw, const void *v_raw,
+                                        const int32_t *cu_seqlens, int32_t N, int32_t T,
+                                        int32_t H, int32_t d, const int32_t *slot_idx,
+                                        int32_t n_slots, void *conv_state, int32_t dtype,
+                                        void *stream) {
+  g_last_error[0] = '\0';
+  if (N < 0 || T < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N, T must be >= 0 and H > 0");
+  if (!head_size_ok(d)) return fail(GDN_ERR_UNSUPPORTED, "%s", "d must be 64 or 128");
+  if (!dtype_ok(dtype)) return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32, GDN_BF16 or GDN_F16");
+  const int64_t slots = slot_idx ? n_slots : N;
+  if (slots < 0) return fail(GDN_ERR_INVALID_ARG, "%s", "n_slots must be >= 0");
+  const int64_t rows = cu_seqlens ? static_cast<int64_t>(T) : static_cast<int64_t>(N) * T;
+  if (rows * H * d >= (int64_t{1} << 40) || static_cast<int64_t>(N) * H >= (int64_t{1} << 31))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "input too large");
+  if (N > 0 && (!q_raw || !k_raw || !v_raw || (slots > 0 && !conv_state)))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "null pointer");
+  if (misaligned(cu_seqlens, 4) || misaligned(slot_idx, 4) || misaligned(conv_state, 4))
+    return fail(GDN_ERR_MISALIGNED, "%s", "cu_seqlens, slot_idx and conv_state need 4-byte alignment");
+  const size_t eb = esize(dtype);
+  const size_t nin = static_cast<size_t>(rows) * H * d * eb;
+  const size_t ncs = static_cast<size_t>(slots) * H * 9 * d * eb;
+  const void *ins[5] = {q_raw, k_raw, v_raw, cu_seqlens, slot_idx};
+  const size_t in_n[5] = {nin, nin, nin, static_cast<size_t>(N + 1) * 4, static_cast<size_t>(N) * 4};
+  for (int i = 0; i < 5; ++i)
+    if (overlap(ins[i], in_n[i], conv_state, ncs))
+      return fail(GDN_ERR_INVALID_ARG, "%s", "an input overlaps conv_state");
+  gdn::ConvStateArgs a;
+  a.xq = q_raw;
+  a.xk = k_raw;
+  a.xv = v_raw;
+  a.cu_seqlens = cu_seqlens;
+  a.slot_idx = slot_idx;
+  a.N = N;
+  a.T = T;
+  a.H = H;
+  a.d = d;
+  a.n_slots = static_cast<int>(slots);
+  a.elem_bytes = static_cast<int>(eb);
+  a.conv_state = conv_state;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_conv_state(a), "gdn_conv_state_from_prefill launch");
+}
+
 }  // extern "C"

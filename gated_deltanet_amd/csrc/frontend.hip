@@ -312,6 +312,50 @@ hipError_t with_type(int code, F &&f) {
 
 }  // namespace
 
+// Convolution cache after a prefill: for each sequence, head and stream the
+// last three raw rows, oldest first, zeros where the sequence is shorter;
+// a plain copy of the raw bits (element type E of the raw projections).
+template <typename E>
+__global__ __launch_bounds__(256) void conv_state_kernel(const ConvStateArgs a) {
+  const int n = blockIdx.x / a.H;
+  const int h = blockIdx.x % a.H;
+  const int slot = a.slot_idx ? a.slot_idx[n] : n;
+  if (slot < 0 || slot >= a.n_slots) return;
+  int64_t bos, len;
+  if (a.cu_seqlens) {
+    int64_t s0 = a.cu_seqlens[n], s1 = a.cu_seqlens[n + 1];
+    s0 = s0 < 0 ? 0 : (s0 > a.T ? a.T : s0);
+    s1 = s1 < s0 ? s0 : (s1 > a.T ? a.T : s1);
+    bos = s0;
+    len = s1 - s0;
+  } else {
+    bos = static_cast<int64_t>(n) * a.T;
+    len = a.T;
+  }
+  const E *src[3] = {static_cast<const E *>(a.xq), static_cast<const E *>(a.xk),
+                     static_cast<const E *>(a.xv)};
+  E *dst = static_cast<E *>(a.conv_state) + (static_cast<size_t>(slot) * a.H + h) * 9 * a.d;
+  for (int idx = threadIdx.x; idx < 9 * a.d; idx += 256) {
+    const int s = idx / (3 * a.d);      // stream
+    const int r = (idx / a.d) % 3;      // 0 = oldest
+    const int c = idx % a.d;
+    const int64_t t = len - 3 + r;      // row inside the sequence
+    dst[idx] = t >= 0 ? src[s][((bos + t) * a.H + h) * a.d + c] : E(0);
+  }
+}
+
+hipError_t launch_conv_state(const ConvStateArgs &a) {
+  const int64_t blocks = static_cast<int64_t>(a.N) * a.H;
+  if (blocks == 0) return hipSuccess;
+  if (a.elem_bytes == 4)
+    hipLaunchKernelGGL(conv_state_kernel<uint32_t>, dim3(static_cast<unsigned>(blocks)), dim3(256),
+                       0, a.stream, a);
+  else
+    hipLaunchKernelGGL(conv_state_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256),
+                       0, a.stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_frontend(const FrontendArgs &a) {
   if (a.rows == 0) return hipSuccess;
   return with_type(a.in_dtype, [&](auto tin) {

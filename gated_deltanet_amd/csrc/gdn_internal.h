@@ -107,6 +107,18 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// Convolution cache of the fused decode from a prefill's raw projections.
+struct ConvStateArgs {
+  const void *xq, *xk, *xv;       // raw projections [rows, H, d]
+  const int32_t *cu_seqlens;      // may be null
+  const int32_t *slot_idx;        // [N] or null (slot n)
+  int N, T, H, d, n_slots;
+  int elem_bytes;
+  void *conv_state;               // [n_slots, H, 3, 3, d]
+  hipStream_t stream;
+};
+
+hipError_t launch_conv_state(const ConvStateArgs &a);
 hipError_t launch_decode_step(const DecodeArgs &a);
 hipError_t launch_chunk_bwd(const BwdArgs &a);
 size_t chunk_bwd_workspace_size(int64_t rows, int N, int H, int dk, int dv);

@@ -387,6 +387,24 @@ GDN_API int gdn_chunk_bwd_gated(const void *q, const void *k, const void *v,
                                 void *workspace, size_t workspace_bytes,
                                 void *stream);
 
+/*
+ * Convolution cache of gdn_decode_fused after a prefill: for every sequence
+ * of a prefill batch (layout as gdn_frontend_qkv's raw inputs) and head,
+ * writes the last three raw rows of q_raw, k_raw and v_raw, oldest first,
+ * with zeros in place of rows before the sequence start, into
+ * conv_state [slots, H, 3, 3, d] (dtype as the raw rows) at slot
+ * slot_idx[n] (int32 device array, or NULL for slot n with slots = N;
+ * entries outside [0, n_slots) are skipped). A pure copy: the rows the
+ * short causal convolution of the next decode token needs.
+ */
+GDN_API int gdn_conv_state_from_prefill(const void *q_raw, const void *k_raw,
+                                        const void *v_raw,
+                                        const int32_t *cu_seqlens, int32_t N,
+                                        int32_t T, int32_t H, int32_t d,
+                                        const int32_t *slot_idx, int32_t n_slots,
+                                        void *conv_state, int32_t dtype,
+                                        void *stream);
+
 /* Human-readable name of a return code (static string, never NULL). */
 GDN_API const char *gdn_status_string(int status);
 

@@ -280,3 +280,29 @@ def test_chunk_bwd_rejects(lib):
     assert bwd(dq=A) == -1                  # dq overlaps q
     assert bwd(dko=B + 64) == -1            # dk overlaps dq
     assert bwd(ws=B) == -1                  # workspace overlaps dq
+
+
+def test_conv_state_and_gated_bwd_reject(lib):
+    v, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.gdn_conv_state_from_prefill.argtypes = [v, v, v, v] + [i32] * 4 + [v, i32, v, i32, v]
+    assert lib.gdn_conv_state_from_prefill(A, A + (1 << 20), A + (2 << 20), None, 2, 10, 2, 96,
+                                           None, 0, B, 1, None) == -2
+    assert lib.gdn_conv_state_from_prefill(A, A + (1 << 20), A + (2 << 20), None, 2, 10, 2, 64,
+                                           None, 0, None, 1, None) == -1
+    # conv_state (2 slots x 2 heads x 9 x 64 x 2 B) overlapping k_raw
+    assert lib.gdn_conv_state_from_prefill(A, A + (1 << 20), A + (2 << 20), None, 2, 10, 2, 64,
+                                           None, 0, A + (1 << 20) + 64, 1, None) == -1
+    assert lib.gdn_conv_state_from_prefill(A, A + (1 << 20), A + (2 << 20), None, 2, 10, 2, 64,
+                                           B, -1, B, 1, None) == -1  # slot table, n_slots < 0
+    lib.gdn_chunk_bwd_gated.argtypes = [v] * 11 + [i32] * 5 + [v] * 8 + [i32, i32, v, sz, v]
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int64, i32, i32, i32, i32]
+    lib.gdn_chunk_bwd_workspace_size.restype = sz
+    need = lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 128, 128)
+    args = [A, A + (1 << 26), A + (2 << 26), A + (3 << 26), A + (4 << 26), None, None, None,
+            A + (5 << 26), None, None, 1, 64, 2, 128, 128, B, B + (1 << 24), B + (2 << 24),
+            B + (3 << 24), B + (4 << 24), B + (5 << 24), B + (5 << 24) + 64, None, 1, 1,
+            B + (1 << 28), need, None]
+    assert lib.gdn_chunk_bwd_gated(*args) == -1                     # A is NULL
+    args[5] = A + (6 << 26)
+    args[21] = None                                                  # dA missing
+    assert lib.gdn_chunk_bwd_gated(*args) == -1

@@ -715,3 +715,86 @@ def test_chunk_bwd_gated(with_bias):
         e = rel_l2(got, w)
         print(nm, "%.2e" % e, flush=True)
         assert e <= 1e-5, (nm, e)
+
+
+# ---------------------------------------------- prefill -> decode handoff -----
+@gpu
+def test_conv_state_from_prefill_is_the_last_raw_rows():
+    g = _lib()
+    lengths = [5, 1, 0, 2, 40]
+    f = gi.frontend_inputs(lengths, 2, 64, 64, "bf16", seed=140)
+    cu = f["cu_seqlens"]
+    slots = torch.tensor([3, 0, 5, -1, 1], dtype=torch.int32)
+    cs = torch.full((6, 2, 3, 3, 64), 7.0, dtype=torch.bfloat16).cuda()
+    g.gdn_conv_state_from_prefill(f["q_raw"].cuda(), f["k_raw"].cuda(), f["v_raw"].cuda(),
+                                  cu_seqlens=cu.cuda(), slot_idx=slots.cuda(), conv_state=cs)
+    torch.cuda.synchronize()
+    cs = cs.cpu()
+    for n, L in enumerate(lengths):
+        sl = int(slots[n])
+        if sl < 0:
+            continue
+        want = torch.zeros(2, 3, 3, 64, dtype=torch.bfloat16)
+        for s, nm in enumerate(("q_raw", "k_raw", "v_raw")):
+            rows = f[nm][int(cu[n]):int(cu[n + 1])]
+            for r in range(3):
+                t = L - 3 + r
+                if t >= 0:
+                    want[:, s, r] = rows[t]
+        assert torch.equal(cs[sl], want), n
+    assert torch.all(cs[2] == 7.0) and torch.all(cs[4] == 7.0)  # untouched slots
+
+
+@gpu
+def test_prefill_then_fused_decode_equals_one_sequence():
+    """Serving path: fused prefill of a varlen batch, conv cache and states
+    seeded into slots, then 3 fused decode tokens; the decode outputs and
+    final states equal the oracle chain run over each whole sequence."""
+    g = _lib()
+    lengths, n_dec, H, d = [50, 3, 1, 97], 3, 2, 64
+    N = len(lengths)
+    total = [L + n_dec for L in lengths]
+    f = gi.frontend_inputs(total, H, d, d, "bf16", seed=141, norm_w_std=0.1)
+    cu_all = f["cu_seqlens"]
+    pre_rows = torch.cat([torch.arange(int(cu_all[n]), int(cu_all[n]) + lengths[n])
+                          for n in range(N)])
+    dec_rows = torch.stack([torch.arange(int(cu_all[n]) + lengths[n], int(cu_all[n + 1]))
+                            for n in range(N)])  # [N, n_dec]
+    cu_pre = gi.cu_from_lengths(lengths)
+    take = lambda x, r: x[r].contiguous()
+    dev = lambda x: x.cuda()
+    # prefill
+    o_pre, S_T = g.gdn_chunk_fwd_fused(*(dev(take(f[nm], pre_rows)) for nm in
+                                         ("q_raw", "k_raw", "v_raw")), dev(f["conv_w"]),
+                                       dev(take(f["log_alpha"], pre_rows)),
+                                       dev(take(f["beta"], pre_rows)), dev(take(f["z"], pre_rows)),
+                                       S0=dev(f["S0"]), norm_w=dev(f["norm_w"]),
+                                       cu_seqlens=dev(cu_pre), out_dtype=torch.float32)
+    # hand-off into a pool of slots
+    n_slots = 8
+    slots = torch.tensor([6, 2, 0, 5], dtype=torch.int32)
+    pool = torch.zeros((n_slots, H, d, d), dtype=torch.float32).cuda()
+    pool[slots.long().cuda()] = S_T
+    cs = g.gdn_conv_state_from_prefill(*(dev(take(f[nm], pre_rows)) for nm in
+                                         ("q_raw", "k_raw", "v_raw")), cu_seqlens=dev(cu_pre),
+                                       slot_idx=dev(slots), n_slots=n_slots)
+    table = torch.cat([slots[:, None], torch.full((N, n_dec - 1), -1, dtype=torch.int32),
+                       slots[:, None]], 1)
+    decin = {nm: dev(f[nm][dec_rows]) for nm in ("q_raw", "k_raw", "v_raw", "z", "log_alpha",
+                                                 "beta")}
+    o_dec = g.gdn_decode_fused(decin["q_raw"], decin["k_raw"], decin["v_raw"], dev(f["conv_w"]),
+                               cs, decin["log_alpha"], decin["beta"], pool, decin["z"],
+                               state_idx=dev(table), norm_w=dev(f["norm_w"]),
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    # the oracle over each whole sequence
+    qkv = [oracle.frontend(f[nm], f["conv_w"][s], cu_seqlens=cu_all, l2=s < 2, eps=1e-6)
+           for s, nm in enumerate(("q_raw", "k_raw", "v_raw"))]
+    y, S_ref = oracle.gdn_fwd(qkv[0], qkv[1], qkv[2], f["log_alpha"], f["beta"], f["S0"],
+                              cu_seqlens=cu_all)
+    o_ref = oracle.output_gate(y, f["z"], f["norm_w"], eps=1e-6)
+    e_o = rel_l2(o_dec.cpu().reshape(-1, H, d), o_ref[dec_rows.reshape(-1).numpy()])
+    e_s = rel_l2(pool.cpu()[slots.long()], S_ref)
+    e_p = rel_l2(o_pre.cpu(), o_ref[pre_rows.numpy()])
+    print("handoff rel_l2 prefill o=%.2e decode o=%.2e S=%.2e" % (e_p, e_o, e_s), flush=True)
+    assert e_p <= 2e-3 and e_o <= 2e-3 and e_s <= 2e-3
