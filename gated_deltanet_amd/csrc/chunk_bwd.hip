@@ -29,7 +29,7 @@
 // Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32) with
 // operands staged in LDS; the work is split into phases separated by
 // workgroup barriers, each phase's 16x16 output tiles dealt round-robin to
-// the four waves.
+// the eight waves (two per SIMD).
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -40,8 +40,8 @@ namespace {
 
 constexpr int kC = 32;     // chunk length
 constexpr int kDVT = 32;   // state columns per workgroup
-constexpr int kNT = 256;   // threads
-constexpr int kNW = 4;     // waves
+constexpr int kNT = 512;   // threads
+constexpr int kNW = 8;     // waves (two per SIMD, so one can issue while the other waits)
 constexpr int kLDV = kDVT + 4;
 constexpr int kLDC = kC + 4;
 
@@ -211,11 +211,11 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   // pieces, zeros past the sequence end) and staged into LDS at the start of
   // the chunk, so their HBM latency hides behind the previous chunk's work.
   constexpr int VG = io<TG>::kVec;
-  constexpr int KI = C * DK / VEC / kNT;                  // K / Q pieces per thread
+  constexpr int KI = (C * DK / VEC + kNT - 1) / kNT;      // K / Q pieces per thread
   constexpr int VI = (C * DVT / VEC + kNT - 1) / kNT;     // V pieces per thread
   constexpr int GI = (C * DVT / VG + kNT - 1) / kNT;      // dY pieces per thread
   constexpr int SI = DK * DVT / 4 / kNT;                  // state f32x4 per thread
-  static_assert(KI * VEC * kNT == C * DK && SI * 4 * kNT == DK * DVT, "staging shape");
+  static_assert(SI * 4 * kNT == DK * DVT, "staging shape");
   struct Pre {
     u32x4 k[KI], q[KI], v[VI], dy[GI];
     f32x4 s[SI];
@@ -229,9 +229,10 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     for (int i = 0; i < KI; ++i) {
       const int idx = tid + kNT * i;
       const int r = idx / (DK / VEC), d0 = (idx % (DK / VEC)) * VEC;
+      const bool in = idx < C * DK / VEC && r < valid;
       const size_t off = ((t0 + r) * H + h) * DK + d0;
-      p.k[i] = r < valid ? *reinterpret_cast<const u32x4 *>(k + off) : zero_raw;
-      if (with_q) p.q[i] = r < valid ? *reinterpret_cast<const u32x4 *>(q + off) : zero_raw;
+      p.k[i] = in ? *reinterpret_cast<const u32x4 *>(k + off) : zero_raw;
+      if (with_q) p.q[i] = in ? *reinterpret_cast<const u32x4 *>(q + off) : zero_raw;
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
@@ -275,6 +276,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int idx = tid + kNT * i;
+      if (idx >= C * DK / VEC) break;
       const int r = idx / (DK / VEC), d0 = (idx % (DK / VEC)) * VEC;
       float x[VEC];
       raw16_to_f32<TIN>(p.k[i], x);
@@ -399,7 +401,6 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       }
     }
     stage(pf, false, false, false);
-    if (c + 1 < nc) fetch(pf, c + 1, false, false, false);
     __syncthreads();
     // A (3 tiles) and X = K S (4 tiles)
     for (int t = wave; t < 7; t += kNW) {
@@ -425,6 +426,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       }
     }
     __syncthreads();
+    if (c + 1 < nc) fetch(pf, c + 1, false, false, false);
     invert();
     // R = beta (V - gamma X), all threads
     for (int idx = tid; idx < C * DVT; idx += kNT) {
@@ -470,7 +472,6 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     const int64_t t0 = bos + static_cast<int64_t>(c) * C;
     const int valid = rows_valid(c);
     stage(pf, true, true, true);
-    if (c > 0) fetch(pf, c - 1, true, true, true);
     __syncthreads();
 
     // ---- P1: A, K K^T o G, P (3 tiles each); X, Q S, Kt dS' (4 each) ----
@@ -675,6 +676,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       float db = s_dbu[0][r] + s_dbu[1][r];
       s_dg[r] = s_qsdy[0][r] + s_qsdy[1][r] + s_dgx[0][r] + s_dgx[1][r];
       float pre = 0.0f;
+#pragma unroll 4
       for (int i = 0; i < C; ++i) {
         const int o = r * LDC + i;
         db = fmaf(dAm[o], KGm[o], db);
@@ -684,6 +686,10 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       s_db[r] = db;
     }
     __syncthreads();
+
+    // the next chunk's inputs: fetched here, so their registers are not
+    // live through the heavy phases above, and still a phase ahead of use
+    if (c > 0) fetch(pf, c - 1, true, true, true);
 
     // ---- P7: dS <- gamma_C dS' + (diag(gamma) Q)^T dY + K^T dX; gates -----
     const float gamC = s_gam[C - 1];
@@ -736,8 +742,12 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       }
       const float ex = __shfl_up(inc, 1, 64);  // the previous lane's inclusive sum
       rs += r > 0 ? ex : 0.0f;
+#pragma unroll 4
       for (int i = r; i < C; ++i) rs += KGm[i * LDC + r];
-      rs += gamC * (s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+      float sred = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) sred += s_red[w];
+      rs += gamC * sred;
       if (r < valid) {
         float *dst = a.ws_part + static_cast<size_t>(2) * n_vt * part_stride * DK;
         dst[(static_cast<size_t>(vt) * 2) * part_stride + (t0 + r) * H + h] = s_db[r];
