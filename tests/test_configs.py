@@ -165,3 +165,51 @@ def test_fused_prefill_matches_chain_and_oracle():
         es = rel_l2(S[n, h], So)
         print("unit (%d, %d) len %d: o %.3e S %.3e" % (n, h, e - s, eo, es), flush=True)
         assert eo <= TOL and es <= TOL
+
+
+@gpu
+def test_backward_B4_H16_T4096_sampled():
+    """gdn_chunk_bwd at the prefill workload's size (bf16 inputs, bf16 dy and
+    gradients, as the benchmark times it), two units checked against the
+    oracle's backward on that unit alone."""
+    g = _lib()
+    inp = gi.workload_inputs(1)
+    dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    T, H = 4096, 16
+    dy = gi.normal((4 * T, H, 128), 13, 40).to(torch.bfloat16)
+    grads = g.gdn_chunk_bwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
+                            dy.cuda(), N=4, want_dS0=True)
+    torch.cuda.synchronize()
+    grads = [x.cpu() for x in grads]
+    for n, h in [(0, 3), (3, 14)]:
+        q, k, v, la, b = _unit(inp, n, h, T)
+        dyu = dy[n * T:(n + 1) * T, h:h + 1]
+        ref = oracle.gdn_bwd(q, k, v, la, b, None, dyu, None, N=1)
+        rows = slice(n * T, (n + 1) * T)
+        got = [grads[0][rows, h:h + 1], grads[1][rows, h:h + 1], grads[2][rows, h:h + 1],
+               grads[3][rows, h:h + 1], grads[4][rows, h:h + 1], grads[5][n:n + 1, h:h + 1]]
+        for nm, gg, rr in zip(("dq", "dk", "dv", "dla", "dbeta", "dS0"), got, ref):
+            e = rel_l2(gg, rr)
+            print("unit", n, h, nm, "%.2e" % e, flush=True)
+            assert e <= TOL, (n, h, nm, e)
+
+
+@gpu
+def test_decode_multi_N256_H32_sampled():
+    """gdn_decode_multi at the decode workload's size with 4 tokens per call
+    (next_n = 4), sampled units against 4 oracle decode steps."""
+    g = _lib()
+    w = gi.WORKLOADS[3]
+    inp = gi.workload_inputs(3, steps=4)
+    tm = {nm: inp[nm].transpose(0, 1).contiguous() for nm in ("q", "k", "v", "log_alpha", "beta")}
+    S = inp["S0"].cuda()
+    y = g.gdn_decode_multi(*(tm[nm].cuda() for nm in ("q", "k", "v", "log_alpha", "beta")), S)
+    torch.cuda.synchronize()
+    y, S = y.cpu(), S.cpu()
+    for n, h in [(0, 0), (77, 31), (255, 9)]:
+        S_or = inp["S0"][n:n + 1, h:h + 1].double().numpy()
+        for t in range(4):
+            yo, S_or = oracle.decode_step(*(inp[nm][t][n:n + 1, h:h + 1] for nm in
+                                            ("q", "k", "v", "log_alpha", "beta")), S_or)
+            assert rel_l2(y[n, t, h:h + 1], yo[0]) <= TOL
+        assert rel_l2(S[n:n + 1, h:h + 1], S_or) <= TOL
