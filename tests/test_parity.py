@@ -798,3 +798,54 @@ def test_prefill_then_fused_decode_equals_one_sequence():
     e_p = rel_l2(o_pre.cpu(), o_ref[pre_rows.numpy()])
     print("handoff rel_l2 prefill o=%.2e decode o=%.2e S=%.2e" % (e_p, e_o, e_s), flush=True)
     assert e_p <= 2e-3 and e_o <= 2e-3 and e_s <= 2e-3
+
+
+@gpu
+def test_chunk_bwd_f16_inputs():
+    inp, dy, dST = _bwd_inputs([45, 70], 2, 128, 128, "f16", seed=150)
+    _check_bwd(inp, dy, dST, tol=1e-5)
+
+
+@gpu
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_fused_f16_and_raw_gates(d):
+    g = _lib()
+    f = gi.decode_fused_inputs(4, 3, 2, d, "f16", seed=151)
+    a, b, A, b_alpha = gi.raw_gates(12, 2, 152)
+    ga, gb = a.reshape(4, 3, 2).contiguous(), b.reshape(4, 3, 2).contiguous()
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in f.items()}
+    cs, S = dev["conv_state"].clone(), dev["S0"].clone()
+    o = g.gdn_decode_fused(dev["q_raw"], dev["k_raw"], dev["v_raw"], dev["conv_w"], cs, ga.cuda(),
+                           gb.cuda(), S, dev["z"], A=A.cuda(), b_alpha=b_alpha.cuda(),
+                           norm_w=dev["norm_w"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    la, bt = oracle.gates_from_raw(a, b, A, b_alpha)
+    o_ref, S_ref = _fused_decode_reference(f, f["conv_state"].double().numpy(), f["S0"],
+                                           la.reshape(4, 3, 2), bt.reshape(4, 3, 2))
+    assert rel_l2(o, o_ref) <= 2e-3 and rel_l2(S, S_ref) <= 2e-3
+
+
+@gpu
+@pytest.mark.parametrize("case", ["no_decay", "strong_decay", "beta0", "beta1"])
+def test_decode_multi_gate_extremes(case):
+    g = _lib()
+    N, H, d, n_tok = 3, 2, 64, 4
+    inp, tm = _multi_inputs(N, H, d, d, n_tok, "f32", seed=153)
+    if case == "no_decay":
+        tm["log_alpha"] = torch.zeros_like(tm["log_alpha"])
+    elif case == "strong_decay":
+        tm["log_alpha"] = torch.full_like(tm["log_alpha"], -30.0)
+    elif case == "beta0":
+        tm["beta"] = torch.zeros_like(tm["beta"])
+    else:
+        tm["beta"] = torch.ones_like(tm["beta"])
+    S = inp["S0"].clone().cuda()
+    y = g.gdn_decode_multi(*(tm[nm].cuda() for nm in ("q", "k", "v", "log_alpha", "beta")), S,
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    S_or = inp["S0"].double().numpy()
+    for t in range(n_tok):
+        yo, S_or = oracle.decode_step(tm["q"][:, t], tm["k"][:, t], tm["v"][:, t],
+                                      tm["log_alpha"][:, t], tm["beta"][:, t], S_or)
+        assert rel_l2(y[:, t], yo) <= 1e-5
+    assert rel_l2(S, S_or) <= 1e-5
