@@ -66,38 +66,79 @@ struct Acc4 {
     acc += (a[0] + a[1]) + (a[2] + a[3]);
   }
 };
+// With 16-bit inputs (H16) the operands are rounded to fp16 as they are
+// loaded and each fragment pair is one v_mfma_f32_16x16x32_f16 (fp32
+// accumulation); fp32 inputs keep every product in fp32.
+__device__ __forceinline__ void load_col_h(Frag<_Float16> &f, const float *base, int ld, int col,
+                                           int r0, int lg) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f.v[j] = (_Float16)base[(r0 + 4 * lg + j) * ld + col];
+    f.v[4 + j] = (_Float16)base[(r0 + 16 + 4 * lg + j) * ld + col];
+  }
+}
+template <bool H16>
 __device__ __forceinline__ void mm_rr(f32x4 &acc, const float *A, int lda, const float *B, int ldb,
                                       int m0, int n0, int K, int lc, int lg) {
-  Acc4 s;
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    Frag<float> fa, fb;
-    fa.load_row(A, lda, m0 + lc, k0, lg);
-    fb.load_row(B, ldb, n0 + lc, k0, lg);
-    s.mma(fa, fb);
+  if constexpr (H16) {
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      Frag<_Float16> fa, fb;
+      fa.load_row_f32(A, lda, m0 + lc, k0, lg);
+      fb.load_row_f32(B, ldb, n0 + lc, k0, lg);
+      mma(acc, fa, fb);
+    }
+  } else {
+    Acc4 s;
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      Frag<float> fa, fb;
+      fa.load_row(A, lda, m0 + lc, k0, lg);
+      fb.load_row(B, ldb, n0 + lc, k0, lg);
+      s.mma(fa, fb);
+    }
+    s.add_to(acc);
   }
-  s.add_to(acc);
 }
+template <bool H16>
 __device__ __forceinline__ void mm_rc(f32x4 &acc, const float *A, int lda, const float *B, int ldb,
                                       int m0, int n0, int K, int lc, int lg) {
-  Acc4 s;
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    Frag<float> fa, fb;
-    fa.load_row(A, lda, m0 + lc, k0, lg);
-    fb.load_col(B, ldb, n0 + lc, k0, lg);
-    s.mma(fa, fb);
+  if constexpr (H16) {
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      Frag<_Float16> fa, fb;
+      fa.load_row_f32(A, lda, m0 + lc, k0, lg);
+      load_col_h(fb, B, ldb, n0 + lc, k0, lg);
+      mma(acc, fa, fb);
+    }
+  } else {
+    Acc4 s;
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      Frag<float> fa, fb;
+      fa.load_row(A, lda, m0 + lc, k0, lg);
+      fb.load_col(B, ldb, n0 + lc, k0, lg);
+      s.mma(fa, fb);
+    }
+    s.add_to(acc);
   }
-  s.add_to(acc);
 }
+template <bool H16>
 __device__ __forceinline__ void mm_cc(f32x4 &acc, const float *A, int lda, const float *B, int ldb,
                                       int m0, int n0, int K, int lc, int lg) {
-  Acc4 s;
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    Frag<float> fa, fb;
-    fa.load_col(A, lda, m0 + lc, k0, lg);
-    fb.load_col(B, ldb, n0 + lc, k0, lg);
-    s.mma(fa, fb);
+  if constexpr (H16) {
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      Frag<_Float16> fa, fb;
+      load_col_h(fa, A, lda, m0 + lc, k0, lg);
+      load_col_h(fb, B, ldb, n0 + lc, k0, lg);
+      mma(acc, fa, fb);
+    }
+  } else {
+    Acc4 s;
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      Frag<float> fa, fb;
+      fa.load_col(A, lda, m0 + lc, k0, lg);
+      fb.load_col(B, ldb, n0 + lc, k0, lg);
+      s.mma(fa, fb);
+    }
+    s.add_to(acc);
   }
-  s.add_to(acc);
 }
 
 // sum over the 16 lanes of a row of the wave (lanes with the same lane / 16)
@@ -128,6 +169,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   constexpr int LDK = DK + 4;
   constexpr int NKT = DK / 16;  // 16-row tiles of the state
   constexpr int VEC = io<TIN>::kVec;
+  constexpr bool H16 = sizeof(TIN) == 2;  // 16-bit inputs: fp16 operands
 
   __shared__ __attribute__((aligned(16))) float Ks[C * LDK];
   __shared__ __attribute__((aligned(16))) float Qs[C * LDK];
@@ -408,7 +450,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       if (t < 3) {
         int rt, ct;
         low_tile(t, rt, ct);
-        mm_rr(acc, Ks, LDK, Ks, LDK, 16 * rt, 16 * ct, DK, lc, lg);
+        mm_rr<H16>(acc, Ks, LDK, Ks, LDK, 16 * rt, 16 * ct, DK, lc, lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * lg + i, col = 16 * ct + lc;
@@ -420,7 +462,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
         }
       } else {
         const int rt = (t - 3) >> 1, nt = (t - 3) & 1;
-        mm_rc(acc, Ks, LDK, Ss, LDV, 16 * rt, 16 * nt, DK, lc, lg);
+        mm_rc<H16>(acc, Ks, LDK, Ss, LDV, 16 * rt, 16 * nt, DK, lc, lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) Xs[(16 * rt + 4 * lg + i) * LDV + 16 * nt + lc] = acc[i];
       }
@@ -438,7 +480,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     for (int t = wave; t < 4; t += kNW) {
       const int rt = t >> 1, nt = t & 1;
       f32x4 acc = zero4();
-      mm_rc(acc, Tm, LDC, Rs, LDV, 16 * rt, 16 * nt, C, lc, lg);
+      mm_rc<H16>(acc, Tm, LDC, Rs, LDV, 16 * rt, 16 * nt, C, lc, lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * lg + i;
@@ -451,7 +493,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     for (int t = wave; t < NKT * 2; t += kNW) {
       const int mt = t >> 1, nt = t & 1;
       f32x4 acc = zero4();
-      mm_cc(acc, Ks, LDK, Es, LDV, 16 * mt, 16 * nt, C, lc, lg);
+      mm_cc<H16>(acc, Ks, LDK, Es, LDV, 16 * mt, 16 * nt, C, lc, lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float *p = Ss + (16 * mt + 4 * lg + i) * LDV + 16 * nt + lc;
@@ -481,7 +523,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
         int rt, ct;
         low_tile(t % 3, rt, ct);
         const bool gram = t < 3;
-        mm_rr(acc, gram ? Ks : Qs, LDK, Ks, LDK, 16 * rt, 16 * ct, DK, lc, lg);
+        mm_rr<H16>(acc, gram ? Ks : Qs, LDK, Ks, LDK, 16 * rt, 16 * ct, DK, lc, lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * lg + i, col = 16 * ct + lc;
@@ -508,7 +550,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       } else {
         const int kind = (t - 6) / 4;  // 0: X, 1: Q S, 2: Kt dS'
         const int rt = ((t - 6) % 4) >> 1, nt = (t - 6) & 1;
-        mm_rc(acc, kind == 1 ? Qs : Ks, LDK, kind == 2 ? dSs : Ss, LDV, 16 * rt, 16 * nt, DK,
+        mm_rc<H16>(acc, kind == 1 ? Qs : Ks, LDK, kind == 2 ? dSs : Ss, LDV, 16 * rt, 16 * nt, DK,
               lc, lg);
         if (kind == 0) {
 #pragma unroll
@@ -545,11 +587,11 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       const int rt = (t & 3) >> 1, nt = t & 1;
       f32x4 acc = zero4();
       if (t < 4) {
-        mm_rc(acc, Tm, LDC, Rs, LDV, 16 * rt, 16 * nt, C, lc, lg);
+        mm_rc<H16>(acc, Tm, LDC, Rs, LDV, 16 * rt, 16 * nt, C, lc, lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) Es[(16 * rt + 4 * lg + i) * LDV + 16 * nt + lc] = acc[i];
       } else {
-        mm_cc(acc, Pm, LDC, dYs, LDV, 16 * rt, 16 * nt, C, lc, lg);
+        mm_cc<H16>(acc, Pm, LDC, dYs, LDV, 16 * rt, 16 * nt, C, lc, lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dEs[(16 * rt + 4 * lg + i) * LDV + 16 * nt + lc] += acc[i];
       }
@@ -560,7 +602,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     for (int t = wave; t < 4; t += kNW) {
       const int rt = t >> 1, nt = t & 1;
       f32x4 acc = zero4();
-      mm_cc(acc, Tm, LDC, dEs, LDV, 16 * rt, 16 * nt, C, lc, lg);
+      mm_cc<H16>(acc, Tm, LDC, dEs, LDV, 16 * rt, 16 * nt, C, lc, lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * lg + i, cc = 16 * nt + lc;
@@ -587,7 +629,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       low_tile(t % 3, rt, ct);
       const bool isA = t < 3;
       f32x4 acc = zero4();
-      mm_rr(acc, isA ? dRs : dYs, LDV, Es, LDV, 16 * rt, 16 * ct, DVT, lc, lg);
+      mm_rr<H16>(acc, isA ? dRs : dYs, LDV, Es, LDV, 16 * rt, 16 * ct, DVT, lc, lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * lg + i, col = 16 * ct + lc;
@@ -636,13 +678,13 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       f32x4 acc = zero4();
       if (isQ) {
         // diag(gamma) dY S^T + (dP o G) K
-        mm_rr(acc, dYs, LDV, Ss, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
+        mm_rr<H16>(acc, dYs, LDV, Ss, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] *= s_gam[16 * rt + 4 * lg + i];
-        mm_rc(acc, dPGm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
+        mm_rc<H16>(acc, dPGm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
       } else {
         // diag(kdec) E dS'^T + (dP o G)^T Q + dX S^T + (N + N^T) K
-        mm_rr(acc, Es, LDV, dSs, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
+        mm_rr<H16>(acc, Es, LDV, dSs, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * lg + i;
@@ -650,10 +692,10 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
           const float cr = sum16(acc[i] * Ks[r * LDK + 16 * kt + lc]);
           if (lc == 0) s_cr[kt][r] = cr;
         }
-        mm_cc(acc, dPGm, LDC, Qs, LDK, 16 * rt, 16 * kt, C, lc, lg);
-        mm_rr(acc, dXs, LDV, Ss, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
-        mm_rc(acc, Nm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
-        mm_cc(acc, Nm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
+        mm_cc<H16>(acc, dPGm, LDC, Qs, LDK, 16 * rt, 16 * kt, C, lc, lg);
+        mm_rr<H16>(acc, dXs, LDV, Ss, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
+        mm_rc<H16>(acc, Nm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
+        mm_cc<H16>(acc, Nm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
       }
       float *dst = a.ws_part + ((static_cast<size_t>(isQ ? 0 : 1) * n_vt + vt) * part_stride) * DK;
 #pragma unroll
@@ -697,7 +739,17 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       const int mt = t >> 1, nt = t & 1;
       f32x4 acc = zero4();
       // (diag(gamma) Q)^T dY: gamma folded into the B operand (rows of dY)
-      {
+      if constexpr (H16) {
+        Frag<_Float16> fa, fb;
+        load_col_h(fa, Qs, LDK, 16 * mt + lc, 0, lg);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          fb.v[j] = (_Float16)(dYs[(4 * lg + j) * LDV + 16 * nt + lc] * s_gam[4 * lg + j]);
+          fb.v[4 + j] =
+              (_Float16)(dYs[(16 + 4 * lg + j) * LDV + 16 * nt + lc] * s_gam[16 + 4 * lg + j]);
+        }
+        mma(acc, fa, fb);
+      } else {
         Acc4 sacc;
         Frag<float> fa, fb;
         fa.load_col(Qs, LDK, 16 * mt + lc, 0, lg);
@@ -710,7 +762,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
         sacc.mma(fa, fb);
         sacc.add_to(acc);
       }
-      mm_cc(acc, Ks, LDK, dXs, LDV, 16 * mt, 16 * nt, C, lc, lg);
+      mm_cc<H16>(acc, Ks, LDK, dXs, LDV, 16 * mt, 16 * nt, C, lc, lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float *p = dSs + (16 * mt + 4 * lg + i) * LDV + 16 * nt + lc;
