@@ -29,7 +29,7 @@
 // Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32) with
 // operands staged in LDS; the work is split into phases separated by
 // workgroup barriers, each phase's 16x16 output tiles dealt round-robin to
-// the eight waves (two per SIMD).
+// the sixteen waves (four per SIMD).
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -40,8 +40,8 @@ namespace {
 
 constexpr int kC = 32;     // chunk length
 constexpr int kDVT = 32;   // state columns per workgroup
-constexpr int kNT = 512;   // threads
-constexpr int kNW = 8;     // waves (two per SIMD, so one can issue while the other waits)
+constexpr int kNT = 1024;  // threads
+constexpr int kNW = 16;    // waves (four per SIMD, so one can issue while the others wait)
 constexpr int kLDV = kDVT + 4;
 constexpr int kLDC = kC + 4;
 
@@ -229,11 +229,15 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   // collide between sequences and stay below rows / C + N
   const int64_t slot0 = bos / C + n;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  // lane indices are re-made opaque at the start of every chunk (see
+  // opaque_lanes): values derived from them are then recomputed inside the
+  // chunk loops instead of being hoisted out of them and spilled
+  int tid = threadIdx.x;
+  int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lc = lane & 15;
-  const int lg = lane >> 4;
+  int lc = lane & 15;
+  int lg = lane >> 4;
+  auto opaque_lanes = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lc), "+v"(lg)); };
   const int v0 = vt * DVT;
   const size_t state_sz = static_cast<size_t>(DK) * DV;
   float *const ws_states = a.ws_states;
@@ -256,8 +260,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   constexpr int KI = (C * DK / VEC + kNT - 1) / kNT;      // K / Q pieces per thread
   constexpr int VI = (C * DVT / VEC + kNT - 1) / kNT;     // V pieces per thread
   constexpr int GI = (C * DVT / VG + kNT - 1) / kNT;      // dY pieces per thread
-  constexpr int SI = DK * DVT / 4 / kNT;                  // state f32x4 per thread
-  static_assert(SI * 4 * kNT == DK * DVT, "staging shape");
+  constexpr int SI = (DK * DVT / 4 + kNT - 1) / kNT;      // state f32x4 per thread
   struct Pre {
     u32x4 k[KI], q[KI], v[VI], dy[GI];
     f32x4 s[SI];
@@ -300,7 +303,8 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       for (int i = 0; i < SI; ++i) {
         const int idx = tid + kNT * i;
         const int r = idx / (DVT / 4), c4 = (idx % (DVT / 4)) * 4;
-        p.s[i] = *reinterpret_cast<const f32x4 *>(src + static_cast<size_t>(r) * DV + c4);
+        if (idx < DK * DVT / 4)
+          p.s[i] = *reinterpret_cast<const f32x4 *>(src + static_cast<size_t>(r) * DV + c4);
       }
     }
     p.la = 0.0f;
@@ -359,7 +363,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       for (int i = 0; i < SI; ++i) {
         const int idx = tid + kNT * i;
         const int r = idx / (DVT / 4), c4 = (idx % (DVT / 4)) * 4;
-        *reinterpret_cast<f32x4 *>(Ss + r * LDV + c4) = p.s[i];
+        if (idx < DK * DVT / 4) *reinterpret_cast<f32x4 *>(Ss + r * LDV + c4) = p.s[i];
       }
     }
     // gates: wave 0 scans the chunk's log decays (rows past the end: 0)
@@ -434,6 +438,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   if (nc > 0) fetch(pf, 0, false, false, false);
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
+    opaque_lanes();
     {
       float *dst = state_tile(c);
       for (int idx = tid; idx < DK * DVT / 4; idx += kNT) {
@@ -511,6 +516,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   }
   if (nc > 0) fetch(pf, nc - 1, true, true, true);
   for (int c = nc - 1; c >= 0; --c) {
+    opaque_lanes();
     const int64_t t0 = bos + static_cast<int64_t>(c) * C;
     const int valid = rows_valid(c);
     stage(pf, true, true, true);
