@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float dPGm[C * LDC];  // dP o G
   __shared__ float s_g[C], s_gam[C], s_beta[C], s_kdec[C];
   __shared__ float s_qsdy[2][C], s_dbu[2][C], s_dgx[2][C], s_cr[NKT][C];
-  __shared__ float s_dg[C], s_db[C], s_red[kNW];
+  __shared__ float s_dg[C], s_db[C], s_red[kNW], s_colp[kNW][C];
 
   const TIN *__restrict__ q = static_cast<const TIN *>(a.q);
   const TIN *__restrict__ k = static_cast<const TIN *>(a.k);
@@ -390,24 +390,27 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     ct = t == 2 ? 1 : 0;
   };
   // T = (I + A)^-1 for C = 32 by wave 0: 16x16 diagonal blocks by forward
-  // substitution (lane (lg < 2, lc) solves column lc of block lg), then
-  // T10 = -T11 (A10 T00) on the matrix cores
+  // substitution (each 16-lane row of the wave solves one block, rows 2 and 3
+  // repeat rows 0 and 1: lane lc holds column lc of the block's A and T, and
+  // the substitution broadcasts A's entries between lanes, unit_lower_solve16),
+  // then T10 = -T11 (A10 T00) on the matrix cores
   auto invert = [&]() {
     if (wave != 0) return;
-    if (lg < 2) {
-      const int b0 = 16 * lg;
-      float x[16];
+    {
+      const int b0 = 16 * (lg & 1);
+      float ac[16], xv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float acc = (r == lc) ? 1.0f : 0.0f;
-#pragma unroll
-        for (int i = 0; i < r; ++i) acc = fmaf(-Am[(b0 + r) * LDC + b0 + i], x[i], acc);
-        x[r] = acc;
+        ac[r] = Am[(b0 + r) * LDC + b0 + lc];
+        xv[r] = (r == lc) ? 1.0f : 0.0f;
       }
+      unit_lower_solve16(ac, xv);
+      if (lg < 2) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDC + b0 + lc] = x[r];
+        for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDC + b0 + lc] = xv[r];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDC + (16 - b0) + lc] = 0.0f;
+        for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDC + (16 - b0) + lc] = 0.0f;
+      }
     }
     // M = A10 T00 (16x16, contraction 16: the upper half of the slice is 0)
     f32x4 M = zero4();
@@ -710,28 +713,40 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
         if (r < valid) dst[((t0 + r) * H + h) * DK + 16 * kt + lc] = acc[i];
       }
     }
-    // Row work for dbeta and d log alpha: lane r < 32 of wave 0 owns row r
-    // (it reads dA, A, dP, P and row r of KG, then reuses row r of KG).
+    // Row work for dbeta and d log alpha, one (row r, column i) element of
+    // the 32x32 chunk matrices per thread (a wave holds two rows).
     // The decay factors G_ri = e^(g_r - g_i) contribute W_ri = dP_ri P_ri +
     // dA_ri A_ri to d g_r and -W_ri to d g_i; summed into d log alpha_s =
     // sum_{r >= s} d g_r, every W_ri with both indices >= s cancels, leaving
     // sum_{r >= s} sum_{i < s} W_ri. That sum is formed directly (row prefix
-    // M_rs = sum_{i < s} W_ri, stored over row r of KG) instead of adding
+    // M_rs = sum_{i < s} W_ri, then column sums over r >= s) instead of adding
     // and subtracting terms that cancel, which loses everything in fp32 when
     // the true gradient is tiny (strong decay).
-    if (wave == 0 && lane < C) {
-      const int r = lane;
-      float db = s_dbu[0][r] + s_dbu[1][r];
-      s_dg[r] = s_qsdy[0][r] + s_qsdy[1][r] + s_dgx[0][r] + s_dgx[1][r];
-      float pre = 0.0f;
-#pragma unroll 4
-      for (int i = 0; i < C; ++i) {
-        const int o = r * LDC + i;
-        db = fmaf(dAm[o], KGm[o], db);
-        KGm[o] = pre;  // M_ri: the prefix before column i
-        if (i < r) pre += dPm[o] * Pm[o] + dAm[o] * Am[o];
+    {
+      static_assert(kNT == C * C, "one thread per element of a chunk matrix");
+      const int r = tid >> 5, i = tid & 31;
+      const int o = r * LDC + i;
+      // dbeta_r: the beta (V - gamma X) terms plus sum_i dA_ri (K K^T o G)_ri
+      float db = row_sum<16>(dAm[o] * KGm[o]);
+      db += __shfl_xor(db, 16, 64);
+      if (i == 0) {
+        s_db[r] = db + s_dbu[0][r] + s_dbu[1][r];
+        s_dg[r] = s_qsdy[0][r] + s_qsdy[1][r] + s_dgx[0][r] + s_dgx[1][r];
       }
-      s_db[r] = db;
+      const float w = i < r ? dPm[o] * Pm[o] + dAm[o] * Am[o] : 0.0f;
+      // inclusive prefix along the row (32 lanes), then shifted by one lane
+      float inc = w;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const float up = __shfl_up(inc, off, 64);
+        if (i >= off) inc += up;
+      }
+      const float up1 = __shfl_up(inc, 1, 64);
+      const float m = i > 0 ? up1 : 0.0f;  // M_ri
+      // column i gets M_ri from every row r >= i; the wave's two rows first
+      float col = r >= i ? m : 0.0f;
+      col += __shfl_xor(col, 32, 64);
+      if (lane < 32) s_colp[wave][i] = col;
     }
     __syncthreads();
 
@@ -800,8 +815,8 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       }
       const float ex = __shfl_up(inc, 1, 64);  // the previous lane's inclusive sum
       rs += r > 0 ? ex : 0.0f;
-#pragma unroll 4
-      for (int i = r; i < C; ++i) rs += KGm[i * LDC + r];
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) rs += s_colp[w][r];
       float sred = 0.0f;
 #pragma unroll
       for (int w = 0; w < kNW; ++w) sred += s_red[w];

@@ -249,6 +249,182 @@ __device__ __forceinline__ f32x4 zero4() {
   return z;
 }
 
+// Unit lower-triangular solve of one 16x16 diagonal block held column-wise
+// across a 16-lane DPP row: lane c holds ac[r] = A[r][c] (strictly lower part
+// used) and, on entry, xv[r] = the right-hand side of column c (e.g. the
+// identity); on exit xv[r] = ((I + A)^-1)[r][c]. Step s subtracts A[r][s] x_s
+// from x_r for r > s, with A[r][s] broadcast from lane s of the row by
+// v_fmac_f32_dpp row_newbcast:s (so A is never re-read from memory). The
+// leading s_nop of each step gives the two wait states a DPP source needs
+// after a VALU write (the compiler does not guard inline asm).
+__device__ __forceinline__ void unit_lower_solve16(const float *ac, float *xv) {
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%15, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%16, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%17, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, -%18, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %4, -%19, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %5, -%20, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %6, -%21, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %7, -%22, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %8, -%23, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %9, -%24, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %10, -%25, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %11, -%26, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %12, -%27, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %13, -%28, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %14, -%29, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]), "+v"(xv[4]), "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[1]), "v"(ac[2]), "v"(ac[3]), "v"(ac[4]), "v"(ac[5]), "v"(ac[6]), "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[0]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%14, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%15, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%16, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, -%17, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %4, -%18, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %5, -%19, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %6, -%20, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %7, -%21, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %8, -%22, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %9, -%23, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %10, -%24, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %11, -%25, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %12, -%26, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %13, -%27, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[2]), "+v"(xv[3]), "+v"(xv[4]), "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[2]), "v"(ac[3]), "v"(ac[4]), "v"(ac[5]), "v"(ac[6]), "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[1]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%13, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%14, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%15, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, -%16, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %4, -%17, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %5, -%18, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %6, -%19, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %7, -%20, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %8, -%21, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %9, -%22, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %10, -%23, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %11, -%24, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %12, -%25, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[3]), "+v"(xv[4]), "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[3]), "v"(ac[4]), "v"(ac[5]), "v"(ac[6]), "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[2]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%12, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%13, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%14, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, -%15, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %4, -%16, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %5, -%17, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %6, -%18, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %7, -%19, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %8, -%20, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %9, -%21, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %10, -%22, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %11, -%23, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[4]), "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[4]), "v"(ac[5]), "v"(ac[6]), "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[3]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%11, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%12, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%13, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, -%14, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %4, -%15, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %5, -%16, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %6, -%17, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %7, -%18, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %8, -%19, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %9, -%20, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %10, -%21, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[5]), "v"(ac[6]), "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[4]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%10, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%11, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%12, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, -%13, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %4, -%14, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %5, -%15, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %6, -%16, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %7, -%17, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %8, -%18, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %9, -%19, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[6]), "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[6]), "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[5]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%9, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%10, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%11, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, -%12, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %4, -%13, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %5, -%14, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %6, -%15, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %7, -%16, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %8, -%17, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[7]), "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[7]), "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[6]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%8, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%9, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%10, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, -%11, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %4, -%12, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %5, -%13, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %6, -%14, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %7, -%15, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[8]), "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[8]), "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[7]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%7, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%8, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%9, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, -%10, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %4, -%11, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %5, -%12, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %6, -%13, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[9]), "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[9]), "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[8]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%6, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%7, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%8, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, -%9, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %4, -%10, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %5, -%11, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[10]), "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[10]), "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[9]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%5, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%6, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%7, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, -%8, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %4, -%9, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[11]), "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[11]), "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[10]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%4, %8 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%5, %8 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%6, %8 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %3, -%7, %8 row_newbcast:11 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[12]), "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[12]), "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[11]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%3, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%4, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %2, -%5, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[13]), "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[13]), "v"(ac[14]), "v"(ac[15]), "v"(xv[12]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%2, %4 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %1, -%3, %4 row_newbcast:13 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[14]), "+v"(xv[15])
+               : "v"(ac[14]), "v"(ac[15]), "v"(xv[13]));
+  asm volatile("s_nop 1\n\t"
+               "v_fmac_f32_dpp %0, -%1, %2 row_newbcast:14 row_mask:0xf bank_mask:0xf"
+               : "+v"(xv[15])
+               : "v"(ac[15]), "v"(xv[14]));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(
