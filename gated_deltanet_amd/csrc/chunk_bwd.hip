@@ -192,8 +192,8 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float dPm[C * LDC];
   __shared__ __attribute__((aligned(16))) float dPGm[C * LDC];  // dP o G
   __shared__ float s_g[C], s_gam[C], s_beta[C], s_kdec[C];
-  __shared__ float s_qsdy[2][C], s_dbu[2][C], s_dgx[2][C], s_cr[NKT][C];
-  __shared__ float s_dg[C], s_db[C], s_red[kNW], s_colp[kNW][C];
+  __shared__ float s_qsdy[NKT][C], s_dbu[2][C], s_dgx[2][C], s_cr[NKT][C];
+  __shared__ float s_db[C], s_red[kNW], s_colp[kNW][C];
 
   const TIN *__restrict__ q = static_cast<const TIN *>(a.q);
   const TIN *__restrict__ k = static_cast<const TIN *>(a.k);
@@ -525,8 +525,8 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     stage(pf, true, true, true);
     __syncthreads();
 
-    // ---- P1: A, K K^T o G, P (3 tiles each); X, Q S, Kt dS' (4 each) ----
-    for (int t = wave; t < 18; t += kNW) {
+    // ---- P1: A, K K^T o G, P (3 tiles each); X, Kt dS' (4 each) ---------
+    for (int t = wave; t < 14; t += kNW) {
       f32x4 acc = zero4();
       if (t < 6) {
         int rt, ct;
@@ -557,21 +557,12 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
           }
         }
       } else {
-        const int kind = (t - 6) / 4;  // 0: X, 1: Q S, 2: Kt dS'
+        const bool isX = t < 10;  // X = K S, else Kt dS'
         const int rt = ((t - 6) % 4) >> 1, nt = (t - 6) & 1;
-        mm_rc<H16>(acc, kind == 1 ? Qs : Ks, LDK, kind == 2 ? dSs : Ss, LDV, 16 * rt, 16 * nt, DK,
-              lc, lg);
-        if (kind == 0) {
+        mm_rc<H16>(acc, Ks, LDK, isX ? Ss : dSs, LDV, 16 * rt, 16 * nt, DK, lc, lg);
+        if (isX) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) Xs[(16 * rt + 4 * lg + i) * LDV + 16 * nt + lc] = acc[i];
-        } else if (kind == 1) {
-          // gamma_r (Q S)_r . dY_r, summed over this tile's 16 columns
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * rt + 4 * lg + i;
-            const float s = sum16(s_gam[r] * acc[i] * dYs[r * LDV + 16 * nt + lc]);
-            if (lc == 0) s_qsdy[nt][r] = s;
-          }
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -686,10 +677,17 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       const int rt = tt / NKT, kt = tt % NKT;
       f32x4 acc = zero4();
       if (isQ) {
-        // diag(gamma) dY S^T + (dP o G) K
+        // diag(gamma) dY S^T + (dP o G) K. The gamma terms of d g,
+        // gamma_r (Q S)_r . dY_r = gamma_r sum_k Q_rk (dY S^T)_rk, are
+        // row sums of Q o (dY S^T) over this tile's 16 keys.
         mm_rr<H16>(acc, dYs, LDV, Ss, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= s_gam[16 * rt + 4 * lg + i];
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * lg + i;
+          acc[i] *= s_gam[r];
+          const float qs = sum16(acc[i] * Qs[r * LDK + 16 * kt + lc]);
+          if (lc == 0) s_qsdy[kt][r] = qs;
+        }
         mm_rc<H16>(acc, dPGm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
       } else {
         // diag(kdec) E dS'^T + (dP o G)^T Q + dX S^T + (N + N^T) K
@@ -729,10 +727,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       // dbeta_r: the beta (V - gamma X) terms plus sum_i dA_ri (K K^T o G)_ri
       float db = row_sum<16>(dAm[o] * KGm[o]);
       db += __shfl_xor(db, 16, 64);
-      if (i == 0) {
-        s_db[r] = db + s_dbu[0][r] + s_dbu[1][r];
-        s_dg[r] = s_qsdy[0][r] + s_qsdy[1][r] + s_dgx[0][r] + s_dgx[1][r];
-      }
+      if (i == 0) s_db[r] = db + s_dbu[0][r] + s_dbu[1][r];
       const float w = i < r ? dPm[o] * Pm[o] + dAm[o] * Am[o] : 0.0f;
       // inclusive prefix along the row (32 lanes), then shifted by one lane
       float inc = w;
@@ -798,7 +793,9 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       // The Kt terms enter d g_r with - and d g_C with +; the exclusive
       // prefix is what survives, again without forming the cancelling pair.
       const int r = lane;
-      float rs = s_dg[r];
+      float rs = s_dgx[0][r] + s_dgx[1][r];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) rs += s_qsdy[kt][r];
 #pragma unroll
       for (int off = 1; off < 32; off <<= 1) {
         const float o = __shfl_down(rs, off, 64);
