@@ -19,9 +19,11 @@
 // d log alpha is its reverse running sum inside the chunk.
 //
 // The dS recurrence is separable by columns of the state, so one workgroup
-// owns one (sequence, head, 32-column tile of S). It first sweeps forward
-// over the chunks to rebuild the tile's chunk-start states (written to a
-// workspace), then sweeps backward. dV and dS0 belong to the tile's columns
+// owns one (sequence, head, 32-column tile of S) and sweeps backward over the
+// chunks, reading the tile's chunk-start states from a workspace. With
+// 16-bit inputs the prefill kernel writes those states in a launch of its own
+// just before; with fp32 inputs the workgroup first sweeps forward to rebuild
+// them. dV and dS0 belong to the tile's columns
 // and are written directly; dq, dk, dbeta and dlog alpha sum over all
 // columns, so each tile writes its partial sums and a second kernel adds the
 // tiles in a fixed order (no atomics: results are deterministic).
@@ -244,8 +246,16 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   const size_t part_stride = static_cast<size_t>(a.rows) * H;  // per tile, in rows*H
 
   const RawGate gate = RawGate::load(a.A, a.b_alpha, h);
+  // chunk-start state tiles in the workspace, [slot][head][column tile] blocks
+  // of DK x DVT floats in the accumulator order of state_row()
   auto state_tile = [&](int c) {
-    return ws_states + (static_cast<size_t>(slot0 + c) * H + h) * state_sz + v0;
+    return ws_states + ((static_cast<size_t>(slot0 + c) * H + h) * n_vt + vt) * (DK * DVT);
+  };
+  // element e of the f32x4 with index idx of a state block: row and column
+  auto state_rc = [&](int idx, int e, int &r, int &cc) {
+    const int slab = idx / (DK / 16 * 64), t = (idx / 64) % (DK / 16), ln = idx % 64;
+    r = state_row(t, ln >> 4, e);
+    cc = 16 * slab + (ln & 15);
   };
 
   // ---- staging helpers ------------------------------------------------
@@ -302,9 +312,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < SI; ++i) {
         const int idx = tid + kNT * i;
-        const int r = idx / (DVT / 4), c4 = (idx % (DVT / 4)) * 4;
-        if (idx < DK * DVT / 4)
-          p.s[i] = *reinterpret_cast<const f32x4 *>(src + static_cast<size_t>(r) * DV + c4);
+        if (idx < DK * DVT / 4) p.s[i] = *reinterpret_cast<const f32x4 *>(src + 4 * idx);
       }
     }
     p.la = 0.0f;
@@ -362,8 +370,14 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < SI; ++i) {
         const int idx = tid + kNT * i;
-        const int r = idx / (DVT / 4), c4 = (idx % (DVT / 4)) * 4;
-        if (idx < DK * DVT / 4) *reinterpret_cast<f32x4 *>(Ss + r * LDV + c4) = p.s[i];
+        if (idx < DK * DVT / 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            int r, cc;
+            state_rc(idx, e, r, cc);
+            Ss[r * LDV + cc] = p.s[i][e];
+          }
+        }
       }
     }
     // gates: wave 0 scans the chunk's log decays (rows past the end: 0)
@@ -432,12 +446,15 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   };
 
   // ======================= forward sweep: chunk-start states =============
-  // Ss holds the tile of the running state
+  // With 16-bit inputs the prefill kernel has written them already (its
+  // states output); fp32 inputs rebuild them here. Ss holds the tile of the
+  // running state.
+  Pre pf;
+  if constexpr (!H16) {
   for (int idx = tid; idx < DK * DVT; idx += kNT) {
     const int r = idx / DVT, cc = idx % DVT;
     Ss[r * LDV + cc] = a.S0 ? a.S0[static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc] : 0.0f;
   }
-  Pre pf;
   if (nc > 0) fetch(pf, 0, false, false, false);
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
@@ -445,9 +462,14 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     {
       float *dst = state_tile(c);
       for (int idx = tid; idx < DK * DVT / 4; idx += kNT) {
-        const int r = idx / (DVT / 4), c4 = (idx % (DVT / 4)) * 4;
-        *reinterpret_cast<f32x4 *>(dst + static_cast<size_t>(r) * DV + c4) =
-            *reinterpret_cast<const f32x4 *>(Ss + r * LDV + c4);
+        f32x4 sv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int r, cc;
+          state_rc(idx, e, r, cc);
+          sv[e] = Ss[r * LDV + cc];
+        }
+        *reinterpret_cast<f32x4 *>(dst + 4 * idx) = sv;
       }
     }
     stage(pf, false, false, false);
@@ -509,6 +531,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       }
     }
     __syncthreads();
+  }
   }
 
   // ======================= backward sweep ================================
@@ -914,6 +937,32 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
   const int n_vt = a.dv_size / kDVT;
   const int64_t units = static_cast<int64_t>(a.N) * a.H;
   if (units > 0) {
+    if constexpr (sizeof(TIN) == 2) {
+      // chunk-start states from the prefill kernel (no y, no final state)
+      ChunkArgs f{};
+      f.q = a.q;
+      f.k = a.k;
+      f.v = a.v;
+      f.log_alpha = a.log_alpha;
+      f.beta = a.beta;
+      f.A = a.A;
+      f.b_alpha = a.b_alpha;
+      f.S0 = a.S0;
+      f.y = nullptr;
+      f.S_T = nullptr;
+      f.cu_seqlens = a.cu_seqlens;
+      f.N = a.N;
+      f.T = a.T;
+      f.H = a.H;
+      f.dk = DK;
+      f.dv = a.dv_size;
+      f.in_dtype = a.in_dtype;
+      f.out_dtype = a.in_dtype;
+      f.stream = a.stream;
+      f.states = a.ws_states;
+      const hipError_t e = launch_chunk_fwd_bf16(f);
+      if (e != hipSuccess) return e;
+    }
     const int64_t blocks = (units + 7) / 8 * 8 * n_vt;
     hipLaunchKernelGGL((chunk_bwd_kernel<DK, TIN, TG>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kNT), 0, a.stream, a);

@@ -102,11 +102,6 @@ struct Lay {
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
-// state tile t, lane group lg, element i  ->  key index
-__device__ __forceinline__ int state_row(int t, int lg, int i) {
-  return 32 * (t >> 1) + 8 * lg + 4 * (t & 1) + i;
-}
-
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   // generic -> LDS address-space conversion yields the 32-bit LDS offset
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
@@ -234,7 +229,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
     const float *__restrict__ gA, const float *__restrict__ gbias,
     const float *__restrict__ S0, TOUT *__restrict__ y, float *__restrict__ S_T,
-    const int32_t *__restrict__ cu_seqlens, int T, int H, int DV, int n_vt, int n_units) {
+    float *__restrict__ states, const int32_t *__restrict__ cu_seqlens, int T, int H, int DV,
+    int n_vt, int n_units) {
   using L = Lay<DK, NS>;
   using KO = KOps<TIN>;
   using kvec = typename KO::vec;
@@ -644,11 +640,22 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       for (int i = 0; i < 4; ++i)
         st[t][i] = S0 ? S0[sbase + static_cast<size_t>(state_row(t, lg, i)) * DV] : 0.0f;
   }
+  // chunk-start states for the backward pass (optional): chunk x of sequence
+  // n goes to slot floor(bos / C) + n + x, this wave's slab of the tile
+  float *const st_out =
+      states ? states + ((static_cast<size_t>(bos / kC + n) * H + h) * n_vt + vt) * DK * DVT +
+                   (static_cast<size_t>(wave) * NST * 64 + lane) * 4
+             : nullptr;
   // byte offset of this lane's first y element inside a chunk's rows
   const uint32_t y_lane =
       static_cast<uint32_t>((4 * lg * hdv + h * DV + v0 + slab + lc) * sizeof(TOUT));
 
   auto state_step = [&](int x) {
+    if (st_out) {
+      float *dst = st_out + static_cast<size_t>(x) * H * n_vt * DK * DVT;
+#pragma unroll
+      for (int t = 0; t < NST; ++t) *reinterpret_cast<f32x4 *>(dst + t * 256) = st[t];
+    }
     const char *slot = ring + (x % kRing) * L::SLOT;
     const char *pb = procb + (x & 1) * L::PROC;
     const float *gt = gate_of(x);
@@ -733,6 +740,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     f32x4 Yt[kNCT];
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt) Yt[rt] = mma_f16(pf[rt], eb, G4[rt] * QS[rt]);
+    if (!y) return;
     const uint32_t rows = static_cast<uint32_t>(rows_of(x));
     const auto ry = __builtin_amdgcn_make_buffer_rsrc(y + row0_of(x) * hdv, 0,
                                                       static_cast<int>(rows * hdv * sizeof(TOUT)),
@@ -827,7 +835,7 @@ hipError_t launch_bf16(const ChunkArgs &a) {
   hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, NS, TIN, TOUT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * (NS + kPrep)), 0, a.stream, static_cast<const TIN *>(a.q),
                      static_cast<const TIN *>(a.k), static_cast<const TIN *>(a.v),
-                     a.log_alpha, a.beta, a.A, a.b_alpha, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.cu_seqlens,
+                     a.log_alpha, a.beta, a.A, a.b_alpha, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.states, a.cu_seqlens,
                      a.T, a.H, a.dv, n_vt, static_cast<int>(units));
   return hipGetLastError();
 }

@@ -470,4 +470,16 @@ struct RawGate {
   __device__ static __forceinline__ float beta(float b) { return 1.0f / (1.0f + expf(-b)); }
 };
 
+// Chunk-start states handed from the prefill kernel to the backward pass.
+// A 32-column tile of one state is kept by two waves, each owning a 16-column
+// slab as dk/16 accumulator tiles; element i of tile t in lane (lg, lc) is
+// state row state_row(t, lg, i) (the key order of the fragment-linear K and
+// Q slices), column 16 * slab + lc. The workspace stores each such f32x4 as
+// it sits in the lane: per (chunk slot, head, column tile) a block of
+// dk x 32 floats ordered [slab][t][lane][i], so every store and load is one
+// coalesced 16-byte access per lane.
+__device__ __forceinline__ int state_row(int t, int lg, int i) {
+  return 32 * (t >> 1) + 8 * lg + 4 * (t & 1) + i;
+}
+
 }  // namespace gdn

@@ -59,6 +59,9 @@ struct ChunkArgs {
   int N, T, H, dk, dv;
   int in_dtype, out_dtype;
   hipStream_t stream;
+  // 16-bit kernel only: chunk-start states in the backward workspace's tile
+  // order (null: not written); y may then be null
+  float *states = nullptr;
 };
 
 struct FrontendArgs {
