@@ -540,6 +540,53 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     dSs[r * LDV + cc] =
         a.dS_T ? a.dS_T[static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc] : 0.0f;
   }
+  // dbeta and d log alpha of a finished chunk (first row t0c, nv valid rows,
+  // gamma_C = gC) from the row and column sums its phases left in LDS; run
+  // by the last wave while the next chunk's first phase keeps the others busy
+  // (those sums are rewritten only from the fourth phase on).
+  auto gate_grads = [&](int64_t t0c, int nv, float gC) {
+    if (lane >= C) return;
+    // d log alpha_s = sum_{r >= s} (gamma and X terms of d g_r)
+    //               + sum_{r >= s} M_rs                  (decays G)
+    //               + sum_{r < s} cr_r                   (Kt: e^(g_C - g_r))
+    //               + gamma_C <S, dS'>                   (gamma_C)
+    // The Kt terms enter d g_r with - and d g_C with +; the exclusive
+    // prefix is what survives, again without forming the cancelling pair.
+    const int r = lane;
+    float rs = s_dgx[0][r] + s_dgx[1][r];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) rs += s_qsdy[kt][r];
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+      const float o = __shfl_down(rs, off, 64);
+      if (r + off < C) rs += o;
+    }
+    float cr = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) cr += s_cr[kt][r];
+    float inc = cr;
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+      const float o = __shfl_up(inc, off, 64);
+      if (r >= off) inc += o;
+    }
+    const float ex = __shfl_up(inc, 1, 64);  // the previous lane's inclusive sum
+    rs += r > 0 ? ex : 0.0f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) rs += s_colp[w][r];
+    float sred = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) sred += s_red[w];
+    rs += gC * sred;
+    if (r < nv) {
+      float *dst = a.ws_part + static_cast<size_t>(2) * n_vt * part_stride * DK;
+      dst[(static_cast<size_t>(vt) * 2) * part_stride + (t0c + r) * H + h] = s_db[r];
+      dst[(static_cast<size_t>(vt) * 2 + 1) * part_stride + (t0c + r) * H + h] = rs;
+    }
+  };
+  int64_t prev_t0 = 0;
+  int prev_valid = 0;
+  float prev_gamC = 0.0f;
   if (nc > 0) fetch(pf, nc - 1, true, true, true);
   for (int c = nc - 1; c >= 0; --c) {
     opaque_lanes();
@@ -549,6 +596,8 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     __syncthreads();
 
     // ---- P1: A, K K^T o G, P (3 tiles each); X, Kt dS' (4 each) ---------
+    static_assert(kNW > 14, "the last wave has no tile in the first phase");
+    if (wave == kNW - 1 && c < nc - 1) gate_grads(prev_t0, prev_valid, prev_gamC);
     for (int t = wave; t < 14; t += kNW) {
       f32x4 acc = zero4();
       if (t < 6) {
@@ -808,47 +857,12 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
         *p = gamC * *p + acc[i];
       }
     }
-    if (wave == 0 && lane < C) {
-      // d log alpha_s = sum_{r >= s} (gamma and X terms of d g_r)
-      //               + sum_{r >= s} M_rs                  (decays G)
-      //               + sum_{r < s} cr_r                   (Kt: e^(g_C - g_r))
-      //               + gamma_C <S, dS'>                   (gamma_C)
-      // The Kt terms enter d g_r with - and d g_C with +; the exclusive
-      // prefix is what survives, again without forming the cancelling pair.
-      const int r = lane;
-      float rs = s_dgx[0][r] + s_dgx[1][r];
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) rs += s_qsdy[kt][r];
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-        const float o = __shfl_down(rs, off, 64);
-        if (r + off < C) rs += o;
-      }
-      float cr = 0.0f;
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) cr += s_cr[kt][r];
-      float inc = cr;
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-        const float o = __shfl_up(inc, off, 64);
-        if (r >= off) inc += o;
-      }
-      const float ex = __shfl_up(inc, 1, 64);  // the previous lane's inclusive sum
-      rs += r > 0 ? ex : 0.0f;
-#pragma unroll
-      for (int w = 0; w < kNW; ++w) rs += s_colp[w][r];
-      float sred = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kNW; ++w) sred += s_red[w];
-      rs += gamC * sred;
-      if (r < valid) {
-        float *dst = a.ws_part + static_cast<size_t>(2) * n_vt * part_stride * DK;
-        dst[(static_cast<size_t>(vt) * 2) * part_stride + (t0 + r) * H + h] = s_db[r];
-        dst[(static_cast<size_t>(vt) * 2 + 1) * part_stride + (t0 + r) * H + h] = rs;
-      }
-    }
+    prev_t0 = t0;
+    prev_valid = valid;
+    prev_gamC = gamC;
     __syncthreads();
   }
+  if (nc > 0 && wave == kNW - 1) gate_grads(prev_t0, prev_valid, prev_gamC);
   // dS0 for this tile
   if (a.dS0) {
     for (int idx = tid; idx < DK * DVT; idx += kNT) {
