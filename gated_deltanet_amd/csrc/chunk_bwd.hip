@@ -172,6 +172,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   constexpr int NKT = DK / 16;  // 16-row tiles of the state
   constexpr int VEC = io<TIN>::kVec;
   constexpr bool H16 = sizeof(TIN) == 2;  // 16-bit inputs: fp16 operands
+  using FragM = typename std::conditional<H16, Frag<_Float16>, Frag<float>>::type;
 
   __shared__ __attribute__((aligned(16))) float Ks[C * LDK];
   __shared__ __attribute__((aligned(16))) float Qs[C * LDK];
@@ -190,9 +191,10 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Pm[C * LDC];   // tril(Q K^T o G)
   __shared__ __attribute__((aligned(16))) float KGm[C * LDC];  // tril(K K^T o G)
   __shared__ __attribute__((aligned(16))) float dAm[C * LDC];
-  __shared__ __attribute__((aligned(16))) float Nm[C * LDC];   // diag(beta)(dA o G)
+  __shared__ __attribute__((aligned(16))) float Mm[C * LDC];   // N + N^T, N = diag(beta)(dA o G)
   __shared__ __attribute__((aligned(16))) float dPm[C * LDC];
   __shared__ __attribute__((aligned(16))) float dPGm[C * LDC];  // dP o G
+  __shared__ __attribute__((aligned(16))) float dPGt[C * LDC];  // (dP o G)^T
   __shared__ float s_g[C], s_gam[C], s_beta[C], s_kdec[C];
   __shared__ float s_qsdy[NKT][C], s_dbu[2][C], s_dgx[2][C], s_cr[NKT][C];
   __shared__ float s_db[C], s_red[kNW], s_colp[kNW][C];
@@ -240,6 +242,15 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   int lc = lane & 15;
   int lg = lane >> 4;
   auto opaque_lanes = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lc), "+v"(lg)); };
+  // one fragment of an fp32 LDS operand: row `row` (contraction along the
+  // row) or column `col` (contraction down the column), from index k0
+  auto ld_row = [&](FragM &f, const float *base, int ld, int row, int k0) {
+    f.load_row_f32(base, ld, row, k0, lg);
+  };
+  auto ld_col = [&](FragM &f, const float *base, int ld, int col, int k0) {
+    if constexpr (H16) load_col_h(f, base, ld, col, k0, lg);
+    else f.load_col(base, ld, col, k0, lg);
+  };
   const int v0 = vt * DVT;
   const size_t state_sz = static_cast<size_t>(DK) * DV;
   float *const ws_states = a.ws_states;
@@ -706,13 +717,24 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * lg + i, col = 16 * ct + lc;
         if (isA) {
+          // N is strictly lower: M = N + N^T gets N_rc at (r, c) and (c, r);
+          // the entries above the diagonal come from the partner lane (or,
+          // for the upper block, from the lower off-diagonal tile)
           const float d = r > col ? -acc[i] : 0.0f;
           dAm[r * LDC + col] = d;
-          Nm[r * LDC + col] = r > col ? s_beta[r] * d * decay(r, col) : 0.0f;
+          const float nv = s_beta[r] * d * decay(r, col);
+          if (r > col) {
+            Mm[r * LDC + col] = nv;
+            Mm[col * LDC + r] = nv;
+          } else if (r == col) {
+            Mm[r * LDC + col] = 0.0f;
+          }
         } else {
           const float d = r >= col ? acc[i] : 0.0f;
           dPm[r * LDC + col] = d;
-          dPGm[r * LDC + col] = r >= col ? d * decay(r, col) : 0.0f;
+          const float dg = r >= col ? d * decay(r, col) : 0.0f;
+          dPGm[r * LDC + col] = dg;
+          dPGt[col * LDC + r] = dg;
         }
       }
       if (rt == 1 && ct == 0) {
@@ -721,10 +743,10 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
           const int o = (4 * lg + i) * LDC + 16 + lc;
           if (isA) {
             dAm[o] = 0.0f;
-            Nm[o] = 0.0f;
           } else {
             dPm[o] = 0.0f;
             dPGm[o] = 0.0f;
+            dPGt[(16 + lc) * LDC + 4 * lg + i] = 0.0f;
           }
         }
       }
@@ -742,45 +764,58 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     }
     __syncthreads();
 
-    // ---- P6: partial dQ and dK (2 x NKT tiles each) ---------------------
-    for (int t = wave; t < 4 * NKT; t += kNW) {
-      const bool isQ = t < 2 * NKT;
-      const int tt = t % (2 * NKT);
-      const int rt = tt / NKT, kt = tt % NKT;
+    // ---- P6: partial dQ and dK, one (row tile, key tile) pair per wave --
+    // The pair's dQ and dK tiles share the S row fragment (dY S^T, dX S^T)
+    // and the K column fragment ((dP o G) K, (N + N^T) K).
+    for (int t = wave; t < 2 * NKT; t += kNW) {
+      const int rt = t / NKT, kt = t % NKT;
+      FragM fS, fK, fa, fb;
+      ld_row(fS, Ss, LDV, 16 * kt + lc, 0);
+      ld_col(fK, Ks, LDK, 16 * kt + lc, 0);
+      // dQ = diag(gamma) dY S^T + (dP o G) K. The gamma terms of d g,
+      // gamma_r (Q S)_r . dY_r = gamma_r sum_k Q_rk (dY S^T)_rk, are row sums
+      // of Q o (dY S^T) over this tile's 16 keys.
       f32x4 acc = zero4();
-      if (isQ) {
-        // diag(gamma) dY S^T + (dP o G) K. The gamma terms of d g,
-        // gamma_r (Q S)_r . dY_r = gamma_r sum_k Q_rk (dY S^T)_rk, are
-        // row sums of Q o (dY S^T) over this tile's 16 keys.
-        mm_rr<H16>(acc, dYs, LDV, Ss, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * lg + i;
-          acc[i] *= s_gam[r];
-          const float qs = sum16(acc[i] * Qs[r * LDK + 16 * kt + lc]);
-          if (lc == 0) s_qsdy[kt][r] = qs;
-        }
-        mm_rc<H16>(acc, dPGm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
-      } else {
-        // diag(kdec) E dS'^T + (dP o G)^T Q + dX S^T + (N + N^T) K
-        mm_rr<H16>(acc, Es, LDV, dSs, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * lg + i;
-          acc[i] *= s_kdec[r];
-          const float cr = sum16(acc[i] * Ks[r * LDK + 16 * kt + lc]);
-          if (lc == 0) s_cr[kt][r] = cr;
-        }
-        mm_cc<H16>(acc, dPGm, LDC, Qs, LDK, 16 * rt, 16 * kt, C, lc, lg);
-        mm_rr<H16>(acc, dXs, LDV, Ss, LDV, 16 * rt, 16 * kt, DVT, lc, lg);
-        mm_rc<H16>(acc, Nm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
-        mm_cc<H16>(acc, Nm, LDC, Ks, LDK, 16 * rt, 16 * kt, C, lc, lg);
-      }
-      float *dst = a.ws_part + ((static_cast<size_t>(isQ ? 0 : 1) * n_vt + vt) * part_stride) * DK;
+      ld_row(fa, dYs, LDV, 16 * rt + lc, 0);
+      mma(acc, fa, fS);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * lg + i;
-        if (r < valid) dst[((t0 + r) * H + h) * DK + 16 * kt + lc] = acc[i];
+        acc[i] *= s_gam[r];
+        const float qs = sum16(acc[i] * Qs[r * LDK + 16 * kt + lc]);
+        if (lc == 0) s_qsdy[kt][r] = qs;
+      }
+      ld_row(fa, dPGm, LDC, 16 * rt + lc, 0);
+      mma(acc, fa, fK);
+      // dK = diag(kdec) E dS'^T + (dP o G)^T Q + dX S^T + (N + N^T) K
+      f32x4 acc2 = zero4();
+      ld_row(fa, Es, LDV, 16 * rt + lc, 0);
+      ld_row(fb, dSs, LDV, 16 * kt + lc, 0);
+      mma(acc2, fa, fb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i;
+        acc2[i] *= s_kdec[r];
+        const float cr = sum16(acc2[i] * Ks[r * LDK + 16 * kt + lc]);
+        if (lc == 0) s_cr[kt][r] = cr;
+      }
+      ld_row(fa, dPGt, LDC, 16 * rt + lc, 0);
+      ld_col(fb, Qs, LDK, 16 * kt + lc, 0);
+      mma(acc2, fa, fb);
+      ld_row(fa, dXs, LDV, 16 * rt + lc, 0);
+      mma(acc2, fa, fS);
+      ld_row(fa, Mm, LDC, 16 * rt + lc, 0);
+      mma(acc2, fa, fK);
+      float *dq_part = a.ws_part + (static_cast<size_t>(vt) * part_stride) * DK;
+      float *dk_part = a.ws_part + ((static_cast<size_t>(n_vt) + vt) * part_stride) * DK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i;
+        if (r < valid) {
+          const size_t o = ((t0 + r) * H + h) * DK + 16 * kt + lc;
+          dq_part[o] = acc[i];
+          dk_part[o] = acc2[i];
+        }
       }
     }
     // Row work for dbeta and d log alpha, one (row r, column i) element of
@@ -974,7 +1009,7 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
       f.out_dtype = a.in_dtype;
       f.stream = a.stream;
       f.states = a.ws_states;
-      const hipError_t e = launch_chunk_fwd_bf16(f);
+      const hipError_t e = launch_chunk_fwd_states(f);
       if (e != hipSuccess) return e;
     }
     const int64_t blocks = (units + 7) / 8 * 8 * n_vt;

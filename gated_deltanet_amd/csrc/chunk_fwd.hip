@@ -223,7 +223,9 @@ __device__ __forceinline__ V lds_read16(const char *p) {
   return *reinterpret_cast<const V *>(p);
 }
 
-template <int DK, int NS, typename TIN, typename TOUT>
+// STATES: write every chunk-start state to `states` (the backward pass's
+// workspace) instead of y and S_T
+template <int DK, int NS, typename TIN, typename TOUT, bool STATES>
 __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     const TIN *__restrict__ q, const TIN *__restrict__ k, const TIN *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
@@ -643,7 +645,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   // chunk-start states for the backward pass (optional): chunk x of sequence
   // n goes to slot floor(bos / C) + n + x, this wave's slab of the tile
   float *const st_out =
-      states ? states + ((static_cast<size_t>(bos / kC + n) * H + h) * n_vt + vt) * DK * DVT +
+      STATES ? states + ((static_cast<size_t>(bos / kC + n) * H + h) * n_vt + vt) * DK * DVT +
                    (static_cast<size_t>(wave) * NST * 64 + lane) * 4
              : nullptr;
   // byte offset of this lane's first y element inside a chunk's rows
@@ -651,7 +653,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       static_cast<uint32_t>((4 * lg * hdv + h * DV + v0 + slab + lc) * sizeof(TOUT));
 
   auto state_step = [&](int x) {
-    if (st_out) {
+    if constexpr (STATES) {
       float *dst = st_out + static_cast<size_t>(x) * H * n_vt * DK * DVT;
 #pragma unroll
       for (int t = 0; t < NST; ++t) *reinterpret_cast<f32x4 *>(dst + t * 256) = st[t];
@@ -740,7 +742,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     f32x4 Yt[kNCT];
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt) Yt[rt] = mma_f16(pf[rt], eb, G4[rt] * QS[rt]);
-    if (!y) return;
+    if constexpr (STATES) return;
     const uint32_t rows = static_cast<uint32_t>(rows_of(x));
     const auto ry = __builtin_amdgcn_make_buffer_rsrc(y + row0_of(x) * hdv, 0,
                                                       static_cast<int>(rows * hdv * sizeof(TOUT)),
@@ -816,7 +818,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     }
   }
 
-  if (is_state && S_T) {
+  if (!STATES && is_state && S_T) {
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
@@ -825,14 +827,14 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   }
 }
 
-template <int DK, int NS, typename TIN, typename TOUT>
+template <int DK, int NS, typename TIN, typename TOUT, bool STATES = false>
 hipError_t launch_bf16(const ChunkArgs &a) {
   constexpr int DVT = 16 * NS;
   const int n_vt = a.dv / DVT;
   const int64_t units = static_cast<int64_t>(a.N) * a.H;
   const int64_t blocks = (units + 7) / 8 * 8 * n_vt;
   if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, NS, TIN, TOUT>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, NS, TIN, TOUT, STATES>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * (NS + kPrep)), 0, a.stream, static_cast<const TIN *>(a.q),
                      static_cast<const TIN *>(a.k), static_cast<const TIN *>(a.v),
                      a.log_alpha, a.beta, a.A, a.b_alpha, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.states, a.cu_seqlens,
@@ -858,6 +860,14 @@ static hipError_t launch_16_out(const ChunkArgs &a) {
 
 hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a) {
   return a.in_dtype == 2 ? launch_16_out<_Float16>(a) : launch_16_out<bf16_t>(a);
+}
+
+hipError_t launch_chunk_fwd_states(const ChunkArgs &a) {
+  if (a.in_dtype == 2)
+    return a.dk == 128 ? launch_bf16<128, 2, _Float16, _Float16, true>(a)
+                       : launch_bf16<64, 2, _Float16, _Float16, true>(a);
+  return a.dk == 128 ? launch_bf16<128, 2, bf16_t, bf16_t, true>(a)
+                     : launch_bf16<64, 2, bf16_t, bf16_t, true>(a);
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a) {

@@ -59,8 +59,8 @@ struct ChunkArgs {
   int N, T, H, dk, dv;
   int in_dtype, out_dtype;
   hipStream_t stream;
-  // 16-bit kernel only: chunk-start states in the backward workspace's tile
-  // order (null: not written); y may then be null
+  // launch_chunk_fwd_states only: chunk-start states in the backward
+  // workspace's tile order
   float *states = nullptr;
 };
 
@@ -132,5 +132,7 @@ hipError_t launch_output_gate(const GateArgs &a);
 hipError_t launch_chunk_fwd(const ChunkArgs &a);      // dispatches on in_dtype
 hipError_t launch_chunk_fwd_f32(const ChunkArgs &a);  // fp32 inputs
 hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a); // bf16 inputs
+// 16-bit inputs: chunk-start states only (a.states; y and S_T not written)
+hipError_t launch_chunk_fwd_states(const ChunkArgs &a);
 
 }  // namespace gdn
