@@ -184,8 +184,13 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Rs[C * LDV];
   __shared__ __attribute__((aligned(16))) float Es[C * LDV];
   __shared__ __attribute__((aligned(16))) float dEs[C * LDV];
-  __shared__ __attribute__((aligned(16))) float dRs[C * LDV];
   __shared__ __attribute__((aligned(16))) float dXs[C * LDV];
+  // transposed copies (DVT rows of C) for the dS update's B operands
+  __shared__ __attribute__((aligned(16))) float dYgt[DVT * LDC];  // (diag(gamma) dY)^T
+  __shared__ __attribute__((aligned(16))) float dXt[DVT * LDC];   // dX^T
+  // dR shares R's buffer: R is last read when E = T R is formed, one phase
+  // before dR is written
+  float *const dRs = Rs;
   __shared__ __attribute__((aligned(16))) float Am[C * LDC];   // A, strictly lower
   __shared__ __attribute__((aligned(16))) float Tm[C * LDC];   // (I + A)^-1
   __shared__ __attribute__((aligned(16))) float Pm[C * LDC];   // tril(Q K^T o G)
@@ -657,11 +662,12 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     }
     __syncthreads();
 
-    // ---- P2: T; R = beta (V - gamma X) --------------------------------
+    // ---- P2: T; R = beta (V - gamma X); (diag(gamma) dY)^T ----------------
     invert();
     for (int idx = tid; idx < C * DVT; idx += kNT) {
       const int r = idx / DVT, cc = idx % DVT;
       Rs[r * LDV + cc] = s_beta[r] * (Vs[r * LDV + cc] - s_gam[r] * Xs[r * LDV + cc]);
+      dYgt[cc * LDC + r] = s_gam[r] * dYs[r * LDV + cc];
     }
     __syncthreads();
 
@@ -694,6 +700,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
         const float bg = s_beta[r] * s_gam[r];
         const float x = Xs[r * LDV + cc];
         dXs[r * LDV + cc] = -bg * dr;
+        dXt[cc * LDC + r] = -bg * dr;
         if (r < valid)
           dv_out[((t0 + r) * H + h) * DV + v0 + cc] = io<TG>::from_f32(s_beta[r] * dr);
         const float su = sum16(dr * (Vs[r * LDV + cc] - s_gam[r] * x));
@@ -766,56 +773,58 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
 
     // ---- P6: partial dQ and dK, one (row tile, key tile) pair per wave --
     // The pair's dQ and dK tiles share the S row fragment (dY S^T, dX S^T)
-    // and the K column fragment ((dP o G) K, (N + N^T) K).
+    // and the K column fragment ((dP o G) K, (N + N^T) K). Both tiles are
+    // formed transposed (operands swapped): lane (lg, lc) then holds keys
+    // 4 lg .. 4 lg + 3 of token row lc, stored with one 16-byte write.
     for (int t = wave; t < 2 * NKT; t += kNW) {
       const int rt = t / NKT, kt = t % NKT;
+      const int r = 16 * rt + lc;      // token row of this lane
+      const int k4 = 16 * kt + 4 * lg; // its first key
       FragM fS, fK, fa, fb;
       ld_row(fS, Ss, LDV, 16 * kt + lc, 0);
       ld_col(fK, Ks, LDK, 16 * kt + lc, 0);
       // dQ = diag(gamma) dY S^T + (dP o G) K. The gamma terms of d g,
-      // gamma_r (Q S)_r . dY_r = gamma_r sum_k Q_rk (dY S^T)_rk, are row sums
-      // of Q o (dY S^T) over this tile's 16 keys.
+      // gamma_r (Q S)_r . dY_r = gamma_r sum_k Q_rk (dY S^T)_rk, are sums of
+      // Q o (dY S^T) over the row's keys: four in the lane, then the four
+      // lane groups.
       f32x4 acc = zero4();
-      ld_row(fa, dYs, LDV, 16 * rt + lc, 0);
-      mma(acc, fa, fS);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i;
-        acc[i] *= s_gam[r];
-        const float qs = sum16(acc[i] * Qs[r * LDK + 16 * kt + lc]);
-        if (lc == 0) s_qsdy[kt][r] = qs;
+      ld_row(fa, dYs, LDV, r, 0);
+      mma(acc, fS, fa);
+      acc *= s_gam[r];
+      {
+        const f32x4 qv = *reinterpret_cast<const f32x4 *>(Qs + r * LDK + k4);
+        float qs = (acc[0] * qv[0] + acc[1] * qv[1]) + (acc[2] * qv[2] + acc[3] * qv[3]);
+        qs += __shfl_xor(qs, 16, 64);
+        qs += __shfl_xor(qs, 32, 64);
+        if (lg == 0) s_qsdy[kt][r] = qs;
       }
-      ld_row(fa, dPGm, LDC, 16 * rt + lc, 0);
-      mma(acc, fa, fK);
+      ld_row(fa, dPGm, LDC, r, 0);
+      mma(acc, fK, fa);
       // dK = diag(kdec) E dS'^T + (dP o G)^T Q + dX S^T + (N + N^T) K
       f32x4 acc2 = zero4();
-      ld_row(fa, Es, LDV, 16 * rt + lc, 0);
+      ld_row(fa, Es, LDV, r, 0);
       ld_row(fb, dSs, LDV, 16 * kt + lc, 0);
-      mma(acc2, fa, fb);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i;
-        acc2[i] *= s_kdec[r];
-        const float cr = sum16(acc2[i] * Ks[r * LDK + 16 * kt + lc]);
-        if (lc == 0) s_cr[kt][r] = cr;
+      mma(acc2, fb, fa);
+      acc2 *= s_kdec[r];
+      {
+        const f32x4 kv = *reinterpret_cast<const f32x4 *>(Ks + r * LDK + k4);
+        float cr = (acc2[0] * kv[0] + acc2[1] * kv[1]) + (acc2[2] * kv[2] + acc2[3] * kv[3]);
+        cr += __shfl_xor(cr, 16, 64);
+        cr += __shfl_xor(cr, 32, 64);
+        if (lg == 0) s_cr[kt][r] = cr;
       }
-      ld_row(fa, dPGt, LDC, 16 * rt + lc, 0);
+      ld_row(fa, dPGt, LDC, r, 0);
       ld_col(fb, Qs, LDK, 16 * kt + lc, 0);
-      mma(acc2, fa, fb);
-      ld_row(fa, dXs, LDV, 16 * rt + lc, 0);
-      mma(acc2, fa, fS);
-      ld_row(fa, Mm, LDC, 16 * rt + lc, 0);
-      mma(acc2, fa, fK);
-      float *dq_part = a.ws_part + (static_cast<size_t>(vt) * part_stride) * DK;
-      float *dk_part = a.ws_part + ((static_cast<size_t>(n_vt) + vt) * part_stride) * DK;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i;
-        if (r < valid) {
-          const size_t o = ((t0 + r) * H + h) * DK + 16 * kt + lc;
-          dq_part[o] = acc[i];
-          dk_part[o] = acc2[i];
-        }
+      mma(acc2, fb, fa);
+      ld_row(fa, dXs, LDV, r, 0);
+      mma(acc2, fS, fa);
+      ld_row(fa, Mm, LDC, r, 0);
+      mma(acc2, fK, fa);
+      if (r < valid) {
+        const size_t o = ((t0 + r) * H + h) * DK + k4;
+        *reinterpret_cast<f32x4 *>(a.ws_part + static_cast<size_t>(vt) * part_stride * DK + o) = acc;
+        *reinterpret_cast<f32x4 *>(a.ws_part + (static_cast<size_t>(n_vt) + vt) * part_stride * DK +
+                                   o) = acc2;
       }
     }
     // Row work for dbeta and d log alpha, one (row r, column i) element of
@@ -860,32 +869,16 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     const float gamC = s_gam[C - 1];
     for (int t = wave; t < NKT * 2; t += kNW) {
       const int mt = t >> 1, nt = t & 1;
+      // A operands: columns of Q and K (contraction over the chunk's rows);
+      // B operands: rows of the transposed copies
       f32x4 acc = zero4();
-      // (diag(gamma) Q)^T dY: gamma folded into the B operand (rows of dY)
-      if constexpr (H16) {
-        Frag<_Float16> fa, fb;
-        load_col_h(fa, Qs, LDK, 16 * mt + lc, 0, lg);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          fb.v[j] = (_Float16)(dYs[(4 * lg + j) * LDV + 16 * nt + lc] * s_gam[4 * lg + j]);
-          fb.v[4 + j] =
-              (_Float16)(dYs[(16 + 4 * lg + j) * LDV + 16 * nt + lc] * s_gam[16 + 4 * lg + j]);
-        }
-        mma(acc, fa, fb);
-      } else {
-        Acc4 sacc;
-        Frag<float> fa, fb;
-        fa.load_col(Qs, LDK, 16 * mt + lc, 0, lg);
-        fb.load_col(dYs, LDV, 16 * nt + lc, 0, lg);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          fb.v[j] *= s_gam[4 * lg + j];
-          fb.v[4 + j] *= s_gam[16 + 4 * lg + j];
-        }
-        sacc.mma(fa, fb);
-        sacc.add_to(acc);
-      }
-      mm_cc<H16>(acc, Ks, LDK, dXs, LDV, 16 * mt, 16 * nt, C, lc, lg);
+      FragM fa, fb;
+      ld_col(fa, Qs, LDK, 16 * mt + lc, 0);
+      ld_row(fb, dYgt, LDC, 16 * nt + lc, 0);
+      mma(acc, fa, fb);
+      ld_col(fa, Ks, LDK, 16 * mt + lc, 0);
+      ld_row(fb, dXt, LDC, 16 * nt + lc, 0);
+      mma(acc, fa, fb);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float *p = dSs + (16 * mt + 4 * lg + i) * LDV + 16 * nt + lc;
