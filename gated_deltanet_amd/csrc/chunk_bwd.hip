@@ -908,14 +908,30 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
   const size_t part_stride = static_cast<size_t>(a.rows) * a.H;
   const size_t total_k = part_stride * DK;
   const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i < total_k) {
-    float sq = 0.0f, sk = 0.0f;
+  // dq, dk: four consecutive elements per thread (16-byte partial loads)
+  if (4 * i < total_k) {
+    f32x4 sq = zero4(), sk = zero4();
     for (int t = 0; t < n_vt; ++t) {
-      sq += a.ws_part[(static_cast<size_t>(0) * n_vt + t) * total_k + i];
-      sk += a.ws_part[(static_cast<size_t>(1) * n_vt + t) * total_k + i];
+      sq += *reinterpret_cast<const f32x4 *>(a.ws_part + static_cast<size_t>(t) * total_k + 4 * i);
+      sk += *reinterpret_cast<const f32x4 *>(a.ws_part + static_cast<size_t>(n_vt + t) * total_k +
+                                             4 * i);
     }
-    static_cast<TG *>(a.dq)[i] = io<TG>::from_f32(sq);
-    static_cast<TG *>(a.dk)[i] = io<TG>::from_f32(sk);
+    TG *dq = static_cast<TG *>(a.dq) + 4 * i;
+    TG *dk = static_cast<TG *>(a.dk) + 4 * i;
+    if constexpr (sizeof(TG) == 4) {
+      *reinterpret_cast<f32x4 *>(dq) = sq;
+      *reinterpret_cast<f32x4 *>(dk) = sk;
+    } else {
+      typedef TG tg4 __attribute__((ext_vector_type(4)));
+      tg4 q4, k4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        q4[e] = io<TG>::from_f32(sq[e]);
+        k4[e] = io<TG>::from_f32(sk[e]);
+      }
+      *reinterpret_cast<tg4 *>(dq) = q4;
+      *reinterpret_cast<tg4 *>(dk) = k4;
+    }
   }
   if (i < part_stride) {
     float *g = a.ws_part + static_cast<size_t>(2) * n_vt * total_k;
@@ -1013,8 +1029,11 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
   }
   const size_t total = static_cast<size_t>(a.rows) * a.H * DK;
   if (total > 0) {
+    // one thread per four dq/dk elements, which also covers the rows * H
+    // gate rows (DK >= 4)
     hipLaunchKernelGGL((bwd_reduce_kernel<DK, TG>),
-                       dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, a.stream, a);
+                       dim3(static_cast<unsigned>((total / 4 + 255) / 256)), dim3(256), 0, a.stream,
+                       a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
