@@ -28,10 +28,12 @@
 // columns, so each tile writes its partial sums and a second kernel adds the
 // tiles in a fixed order (no atomics: results are deterministic).
 //
-// Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32) with
-// operands staged in LDS; the work is split into phases separated by
-// workgroup barriers, each phase's 16x16 output tiles dealt round-robin to
-// the sixteen waves (four per SIMD).
+// Operands are staged in LDS in fp32. With fp32 inputs every product runs on
+// v_mfma_f32_16x16x4_f32; with 16-bit inputs the operands are rounded to
+// fp16 as fragments are loaded and run on v_mfma_f32_16x16x32_f16 (fp32
+// accumulation). The work is split into phases separated by workgroup
+// barriers, each phase's 16x16 output tiles dealt round-robin to the sixteen
+// waves (four per SIMD).
 #include <type_traits>
 
 #include "gdn_device.h"
