@@ -421,29 +421,32 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     rt = t >= 1 ? 1 : 0;
     ct = t == 2 ? 1 : 0;
   };
-  // T = (I + A)^-1 for C = 32 by wave 0: 16x16 diagonal blocks by forward
-  // substitution (each 16-lane row of the wave solves one block, rows 2 and 3
-  // repeat rows 0 and 1: lane lc holds column lc of the block's A and T, and
-  // the substitution broadcasts A's entries between lanes, unit_lower_solve16),
-  // then T10 = -T11 (A10 T00) on the matrix cores
-  auto invert = [&]() {
-    if (wave != 0) return;
-    {
-      const int b0 = 16 * (lg & 1);
-      float ac[16], xv[16];
+  // T = (I + A)^-1 for C = 32 in two parts, each run by one wave. solve_diag:
+  // the 16x16 diagonal blocks by forward substitution (each 16-lane row of the
+  // wave solves one block, rows 2 and 3 repeat rows 0 and 1: lane lc holds
+  // column lc of the block's A and T, and the substitution broadcasts A's
+  // entries between lanes, unit_lower_solve16); the off-diagonal blocks are
+  // set to zero. t10: T10 = -T11 (A10 T00) on the matrix cores, written over
+  // the zero block.
+  // block: 0 or 16 for one diagonal block (every DPP row of the wave solves
+  // it), -1 for both (rows 0 and 2 solve the first, rows 1 and 3 the second)
+  auto solve_diag = [&](int block) {
+    const int b0 = block < 0 ? 16 * (lg & 1) : block;
+    float ac[16], xv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        ac[r] = Am[(b0 + r) * LDC + b0 + lc];
-        xv[r] = (r == lc) ? 1.0f : 0.0f;
-      }
-      unit_lower_solve16(ac, xv);
-      if (lg < 2) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDC + b0 + lc] = xv[r];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDC + (16 - b0) + lc] = 0.0f;
-      }
+    for (int r = 0; r < 16; ++r) {
+      ac[r] = Am[(b0 + r) * LDC + b0 + lc];
+      xv[r] = (r == lc) ? 1.0f : 0.0f;
     }
+    unit_lower_solve16(ac, xv);
+    if (block < 0 ? lg < 2 : lg == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDC + b0 + lc] = xv[r];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDC + (16 - b0) + lc] = 0.0f;
+    }
+  };
+  auto t10 = [&]() {
     // M = A10 T00 (16x16, contraction 16: the upper half of the slice is 0)
     f32x4 M = zero4();
     {
@@ -461,6 +464,27 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) Tm[(16 + 4 * lg + i) * LDC + lc] = -T10[i];
+  };
+  // LDS written by this wave is read back by it: keep the compiler from
+  // moving the reads ahead and wait for the writes (LDS serves a wave's
+  // requests in order)
+  auto lds_fence = [&]() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+  // issue priority of this wave on its SIMD (shared with three others): raised
+  // for the serial chains that set a phase's length
+  auto prio = [](bool high) {
+    if (high) __builtin_amdgcn_s_setprio(2);
+    else __builtin_amdgcn_s_setprio(0);
+  };
+  // column `col` of R = diag(beta)(V - diag(gamma) X) as a B fragment over
+  // the chunk's 32 rows, formed from V and X as it is loaded
+  auto ld_col_R = [&](FragM &f, int col) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = j < 4 ? 4 * lg + j : 16 + 4 * lg + (j - 4);
+      const float rv = s_beta[r] * (Vs[r * LDV + col] - s_gam[r] * Xs[r * LDV + col]);
+      if constexpr (H16) f.v[j] = (_Float16)rv;
+      else f.v[j] = rv;
+    }
   };
 
   // ======================= forward sweep: chunk-start states =============
@@ -517,7 +541,11 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     }
     __syncthreads();
     if (c + 1 < nc) fetch(pf, c + 1, false, false, false);
-    invert();
+    if (wave == 0) {
+      solve_diag(-1);
+      lds_fence();
+      t10();
+    }
     // R = beta (V - gamma X), all threads
     for (int idx = tid; idx < C * DVT; idx += kNT) {
       const int r = idx / DVT, cc = idx % DVT;
@@ -594,7 +622,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     for (int w = 0; w < kNW; ++w) rs += s_colp[w][r];
     float sred = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) sred += s_red[w];
+    for (int w = 0; w < kNW / 2; ++w) sred += s_red[w];
     rs += gC * sred;
     if (r < nv) {
       float *dst = a.ws_part + static_cast<size_t>(2) * n_vt * part_stride * DK;
@@ -613,42 +641,62 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     stage(pf, true, true, true);
     __syncthreads();
 
-    // ---- P1: A, K K^T o G, P (3 tiles each); X, Kt dS' (4 each) ---------
-    static_assert(kNW > 14, "the last wave has no tile in the first phase");
-    if (wave == kNW - 1 && c < nc - 1) gate_grads(prev_t0, prev_valid, prev_gamC);
-    for (int t = wave; t < 14; t += kNW) {
+    // ---- P1 -------------------------------------------------------------
+    // waves 0-2: P = tril(Q K^T o G); 3-6: X = K S; 7-10: Kt dS'; 12-14:
+    // K K^T o G and A, one tile each, the waves with a diagonal tile (14:
+    // rows 0-15, 12: rows 16-31) then solving that diagonal block of
+    // T = (I + A)^-1; 15: gate gradients of the chunk before.
+    static_assert(kNW == 16, "the first phase deals its work to sixteen waves");
+    auto gram_tile = [&](int t) {
+      int rt, ct;
+      low_tile(t, rt, ct);
       f32x4 acc = zero4();
-      if (t < 6) {
+      mm_rr<H16>(acc, Ks, LDK, Ks, LDK, 16 * rt, 16 * ct, DK, lc, lg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i, col = 16 * ct + lc;
+        const float gv = r >= col ? decay(r, col) * acc[i] : 0.0f;
+        KGm[r * LDC + col] = gv;
+        Am[r * LDC + col] = r > col ? s_beta[r] * gv : 0.0f;
+      }
+      if (rt == 1 && ct == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int o = (4 * lg + i) * LDC + 16 + lc;
+          KGm[o] = 0.0f;
+          Am[o] = 0.0f;
+        }
+      }
+    };
+    if (wave == 15) {
+      if (c < nc - 1) gate_grads(prev_t0, prev_valid, prev_gamC);
+    } else if (wave == 14 || wave == 12) {
+      prio(true);
+      gram_tile(wave == 14 ? 0 : 2);
+      lds_fence();
+      solve_diag(wave == 14 ? 0 : 16);
+      prio(false);
+    } else if (wave == 13) {
+      gram_tile(1);
+    } else if (wave < 11) {
+      const int t = wave;
+      f32x4 acc = zero4();
+      if (t < 3) {
         int rt, ct;
-        low_tile(t % 3, rt, ct);
-        const bool gram = t < 3;
-        mm_rr<H16>(acc, gram ? Ks : Qs, LDK, Ks, LDK, 16 * rt, 16 * ct, DK, lc, lg);
+        low_tile(t, rt, ct);
+        mm_rr<H16>(acc, Qs, LDK, Ks, LDK, 16 * rt, 16 * ct, DK, lc, lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * rt + 4 * lg + i, col = 16 * ct + lc;
-          const float gv = r >= col ? decay(r, col) * acc[i] : 0.0f;
-          if (gram) {
-            KGm[r * LDC + col] = gv;
-            Am[r * LDC + col] = r > col ? s_beta[r] * gv : 0.0f;
-          } else {
-            Pm[r * LDC + col] = gv;
-          }
+          Pm[r * LDC + col] = r >= col ? decay(r, col) * acc[i] : 0.0f;
         }
         if (rt == 1 && ct == 0) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int o = (4 * lg + i) * LDC + 16 + lc;
-            if (gram) {
-              KGm[o] = 0.0f;
-              Am[o] = 0.0f;
-            } else {
-              Pm[o] = 0.0f;
-            }
-          }
+          for (int i = 0; i < 4; ++i) Pm[(4 * lg + i) * LDC + 16 + lc] = 0.0f;
         }
       } else {
-        const bool isX = t < 10;  // X = K S, else Kt dS'
-        const int rt = ((t - 6) % 4) >> 1, nt = (t - 6) & 1;
+        const bool isX = t < 7;  // X = K S, else Kt dS'
+        const int rt = ((t - 3) % 4) >> 1, nt = (t - 3) & 1;
         mm_rc<H16>(acc, Ks, LDK, isX ? Ss : dSs, LDV, 16 * rt, 16 * nt, DK, lc, lg);
         if (isX) {
 #pragma unroll
@@ -664,34 +712,54 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     }
     __syncthreads();
 
-    // ---- P2: T; R = beta (V - gamma X); (diag(gamma) dY)^T ----------------
-    invert();
-    for (int idx = tid; idx < C * DVT; idx += kNT) {
-      const int r = idx / DVT, cc = idx % DVT;
-      Rs[r * LDV + cc] = s_beta[r] * (Vs[r * LDV + cc] - s_gam[r] * Xs[r * LDV + cc]);
-      dYgt[cc * LDC + r] = s_gam[r] * dYs[r * LDV + cc];
-    }
-    __syncthreads();
-
-    // ---- P3: E = T R; dE += P^T dY -------------------------------------
-    for (int t = wave; t < 8; t += kNW) {
+    // ---- P2: E = T R (R formed on load); dE += P^T dY; gamma_C <S, dS'> ----
+    // The two waves of E's lower row tile first complete T with T10 (both
+    // write the same values).
+    if (wave < 8) {
+      const int t = wave;
       const int rt = (t & 3) >> 1, nt = t & 1;
       f32x4 acc = zero4();
       if (t < 4) {
-        mm_rc<H16>(acc, Tm, LDC, Rs, LDV, 16 * rt, 16 * nt, C, lc, lg);
+        if (rt == 1) {
+          prio(true);
+          t10();
+          lds_fence();
+        }
+        FragM fa, fb;
+        ld_row(fa, Tm, LDC, 16 * rt + lc, 0);
+        ld_col_R(fb, 16 * nt + lc);
+        mma(acc, fa, fb);
 #pragma unroll
         for (int i = 0; i < 4; ++i) Es[(16 * rt + 4 * lg + i) * LDV + 16 * nt + lc] = acc[i];
+        if (rt == 1) prio(false);
       } else {
         mm_cc<H16>(acc, Pm, LDC, dYs, LDV, 16 * rt, 16 * nt, C, lc, lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dEs[(16 * rt + 4 * lg + i) * LDV + 16 * nt + lc] += acc[i];
       }
+    } else {
+      // (diag(gamma) dY)^T for the dS update, and <S, dS'> over the tile,
+      // one sum per wave, by the other eight waves
+      for (int idx = tid - kNT / 2; idx < C * DVT; idx += kNT / 2) {
+        const int r = idx / DVT, cc = idx % DVT;
+        dYgt[cc * LDC + r] = s_gam[r] * dYs[r * LDV + cc];
+      }
+      float acc = 0.0f;
+      for (int idx = tid - kNT / 2; idx < DK * DVT; idx += kNT / 2) {
+        const int r = idx / DVT, cc = idx % DVT;
+        acc = fmaf(Ss[r * LDV + cc], dSs[r * LDV + cc], acc);
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
+      if (lane == 0) s_red[wave - kNW / 2] = acc;
     }
     __syncthreads();
 
-    // ---- P4: dR = T^T dE; dV, dX and their row sums ---------------------
-    for (int t = wave; t < 4; t += kNW) {
+    // ---- P3: dR = T^T dE; dV, dX and their row sums; dP = tril(dY E^T) ---
+    if (wave < 4) {
+      const int t = wave;
       const int rt = t >> 1, nt = t & 1;
+      prio(true);
       f32x4 acc = zero4();
       mm_cc<H16>(acc, Tm, LDC, dEs, LDV, 16 * rt, 16 * nt, C, lc, lg);
 #pragma unroll
@@ -712,64 +780,59 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
           s_dgx[nt][r] = sx;
         }
       }
-    }
-    __syncthreads();
-
-    // ---- P5: dA = -strictly_lower(dR E^T), dP = tril(dY E^T) ------------
-    for (int t = wave; t < 6; t += kNW) {
+      prio(false);
+    } else if (wave < 7) {
       int rt, ct;
-      low_tile(t % 3, rt, ct);
-      const bool isA = t < 3;
+      low_tile(wave - 4, rt, ct);
       f32x4 acc = zero4();
-      mm_rr<H16>(acc, isA ? dRs : dYs, LDV, Es, LDV, 16 * rt, 16 * ct, DVT, lc, lg);
+      mm_rr<H16>(acc, dYs, LDV, Es, LDV, 16 * rt, 16 * ct, DVT, lc, lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * lg + i, col = 16 * ct + lc;
-        if (isA) {
-          // N is strictly lower: M = N + N^T gets N_rc at (r, c) and (c, r);
-          // the entries above the diagonal come from the partner lane (or,
-          // for the upper block, from the lower off-diagonal tile)
-          const float d = r > col ? -acc[i] : 0.0f;
-          dAm[r * LDC + col] = d;
-          const float nv = s_beta[r] * d * decay(r, col);
-          if (r > col) {
-            Mm[r * LDC + col] = nv;
-            Mm[col * LDC + r] = nv;
-          } else if (r == col) {
-            Mm[r * LDC + col] = 0.0f;
-          }
-        } else {
-          const float d = r >= col ? acc[i] : 0.0f;
-          dPm[r * LDC + col] = d;
-          const float dg = r >= col ? d * decay(r, col) : 0.0f;
-          dPGm[r * LDC + col] = dg;
-          dPGt[col * LDC + r] = dg;
-        }
+        const float d = r >= col ? acc[i] : 0.0f;
+        dPm[r * LDC + col] = d;
+        const float dg = r >= col ? d * decay(r, col) : 0.0f;
+        dPGm[r * LDC + col] = dg;
+        dPGt[col * LDC + r] = dg;
       }
       if (rt == 1 && ct == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int o = (4 * lg + i) * LDC + 16 + lc;
-          if (isA) {
-            dAm[o] = 0.0f;
-          } else {
-            dPm[o] = 0.0f;
-            dPGm[o] = 0.0f;
-            dPGt[(16 + lc) * LDC + 4 * lg + i] = 0.0f;
-          }
+          dPm[o] = 0.0f;
+          dPGm[o] = 0.0f;
+          dPGt[(16 + lc) * LDC + 4 * lg + i] = 0.0f;
         }
       }
     }
-    // gamma_C <S, dS'> over the tile (every thread, then per wave)
-    {
-      float acc = 0.0f;
-      for (int idx = tid; idx < DK * DVT; idx += kNT) {
-        const int r = idx / DVT, cc = idx % DVT;
-        acc = fmaf(Ss[r * LDV + cc], dSs[r * LDV + cc], acc);
-      }
+    __syncthreads();
+
+    // ---- P4: dA = -strictly_lower(dR E^T); M = N + N^T ------------------
+    if (wave < 3) {
+      int rt, ct;
+      low_tile(wave, rt, ct);
+      f32x4 acc = zero4();
+      mm_rr<H16>(acc, dRs, LDV, Es, LDV, 16 * rt, 16 * ct, DVT, lc, lg);
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
-      if (lane == 0) s_red[wave] = acc;
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i, col = 16 * ct + lc;
+        // N is strictly lower: M = N + N^T gets N_rc at (r, c) and (c, r);
+        // the entries above the diagonal come from the partner lane (or,
+        // for the upper block, from the lower off-diagonal tile)
+        const float d = r > col ? -acc[i] : 0.0f;
+        dAm[r * LDC + col] = d;
+        const float nv = s_beta[r] * d * decay(r, col);
+        if (r > col) {
+          Mm[r * LDC + col] = nv;
+          Mm[col * LDC + r] = nv;
+        } else if (r == col) {
+          Mm[r * LDC + col] = 0.0f;
+        }
+      }
+      if (rt == 1 && ct == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dAm[(4 * lg + i) * LDC + 16 + lc] = 0.0f;
+      }
     }
     __syncthreads();
 
