@@ -289,99 +289,138 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   constexpr int VI = (C * DVT / VEC + kNT - 1) / kNT;     // V pieces per thread
   constexpr int GI = (C * DVT / VG + kNT - 1) / kNT;      // dY pieces per thread
   constexpr int SI = (DK * DVT / 4 + kNT - 1) / kNT;      // state f32x4 per thread
+  // Pieces are spread over the waves so that none issues (and stages) more
+  // than three: K from thread 0, Q from thread kNT / 2 when it fits in half
+  // the workgroup, V from thread 256, dY after it, the gates on the last wave.
+  constexpr int KP = C * DK / VEC, VP = C * DVT / VEC, GP = C * DVT / VG;
+  constexpr int QOFF = KP <= kNT / 2 ? kNT / 2 : 0;
+  constexpr int VOFF = 256, GOFF = VOFF + (VP + 63) / 64 * 64;
+  static_assert(VOFF + VP <= kNT && GOFF + GP <= kNT && VI == 1 && GI == 1,
+                "V and dY pieces fit the workgroup once");
+  constexpr int kGateWave = kNW - 1;
   struct Pre {
     u32x4 k[KI], q[KI], v[VI], dy[GI];
     f32x4 s[SI];
     float la, bt;
   };
   const u32x4 zero_raw = {0u, 0u, 0u, 0u};
+  // Every load goes through a buffer resource that covers the chunk's valid
+  // rows (all heads), so rows past the sequence end and threads without a
+  // piece (offset kNone) read zeros without a branch: with no branch around
+  // the loads the compiler knows how many are in flight and waits for the
+  // ones it needs, not for all of them.
+  constexpr uint32_t kNone = 0x80000000u;
+  auto rsrc = [](const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
+                                             static_cast<int>(bytes), 0x00020000);
+  };
   auto fetch = [&](Pre &p, int c, bool with_q, bool with_dy, bool with_state) {
     const int64_t t0 = bos + static_cast<int64_t>(c) * C;
     const int valid = rows_valid(c);
+    const int64_t rows_b = static_cast<int64_t>(valid) * H;  // head-rows of the chunk
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const int idx = tid + kNT * i;
-      const int r = idx / (DK / VEC), d0 = (idx % (DK / VEC)) * VEC;
-      const bool in = idx < C * DK / VEC && r < valid;
-      const size_t off = ((t0 + r) * H + h) * DK + d0;
-      p.k[i] = in ? *reinterpret_cast<const u32x4 *>(k + off) : zero_raw;
-      if (with_q) p.q[i] = in ? *reinterpret_cast<const u32x4 *>(q + off) : zero_raw;
-    }
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int idx = tid + kNT * i;
-      const int r = idx / (DVT / VEC), d0 = (idx % (DVT / VEC)) * VEC;
-      p.v[i] = (idx < C * DVT / VEC && r < valid)
-                   ? *reinterpret_cast<const u32x4 *>(v + ((t0 + r) * H + h) * DV + v0 + d0)
-                   : zero_raw;
-    }
-    if (with_dy) {
-#pragma unroll
-      for (int i = 0; i < GI; ++i) {
+      {
         const int idx = tid + kNT * i;
-        const int r = idx / (DVT / VG), d0 = (idx % (DVT / VG)) * VG;
-        p.dy[i] = (idx < C * DVT / VG && r < valid)
-                      ? *reinterpret_cast<const u32x4 *>(dy + ((t0 + r) * H + h) * DV + v0 + d0)
-                      : zero_raw;
+        const int r = idx / (DK / VEC), d0 = (idx % (DK / VEC)) * VEC;
+        const uint32_t off = idx < KP ? static_cast<uint32_t>(((r * H + h) * DK + d0) * sizeof(TIN))
+                                      : kNone;
+        p.k[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rsrc(k + t0 * H * DK, rows_b * DK * sizeof(TIN)), off, 0, 0));
+      }
+      if (with_q) {
+        const int idx = tid + kNT * i - QOFF;
+        const int r = idx / (DK / VEC), d0 = (idx % (DK / VEC)) * VEC;
+        const uint32_t off = (idx >= 0 && idx < KP)
+                                 ? static_cast<uint32_t>(((r * H + h) * DK + d0) * sizeof(TIN))
+                                 : kNone;
+        p.q[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rsrc(q + t0 * H * DK, rows_b * DK * sizeof(TIN)), off, 0, 0));
       }
     }
+    {
+      const int idx = tid - VOFF;
+      const int r = idx / (DVT / VEC), d0 = (idx % (DVT / VEC)) * VEC;
+      const uint32_t off = (idx >= 0 && idx < VP)
+                               ? static_cast<uint32_t>(((r * H + h) * DV + v0 + d0) * sizeof(TIN))
+                               : kNone;
+      p.v[0] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rsrc(v + t0 * H * DV, rows_b * DV * sizeof(TIN)), off, 0, 0));
+    }
+    if (with_dy) {
+      const int idx = tid - GOFF;
+      const int r = idx / (DVT / VG), d0 = (idx % (DVT / VG)) * VG;
+      const uint32_t off = (idx >= 0 && idx < GP)
+                               ? static_cast<uint32_t>(((r * H + h) * DV + v0 + d0) * sizeof(TG))
+                               : kNone;
+      p.dy[0] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rsrc(dy + t0 * H * DV, rows_b * DV * sizeof(TG)), off, 0, 0));
+    }
     if (with_state) {
-      const float *src = state_tile(c);
+      // streamed once: non-temporal
+      const auto rs = rsrc(state_tile(c), DK * DVT * 4);
 #pragma unroll
       for (int i = 0; i < SI; ++i) {
         const int idx = tid + kNT * i;
-        if (idx < DK * DVT / 4) p.s[i] = *reinterpret_cast<const f32x4 *>(src + 4 * idx);
+        const uint32_t off = idx < DK * DVT / 4 ? static_cast<uint32_t>(16 * idx) : kNone;
+        p.s[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
       }
     }
     p.la = 0.0f;
     p.bt = 0.0f;
-    if (wave == 0 && lane < valid) {
-      p.la = a.log_alpha[(t0 + lane) * H + h];
-      p.bt = a.beta[(t0 + lane) * H + h];
-      if (gate.raw()) {
-        p.la = gate.log_alpha(p.la);
-        p.bt = RawGate::beta(p.bt);
-      }
+    if (wave == kGateWave) {
+      const uint32_t off = lane < C ? static_cast<uint32_t>((lane * H + h) * 4) : kNone;
+      p.la = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rsrc(a.log_alpha + t0 * H, rows_b * 4), off, 0, 0));
+      p.bt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rsrc(a.beta + t0 * H, rows_b * 4), off, 0, 0));
     }
   };
-  auto stage = [&](const Pre &p, bool with_q, bool with_dy, bool with_state) {
+  auto stage = [&](const Pre &p, int stage_valid, bool with_q, bool with_dy, bool with_state) {
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const int idx = tid + kNT * i;
-      if (idx >= C * DK / VEC) break;
-      const int r = idx / (DK / VEC), d0 = (idx % (DK / VEC)) * VEC;
       float x[VEC];
-      raw16_to_f32<TIN>(p.k[i], x);
+      {
+        const int idx = tid + kNT * i;
+        if (idx < KP) {
+          const int r = idx / (DK / VEC), d0 = (idx % (DK / VEC)) * VEC;
+          raw16_to_f32<TIN>(p.k[i], x);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) Ks[r * LDK + d0 + e] = x[e];
+          for (int e = 0; e < VEC; ++e) Ks[r * LDK + d0 + e] = x[e];
+        }
+      }
       if (with_q) {
-        raw16_to_f32<TIN>(p.q[i], x);
+        const int idx = tid + kNT * i - QOFF;
+        if (idx >= 0 && idx < KP) {
+          const int r = idx / (DK / VEC), d0 = (idx % (DK / VEC)) * VEC;
+          raw16_to_f32<TIN>(p.q[i], x);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) Qs[r * LDK + d0 + e] = x[e];
+          for (int e = 0; e < VEC; ++e) Qs[r * LDK + d0 + e] = x[e];
+        }
       }
     }
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int idx = tid + kNT * i;
-      if (idx < C * DVT / VEC) {
+    {
+      const int idx = tid - VOFF;
+      if (idx >= 0 && idx < VP) {
         const int r = idx / (DVT / VEC), d0 = (idx % (DVT / VEC)) * VEC;
         float x[VEC];
-        raw16_to_f32<TIN>(p.v[i], x);
+        raw16_to_f32<TIN>(p.v[0], x);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) Vs[r * LDV + d0 + e] = x[e];
       }
     }
     if (with_dy) {
+      const int idx = tid - GOFF;
+      if (idx >= 0 && idx < GP) {
+        const int r = idx / (DVT / VG), d0 = (idx % (DVT / VG)) * VG;
+        float x[VG];
+        raw16_to_f32<TG>(p.dy[0], x);
 #pragma unroll
-      for (int i = 0; i < GI; ++i) {
-        const int idx = tid + kNT * i;
-        if (idx < C * DVT / VG) {
-          const int r = idx / (DVT / VG), d0 = (idx % (DVT / VG)) * VG;
-          float x[VG];
-          raw16_to_f32<TG>(p.dy[i], x);
-#pragma unroll
-          for (int e = 0; e < VG; ++e) dYs[r * LDV + d0 + e] = x[e];
-        }
+        for (int e = 0; e < VG; ++e) dYs[r * LDV + d0 + e] = x[e];
       }
     }
     if (with_state) {
@@ -398,9 +437,13 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
         }
       }
     }
-    // gates: wave 0 scans the chunk's log decays (rows past the end: 0)
-    if (wave == 0) {
-      float g = p.la;
+    // gates: the gate wave scans the chunk's log decays (rows past the end: 0)
+    if (wave == kGateWave) {
+      float g = p.la, bt = p.bt;
+      if (gate.raw() && lane < stage_valid) {
+        g = gate.log_alpha(g);
+        bt = RawGate::beta(bt);
+      }
 #pragma unroll
       for (int off = 1; off < 32; off <<= 1) {
         const float o = __shfl_up(g, off, 64);
@@ -410,7 +453,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       if (lane < C) {
         s_g[lane] = g;
         s_gam[lane] = __expf(g);
-        s_beta[lane] = p.bt;
+        s_beta[lane] = bt;
         s_kdec[lane] = __expf(gC - g);
       }
     }
@@ -514,7 +557,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
         *reinterpret_cast<f32x4 *>(dst + 4 * idx) = sv;
       }
     }
-    stage(pf, false, false, false);
+    stage(pf, rows_valid(c), false, false, false);
     __syncthreads();
     // A (3 tiles) and X = K S (4 tiles)
     for (int t = wave; t < 7; t += kNW) {
@@ -638,7 +681,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     opaque_lanes();
     const int64_t t0 = bos + static_cast<int64_t>(c) * C;
     const int valid = rows_valid(c);
-    stage(pf, true, true, true);
+    stage(pf, valid, true, true, true);
     __syncthreads();
 
     // ---- P1 -------------------------------------------------------------
@@ -836,6 +879,11 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     }
     __syncthreads();
 
+    // the next chunk's inputs, fetched before this phase's partial stores:
+    // a later wait for a store (before its data registers are reused) would
+    // also wait for loads issued after it
+    if (c > 0) fetch(pf, c - 1, true, true, true);
+
     // ---- P6: partial dQ and dK, one (row tile, key tile) pair per wave --
     // The pair's dQ and dK tiles share the S row fragment (dY S^T, dX S^T)
     // and the K column fragment ((dP o G) K, (N + N^T) K). Both tiles are
@@ -926,9 +974,6 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     }
     __syncthreads();
 
-    // the next chunk's inputs: fetched here, so their registers are not
-    // live through the heavy phases above, and still a phase ahead of use
-    if (c > 0) fetch(pf, c - 1, true, true, true);
 
     // ---- P7: dS <- gamma_C dS' + (diag(gamma) Q)^T dY + K^T dX; gates -----
     const float gamC = s_gam[C - 1];
