@@ -496,14 +496,14 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       Frag<float> fa, fb;
       fa.load_row_lo(Am, LDC, 16 + lc, 0, lg);
       fb.load_col_lo(Tm, LDC, lc, 0, lg);
-      mma(M, fa, fb);
+      mma_lo(M, fa, fb);
     }
     f32x4 T10 = zero4();
     {
       Frag<float> fa, fb;
       fa.load_row_lo(Tm, LDC, 16 + lc, 16, lg);
       fb.from_acc_lo(M);
-      mma(T10, fa, fb);
+      mma_lo(T10, fa, fb);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) Tm[(16 + 4 * lg + i) * LDC + lc] = -T10[i];
@@ -757,28 +757,32 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
 
     // ---- P2: E = T R (R formed on load); dE += P^T dY; gamma_C <S, dS'> ----
     // The two waves of E's lower row tile first complete T with T10 (both
-    // write the same values).
+    // write the same values). Tiles here and in the next phase are formed
+    // transposed (operands swapped): lane (lg, lc) holds columns 4 lg ..
+    // 4 lg + 3 of token row lc, one 16-byte LDS access.
     if (wave < 8) {
       const int t = wave;
       const int rt = (t & 3) >> 1, nt = t & 1;
+      const int r = 16 * rt + lc, c4 = 16 * nt + 4 * lg;
       f32x4 acc = zero4();
+      FragM fa, fb;
       if (t < 4) {
         if (rt == 1) {
           prio(true);
           t10();
           lds_fence();
         }
-        FragM fa, fb;
-        ld_row(fa, Tm, LDC, 16 * rt + lc, 0);
+        ld_row(fa, Tm, LDC, r, 0);
         ld_col_R(fb, 16 * nt + lc);
-        mma(acc, fa, fb);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Es[(16 * rt + 4 * lg + i) * LDV + 16 * nt + lc] = acc[i];
+        mma(acc, fb, fa);
+        *reinterpret_cast<f32x4 *>(Es + r * LDV + c4) = acc;
         if (rt == 1) prio(false);
       } else {
-        mm_cc<H16>(acc, Pm, LDC, dYs, LDV, 16 * rt, 16 * nt, C, lc, lg);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dEs[(16 * rt + 4 * lg + i) * LDV + 16 * nt + lc] += acc[i];
+        ld_col(fa, Pm, LDC, r, 0);
+        ld_col(fb, dYs, LDV, 16 * nt + lc, 0);
+        mma(acc, fb, fa);
+        f32x4 *de = reinterpret_cast<f32x4 *>(dEs + r * LDV + c4);
+        *de = *de + acc;
       }
     } else {
       // (diag(gamma) dY)^T for the dS update, and <S, dS'> over the tile,
@@ -802,26 +806,50 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     if (wave < 4) {
       const int t = wave;
       const int rt = t >> 1, nt = t & 1;
+      const int r = 16 * rt + lc, c4 = 16 * nt + 4 * lg;  // transposed tile
       prio(true);
-      f32x4 acc = zero4();
-      mm_cc<H16>(acc, Tm, LDC, dEs, LDV, 16 * rt, 16 * nt, C, lc, lg);
+      f32x4 dr = zero4();
+      {
+        FragM fa, fb;
+        ld_col(fa, Tm, LDC, r, 0);
+        ld_col(fb, dEs, LDV, 16 * nt + lc, 0);
+        mma(dr, fb, fa);
+      }
+      const float br = s_beta[r], gr = s_gam[r], bg = br * gr;
+      const f32x4 x = *reinterpret_cast<const f32x4 *>(Xs + r * LDV + c4);
+      const f32x4 vv = *reinterpret_cast<const f32x4 *>(Vs + r * LDV + c4);
+      const f32x4 dx = -bg * dr;
+      *reinterpret_cast<f32x4 *>(dRs + r * LDV + c4) = dr;
+      *reinterpret_cast<f32x4 *>(dXs + r * LDV + c4) = dx;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i, cc = 16 * nt + lc;
-        const float dr = acc[i];
-        dRs[r * LDV + cc] = dr;
-        const float bg = s_beta[r] * s_gam[r];
-        const float x = Xs[r * LDV + cc];
-        dXs[r * LDV + cc] = -bg * dr;
-        dXt[cc * LDC + r] = -bg * dr;
-        if (r < valid)
-          dv_out[((t0 + r) * H + h) * DV + v0 + cc] = io<TG>::from_f32(s_beta[r] * dr);
-        const float su = sum16(dr * (Vs[r * LDV + cc] - s_gam[r] * x));
-        const float sx = sum16(-bg * dr * x);
-        if (lc == 0) {
-          s_dbu[nt][r] = su;
-          s_dgx[nt][r] = sx;
+      for (int e = 0; e < 4; ++e) dXt[(c4 + e) * LDC + r] = dx[e];
+      if (r < valid) {
+        TG *dst = dv_out + ((t0 + r) * H + h) * DV + v0 + c4;
+        if constexpr (sizeof(TG) == 4) {
+          *reinterpret_cast<f32x4 *>(dst) = br * dr;
+        } else {
+          typedef TG tg4 __attribute__((ext_vector_type(4)));
+          tg4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = io<TG>::from_f32(br * dr[e]);
+          *reinterpret_cast<tg4 *>(dst) = o;
         }
+      }
+      // row sums over this tile's 16 columns: four in the lane, then the
+      // four lane groups
+      float su = 0.0f, sx = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        su += dr[e] * (vv[e] - gr * x[e]);
+        sx += dx[e] * x[e];
+      }
+      su += __shfl_xor(su, 16, 64);
+      sx += __shfl_xor(sx, 16, 64);
+      su += __shfl_xor(su, 32, 64);
+      sx += __shfl_xor(sx, 32, 64);
+      if (lg == 0) {
+        s_dbu[nt][r] = su;
+        s_dgx[nt][r] = sx;
       }
       prio(false);
     } else if (wave < 7) {

@@ -243,6 +243,11 @@ __device__ __forceinline__ void mma(f32x4 &acc, const Frag<float> &a, const Frag
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
 }
+// the same for a 16-deep slice (slots 4..7 zero): half the instructions
+__device__ __forceinline__ void mma_lo(f32x4 &acc, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
 
 __device__ __forceinline__ f32x4 zero4() {
   f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
