@@ -188,8 +188,12 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float dEs[C * LDV];
   __shared__ __attribute__((aligned(16))) float dXs[C * LDV];
   // transposed copies (DVT rows of C) for the dS update's B operands
-  __shared__ __attribute__((aligned(16))) float dYgt[DVT * LDC];  // (diag(gamma) dY)^T
-  __shared__ __attribute__((aligned(16))) float dXt[DVT * LDC];   // dX^T
+  // Both carry e^(g_r - g_0) = gamma_r / gamma_0 in place of gamma_r (at most
+  // 1, the first row's exactly 1), and the product is scaled by gamma_0 in
+  // fp32: with strong decay gamma_r itself can fall below the fp16 range of
+  // the 16-bit operands, while the ratios keep the leading terms.
+  __shared__ __attribute__((aligned(16))) float dYgt[DVT * LDC];  // (diag(gamma/gamma_0) dY)^T
+  __shared__ __attribute__((aligned(16))) float dXt[DVT * LDC];   // (dX / gamma_0)^T
   // dR shares R's buffer: R is last read when E = T R is formed, one phase
   // before dR is written
   float *const dRs = Rs;
@@ -785,11 +789,11 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
         *de = *de + acc;
       }
     } else {
-      // (diag(gamma) dY)^T for the dS update, and <S, dS'> over the tile,
-      // one sum per wave, by the other eight waves
+      // (diag(gamma / gamma_0) dY)^T for the dS update, and <S, dS'> over the
+      // tile, one sum per wave, by the other eight waves
       for (int idx = tid - kNT / 2; idx < C * DVT; idx += kNT / 2) {
         const int r = idx / DVT, cc = idx % DVT;
-        dYgt[cc * LDC + r] = s_gam[r] * dYs[r * LDV + cc];
+        dYgt[cc * LDC + r] = __expf(s_g[r] - s_g[0]) * dYs[r * LDV + cc];
       }
       float acc = 0.0f;
       for (int idx = tid - kNT / 2; idx < DK * DVT; idx += kNT / 2) {
@@ -821,8 +825,9 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       const f32x4 dx = -bg * dr;
       *reinterpret_cast<f32x4 *>(dRs + r * LDV + c4) = dr;
       *reinterpret_cast<f32x4 *>(dXs + r * LDV + c4) = dx;
+      const float brel = -br * __expf(s_g[r] - s_g[0]);  // dX / gamma_0 per dR
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dXt[(c4 + e) * LDC + r] = dx[e];
+      for (int e = 0; e < 4; ++e) dXt[(c4 + e) * LDC + r] = brel * dr[e];
       if (r < valid) {
         TG *dst = dv_out + ((t0 + r) * H + h) * DV + v0 + c4;
         if constexpr (sizeof(TG) == 4) {
@@ -1003,12 +1008,12 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     __syncthreads();
 
 
-    // ---- P7: dS <- gamma_C dS' + (diag(gamma) Q)^T dY + K^T dX; gates -----
-    const float gamC = s_gam[C - 1];
+    // ---- P7: dS <- gamma_C dS' + (diag(gamma) Q)^T dY + K^T dX -----------
+    const float gamC = s_gam[C - 1], gam0 = s_gam[0];
     for (int t = wave; t < NKT * 2; t += kNW) {
       const int mt = t >> 1, nt = t & 1;
       // A operands: columns of Q and K (contraction over the chunk's rows);
-      // B operands: rows of the transposed copies
+      // B operands: rows of the transposed copies, relative to gamma_0
       f32x4 acc = zero4();
       FragM fa, fb;
       ld_col(fa, Qs, LDK, 16 * mt + lc, 0);
@@ -1020,7 +1025,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float *p = dSs + (16 * mt + 4 * lg + i) * LDV + 16 * nt + lc;
-        *p = gamC * *p + acc[i];
+        *p = gamC * *p + gam0 * acc[i];
       }
     }
     prev_t0 = t0;

@@ -658,6 +658,31 @@ def test_chunk_bwd_rect_heads_no_state(dk, dv):
 
 
 @gpu
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+def test_chunk_bwd_rect_heads_bf16(dk, dv):
+    # 16-bit inputs: the chunk-start states come from the prefill kernel
+    inp, dy, dST = _bwd_inputs([70, 9, 33], 3, dk, dv, "bf16", seed=dk + 3 * dv)
+    _check_bwd(inp, dy, dST, tol=TOL["bf16"])
+
+
+@gpu
+@pytest.mark.parametrize("case", ["no_decay", "strong_decay", "beta0", "beta1"])
+def test_chunk_bwd_gate_extremes_bf16(case):
+    # strong decay also takes the prefill kernel's per-element decay path
+    inp, dy, dST = _bwd_inputs([90, 40], 2, 128, 128, "bf16", seed=125)
+    rows = inp["q"].shape[0]
+    if case == "no_decay":
+        inp["log_alpha"] = torch.zeros(rows, 2)
+    elif case == "strong_decay":
+        inp["log_alpha"] = torch.full((rows, 2), -30.0)
+    elif case == "beta0":
+        inp["beta"] = torch.zeros(rows, 2)
+    else:
+        inp["beta"] = torch.ones(rows, 2)
+    _check_bwd(inp, dy, dST, tol=TOL["bf16"])
+
+
+@gpu
 def test_chunk_bwd_equal_length_bf16_grads_and_deterministic():
     g = _lib()
     inp = gi.prefill_inputs(2, 4, 200, 128, 128, "bf16", s0_std=0.02, seed=110)
