@@ -666,9 +666,11 @@ def test_chunk_bwd_rect_heads_bf16(dk, dv):
 
 
 @gpu
-@pytest.mark.parametrize("case", ["no_decay", "strong_decay", "beta0", "beta1"])
+@pytest.mark.parametrize("case", ["no_decay", "strong_decay", "beta0", "beta1", "repeated_keys",
+                                  "near_parallel", "large_v", "banded_decay"])
 def test_chunk_bwd_gate_extremes_bf16(case):
-    # strong decay also takes the prefill kernel's per-element decay path
+    # 16-bit inputs (fp16 operands); strong and banded decay also take the
+    # prefill kernel's per-element decay path for the chunk-start states
     inp, dy, dST = _bwd_inputs([90, 40], 2, 128, 128, "bf16", seed=125)
     rows = inp["q"].shape[0]
     if case == "no_decay":
@@ -677,8 +679,19 @@ def test_chunk_bwd_gate_extremes_bf16(case):
         inp["log_alpha"] = torch.full((rows, 2), -30.0)
     elif case == "beta0":
         inp["beta"] = torch.zeros(rows, 2)
-    else:
+    elif case == "beta1":
         inp["beta"] = torch.ones(rows, 2)
+    elif case == "repeated_keys":
+        inp["k"][1::2] = inp["k"][0::2][: inp["k"][1::2].shape[0]]
+    elif case == "near_parallel":
+        base = inp["k"][:1].float()
+        kk = base + gi.normal(inp["k"].shape, 78, 1) * 1e-2
+        inp["k"] = (kk / kk.norm(dim=-1, keepdim=True)).to(inp["k"].dtype)
+    elif case == "large_v":
+        inp["v"] = (inp["v"].float() * 64.0).to(inp["v"].dtype)
+    else:  # banded decay: 40-token bands alternate between none and log alpha = -12
+        band = (torch.arange(rows) // 40) % 2 == 1
+        inp["log_alpha"][band] = -12.0
     _check_bwd(inp, dy, dST, tol=TOL["bf16"])
 
 
