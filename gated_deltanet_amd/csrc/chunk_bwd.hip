@@ -917,7 +917,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     // also wait for loads issued after it
     if (c > 0) fetch(pf, c - 1, true, true, true);
 
-    // ---- P6: partial dQ and dK, one (row tile, key tile) pair per wave --
+    // ---- P5: partial dQ and dK, one (row tile, key tile) pair per wave --
     // The pair's dQ and dK tiles share the S row fragment (dY S^T, dX S^T)
     // and the K column fragment ((dP o G) K, (N + N^T) K). Both tiles are
     // formed transposed (operands swapped): lane (lg, lc) then holds keys
@@ -1008,7 +1008,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     __syncthreads();
 
 
-    // ---- P7: dS <- gamma_C dS' + (diag(gamma) Q)^T dY + K^T dX -----------
+    // ---- P6: dS <- gamma_C dS' + (diag(gamma) Q)^T dY + K^T dX -----------
     const float gamC = s_gam[C - 1], gam0 = s_gam[0];
     for (int t = wave; t < NKT * 2; t += kNW) {
       const int mt = t >> 1, nt = t & 1;
