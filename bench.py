@@ -288,6 +288,32 @@ def bench_longctx(g, steps=3, warmup=1):
                 hbm_GBps=nbytes / (ms * 1e-3) / 1e9)
 
 
+def bench_longctx_segmented(g, segment_counts=(2, 3, 4), steps=3, warmup=1):
+    """The long-context workload through gdn_chunk_fwd_segmented (each
+    sequence cut into P pieces whose state summaries are chained), per P."""
+    w = gi.WORKLOADS[2]
+    inp = gi.workload_inputs(2)
+    dev = torch.device("cuda", 0)
+    d = {k: inp[k].to(dev) for k in ("q", "k", "v", "log_alpha", "beta", "S0")}
+    y = torch.empty(d["v"].shape, dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty_like(d["S0"])
+    stream = torch.cuda.current_stream(dev)
+    rows = w.B * w.T
+    out = dict(workload=w.name, entry_point="gdn_chunk_fwd_segmented", ms_per_call={})
+    for P in segment_counts:
+        ws = torch.empty(g.gdn_chunk_fwd_segmented_workspace_size(rows, w.B, w.H, w.dk, w.dv, P,
+                                                                  torch.bfloat16),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            g.gdn_chunk_fwd_segmented(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], P,
+                                      d["S0"], y=y, S_T=S_T, workspace=ws)
+
+        out["ms_per_call"][str(P)] = time_launches(step, steps, warmup, stream) / steps
+        del ws
+    return out
+
+
 def bench_varlen_frontend(g, steps=3, warmup=1):
     """64 packed sequences (lengths U[512, 8192]), H=16, d=128 through
     gdn_chunk_fwd_fused: front end -> chunked prefill -> output gate (q/k/v
@@ -446,6 +472,11 @@ def main():
         print("[bench] long-context prefill workload 2: B=1 H=32 T=65536", file=sys.stderr,
               flush=True)
         rec["longctx"] = bench_longctx(g)
+        print("[bench] long-context prefill, segment-parallel form", file=sys.stderr, flush=True)
+        rec["longctx_segmented"] = bench_longctx_segmented(g)
+        rec["longctx_segmented"]["ms_vs_serial"] = {
+            P: t / rec["longctx"]["ms_per_call"]
+            for P, t in rec["longctx_segmented"]["ms_per_call"].items()}
         print("[bench] varlen front-end workload 4: 64 sequences, H=16", file=sys.stderr,
               flush=True)
         rec["varlen_frontend"] = bench_varlen_frontend(g)

@@ -17,6 +17,10 @@ Functions carry the names of the C entry points declared in include/gdn.h:
   S0=None, norm_w=None, l2_eps=1e-6, rms_eps=1e-6, cu_seqlens=None, N=None,
   out_dtype=None)`` -> (o, S_T)
 * ``gdn_fused_workspace_size(rows, H, d)`` -> bytes
+* ``gdn_chunk_fwd_segmented(q, k, v, log_alpha, beta, segments, S0=None,
+  cu_seqlens=None, out_dtype=None, ...)`` -> (y, S_T)
+* ``gdn_chunk_fwd_segmented_workspace_size(rows, N, H, dk, dv, segments,
+  in_dtype)`` -> bytes
 """
 from __future__ import annotations
 
@@ -91,6 +95,11 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_conv_state_from_prefill.argtypes = [vp, vp, vp, ip, i32, i32, i32, i32, ip, i32, vp,
                                                 i32, vp]
     lib.gdn_conv_state_from_prefill.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_segmented_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+    lib.gdn_chunk_fwd_segmented_workspace_size.restype = sz
+    lib.gdn_chunk_fwd_segmented.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, ip, i32, i32, i32,
+                                            i32, i32, i32, vp, sz, i32, i32, vp]
+    lib.gdn_chunk_fwd_segmented.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -188,6 +197,40 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, out_dtype=
                            _p(cu_seqlens), N, T, H, dk, dv, _dt(in_dtype), _dt(out_dtype),
                            _stream(v.device))
     _check(rc, lib, "gdn_chunk_fwd")
+    return y, S_T
+
+
+def gdn_chunk_fwd_segmented_workspace_size(rows: int, N: int, H: int, dk: int, dv: int,
+                                           segments: int, in_dtype: torch.dtype) -> int:
+    return int(load_library().gdn_chunk_fwd_segmented_workspace_size(
+        rows, N, H, dk, dv, segments, _dt(in_dtype)))
+
+
+def gdn_chunk_fwd_segmented(q, k, v, log_alpha, beta, segments, S0=None, cu_seqlens=None,
+                            out_dtype=None, S_T=None, y=None, want_state=True, N=None,
+                            workspace=None):
+    """Segment-parallel prefill: each sequence cut into `segments` pieces whose
+    state summaries are computed independently and chained. Arguments and
+    results as gdn_chunk_fwd; `workspace` (uint8 device tensor) is allocated
+    when not given."""
+    lib = load_library()
+    in_dtype = _prefill_checked(q, k, v, log_alpha, beta, ("log_alpha", "beta"))
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    N, T, H, dk, dv = _prefill_shape(q, v, S0, cu_seqlens, N)
+    rows = T if cu_seqlens is not None else N * T
+    if y is None:
+        y = torch.empty(v.shape, dtype=out_dtype, device=v.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=v.device)
+    nbytes = lib.gdn_chunk_fwd_segmented_workspace_size(rows, N, H, dk, dv, segments,
+                                                        _dt(in_dtype))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=v.device)
+    rc = lib.gdn_chunk_fwd_segmented(_p(q), _p(k), _p(v), _p(log_alpha), _p(beta), _p(S0), _p(y),
+                                     _p(S_T), _p(cu_seqlens), N, T, H, dk, dv, segments,
+                                     _p(workspace), workspace.numel(), _dt(in_dtype),
+                                     _dt(out_dtype), _stream(v.device))
+    _check(rc, lib, "gdn_chunk_fwd_segmented")
     return y, S_T
 
 

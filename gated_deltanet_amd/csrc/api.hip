@@ -68,7 +68,7 @@ int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log
                    const float *beta, const float *A, const float *b_alpha, const float *S0,
                    void *y, float *S_T, const int32_t *cu_seqlens, int32_t N, int32_t T,
                    int32_t H, int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype,
-                   void *stream, const char *name) {
+                   void *stream, const char *name, gdn::ChunkArgs *prepared = nullptr) {
   g_last_error[0] = '\0';
   if (N < 0 || T < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N, T must be >= 0 and H > 0");
   if (!head_size_ok(dk) || !head_size_ok(dv))
@@ -133,9 +133,48 @@ int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log
   a.in_dtype = in_dtype;
   a.out_dtype = out_dtype;
   a.stream = static_cast<hipStream_t>(stream);
+  if (prepared) {  // validated only: the caller launches
+    *prepared = a;
+    return GDN_OK;
+  }
   char where[64];
   snprintf(where, sizeof(where), "%s launch", name);
   return hip_status(gdn::launch_chunk_fwd(a), where);
+}
+
+// Workspace of gdn_chunk_fwd_segmented, byte offsets (each 256-aligned).
+struct SegLayout {
+  size_t cu, s0seg, nst, sin, sfin, mst, ident, vzero, yscr, vzero_bytes, total;
+};
+
+SegLayout seg_layout(int64_t rows, int N, int H, int dk, int dv, int P, int in_dtype) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t per = static_cast<size_t>(H) * dk * dv * 4;
+  const size_t mper = static_cast<size_t>(H) * dk * dk * 4;
+  const size_t nm = P > 2 ? static_cast<size_t>(P - 2) : 0;
+  SegLayout L;
+  size_t off = 0;
+  L.cu = off;
+  off += al(static_cast<size_t>(N) * (P + 1) * 4);
+  L.s0seg = off;
+  off += al(static_cast<size_t>(N) * (P - 1) * per);
+  L.nst = off;
+  off += al(static_cast<size_t>(N) * (P - 1) * per);
+  L.sin = off;
+  off += al(static_cast<size_t>(N) * (P - 1) * per);
+  L.sfin = off;
+  off += al(static_cast<size_t>(P - 1) * per);
+  L.mst = off;
+  off += al(static_cast<size_t>(N) * nm * mper);
+  L.ident = off;
+  off += al(nm * mper);
+  L.vzero_bytes = nm > 0 ? static_cast<size_t>(rows) * H * dk * esize(in_dtype) : 0;
+  L.vzero = off;
+  off += al(L.vzero_bytes);
+  L.yscr = off;
+  off += al(L.vzero_bytes);
+  L.total = off;
+  return L;
 }
 
 // Shared by every decode entry point. state_idx (may be null) is an int32
@@ -273,6 +312,133 @@ GDN_API int gdn_chunk_fwd_gated(const void *q, const void *k, const void *v, con
   if (H > 0 && !A) return fail(GDN_ERR_INVALID_ARG, "%s", "A is required");
   return chunk_fwd_impl(q, k, v, a, b, A, b_alpha, S0, y, S_T, cu_seqlens, N, T, H, dk, dv,
                         in_dtype, out_dtype, stream, "gdn_chunk_fwd_gated");
+}
+
+GDN_API size_t gdn_chunk_fwd_segmented_workspace_size(int64_t rows, int32_t N, int32_t H,
+                                                      int32_t dk, int32_t dv, int32_t segments,
+                                                      int32_t in_dtype) {
+  if (rows < 0 || N < 0 || H <= 0 || !head_size_ok(dk) || !head_size_ok(dv) || segments < 2 ||
+      segments > 64 || !dtype_ok(in_dtype))
+    return 0;
+  return seg_layout(rows, N, H, dk, dv, segments, in_dtype).total;
+}
+
+GDN_API int gdn_chunk_fwd_segmented(const void *q, const void *k, const void *v,
+                                    const float *log_alpha, const float *beta, const float *S0,
+                                    void *y, float *S_T, const int32_t *cu_seqlens, int32_t N,
+                                    int32_t T, int32_t H, int32_t dk, int32_t dv,
+                                    int32_t segments, void *workspace, size_t workspace_bytes,
+                                    int32_t in_dtype, int32_t out_dtype, void *stream) {
+  g_last_error[0] = '\0';
+  const int P = segments;
+  if (P < 2 || P > 64) return fail(GDN_ERR_INVALID_ARG, "%s", "segments must be in [2, 64]");
+  gdn::ChunkArgs base;
+  const int st = chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, nullptr, S0, y, S_T,
+                                cu_seqlens, N, T, H, dk, dv, in_dtype, out_dtype, stream,
+                                "gdn_chunk_fwd_segmented", &base);
+  if (st != GDN_OK) return st;
+  const int64_t rows = cu_seqlens ? static_cast<int64_t>(T) : static_cast<int64_t>(N) * T;
+  if (rows >= (int64_t{1} << 31))
+    return fail(GDN_ERR_INVALID_ARG, "%s", "more than 2^31 - 1 rows");
+  const SegLayout L = seg_layout(rows, N, H, dk, dv, P, in_dtype);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDN_ERR_INVALID_ARG, "%s", "workspace missing or smaller than "
+                                           "gdn_chunk_fwd_segmented_workspace_size");
+  if (misaligned(workspace, 256))
+    return fail(GDN_ERR_MISALIGNED, "%s", "workspace needs 256-byte alignment");
+  {
+    const size_t nq = static_cast<size_t>(rows) * H * dk * esize(in_dtype);
+    const size_t nv = static_cast<size_t>(rows) * H * dv * esize(in_dtype);
+    const size_t ng = static_cast<size_t>(rows) * H * 4;
+    const size_t ny = static_cast<size_t>(rows) * H * dv * esize(out_dtype);
+    const size_t ns = static_cast<size_t>(N) * H * dk * dv * 4;
+    const void *args[9] = {q, k, v, log_alpha, beta, S0, y, S_T, cu_seqlens};
+    const size_t sizes[9] = {nq, nq, nv, ng, ng, ns, ny, ns, static_cast<size_t>(N + 1) * 4};
+    for (int i = 0; i < 9; ++i)
+      if (overlap(workspace, L.total, args[i], sizes[i]))
+        return fail(GDN_ERR_INVALID_ARG, "%s", "the workspace overlaps an argument");
+  }
+  if (N == 0) return GDN_OK;
+
+  char *w = static_cast<char *>(workspace);
+  int32_t *cu_seg = reinterpret_cast<int32_t *>(w + L.cu);
+  float *s0seg = reinterpret_cast<float *>(w + L.s0seg);
+  float *nst = reinterpret_cast<float *>(w + L.nst);
+  float *sinit = reinterpret_cast<float *>(w + L.sin);
+  float *sfin = reinterpret_cast<float *>(w + L.sfin);
+  float *mst = reinterpret_cast<float *>(w + L.mst);
+  float *ident = reinterpret_cast<float *>(w + L.ident);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  gdn::SegPrepArgs pa;
+  pa.cu_seqlens = cu_seqlens;
+  pa.N = N;
+  pa.T = T;
+  pa.H = H;
+  pa.dk = dk;
+  pa.dv = dv;
+  pa.P = P;
+  pa.S0 = S0;
+  pa.cu_seg = cu_seg;
+  pa.S0seg = s0seg;
+  pa.ident = ident;
+  pa.n_ident = P > 2 ? static_cast<size_t>(P - 2) * H : 0;
+  pa.vzero = w + L.vzero;
+  pa.vzero_bytes = L.vzero_bytes;
+  pa.stream = s;
+  hipError_t e = gdn::launch_seg_prep(pa);
+  if (e != hipSuccess) return hip_status(e, "gdn_chunk_fwd_segmented bookkeeping");
+
+  const size_t per = static_cast<size_t>(H) * dk * dv;  // floats per state
+  const size_t mper = static_cast<size_t>(H) * dk * dk;
+  const int32_t Tall = static_cast<int32_t>(rows);      // row bound of the packed form
+  for (int n = 0; n < N; ++n) {
+    int32_t *cu_n = cu_seg + static_cast<size_t>(n) * (P + 1);
+    float *nst_n = nst + static_cast<size_t>(n) * (P - 1) * per;
+    float *sin_n = sinit + static_cast<size_t>(n) * (P - 1) * per;
+    float *mst_n = mst + static_cast<size_t>(n) * (P > 2 ? P - 2 : 0) * mper;
+    // segments 0 .. P-2 from zero (segment 0 from S0): summaries N, and y of
+    // segment 0
+    gdn::ChunkArgs a = base;
+    a.cu_seqlens = cu_n;
+    a.N = P - 1;
+    a.T = Tall;
+    a.S0 = s0seg + static_cast<size_t>(n) * (P - 1) * per;
+    a.S_T = nst_n;
+    e = gdn::launch_chunk_fwd(a);
+    if (e != hipSuccess) return hip_status(e, "gdn_chunk_fwd_segmented summaries");
+    // transitions M of segments 1 .. P-2: from the identity with v = 0
+    if (P > 2) {
+      gdn::ChunkArgs b = base;
+      b.v = w + L.vzero;
+      b.dv = dk;
+      b.S0 = ident;
+      b.y = w + L.yscr;
+      b.out_dtype = in_dtype;
+      b.S_T = mst_n;
+      b.cu_seqlens = cu_n + 1;
+      b.N = P - 2;
+      b.T = Tall;
+      e = gdn::launch_chunk_fwd(b);
+      if (e != hipSuccess) return hip_status(e, "gdn_chunk_fwd_segmented transitions");
+    }
+    e = gdn::launch_seg_combine(nst_n, mst_n, sin_n, H, dk, dv, P, s);
+    if (e != hipSuccess) return hip_status(e, "gdn_chunk_fwd_segmented chain");
+    // segments 1 .. P-1 again from their true initial states: y and S_T
+    gdn::ChunkArgs c = base;
+    c.cu_seqlens = cu_n + 1;
+    c.N = P - 1;
+    c.T = Tall;
+    c.S0 = sin_n;
+    c.S_T = S_T ? sfin : nullptr;
+    e = gdn::launch_chunk_fwd(c);
+    if (e != hipSuccess) return hip_status(e, "gdn_chunk_fwd_segmented outputs");
+    if (S_T) {
+      e = hipMemcpyAsync(S_T + static_cast<size_t>(n) * per, sfin + static_cast<size_t>(P - 2) * per,
+                         per * sizeof(float), hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_status(e, "gdn_chunk_fwd_segmented final state");
+    }
+  }
+  return GDN_OK;
 }
 
 GDN_API int gdn_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,

@@ -122,6 +122,27 @@ struct ConvStateArgs {
 };
 
 hipError_t launch_conv_state(const ConvStateArgs &a);
+
+// Bookkeeping of the segment-parallel prefill (segment.hip): segment bounds
+// (N x (P + 1)), initial states of the zero-start runs (N x (P - 1) states,
+// the first of each sequence the caller's S0), n_ident identity matrices and
+// vzero_bytes of zeros (the values of the transition runs).
+struct SegPrepArgs {
+  const int32_t *cu_seqlens;  // may be null
+  int N, T, H, dk, dv, P;
+  const float *S0;            // may be null
+  int32_t *cu_seg;
+  float *S0seg;
+  float *ident;
+  size_t n_ident;
+  void *vzero;
+  size_t vzero_bytes;
+  hipStream_t stream;
+};
+hipError_t launch_seg_prep(const SegPrepArgs &a);
+// The chain of one sequence's segment summaries into initial states.
+hipError_t launch_seg_combine(const float *Nst, const float *Mst, float *Sin, int H, int dk,
+                              int dv, int P, hipStream_t stream);
 hipError_t launch_decode_step(const DecodeArgs &a);
 hipError_t launch_chunk_bwd(const BwdArgs &a);
 size_t chunk_bwd_workspace_size(int64_t rows, int N, int H, int dk, int dv);

@@ -143,6 +143,48 @@ GDN_API int gdn_chunk_fwd_gated(const void *q, const void *k, const void *v,
                                 int32_t out_dtype, void *stream);
 
 /*
+ * Segment-parallel chunked prefill. The recurrence of the page
+ * "NLP——技术报告解读-Qwen3.8-Flash-Next", section "Gated DeltaNet 核心机制",
+ * is affine in the state, so over a stretch of tokens S_out = M S_in + N
+ * (M: the product of the per-token factors alpha_t (I - beta_t k_t k_t^T);
+ * N: the stretch run from a zero state). Each sequence is cut into
+ * `segments` pieces of whole 32-token chunks; the summaries (M, N) of the
+ * pieces are computed independently, chained into each piece's true initial
+ * state, and every piece after the first is run again from it for y. This
+ * is the one-GPU form of splitting a long sequence over several GPUs; on
+ * one GPU it does more work than gdn_chunk_fwd and is not faster (it cannot
+ * shorten the serial chain inside each workgroup).
+ *
+ *   segments   2 .. 64.
+ *   workspace  device memory of at least
+ *              gdn_chunk_fwd_segmented_workspace_size(...) bytes, 256-byte
+ *              aligned, not overlapping any argument; its contents on entry
+ *              do not matter and are overwritten.
+ * Every other argument as gdn_chunk_fwd (y and S_T equal gdn_chunk_fwd's up
+ * to rounding). Errors as gdn_chunk_fwd, plus GDN_ERR_INVALID_ARG for a bad
+ * segment count or a workspace that is missing or too small.
+ */
+GDN_API int gdn_chunk_fwd_segmented(const void *q, const void *k, const void *v,
+                                    const float *log_alpha, const float *beta,
+                                    const float *S0, void *y, float *S_T,
+                                    const int32_t *cu_seqlens, int32_t N, int32_t T,
+                                    int32_t H, int32_t dk, int32_t dv,
+                                    int32_t segments, void *workspace,
+                                    size_t workspace_bytes, int32_t in_dtype,
+                                    int32_t out_dtype, void *stream);
+
+/*
+ * Bytes of workspace gdn_chunk_fwd_segmented needs (0 for invalid sizes):
+ * segment bounds and per-segment states of all N sequences, plus zeros for
+ * the transition runs' values and a scratch for their outputs
+ * (2 * rows * H * dk elements of in_dtype). `rows` as for gdn_chunk_fwd:
+ * N * T, or T with cu_seqlens.
+ */
+GDN_API size_t gdn_chunk_fwd_segmented_workspace_size(int64_t rows, int32_t N, int32_t H,
+                                                      int32_t dk, int32_t dv,
+                                                      int32_t segments, int32_t in_dtype);
+
+/*
  * Decode step with raw gates and, for serving, an optional pool of state
  * slots (the fixed-size state per sequence of the same section makes a slot
  * pool the natural cache).

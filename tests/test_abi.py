@@ -306,3 +306,38 @@ def test_conv_state_and_gated_bwd_reject(lib):
     args[5] = A + (6 << 26)
     args[21] = None                                                  # dA missing
     assert lib.gdn_chunk_bwd_gated(*args) == -1
+
+
+def test_segmented_rejects(lib):
+    v, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.gdn_chunk_fwd_segmented_workspace_size.argtypes = [ctypes.c_int64] + [i32] * 6
+    lib.gdn_chunk_fwd_segmented_workspace_size.restype = sz
+    lib.gdn_chunk_fwd_segmented.argtypes = [v] * 9 + [i32] * 6 + [v, sz, i32, i32, v]
+    # rows 64, N 1, H 2, d 128, 3 segments, bf16: bounds (256 B padded), four
+    # sets of 2 states of 2 x 128 x 128 fp32 (zero-start initial and final,
+    # chained initial, rerun final), one transition and one identity, and
+    # 2 x 64 x 2 x 128 bf16 of zeros and scratch
+    need = lib.gdn_chunk_fwd_segmented_workspace_size(64, 1, 2, 128, 128, 3, 1)
+    per = 2 * 128 * 128 * 4
+    assert need == 256 + 4 * 2 * per + 2 * per + 2 * 64 * 2 * 128 * 2
+    assert lib.gdn_chunk_fwd_segmented_workspace_size(64, 1, 2, 128, 128, 1, 1) == 0
+    assert lib.gdn_chunk_fwd_segmented_workspace_size(64, 1, 2, 96, 128, 3, 1) == 0
+
+    def seg(**kw):
+        a = dict(q=A, k=A + (1 << 26), v=A + (2 << 26), la=A + (3 << 26), b=A + (4 << 26),
+                 S0=None, y=B, ST=B + (1 << 24), cu=None, N=1, T=64, H=2, dk=128, dv=128, P=3,
+                 ws=B + (1 << 28), wsb=need, it=1, ot=1)
+        a.update(kw)
+        return lib.gdn_chunk_fwd_segmented(a["q"], a["k"], a["v"], a["la"], a["b"], a["S0"],
+                                           a["y"], a["ST"], a["cu"], a["N"], a["T"], a["H"],
+                                           a["dk"], a["dv"], a["P"], a["ws"], a["wsb"], a["it"],
+                                           a["ot"], None)
+
+    assert seg(P=1) == -1
+    assert seg(P=65) == -1
+    assert seg(dk=96) == -2
+    assert seg(ws=None) == -1
+    assert seg(wsb=need - 1) == -1
+    assert seg(ws=B + (1 << 28) + 16) == -3
+    assert seg(ws=B + 4096) == -1           # workspace overlaps y
+    assert seg(ws=A + (2 << 26)) == -1      # workspace overlaps v

@@ -65,6 +65,27 @@ def test_prefill_B1_H32_T65536_sampled():
 
 
 @gpu
+def test_prefill_B1_H32_T65536_segmented_sampled():
+    """The long-context workload through the segment-parallel form (4
+    segments of 16 384 tokens), on two heads the oracle recomputes."""
+    g = _lib()
+    inp = gi.workload_inputs(2)
+    dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    y, S = g.gdn_chunk_fwd_segmented(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
+                                     4, dev["S0"])
+    torch.cuda.synchronize()
+    y, S = y.cpu(), S.cpu()
+    T = 65536
+    for h in (3, 20):
+        q, k, v, la, b = _unit(inp, 0, h, T)
+        yo, So = oracle.gdn_fwd(q, k, v, la, b, inp["S0"][:, h:h + 1], col_blocks=16)
+        ey = rel_l2(y[:, h], yo[:, 0])
+        es = rel_l2(S[0, h], So[0, 0])
+        print("head %d: y %.3e S %.3e" % (h, ey, es), flush=True)
+        assert ey <= TOL and es <= TOL
+
+
+@gpu
 def test_decode_N256_H32_sampled():
     g = _lib()
     steps = 8

@@ -888,3 +888,61 @@ def test_decode_multi_gate_extremes(case):
                                       tm["log_alpha"][:, t], tm["beta"][:, t], S_or)
         assert rel_l2(y[:, t], yo) <= 1e-5
     assert rel_l2(S, S_or) <= 1e-5
+
+
+def _check_segmented(inp, segments, out_dtype=None, tol=None):
+    tol = TOL[inp["dtype"]] if tol is None else tol
+    g = _lib()
+    d = to_dev(inp)
+    y, S = g.gdn_chunk_fwd_segmented(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], segments,
+                                     d["S0"], cu_seqlens=d["cu_seqlens"], out_dtype=out_dtype,
+                                     N=d["N"])
+    torch.cuda.synchronize()
+    yo, So = _oracle_chunk(inp)
+    ey, es = rel_l2(_flat(inp, y), yo), rel_l2(S, So)
+    print("segments=%d rel_l2 y=%.3e S=%.3e" % (segments, ey, es), flush=True)
+    assert np.isfinite(ey) and np.isfinite(es)
+    assert ey <= tol and es <= tol, (ey, es)
+
+
+@gpu
+@pytest.mark.parametrize("segments", [2, 3, 5])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_segmented_equal_length(segments, dtype):
+    # two sequences of 700 tokens; segments are whole 32-token chunks (352 + 348
+    # for two, 256 + 256 + 188 for three)
+    inp = gi.prefill_inputs(2, 3, 700, 128, 128, dtype, s0_std=0.02, seed=40 + segments)
+    _check_segmented(inp, segments, out_dtype=torch.float32)
+
+
+@gpu
+@pytest.mark.parametrize("segments", [2, 4])
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunk_segmented_varlen(segments, d):
+    # sequences shorter than one segment's chunk leave later segments empty
+    lengths = [1, 40, 0, 300, 97, 129]
+    inp = gi.prefill_inputs(0, 2, 0, d, d, "bf16", s0_std=0.02, seed=50 + d, lengths=lengths)
+    _check_segmented(inp, segments, out_dtype=torch.float32)
+
+
+@gpu
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+def test_chunk_segmented_rect_heads(dk, dv):
+    # the transition runs use dv = dk whatever the value width
+    inp = gi.prefill_inputs(1, 2, 400, dk, dv, "f32", s0_std=0.02, seed=dk + 5 * dv)
+    _check_segmented(inp, 3, out_dtype=torch.float32)
+
+
+@gpu
+def test_chunk_segmented_matches_serial_bf16_out():
+    """Same outputs as the serial prefill up to rounding, y in bf16."""
+    g = _lib()
+    inp = gi.prefill_inputs(1, 4, 1000, 128, 128, "bf16", s0_std=0.02, seed=60)
+    d = to_dev(inp)
+    y1, S1 = g.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"], N=1)
+    y2, S2 = g.gdn_chunk_fwd_segmented(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], 4,
+                                       d["S0"], N=1)
+    torch.cuda.synchronize()
+    assert rel_l2(y2.float().cpu(), y1.float().cpu()) <= 2e-3
+    assert rel_l2(S2.cpu(), S1.cpu()) <= 2e-3
+    _check_segmented(inp, 4)
