@@ -1045,19 +1045,28 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
 
 // Sum of the column tiles' partial dq, dk (C x dk rows) and dbeta, dlog
 // alpha, in tile order.
-template <int DK, typename TG>
+template <int DK, int NVT, typename TG>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
-  const int n_vt = a.dv_size / kDVT;
+  constexpr int n_vt = NVT;  // column tiles (dv / 32)
   const size_t part_stride = static_cast<size_t>(a.rows) * a.H;
   const size_t total_k = part_stride * DK;
   const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   // dq, dk: four consecutive elements per thread (16-byte partial loads)
   if (4 * i < total_k) {
+    // every partial is read once: all loads issued before the sums, streamed
+    f32x4 pq[NVT], pk[NVT];
+#pragma unroll
+    for (int t = 0; t < NVT; ++t) {
+      pq[t] = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4 *>(a.ws_part + static_cast<size_t>(t) * total_k + 4 * i));
+      pk[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
+          a.ws_part + static_cast<size_t>(NVT + t) * total_k + 4 * i));
+    }
     f32x4 sq = zero4(), sk = zero4();
-    for (int t = 0; t < n_vt; ++t) {
-      sq += *reinterpret_cast<const f32x4 *>(a.ws_part + static_cast<size_t>(t) * total_k + 4 * i);
-      sk += *reinterpret_cast<const f32x4 *>(a.ws_part + static_cast<size_t>(n_vt + t) * total_k +
-                                             4 * i);
+#pragma unroll
+    for (int t = 0; t < NVT; ++t) {  // tiles in order: deterministic
+      sq += pq[t];
+      sk += pk[t];
     }
     TG *dq = static_cast<TG *>(a.dq) + 4 * i;
     TG *dk = static_cast<TG *>(a.dk) + 4 * i;
@@ -1174,9 +1183,11 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
   if (total > 0) {
     // one thread per four dq/dk elements, which also covers the rows * H
     // gate rows (DK >= 4)
-    hipLaunchKernelGGL((bwd_reduce_kernel<DK, TG>),
-                       dim3(static_cast<unsigned>((total / 4 + 255) / 256)), dim3(256), 0, a.stream,
-                       a);
+    const dim3 grid(static_cast<unsigned>((total / 4 + 255) / 256));
+    if (a.dv_size == 128)
+      hipLaunchKernelGGL((bwd_reduce_kernel<DK, 128 / kDVT, TG>), grid, dim3(256), 0, a.stream, a);
+    else
+      hipLaunchKernelGGL((bwd_reduce_kernel<DK, 64 / kDVT, TG>), grid, dim3(256), 0, a.stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
