@@ -403,8 +403,8 @@ def main():
                          "reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the GDN mixer shards over (sequence, head) with no "
-              "exchange, so --gpus %d is not a configuration this build runs." % args.gpus,
+        print("bench.py measures one GPU only (--gpus %d given): the GDN mixer shards over "
+              "(sequence, head) with no exchange, and a multi-GPU run is not provided." % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
