@@ -60,6 +60,7 @@ constexpr int kC = 32;     // tokens per chunk
 constexpr int kNCT = 2;    // 16-token tiles per chunk
 constexpr int kRing = 6;   // raw-tile ring slots
 constexpr int kPrep = 6;   // prep waves per workgroup (four compute, two load)
+constexpr int kLptMax = 256;  // packed batches up to this many sequences are run longest first
 
 // LDS layout (bytes) for key size DK and NS state waves.
 template <int DK, int NS>
@@ -224,8 +225,10 @@ __device__ __forceinline__ V lds_read16(const char *p) {
 }
 
 // STATES: write every chunk-start state to `states` (the backward pass's
-// workspace) instead of y and S_T
-template <int DK, int NS, typename TIN, typename TOUT, bool STATES>
+// workspace) instead of y and S_T. LPT (packed batches of at most kLptMax
+// sequences): workgroups take the sequences longest first, so the short ones
+// fill in at the end instead of a long one running alone.
+template <int DK, int NS, typename TIN, typename TOUT, bool STATES, bool LPT>
 __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     const TIN *__restrict__ q, const TIN *__restrict__ k, const TIN *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
@@ -252,7 +255,34 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   const int unit = grp * 8 + rem % 8;
   if (unit >= units) return;
   const int h = unit % H;
-  const int n = unit / H;
+  int n = unit / H;
+  if constexpr (LPT) {
+    // dispatch position n takes the sequence of rank n by length (longest
+    // first, ties by index); every workgroup ranks the lengths itself, in the
+    // LDS before it is cleared
+    int *lens = reinterpret_cast<int *>(smem);
+    int *pick = lens + kLptMax;
+    const int N = units / H;
+    for (int j = threadIdx.x; j < N; j += NTHR) {
+      int64_t a = cu_seqlens[j], b = cu_seqlens[j + 1];
+      a = a < 0 ? 0 : (a > T ? T : a);
+      b = b < a ? a : (b > T ? T : b);
+      lens[j] = static_cast<int>(b - a);
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < N; j += NTHR) {
+      const int lj = lens[j];
+      int rank = 0;
+      for (int m = 0; m < N; ++m) {
+        const int lm = lens[m];
+        rank += (lm > lj) || (lm == lj && m < j);
+      }
+      if (rank == n) *pick = j;
+    }
+    __syncthreads();
+    n = *pick;
+    __syncthreads();
+  }
   int64_t bos, len;
   if (cu_seqlens) {
     int64_t a = cu_seqlens[n], b = cu_seqlens[n + 1];
@@ -827,14 +857,14 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   }
 }
 
-template <int DK, int NS, typename TIN, typename TOUT, bool STATES = false>
+template <int DK, int NS, typename TIN, typename TOUT, bool STATES = false, bool LPT = false>
 hipError_t launch_bf16(const ChunkArgs &a) {
   constexpr int DVT = 16 * NS;
   const int n_vt = a.dv / DVT;
   const int64_t units = static_cast<int64_t>(a.N) * a.H;
   const int64_t blocks = (units + 7) / 8 * 8 * n_vt;
   if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, NS, TIN, TOUT, STATES>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, NS, TIN, TOUT, STATES, LPT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * (NS + kPrep)), 0, a.stream, static_cast<const TIN *>(a.q),
                      static_cast<const TIN *>(a.k), static_cast<const TIN *>(a.v),
                      a.log_alpha, a.beta, a.A, a.b_alpha, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.states, a.cu_seqlens,
@@ -846,6 +876,9 @@ hipError_t launch_bf16(const ChunkArgs &a) {
 
 template <typename TIN, typename TOUT>
 static hipError_t launch_16(const ChunkArgs &a) {
+  if (a.cu_seqlens && a.N > 1 && a.N <= kLptMax)
+    return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT, false, true>(a)
+                       : launch_bf16<64, 2, TIN, TOUT, false, true>(a);
   return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT>(a) : launch_bf16<64, 2, TIN, TOUT>(a);
 }
 
