@@ -689,10 +689,12 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     __syncthreads();
 
     // ---- P1 -------------------------------------------------------------
-    // waves 0-2: P = tril(Q K^T o G); 3-6: X = K S; 7-10: Kt dS'; 12-14:
-    // K K^T o G and A, one tile each, the waves with a diagonal tile (14:
-    // rows 0-15, 12: rows 16-31) then solving that diagonal block of
-    // T = (I + A)^-1; 15: gate gradients of the chunk before.
+    // Eleven product tiles: P = tril(Q K^T o G) (0-2), X = K S (3-6) and
+    // Kt dS' (7-10), on waves 0-8, 10 and 14. K K^T o G and A, one tile per
+    // wave: 11 and 13 take a diagonal tile (rows 0-15, 16-31) and then solve
+    // that diagonal block of T = (I + A)^-1, 12 the off-diagonal tile.
+    // 15: gate gradients of the chunk before; 9 idle. Wave w runs on SIMD
+    // w mod 4, so each solving wave shares its SIMD with two tile waves only.
     static_assert(kNW == 16, "the first phase deals its work to sixteen waves");
     auto gram_tile = [&](int t) {
       int rt, ct;
@@ -717,16 +719,16 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     };
     if (wave == 15) {
       if (c < nc - 1) gate_grads(prev_t0, prev_valid, prev_gamC);
-    } else if (wave == 14 || wave == 12) {
+    } else if (wave == 11 || wave == 13) {
       prio(true);
-      gram_tile(wave == 14 ? 0 : 2);
+      gram_tile(wave == 11 ? 0 : 2);
       lds_fence();
-      solve_diag(wave == 14 ? 0 : 16);
+      solve_diag(wave == 11 ? 0 : 16);
       prio(false);
-    } else if (wave == 13) {
+    } else if (wave == 12) {
       gram_tile(1);
-    } else if (wave < 11) {
-      const int t = wave;
+    } else if (wave != 9) {
+      const int t = wave < 9 ? wave : (wave == 10 ? 9 : 10);
       f32x4 acc = zero4();
       if (t < 3) {
         int rt, ct;
