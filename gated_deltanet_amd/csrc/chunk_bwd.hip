@@ -448,12 +448,8 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
         g = gate.log_alpha(g);
         bt = RawGate::beta(bt);
       }
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-        const float o = __shfl_up(g, off, 64);
-        if (lane >= off) g += o;
-      }
-      const float gC = __shfl(g, C - 1, 64);
+      g = scan32(g, lane);
+      const float gC = lane_value(g, C - 1);
       if (lane < C) {
         s_g[lane] = g;
         s_gam[lane] = __expf(g);
@@ -993,15 +989,13 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       db += __shfl_xor(db, 16, 64);
       if (i == 0) s_db[r] = db + s_dbu[0][r] + s_dbu[1][r];
       const float w = i < r ? dPm[o] * Pm[o] + dAm[o] * Am[o] : 0.0f;
-      // inclusive prefix along the row (32 lanes), then shifted by one lane
-      float inc = w;
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-        const float up = __shfl_up(inc, off, 64);
-        if (i >= off) inc += up;
-      }
-      const float up1 = __shfl_up(inc, 1, 64);
-      const float m = i > 0 ? up1 : 0.0f;  // M_ri
+      // inclusive prefix along the row (32 lanes), then shifted by one lane:
+      // M_ri = the previous lane's inclusive sum (0 at i = 0); the first lane
+      // of a DPP row takes the last of the row before
+      const float inc = scan32(w, lane);
+      const float last15 = lane_value(inc, 15), last47 = lane_value(inc, 47);
+      float m = row_shr<1>(inc);
+      if (i == 16) m = lane < 32 ? last15 : last47;
       // column i gets M_ri from every row r >= i; the wave's two rows first
       float col = r >= i ? m : 0.0f;
       col += __shfl_xor(col, 32, 64);

@@ -436,6 +436,28 @@ __device__ __forceinline__ float dpp(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// row_shr:N inside each 16-lane DPP row; lanes without a source read 0
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, true));
+}
+// value of lane l (uniform)
+__device__ __forceinline__ float lane_value(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+// inclusive prefix sums over each 32-lane half of the wave: within 16-lane
+// rows by DPP shifts, then the second row of each half adds the first's last
+__device__ __forceinline__ float scan32(float x, int lane) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  x += row_shr<8>(x);
+  const float r15 = lane_value(x, 15), r47 = lane_value(x, 47);
+  if ((lane & 31) >= 16) x += lane < 32 ? r15 : r47;
+  return x;
+}
+
 // sum over the G consecutive lanes that own one row (G = 8 or 16: a half or a
 // whole 16-lane DPP row): pairs and quads by quad permutes, then quads joined
 // by the half-row and row mirrors; every lane ends with the row's sum
