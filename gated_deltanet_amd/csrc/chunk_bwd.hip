@@ -846,10 +846,8 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
         su += dr[e] * (vv[e] - gr * x[e]);
         sx += dx[e] * x[e];
       }
-      su += __shfl_xor(su, 16, 64);
-      sx += __shfl_xor(sx, 16, 64);
-      su += __shfl_xor(su, 32, 64);
-      sx += __shfl_xor(sx, 32, 64);
+      su = xor32_sum(xor16_sum(su));
+      sx = xor32_sum(xor16_sum(sx));
       if (lg == 0) {
         s_dbu[nt][r] = su;
         s_dgx[nt][r] = sx;
@@ -938,8 +936,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       {
         const f32x4 qv = *reinterpret_cast<const f32x4 *>(Qs + r * LDK + k4);
         float qs = (acc[0] * qv[0] + acc[1] * qv[1]) + (acc[2] * qv[2] + acc[3] * qv[3]);
-        qs += __shfl_xor(qs, 16, 64);
-        qs += __shfl_xor(qs, 32, 64);
+        qs = xor32_sum(xor16_sum(qs));
         if (lg == 0) s_qsdy[kt][r] = qs;
       }
       ld_row(fa, dPGm, LDC, r, 0);
@@ -953,8 +950,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       {
         const f32x4 kv = *reinterpret_cast<const f32x4 *>(Ks + r * LDK + k4);
         float cr = (acc2[0] * kv[0] + acc2[1] * kv[1]) + (acc2[2] * kv[2] + acc2[3] * kv[3]);
-        cr += __shfl_xor(cr, 16, 64);
-        cr += __shfl_xor(cr, 32, 64);
+        cr = xor32_sum(xor16_sum(cr));
         if (lg == 0) s_cr[kt][r] = cr;
       }
       ld_row(fa, dPGt, LDC, r, 0);
@@ -986,7 +982,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       const int o = r * LDC + i;
       // dbeta_r: the beta (V - gamma X) terms plus sum_i dA_ri (K K^T o G)_ri
       float db = row_sum<16>(dAm[o] * KGm[o]);
-      db += __shfl_xor(db, 16, 64);
+      db = xor16_sum(db);
       if (i == 0) s_db[r] = db + s_dbu[0][r] + s_dbu[1][r];
       const float w = i < r ? dPm[o] * Pm[o] + dAm[o] * Am[o] : 0.0f;
       // inclusive prefix along the row (32 lanes), then shifted by one lane:
@@ -998,7 +994,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       if (i == 16) m = lane < 32 ? last15 : last47;
       // column i gets M_ri from every row r >= i; the wave's two rows first
       float col = r >= i ? m : 0.0f;
-      col += __shfl_xor(col, 32, 64);
+      col = xor32_sum(col);
       if (lane < 32) s_colp[wave][i] = col;
     }
     __syncthreads();

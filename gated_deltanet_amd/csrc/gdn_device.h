@@ -471,6 +471,25 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
+// x + (the value of lane ^ 16) and x + (the value of lane ^ 32), by the CDNA4
+// lane-swap instructions (VALU, no LDS round trip): v_permlane16_swap trades
+// the odd 16-lane rows of its first operand with the even rows of its second,
+// v_permlane32_swap the upper half of the first with the lower half of the
+// second; with two copies of x the pair then holds both values of every
+// lane pair. Written as inline asm since the compiler's builtin returns its
+// second result wrongly; the s_nop gives the two wait states a VALU write
+// needs before these instructions read it.
+__device__ __forceinline__ float xor16_sum(float x) {
+  float a = x, b = x;
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  float a = x, b = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+
 // Gates from raw per-head pre-activations (page "NLP——技术报告解读-
 // Qwen3.8-Flash-Next", section "GDN 参数化细节"): the decay gate is
 // alpha = exp(-exp(A) softplus(a + b_alpha)) and the write gate is
