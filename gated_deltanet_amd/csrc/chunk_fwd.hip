@@ -493,6 +493,11 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   auto inverse = [&](int c) {
     const float *amt = amt_of(c);
     char *pb = procb + (c & 1) * L::PROC;
+    // A_10 in the layout of an MFMA A operand, read ahead of the solve:
+    // slot j of lane (lg, lc) is A[16 + lc][4 lg + j] (A is stored transposed)
+    float a10[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a10[j] = amt[(4 * lg + j) * L::LDA + 16 + lc];
     // Diagonal 16x16 blocks by forward substitution. Each 16-lane row works
     // on one block (rows 2 and 3 repeat rows 0 and 1); lane lc holds column lc
     // of T and column lc of A, so A is read from LDS once (unit_lower_solve16).
@@ -516,38 +521,35 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       }
     }
     wait_lds();
-    // off-diagonal block: T_10 = -T_11 (A_10 T_00)
+    // off-diagonal block: T_10 = -T_11 (A_10 T_00). The second product is
+    // formed with its operands swapped, which yields (T_11 M)^T: lane (lg, lc)
+    // then holds T_10[lc][4 lg + i], the row layout T is stored in, so T_10
+    // goes straight from the matrix core into the T fragments.
     {
       f16x8 a, bb;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        a[j] = (_Float16)amt[(4 * lg + j) * L::LDA + 16 + lc];  // A[16 + lc][4 lg + j]
-        bb[j] = (_Float16)tmp[(4 * lg + j) * L::LDT + lc];        // T_00[4 lg + j][lc]
+        a[j] = (_Float16)a10[j];
+        bb[j] = (_Float16)tmp[(4 * lg + j) * L::LDT + lc];  // T_00[4 lg + j][lc]
         a[4 + j] = (_Float16)0.0f;
         bb[4 + j] = (_Float16)0.0f;
       }
-      const f32x4 M = mma_f16(a, bb, zero4());
-      f16x8 t11, mb;
+      const f32x4 t00r = *reinterpret_cast<const f32x4 *>(tmp + lc * L::LDT + 4 * lg);
       const f32x4 t11r = *reinterpret_cast<const f32x4 *>(tmp + (16 + lc) * L::LDT + 16 + 4 * lg);
+      const f32x4 M = mma_f16(a, bb, zero4());  // M[4 lg + i][lc] = (A_10 T_00)
+      f16x8 mb, t11;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        t11[j] = (_Float16)t11r[j];  // T_11[lc][4 lg + j]
-        mb[j] = (_Float16)M[j];
-        t11[4 + j] = (_Float16)0.0f;
+        mb[j] = (_Float16)M[j];      // M^T as the A operand
+        t11[j] = (_Float16)t11r[j];  // T_11^T as the B operand: T_11[lc][4 lg + j]
         mb[4 + j] = (_Float16)0.0f;
+        t11[4 + j] = (_Float16)0.0f;
       }
-      const f32x4 D = mma_f16(t11, mb, zero4());
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tmp[(16 + 4 * lg + i) * L::LDT + lc] = -D[i];
-    }
-    wait_lds();
-    // T in fragment-linear fp16: row 16 mt + lc, slot j <-> token 16(j>>2) + 4 lg + (j&3)
-#pragma unroll
-    for (int mt = 0; mt < kNCT; ++mt) {
-      const float *trow = tmp + (16 * mt + lc) * L::LDT + 4 * lg;
-      const f32x4 lo = *reinterpret_cast<const f32x4 *>(trow);
-      const f32x4 hi = *reinterpret_cast<const f32x4 *>(trow + 16);
-      *reinterpret_cast<f16x8 *>(pb + L::T_OFF + mt * 1024 + 16 * lane) = pack_f16(lo, hi);
+      const f32x4 D = mma_f16(mb, t11, zero4());
+      // T in fragment-linear fp16: row 16 mt + lc, slot j <-> token
+      // 16 (j >> 2) + 4 lg + (j & 3); the upper right block is zero
+      *reinterpret_cast<f16x8 *>(pb + L::T_OFF + 16 * lane) = pack_f16(t00r, zero4());
+      *reinterpret_cast<f16x8 *>(pb + L::T_OFF + 1024 + 16 * lane) = pack_f16(-D, t11r);
     }
   };
 
@@ -575,6 +577,17 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       }
     const bool fast = __builtin_amdgcn_readfirstlane(
                           __builtin_bit_cast(int, gt[L::GB_MISC / 4])) != 0;
+    // decay factors of both forms, read with the operands: reads issued
+    // after this wave's LDS writes below would wait behind them
+    float ar[kNCT], gr[kNCT];
+    f32x4 cb[kNCT], gc[kNCT];
+#pragma unroll
+    for (int t = 0; t < kNCT; ++t) {
+      ar[t] = gt[L::GB_RA / 4 + 16 * t + lc];
+      cb[t] = *reinterpret_cast<const f32x4 *>(gt + L::GB_CB / 4 + 16 * t + 4 * lg);
+      gr[t] = gt[L::GB_G2 / 4 + 16 * t + lc];
+      gc[t] = *reinterpret_cast<const f32x4 *>(gt + L::GB_G2 / 4 + 16 * t + 4 * lg);
+    }
     // K Q^T: element i of lane (lg, lc) in tile (ct, rt) is P[16 rt + lc][16 ct + 4 lg + i],
     // i.e. slot i (ct = 0) or 4 + i (ct = 1) of P's operand fragment for row tile rt
     f32x4 pk[3];  // (ct, rt) = (0, 0), (0, 1), (1, 1)
@@ -608,20 +621,16 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         const int ct = t == 2 ? 1 : 0, rt = t == 0 ? 0 : 1;
-        const float ar = gt[L::GB_RA / 4 + 16 * rt + lc];
-        const f32x4 cb = *reinterpret_cast<const f32x4 *>(gt + L::GB_CB / 4 + 16 * ct + 4 * lg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[t][i] = ar * cb[i] * pk[t][i];
+        for (int i = 0; i < 4; ++i) pv[t][i] = ar[rt] * cb[ct][i] * pk[t][i];
       }
     } else {
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         const int ct = t == 2 ? 1 : 0, rt = t == 0 ? 0 : 1;
-        const float gr = gt[L::GB_G2 / 4 + 16 * rt + lc];
-        const f32x4 gc = *reinterpret_cast<const f32x4 *>(gt + L::GB_G2 / 4 + 16 * ct + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          pv[t][i] = __builtin_amdgcn_exp2f(fminf(gr - gc[i], 0.0f)) * pk[t][i];
+          pv[t][i] = __builtin_amdgcn_exp2f(fminf(gr[rt] - gc[ct][i], 0.0f)) * pk[t][i];
       }
     }
     // causal mask on the diagonal tiles: column 4 lg + i <= row lc
