@@ -16,16 +16,15 @@
 // the state) and walks the sequence's chunks in order. Its NS "state" waves
 // keep their 16-column slabs of the fp32 state in registers for the whole
 // sequence and run the serial part: X = K S (bf16 MFMA, A operands straight
-// from the raw K tile), Q S (fp16 MFMA on queries converted to fp16 in
-// place), R, E = T R, Y = gamma QS + P E and the state update (fp16 MFMA).
+// from the raw K tile), Q S (fp16 MFMA on queries widened to fp16 in their
+// registers), R, E = T R, Y = gamma QS + P E and the state update (fp16 MFMA).
 // Four "prep" waves produce everything that does not depend on the state,
 // pipelined ahead of the state waves:
 //   * gram    (two chunks ahead): the Gram tiles K K^T on MFMA and A;
 //   * inverse (one chunk ahead): T = (I + A)^{-1}: 16x16 diagonal blocks by
 //             forward substitution in fp32, the off-diagonal block on MFMA;
 //   * qk      (one chunk ahead): P = tril(Q K^T o G) computed as K Q^T so
-//             that the MFMA result already sits in P's operand layout, and Q
-//             converted to fp16;
+//             that the MFMA result already sits in P's operand layout;
 //   * kt      (one chunk ahead): half of the Kt^T tiles, transposed on the
 //             matrix cores with a 0/1 selector operand (exact) and scaled
 //             per token.
@@ -196,8 +195,8 @@ __device__ __forceinline__ void store_y(float v, __amdgpu_buffer_rsrc_t r, uint3
 
 // Operations on the raw 16-bit input tiles (K, Q, V) for each input type.
 // bf16 inputs keep bf16 operands for the key-side products (exact inputs;
-// the state operand of K S is rounded to bf16) and have Q converted to fp16
-// by a prep wave for Q S; fp16 inputs use fp16 operands throughout.
+// the state operand of K S is rounded to bf16) and have Q widened to fp16 in
+// the state waves' registers for Q S; fp16 inputs use fp16 operands throughout.
 template <typename TIN>
 struct KOps;
 template <>
@@ -562,9 +561,9 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     return s_;
   };
 
-  // ---- qk wave: P = tril(Q K^T o G), Q -> fp16 -------------------------------
+  // ---- qk wave: P = tril(Q K^T o G) -----------------------------------------
   auto qkp = [&](int c) {
-    char *slot = ring + (c % kRing) * L::SLOT;
+    const char *slot = ring + (c % kRing) * L::SLOT;
     char *pb = procb + (c & 1) * L::PROC;
     const float *gt = gate_of(c);
     kvec kf[kNCT][NKB], qf[kNCT][NKB];
@@ -598,23 +597,6 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       pk[0] = KO::mma(kf[0][kb], qf[0][kb], pk[0]);
       pk[1] = KO::mma(kf[0][kb], qf[1][kb], pk[1]);
       pk[2] = KO::mma(kf[1][kb], qf[1][kb], pk[2]);
-    }
-    // Q in fp16 for the state waves' Q S: D_u = Sel_u x Q^T puts keys
-    // 8 lg + 4u + i of token lc in lane (lg, lc), i.e. the A-operand slots;
-    // exact, then rounded from bf16 values that fp16 represents exactly.
-    // Written back over the raw Q of this slot, which no other wave reads
-    // during this chunk step.
-    if constexpr (KO::kConvertQ) {
-      const kvec sel[2] = {selector(0), selector(1)};
-#pragma unroll
-      for (int rt = 0; rt < kNCT; ++rt)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const f32x4 d0 = KO::mma(sel[0], qf[rt][kb], zero4());
-          const f32x4 d1 = KO::mma(sel[1], qf[rt][kb], zero4());
-          *reinterpret_cast<f16x8 *>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane) =
-              pack_f16(d0, d1);
-        }
     }
     f32x4 pv[3];
     if (fast) {
@@ -722,11 +704,16 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     const float gC = gt[L::GB_GAM / 4 + kC - 1];
 #pragma unroll
     for (int t = 0; t < NST; ++t) ktf[t] = lds_read16<f16x8>(pb + L::KT_OFF + t * 1024 + 16 * lane);
+    kvec qraw[kNCT][NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int rt = 0; rt < kNCT; ++rt)
-        qf[rt][kb] = lds_read16<f16x8>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+      for (int rt = 0; rt < kNCT; ++rt) {
+        if constexpr (KO::kConvertQ)
+          qraw[rt][kb] = lds_read16<kvec>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+        else
+          qf[rt][kb] = lds_read16<f16x8>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+      }
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt) pf[rt] = lds_read16<f16x8>(pb + L::P_OFF + rt * 1024 + 16 * lane);
 
@@ -755,6 +742,20 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
         Xa[rt] = KO::mma(kf[rt][kb], sb[kb], Xa[rt]);
         Xb[rt] = KO::mma(kf[rt][kb + 1], sb[kb + 1], Xb[rt]);
       }
+    // Q in fp16 for Q S (bf16 inputs): D_u = Sel_u x Q^T puts keys
+    // 8 lg + 4u + i of token lc in lane (lg, lc), the A-operand slots the raw
+    // tile already has, so the matrix cores only widen it (exact), and the
+    // rounding to fp16 is exact for all but tiny values. Off the X -> R -> E
+    // chain, so these products fill issue gaps of the state waves.
+    if constexpr (KO::kConvertQ) {
+      const kvec sel[2] = {selector(0), selector(1)};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < kNCT; ++rt)
+          qf[rt][kb] = pack_f16(KO::mma(sel[0], qraw[rt][kb], zero4()),
+                                KO::mma(sel[1], qraw[rt][kb], zero4()));
+    }
     f32x4 QS[kNCT];
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt) QS[rt] = zero4();
