@@ -369,12 +369,14 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     char *slot = ring + (c % kRing) * L::SLOT;
     const int64_t r0 = row0_of(c);
     const uint32_t rows = static_cast<uint32_t>(rows_of(c));
-    const i32x4 rq = buffer_rsrc(q + r0 * hdk, rows * hdk * 2);
+    if constexpr (!STATES) {  // the states-only variant never reads Q
+      const i32x4 rq = buffer_rsrc(q + r0 * hdk, rows * hdk * 2);
 #pragma unroll
-    for (int rt = 0; rt < kNCT; ++rt)
+      for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        dma16(rq, kq_lane + static_cast<uint32_t>(16 * rt * hdk * 2 + 64 * kb), lds_addr(slot + L::Q_OFF + (rt * NKB + kb) * 1024));
+        for (int kb = 0; kb < NKB; ++kb)
+          dma16(rq, kq_lane + static_cast<uint32_t>(16 * rt * hdk * 2 + 64 * kb), lds_addr(slot + L::Q_OFF + (rt * NKB + kb) * 1024));
+    }
     const i32x4 rv = buffer_rsrc(v + r0 * hdv, rows * hdv * 2);
 #pragma unroll
     for (int p = 0; p < L::NV; ++p) dma16(rv, v_lane(p), lds_addr(slot + L::V_OFF + p * 1024));
@@ -806,7 +808,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   // (nc + 3 in all).
   constexpr int kLdK = kRing - 4;
   constexpr int kLdQ = kRing - 3;
-  static_assert((kLdK + 1) * L::LOADS_GRAM < 64 && (kLdQ + 1) * L::LOADS_QK < 64, "vmcnt range");
+  constexpr int kLoadsQV = STATES ? L::NV : L::LOADS_QK;  // loads per chunk of the Q/V wave
+  static_assert((kLdK + 1) * L::LOADS_GRAM < 64 && (kLdQ + 1) * kLoadsQV < 64, "vmcnt range");
   auto step_barrier = [&]() { wg_barrier(); };
   auto in_range = [&](int c) { return c >= 0 && c < nc; };
   if (nc > 0) {
@@ -837,7 +840,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       for (int it = -3; it < nc; ++it) {
         issue_qk(it + 2 + kLdQ);
         if (in_range(it + 1)) ktt(it + 1, 1);
-        wait_vmcnt<kLdQ * L::LOADS_QK>();
+        wait_vmcnt<kLdQ * kLoadsQV>();
         step_barrier();
       }
       wait_vmcnt<0>();
@@ -847,7 +850,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
         if (is_gram) {
           if (in_range(it + 2)) gram(it + 2);
         } else if (is_qk) {
-          if (in_range(it + 1)) qkp(it + 1);
+          if (!STATES && in_range(it + 1)) qkp(it + 1);  // P only feeds y
         } else if (is_inv) {
           if (in_range(it + 1)) inverse(it + 1);
         } else {
