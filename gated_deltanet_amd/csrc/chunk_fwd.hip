@@ -578,8 +578,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       }
     const bool fast = __builtin_amdgcn_readfirstlane(
                           __builtin_bit_cast(int, gt[L::GB_MISC / 4])) != 0;
-    // decay factors of both forms, read with the operands: reads issued
-    // after this wave's LDS writes below would wait behind them
+    // decay factors of both forms, read up front with the operands so that
+    // their latency overlaps the products
     float ar[kNCT], gr[kNCT];
     f32x4 cb[kNCT], gc[kNCT];
 #pragma unroll
