@@ -32,13 +32,16 @@ sys.path.insert(0, ROOT)
 import gdn_inputs as gi  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
-CHUNK = 32  # tokens per chunk in the prefill kernel
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak, AMD's published figure
+ALG_CHUNK = 64  # chunk size the algorithmic flop count is defined at, whatever the kernel uses
+KERNEL_CHUNK = 32  # tokens per chunk inside the 16-bit prefill kernel
 
 
-def prefill_flops_per_token_head(dk, dv, C=CHUNK):
+def prefill_flops_per_token_head(dk, dv, C=ALG_CHUNK):
     """Algorithmic work of chunked prefill per token per head (triangles
-    halved): 6 dk dv + C (3 dk + 2 dv) + C^2 / 3."""
+    halved): 6 dk dv + C (3 dk + 2 dv) + C^2 / 3, counted at C = 64 so the
+    figure does not depend on the kernel's own chunk size (140 629 at
+    dk = dv = 128)."""
     return 6 * dk * dv + C * (3 * dk + 2 * dv) + C * C / 3.0
 
 
@@ -68,10 +71,49 @@ def measured_traffic(key, source):
     return rec["bytes"]
 
 
+def measured_mfma(key, source):
+    """MFMA counters per dispatch from rocprofv3 (profiles/): busy fraction
+    and issued flops, or None when the kernel source changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "mfma_per_dispatch.json")))[key]
+        src = open(os.path.join(ROOT, "gated_deltanet_amd", "csrc", source), "rb").read()
+    except (OSError, KeyError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != rec.get("source_sha256_16"):
+        return None
+    return dict(mfma_busy=rec["mfma_busy"], issued_flops=rec["issued_flops"])
+
+
 def rel_l2(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def row_errors(got, ref, block=32, floor_frac=0.05):
+    """Worst per-row relative error over the rows of [rows, d] (each row's
+    error over max(its norm, floor_frac x the RMS row norm), so near-zero rows
+    do not divide by ~0) and worst rel-L2 over blocks of `block` rows."""
+    got = np.asarray(got, dtype=np.float64).reshape(len(got), -1)
+    ref = np.asarray(ref, dtype=np.float64).reshape(len(ref), -1)
+    err = np.linalg.norm(got - ref, axis=1)
+    nrm = np.linalg.norm(ref, axis=1)
+    floor = floor_frac * float(np.sqrt(np.mean(nrm ** 2))) if len(nrm) else 0.0
+    row = float(np.max(err / np.maximum(nrm, max(floor, 1e-300)))) if len(nrm) else 0.0
+    worst = 0.0
+    for s0 in range(0, len(ref), block):
+        worst = max(worst, rel_l2(got[s0:s0 + block], ref[s0:s0 + block]))
+    return row, worst
+
+
+def _roofline(kernel, nbytes, flops, ms):
+    """HBM roofline record of one call from its algorithmic bytes and flops."""
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    return dict(kernel=kernel, bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=gbs / HBM_PEAK_GBS, alg_bytes_per_launch=nbytes,
+                alg_flops_per_launch=flops, mfma_tflops=tf, mfma_frac_bf16_peak=tf / BF16_PEAK_TFLOPS)
 
 
 WARM_SECONDS = 0.5
@@ -208,7 +250,16 @@ def bench_decode(g, n_steps=128, reps=2):
     us_step = ms * 1e3 / (reps * n_steps)
     bytes_step = decode_bytes_per_step(N, H, dk, dv)
     gbs = bytes_step / (us_step * 1e-6) / 1e9
-    return dict(workload=w.name, us_per_step=us_step, GBps=gbs, frac_hbm=gbs / HBM_PEAK_GBS,
+    # one more pass from the initial states, whose outputs the oracle checks
+    # on sampled (sequence, head) units over all n_steps steps
+    S.copy_(inp["S0"].to(dev))
+    one_pass()
+    torch.cuda.synchronize()
+    units = [(0, 0), (255, 31), (17, 5), (128, 16), (200, 2)]
+    check = dict(inp=inp, units=units, y={u: y[:, u[0], u[1]].float().cpu() for u in units},
+                 S={u: S[u[0], u[1]].cpu() for u in units})
+    return dict(_check=check, workload=w.name, us_per_step=us_step, GBps=gbs,
+                frac_hbm=gbs / HBM_PEAK_GBS,
                 tokens_per_s=N / (us_step * 1e-6), bytes_per_step=bytes_step, steps=n_steps,
                 roofline=dict(kernel="decode_kernel<128,128,bf16,bf16,unfused> (n_tok = 1)", bound="hbm",
                               achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
@@ -285,7 +336,8 @@ def bench_longctx(g, steps=3, warmup=1):
     nbytes = prefill_bytes(tokens, w.H, w.dk, w.dv, w.B, s0=True)
     return dict(workload=w.name, ms_per_call=ms, tokens_per_s=tokens / (ms * 1e-3),
                 pct_bf16_mfma_peak=100.0 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                hbm_GBps=nbytes / (ms * 1e-3) / 1e9)
+                hbm_GBps=nbytes / (ms * 1e-3) / 1e9,
+                roofline=_roofline("chunk_fwd_bf16_kernel<128,2,bf16,bf16>", nbytes, flops, ms))
 
 
 def bench_longctx_segmented(g, segment_counts=(2, 3, 4), steps=3, warmup=1):
@@ -337,11 +389,25 @@ def bench_varlen_frontend(g, steps=3, warmup=1):
 
     ms = time_launches(step, steps, warmup, stream) / steps
     flops = rows * w.H * prefill_flops_per_token_head(w.dk, w.dv)
+    # raw q, k, v and z read, o written, gates read, S0 read and S_T written
     fused_bytes = rows * w.H * (3 * 128 * 2 + 128 * 2 + 128 * 2 + 8) + 2 * w.n_seqs * w.H * 128 * 128 * 4
-    return dict(workload=w.name, tokens=rows, ms_per_call=ms, tokens_per_s=rows / (ms * 1e-3),
+    # outputs of the last timed call on sampled units: the longest and the
+    # shortest sequence and four more, one head each, for the oracle chain
+    cu = f["cu_seqlens"]
+    lens = (cu[1:] - cu[:-1]).tolist()
+    order = sorted(range(len(lens)), key=lambda n: lens[n])
+    picks = [order[-1], order[0], order[len(order) // 2], 7, 31, 50]
+    units = [(n, (5 * i + 3) % w.H) for i, n in enumerate(picks)]
+    torch.cuda.synchronize()
+    check = dict(f=f, units=units,
+                 o={u: o[int(cu[u[0]]):int(cu[u[0] + 1]), u[1]].float().cpu() for u in units},
+                 S={u: S_T[u[0], u[1]].cpu() for u in units})
+    return dict(_check=check, workload=w.name, tokens=rows, ms_per_call=ms,
+                tokens_per_s=rows / (ms * 1e-3),
                 pct_bf16_mfma_peak=100.0 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                 hbm_GBps_of_fused_bytes=fused_bytes / (ms * 1e-3) / 1e9,
-                entry_point="gdn_chunk_fwd_fused (front end + prefill + gate kernels)")
+                roofline=_roofline("gdn_chunk_fwd_fused (whole call)", fused_bytes, flops, ms),
+                entry_point="gdn_chunk_fwd_fused")
 
 
 def cpu_baseline(pf, max_seconds=30.0, min_seconds=10.0):
@@ -382,6 +448,57 @@ def cpu_baseline(pf, max_seconds=30.0, min_seconds=10.0):
                sample="%s (all %d heads, %d tokens each), fp64 token recurrence, %.1f s"
                       % (what, H, T, spent))
     return rec, outs
+
+
+def decode_parity(chk):
+    """All decode steps of sampled (sequence, head) units against the oracle's
+    decode step applied the same number of times from the same state."""
+    import oracle
+    inp = chk["inp"]
+    ey, es, er = [], [], []
+    steps = inp["q"].shape[0]
+    for n, h in chk["units"]:
+        S = inp["S0"][n:n + 1, h:h + 1].double().numpy()
+        yo = []
+        for t in range(steps):
+            args = [inp[key][t, n:n + 1, h:h + 1] for key in ("q", "k", "v", "log_alpha", "beta")]
+            yt, S = oracle.decode_step(*args, S)
+            yo.append(yt[0, 0])
+        yo = np.stack(yo)
+        got = chk["y"][(n, h)].numpy()
+        ey.append(rel_l2(got, yo))
+        er.append(row_errors(got, yo)[0])
+        es.append(rel_l2(chk["S"][(n, h)].numpy(), S[0, 0]))
+    return dict(units=len(chk["units"]), steps=steps, y_rel_l2=max(ey), S_rel_l2=max(es),
+                y_row_rel_max=max(er))
+
+
+def varlen_parity(chk):
+    """Sampled (sequence, head) units of the fused varlen call against the
+    oracle chain: front end, token recurrence from S0, output gate."""
+    import oracle
+    f = chk["f"]
+    cu, w, H, d = f["cu_seqlens"], f["conv_w"], f["H"], f["dk"]
+    eo, es, er, eb = [], [], [], []
+    for n, h in chk["units"]:
+        s0, e0 = int(cu[n]), int(cu[n + 1])
+        sl = lambda x: x[s0:e0, h:h + 1]
+        wsl = lambda i: w[i].reshape(H, d, -1)[h]
+        q = oracle.frontend(sl(f["q_raw"]), wsl(0), l2=True, eps=1e-6)
+        k = oracle.frontend(sl(f["k_raw"]), wsl(1), l2=True, eps=1e-6)
+        v = oracle.frontend(sl(f["v_raw"]), wsl(2), l2=False)
+        y, S = oracle.gdn_fwd(q, k, v, sl(f["log_alpha"]), sl(f["beta"]),
+                              f["S0"][n:n + 1, h:h + 1], col_blocks=8)
+        oo = oracle.output_gate(y, sl(f["z"]), f["norm_w"], eps=1e-6)[:, 0]
+        got = chk["o"][(n, h)].numpy()
+        eo.append(rel_l2(got, oo))
+        r, b = row_errors(got, oo)
+        er.append(r)
+        eb.append(b)
+        es.append(rel_l2(chk["S"][(n, h)].numpy(), S[0, 0]))
+    lens = [int(cu[n + 1] - cu[n]) for n, _ in chk["units"]]
+    return dict(units=len(chk["units"]), lengths=lens, o_rel_l2=max(eo), S_T_rel_l2=max(es),
+                o_row_rel_max=max(er), o_chunk_rel_l2_max=max(eb))
 
 
 def main():
@@ -437,18 +554,22 @@ def main():
     achieved_gbs = nbytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic("chunk_fwd_bf16_kernel_B4_H16_T4096_d128", "chunk_fwd.hip")
+    mfma = measured_mfma("chunk_fwd_bf16_kernel_B4_H16_T4096_d128", "chunk_fwd.hip")
     roofline = dict(kernel="chunk_fwd_bf16_kernel<128,2,bf16,bf16>", bound="hbm",
                     achieved=achieved_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=achieved_gbs / HBM_PEAK_GBS, traffic=traffic,
                     alg_bytes_per_launch=nbytes, alg_flops_per_launch=flops,
-                    mfma_tflops=tflops, mfma_frac_bf16_peak=tflops / BF16_PEAK_TFLOPS)
+                    mfma_tflops=tflops, mfma_frac_bf16_peak=tflops / BF16_PEAK_TFLOPS,
+                    mfma_busy=None if mfma is None else mfma["mfma_busy"],
+                    mfma_issued_flops_per_launch=None if mfma is None else mfma["issued_flops"])
 
     rec = dict(metric="GDN prefill tokens/s (% bf16 MFMA peak); decode state GB/s (% HBM peak)",
                value=value, unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
                ms_per_step=ms, higher_is_better=True, scaling="weak", vs_baseline=None,
                dtype="bf16", data="synthetic",
                config=dict(workload=gi.WORKLOADS[1].name, B=N, H=H, T=pf["T"], dk=dk, dv=dv,
-                           chunk=CHUNK, q_k_v="bf16", y="bf16", state="fp32", S0="zeros"),
+                           flop_count_chunk=ALG_CHUNK, kernel_chunk=KERNEL_CHUNK, q_k_v="bf16",
+                           y="bf16", state="fp32", S0="zeros"),
                pct_bf16_mfma_peak=100.0 * tflops / BF16_PEAK_TFLOPS,
                roofline=roofline)
 
@@ -481,17 +602,31 @@ def main():
               flush=True)
         rec["varlen_frontend"] = bench_varlen_frontend(g)
 
+    checks = {key: rec[key].pop("_check") for key in ("decode", "varlen_frontend")
+              if key in rec and "_check" in rec[key]}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cb, outs = cpu_baseline(pf)
         rec["cpu_baseline"] = cb
-        ey, es = [], []
+        ey, es, er, eb = [], [], [], []
         T = pf["T"]
         for n, yo, So in outs:
-            ey.append(rel_l2(pf["y"][n * T:(n + 1) * T].numpy(), yo))
+            got = pf["y"][n * T:(n + 1) * T].numpy()
+            ey.append(rel_l2(got, yo))
             es.append(rel_l2(pf["S_T"][n].numpy(), So[0]))
-        rec["parity"] = dict(y_rel_l2=max(ey), S_T_rel_l2=max(es), sequences=len(outs),
-                             tolerance=2e-3)
+            for h in range(H):
+                r, b = row_errors(got[:, h], yo[:, h])
+                er.append(r)
+                eb.append(b)
+        rec["parity"] = dict(y_rel_l2=max(ey), S_T_rel_l2=max(es), y_row_rel_max=max(er),
+                             y_chunk_rel_l2_max=max(eb), sequences=len(outs), tolerance=2e-3,
+                             row_tolerance=1e-2)
+        print("[bench] parity of the timed decode and varlen workloads", file=sys.stderr,
+              flush=True)
+        if "decode" in checks:
+            rec["parity"]["decode"] = decode_parity(checks["decode"])
+        if "varlen_frontend" in checks:
+            rec["parity"]["varlen_frontend"] = varlen_parity(checks["varlen_frontend"])
     print(json.dumps(rec))
 
 

@@ -135,27 +135,62 @@ def _stream(dev):
 
 
 def _need(t, name, dtype=None):
-    if not t.is_cuda:
-        raise GdnError("%s must be a device tensor" % name)
+    """Layout and dtype of a tensor argument. The device is checked last, by
+    _devices, after every shape: a short or mis-shaped tensor is rejected
+    here, before the library sees a pointer it would read or write past."""
+    if not isinstance(t, torch.Tensor):
+        raise GdnError("%s must be a tensor" % name)
     if not t.is_contiguous():
         raise GdnError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:
         raise GdnError("%s must be %s" % (name, dtype))
 
 
+def _shape(t, name, shape):
+    """t (if given) has exactly this shape."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise GdnError("%s must have shape %s, not %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _devices(*named):
+    """Every given (tensor, name) lives on one GPU device; returns it."""
+    dev = None
+    for t, name in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise GdnError("%s must be a device tensor" % name)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise GdnError("%s is on %s, the other arguments on %s" % (name, t.device, dev))
+    return dev
+
+
+def _rows_layout(q, name="q"):
+    """(rows, H, d) of a token-major tensor [rows, H, d] or [N, T, H, d]."""
+    if q.dim() not in (3, 4):
+        raise GdnError("%s must be [rows, H, d] or [N, T, H, d]" % name)
+    H, d = q.shape[-2], q.shape[-1]
+    if H <= 0 or d <= 0:
+        raise GdnError("%s has an empty head dimension" % name)
+    return q.numel() // (H * d), H, d
+
+
 def _prefill_shape(q, v, S0, cu_seqlens, N):
     """(N, T, H, dk, dv) of a prefill call; T is the per-sequence length, or
     the total row count when cu_seqlens is given."""
-    dk, dv = q.shape[-1], v.shape[-1]
-    H = q.shape[-2]
+    rows, H, dk = _rows_layout(q)
+    dv = v.shape[-1]
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise GdnError("cu_seqlens must be [N + 1]")
         N = cu_seqlens.numel() - 1
-        T = q.numel() // (H * dk)  # total rows
+        T = rows
     elif q.dim() == 4:
         N, T = q.shape[0], q.shape[1]
     else:
-        rows = q.shape[0]
         if N is None:
             N = S0.shape[0] if S0 is not None else 1
         if N <= 0 or rows % N:
@@ -163,18 +198,35 @@ def _prefill_shape(q, v, S0, cu_seqlens, N):
         T = rows // N
     if S0 is not None:
         _need(S0, "S0", torch.float32)
-        if tuple(S0.shape) != (N, H, dk, dv):
-            raise GdnError("S0 must be [N, H, dk, dv] = %s" % ((N, H, dk, dv),))
+        _shape(S0, "S0", (N, H, dk, dv))
     return N, T, H, dk, dv
 
 
 def _prefill_checked(q, k, v, g1, g2, names):
+    """dtypes and shapes of the token inputs of a prefill call: k like q,
+    v like q with its own last size, the two per-token gates [.., H]."""
     in_dtype = q.dtype
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, in_dtype)
     _need(g1, names[0], torch.float32)
     _need(g2, names[1], torch.float32)
+    _rows_layout(q)
+    _shape(k, "k", q.shape)
+    if v.dim() != q.dim() or tuple(v.shape[:-1]) != tuple(q.shape[:-1]):
+        raise GdnError("v must be %s + [dv], not %s" % (list(q.shape[:-1]), list(v.shape)))
+    _shape(g1, names[0], q.shape[:-1])
+    _shape(g2, names[1], q.shape[:-1])
     return in_dtype
+
+
+def _outputs(y, y_shape, y_dtype, S_T, s_shape):
+    """Caller-supplied outputs have the shapes and dtypes the call writes."""
+    if y is not None:
+        _need(y, "y", y_dtype)
+        _shape(y, "y", y_shape)
+    if S_T is not None:
+        _need(S_T, "S_T", torch.float32)
+        _shape(S_T, "S_T", s_shape)
 
 
 def gdn_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, out_dtype=None,
@@ -189,6 +241,10 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, out_dtype=
     in_dtype = _prefill_checked(q, k, v, log_alpha, beta, ("log_alpha", "beta"))
     out_dtype = in_dtype if out_dtype is None else out_dtype
     N, T, H, dk, dv = _prefill_shape(q, v, S0, cu_seqlens, N)
+    _dt(out_dtype)
+    _outputs(y, v.shape, out_dtype, S_T, (N, H, dk, dv))
+    _devices((q, "q"), (k, "k"), (v, "v"), (log_alpha, "log_alpha"), (beta, "beta"), (S0, "S0"),
+             (cu_seqlens, "cu_seqlens"), (y, "y"), (S_T, "S_T"))
     if y is None:
         y = torch.empty(v.shape, dtype=out_dtype, device=v.device)
     if S_T is None and want_state:
@@ -218,6 +274,12 @@ def gdn_chunk_fwd_segmented(q, k, v, log_alpha, beta, segments, S0=None, cu_seql
     out_dtype = in_dtype if out_dtype is None else out_dtype
     N, T, H, dk, dv = _prefill_shape(q, v, S0, cu_seqlens, N)
     rows = T if cu_seqlens is not None else N * T
+    _dt(out_dtype)
+    _outputs(y, v.shape, out_dtype, S_T, (N, H, dk, dv))
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _devices((q, "q"), (k, "k"), (v, "v"), (log_alpha, "log_alpha"), (beta, "beta"), (S0, "S0"),
+             (cu_seqlens, "cu_seqlens"), (y, "y"), (S_T, "S_T"), (workspace, "workspace"))
     if y is None:
         y = torch.empty(v.shape, dtype=out_dtype, device=v.device)
     if S_T is None and want_state:
@@ -228,7 +290,8 @@ def gdn_chunk_fwd_segmented(q, k, v, log_alpha, beta, segments, S0=None, cu_seql
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=v.device)
     rc = lib.gdn_chunk_fwd_segmented(_p(q), _p(k), _p(v), _p(log_alpha), _p(beta), _p(S0), _p(y),
                                      _p(S_T), _p(cu_seqlens), N, T, H, dk, dv, segments,
-                                     _p(workspace), workspace.numel(), _dt(in_dtype),
+                                     _p(workspace), workspace.numel() * workspace.element_size(),
+                                     _dt(in_dtype),
                                      _dt(out_dtype), _stream(v.device))
     _check(rc, lib, "gdn_chunk_fwd_segmented")
     return y, S_T
@@ -249,15 +312,19 @@ def gdn_chunk_bwd(q, k, v, log_alpha, beta, dy, S0=None, dS_T=None, cu_seqlens=N
     grad_dtype = dy.dtype if grad_dtype is None else grad_dtype
     _need(dy, "dy", grad_dtype)
     N, T, H, dk, dv = _prefill_shape(q, v, S0, cu_seqlens, N)
+    _shape(dy, "dy", v.shape)
     if dS_T is not None:
         _need(dS_T, "dS_T", torch.float32)
-        if tuple(dS_T.shape) != (N, H, dk, dv):
-            raise GdnError("dS_T must be [N, H, dk, dv]")
+        _shape(dS_T, "dS_T", (N, H, dk, dv))
+    if workspace is not None:
+        _need(workspace, "workspace")
+    dev = _devices((q, "q"), (k, "k"), (v, "v"), (log_alpha, "log_alpha"), (beta, "beta"),
+                   (S0, "S0"), (dy, "dy"), (dS_T, "dS_T"), (cu_seqlens, "cu_seqlens"),
+                   (workspace, "workspace"))
     rows = q.numel() // (H * dk)
     need = gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dev = q.device
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     dq = torch.empty(q.shape, dtype=grad_dtype, device=dev)
     dk_ = torch.empty(k.shape, dtype=grad_dtype, device=dev)
     dv_ = torch.empty(v.shape, dtype=grad_dtype, device=dev)
@@ -281,14 +348,20 @@ def gdn_chunk_bwd_gated(q, k, v, a, b, A, dy, b_alpha=None, S0=None, dS_T=None,
     grad_dtype = dy.dtype if grad_dtype is None else grad_dtype
     _need(dy, "dy", grad_dtype)
     N, T, H, dk, dv = _prefill_shape(q, v, S0, cu_seqlens, N)
+    _shape(dy, "dy", v.shape)
     _head_params(A, b_alpha, H)
     if dS_T is not None:
         _need(dS_T, "dS_T", torch.float32)
+        _shape(dS_T, "dS_T", (N, H, dk, dv))
+    if workspace is not None:
+        _need(workspace, "workspace")
+    dev = _devices((q, "q"), (k, "k"), (v, "v"), (a, "a"), (b, "b"), (A, "A"),
+                   (b_alpha, "b_alpha"), (S0, "S0"), (dy, "dy"), (dS_T, "dS_T"),
+                   (cu_seqlens, "cu_seqlens"), (workspace, "workspace"))
     rows = q.numel() // (H * dk)
     need = gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dev = q.device
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     dq = torch.empty(q.shape, dtype=grad_dtype, device=dev)
     dk_ = torch.empty(k.shape, dtype=grad_dtype, device=dev)
     dv_ = torch.empty(v.shape, dtype=grad_dtype, device=dev)
@@ -316,10 +389,13 @@ def gdn_conv_state_from_prefill(q_raw, k_raw, v_raw, cu_seqlens=None, N=None, sl
     dt = q_raw.dtype
     for t, nm in ((q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw")):
         _need(t, nm, dt)
-    H, d = q_raw.shape[-2], q_raw.shape[-1]
-    rows = q_raw.numel() // (H * d)
+    rows, H, d = _rows_layout(q_raw, "q_raw")
+    _shape(k_raw, "k_raw", q_raw.shape)
+    _shape(v_raw, "v_raw", q_raw.shape)
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise GdnError("cu_seqlens must be [N + 1]")
         N = cu_seqlens.numel() - 1
         T = rows
     else:
@@ -329,10 +405,18 @@ def gdn_conv_state_from_prefill(q_raw, k_raw, v_raw, cu_seqlens=None, N=None, sl
         T = rows // N
     if slot_idx is not None:
         _need(slot_idx, "slot_idx", torch.int32)
+        _shape(slot_idx, "slot_idx", (N,))
+    if conv_state is not None:
+        _need(conv_state, "conv_state", dt)
+        if conv_state.dim() != 5 or tuple(conv_state.shape[1:]) != (H, 3, 3, d):
+            raise GdnError("conv_state must be [slots, H, 3, 3, d]")
+        if slot_idx is None and conv_state.shape[0] != N:
+            raise GdnError("conv_state must hold one slot per sequence without slot_idx")
+    dev = _devices((q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw"),
+                   (cu_seqlens, "cu_seqlens"), (slot_idx, "slot_idx"), (conv_state, "conv_state"))
     if conv_state is None:
         slots = N if slot_idx is None else int(n_slots)
-        conv_state = torch.zeros((slots, H, 3, 3, d), dtype=dt, device=q_raw.device)
-    _need(conv_state, "conv_state", dt)
+        conv_state = torch.zeros((slots, H, 3, 3, d), dtype=dt, device=dev)
     slots = conv_state.shape[0]
     rc = lib.gdn_conv_state_from_prefill(_p(q_raw), _p(k_raw), _p(v_raw), _p(cu_seqlens), N, T,
                                          H, d, _p(slot_idx), slots, _p(conv_state), _dt(dt),
@@ -362,6 +446,10 @@ def gdn_chunk_fwd_gated(q, k, v, a, b, A, b_alpha=None, S0=None, cu_seqlens=None
     out_dtype = in_dtype if out_dtype is None else out_dtype
     N, T, H, dk, dv = _prefill_shape(q, v, S0, cu_seqlens, N)
     _head_params(A, b_alpha, H)
+    _dt(out_dtype)
+    _outputs(y, v.shape, out_dtype, S_T, (N, H, dk, dv))
+    _devices((q, "q"), (k, "k"), (v, "v"), (a, "a"), (b, "b"), (A, "A"), (b_alpha, "b_alpha"),
+             (S0, "S0"), (cu_seqlens, "cu_seqlens"), (y, "y"), (S_T, "S_T"))
     if y is None:
         y = torch.empty(v.shape, dtype=out_dtype, device=v.device)
     if S_T is None and want_state:
@@ -384,8 +472,21 @@ def gdn_decode_step(q, k, v, log_alpha, beta, S, out_dtype=None, y=None):
     _need(log_alpha, "log_alpha", torch.float32)
     _need(beta, "beta", torch.float32)
     _need(S, "S", torch.float32)
+    if q.dim() != 3:
+        raise GdnError("q must be [N, H, dk]")
     N, H, dk = q.shape
     dv = v.shape[-1]
+    _shape(k, "k", q.shape)
+    _shape(v, "v", (N, H, dv))
+    _shape(log_alpha, "log_alpha", (N, H))
+    _shape(beta, "beta", (N, H))
+    _shape(S, "S", (N, H, dk, dv))
+    _dt(out_dtype)
+    if y is not None:
+        _need(y, "y", out_dtype)
+        _shape(y, "y", (N, H, dv))
+    _devices((q, "q"), (k, "k"), (v, "v"), (log_alpha, "log_alpha"), (beta, "beta"), (S, "S"),
+             (y, "y"))
     if y is None:
         y = torch.empty((N, H, dv), dtype=out_dtype, device=v.device)
     rc = lib.gdn_decode_step(_p(q), _p(k), _p(v), _p(log_alpha), _p(beta), _p(S), _p(y), N, H,
@@ -409,8 +510,14 @@ def gdn_decode_step_gated(q, k, v, a, b, A, S, b_alpha=None, state_idx=None, out
     _need(a, "a", torch.float32)
     _need(b, "b", torch.float32)
     _need(S, "S", torch.float32)
+    if q.dim() != 3:
+        raise GdnError("q must be [N, H, dk]")
     N, H, dk = q.shape
     dv = v.shape[-1]
+    _shape(k, "k", q.shape)
+    _shape(v, "v", (N, H, dv))
+    _shape(a, "a", (N, H))
+    _shape(b, "b", (N, H))
     _head_params(A, b_alpha, H)
     n_slots = 0
     if state_idx is not None:
@@ -422,6 +529,12 @@ def gdn_decode_step_gated(q, k, v, a, b, A, S, b_alpha=None, state_idx=None, out
         raise GdnError("S must be [N, H, dk, dv]")
     if tuple(S.shape[1:]) != (H, dk, dv):
         raise GdnError("S must be [slots, H, dk, dv] with H, dk, dv = %s" % ((H, dk, dv),))
+    _dt(out_dtype)
+    if y is not None:
+        _need(y, "y", out_dtype)
+        _shape(y, "y", (N, H, dv))
+    _devices((q, "q"), (k, "k"), (v, "v"), (a, "a"), (b, "b"), (A, "A"), (b_alpha, "b_alpha"),
+             (S, "S"), (state_idx, "state_idx"), (y, "y"))
     if y is None:
         y = torch.empty((N, H, dv), dtype=out_dtype, device=v.device)
     rc = lib.gdn_decode_step_gated(_p(q), _p(k), _p(v), _p(a), _p(b), _p(A), _p(b_alpha), _p(S),
@@ -451,6 +564,10 @@ def gdn_decode_multi(q, k, v, g_a, g_b, S, A=None, b_alpha=None, state_idx=None,
         raise GdnError("q must be [N, n_tok, H, dk]")
     N, n_tok, H, dk = q.shape
     dv = v.shape[-1]
+    _shape(k, "k", q.shape)
+    _shape(v, "v", (N, n_tok, H, dv))
+    _shape(g_a, "g_a", (N, n_tok, H))
+    _shape(g_b, "g_b", (N, n_tok, H))
     if A is not None:
         _head_params(A, b_alpha, H)
     elif b_alpha is not None:
@@ -463,8 +580,14 @@ def gdn_decode_multi(q, k, v, g_a, g_b, S, A=None, b_alpha=None, state_idx=None,
         n_slots = S.shape[0]
     elif S.shape[0] != N:
         raise GdnError("S must be [N, H, dk, dv]")
-    if tuple(S.shape[1:]) != (H, dk, dv):
+    if S.dim() != 4 or tuple(S.shape[1:]) != (H, dk, dv):
         raise GdnError("S must be [slots, H, dk, dv] with H, dk, dv = %s" % ((H, dk, dv),))
+    _dt(out_dtype)
+    if y is not None:
+        _need(y, "y", out_dtype)
+        _shape(y, "y", (N, n_tok, H, dv))
+    _devices((q, "q"), (k, "k"), (v, "v"), (g_a, "g_a"), (g_b, "g_b"), (A, "A"),
+             (b_alpha, "b_alpha"), (S, "S"), (state_idx, "state_idx"), (y, "y"))
     if y is None:
         y = torch.empty((N, n_tok, H, dv), dtype=out_dtype, device=v.device)
     rc = lib.gdn_decode_multi(_p(q), _p(k), _p(v), _p(g_a), _p(g_b), _p(A), _p(b_alpha), _p(S),
@@ -498,12 +621,18 @@ def gdn_decode_fused(q_raw, k_raw, v_raw, conv_w, conv_state, g_a, g_b, S, z, A=
     if q_raw.dim() != 4:
         raise GdnError("q_raw must be [N, n_tok, H, d]")
     N, n_tok, H, d = q_raw.shape
+    for t, nm in ((k_raw, "k_raw"), (v_raw, "v_raw"), (z, "z")):
+        _shape(t, nm, q_raw.shape)
+    _shape(g_a, "g_a", (N, n_tok, H))
+    _shape(g_b, "g_b", (N, n_tok, H))
+    _shape(conv_w, "conv_w", (3, H * d, 4))
     if A is not None:
         _head_params(A, b_alpha, H)
     elif b_alpha is not None:
         raise GdnError("b_alpha needs A")
     if norm_w is not None:
         _need(norm_w, "norm_w", torch.float32)
+        _shape(norm_w, "norm_w", (d,))
     n_slots = 0
     if state_idx is not None:
         _need(state_idx, "state_idx", torch.int32)
@@ -514,6 +643,14 @@ def gdn_decode_fused(q_raw, k_raw, v_raw, conv_w, conv_state, g_a, g_b, S, z, A=
         raise GdnError("S must be [N, H, d, d]")
     if tuple(S.shape[1:]) != (H, d, d) or tuple(conv_state.shape) != (S.shape[0], H, 3, 3, d):
         raise GdnError("S must be [slots, H, d, d] and conv_state [slots, H, 3, 3, d]")
+    _dt(out_dtype)
+    if o is not None:
+        _need(o, "o", out_dtype)
+        _shape(o, "o", q_raw.shape)
+    _devices((q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw"), (conv_w, "conv_w"),
+             (conv_state, "conv_state"), (g_a, "g_a"), (g_b, "g_b"), (A, "A"),
+             (b_alpha, "b_alpha"), (S, "S"), (state_idx, "state_idx"), (z, "z"),
+             (norm_w, "norm_w"), (o, "o"))
     if o is None:
         o = torch.empty((N, n_tok, H, d), dtype=out_dtype, device=q_raw.device)
     rc = lib.gdn_decode_fused(_p(q_raw), _p(k_raw), _p(v_raw), _p(conv_w), _p(conv_state),
@@ -536,18 +673,31 @@ def gdn_frontend_qkv(q_raw, k_raw, v_raw, conv_w, cu_seqlens=None, N=None, l2_ep
     for t, nm in ((q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw")):
         _need(t, nm, in_dtype)
     _need(conv_w, "conv_w", torch.float32)
-    H, d = q_raw.shape[-2], q_raw.shape[-1]
-    rows = q_raw.numel() // (H * d)
+    rows, H, d = _rows_layout(q_raw, "q_raw")
+    _shape(k_raw, "k_raw", q_raw.shape)
+    _shape(v_raw, "v_raw", q_raw.shape)
     if tuple(conv_w.shape) != (3, H * d, 4):
         raise GdnError("conv_w must be [3, H*d, 4]")
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise GdnError("cu_seqlens must be [N + 1]")
         N, T = cu_seqlens.numel() - 1, rows
     else:
         N = 1 if N is None else N
         if N <= 0 or rows % N:
             raise GdnError("rows (%d) must be a multiple of N (%d)" % (rows, N))
         T = rows // N
+    _dt(out_dtype)
+    if out is not None:
+        if len(out) != 3:
+            raise GdnError("out must be a (q, k, v) triple")
+        for t, nm in zip(out, ("q", "k", "v")):
+            _need(t, nm, out_dtype)
+            _shape(t, nm, q_raw.shape)
+    outs = () if out is None else tuple(zip(out, ("q", "k", "v")))
+    _devices((q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw"), (conv_w, "conv_w"),
+             (cu_seqlens, "cu_seqlens"), *outs)
     if out is None:
         out = tuple(torch.empty(q_raw.shape, dtype=out_dtype, device=q_raw.device)
                     for _ in range(3))
@@ -569,10 +719,18 @@ def gdn_output_gate(y, z, norm_w=None, rms_eps=1e-6, out_dtype=None, o=None):
     _need(z, "z", z.dtype)
     if z.shape != y.shape:
         raise GdnError("z must have the shape of y")
+    if y.dim() < 1:
+        raise GdnError("y must have a feature dimension")
+    d = y.shape[-1]
     if norm_w is not None:
         _need(norm_w, "norm_w", torch.float32)
-    d = y.shape[-1]
-    rows = y.numel() // d
+        _shape(norm_w, "norm_w", (d,))
+    rows = y.numel() // d if d > 0 else 0
+    _dt(out_dtype)
+    if o is not None:
+        _need(o, "o", out_dtype)
+        _shape(o, "o", y.shape)
+    _devices((y, "y"), (z, "z"), (norm_w, "norm_w"), (o, "o"))
     if o is None:
         o = torch.empty(y.shape, dtype=out_dtype, device=y.device)
     rc = lib.gdn_output_gate(_p(y), _p(z), _p(norm_w), float(rms_eps), _p(o), rows, d,
@@ -602,12 +760,17 @@ def gdn_chunk_fwd_fused(q_raw, k_raw, v_raw, conv_w, log_alpha, beta, z, S0=None
     _need(conv_w, "conv_w", torch.float32)
     _need(log_alpha, "log_alpha", torch.float32)
     _need(beta, "beta", torch.float32)
-    H, d = q_raw.shape[-2], q_raw.shape[-1]
-    rows = q_raw.numel() // (H * d)
+    rows, H, d = _rows_layout(q_raw, "q_raw")
+    for t, nm in ((k_raw, "k_raw"), (v_raw, "v_raw"), (z, "z")):
+        _shape(t, nm, q_raw.shape)
+    _shape(log_alpha, "log_alpha", q_raw.shape[:-1])
+    _shape(beta, "beta", q_raw.shape[:-1])
     if tuple(conv_w.shape) != (3, H * d, 4):
         raise GdnError("conv_w must be [3, H*d, 4]")
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise GdnError("cu_seqlens must be [N + 1]")
         N, T = cu_seqlens.numel() - 1, rows
     else:
         if N is None:
@@ -621,7 +784,18 @@ def gdn_chunk_fwd_fused(q_raw, k_raw, v_raw, conv_w, log_alpha, beta, z, S0=None
             raise GdnError("S0 must be [N, H, d, d] = %s" % ((N, H, d, d),))
     if norm_w is not None:
         _need(norm_w, "norm_w", torch.float32)
-    dev = q_raw.device
+        _shape(norm_w, "norm_w", (d,))
+    _dt(out_dtype)
+    if o is not None:
+        _need(o, "o", out_dtype)
+        _shape(o, "o", q_raw.shape)
+    _outputs(None, None, None, S_T, (N, H, d, d))
+    if workspace is not None:
+        _need(workspace, "workspace")
+    dev = _devices((q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw"), (conv_w, "conv_w"),
+                   (log_alpha, "log_alpha"), (beta, "beta"), (z, "z"), (S0, "S0"),
+                   (norm_w, "norm_w"), (cu_seqlens, "cu_seqlens"), (o, "o"), (S_T, "S_T"),
+                   (workspace, "workspace"))
     if o is None:
         o = torch.empty(q_raw.shape, dtype=out_dtype, device=dev)
     if S_T is None and want_state:

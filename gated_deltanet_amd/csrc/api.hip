@@ -607,6 +607,12 @@ GDN_API int gdn_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void
   if (!head_size_ok(d)) return fail(GDN_ERR_UNSUPPORTED, "%s", "d must be 64 or 128");
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
     return fail(GDN_ERR_UNSUPPORTED, "%s", "dtype must be GDN_F32, GDN_BF16 or GDN_F16");
+  // q, k, v and y pass between the stages in fp16: fp32 inputs would lose
+  // the precision they are given for, so they take the three separate calls
+  if (in_dtype == GDN_F32)
+    return fail(GDN_ERR_UNSUPPORTED, "%s",
+                "the fused prefill takes 16-bit inputs (fp32: gdn_frontend_qkv, gdn_chunk_fwd, "
+                "gdn_output_gate)");
   if (!(l2_eps >= 0.0f) || !(rms_eps >= 0.0f))
     return fail(GDN_ERR_INVALID_ARG, "%s", "l2_eps and rms_eps must be >= 0");
   const int64_t rows = cu_seqlens ? static_cast<int64_t>(T) : static_cast<int64_t>(N) * T;

@@ -305,9 +305,13 @@ GDN_API size_t gdn_fused_workspace_size(int64_t rows, int32_t H, int32_t d);
  * (device memory, 256-byte aligned, at least
  * gdn_fused_workspace_size(rows, H, d) bytes, overwritten by the call):
  * q, k, v and y are kept in fp16, so the result equals the three separate
- * calls made with those intermediate dtypes.
+ * calls made with those intermediate dtypes. in_dtype must be GDN_BF16 or
+ * GDN_F16 (GDN_F32 returns GDN_ERR_UNSUPPORTED: fp32 inputs take the three
+ * separate calls, which keep their precision). Range: q and k leave the front
+ * end L2-normalised, but v = SiLU(conv) and y are held in fp16, so |v|, |y|
+ * must stay below 65504; larger values overflow to inf (and NaN in the gate).
  *
- *   q_raw, k_raw, v_raw, z  [rows, H, d] in in_dtype.
+ *   q_raw, k_raw, v_raw, z  [rows, H, d] in in_dtype (bf16 or fp16).
  *   conv_w                  float32 [3][H*d][4] (as gdn_frontend_qkv).
  *   log_alpha, beta         float32 [rows, H].
  *   S0, S_T                 float32 [N, H, d, d]; S0 NULL = zeros, S_T NULL =
@@ -392,7 +396,11 @@ GDN_API int gdn_decode_fused(const void *q_raw, const void *k_raw,
  *                 overwritten (it holds the state at every chunk start and
  *                 per-column-tile partial sums).
  * The states are recomputed from S0 (the forward's outputs are not needed).
- * Every product runs in fp32. Rows must be covered by the sequences
+ * Precision: with fp32 inputs every product runs in fp32 (fp32 MFMA) and the
+ * gradients meet the fp32 bar (relative L2 1e-5); with bf16/fp16 inputs the
+ * operands are rounded to fp16 for the 16-bit MFMA (fp32 accumulation, fp32
+ * state) and the chunk-start states come from the 16-bit prefill kernel, so
+ * the 16-bit bar (2e-3) applies. Rows must be covered by the sequences
  * (cu_seqlens[N] = rows). Inputs must not overlap outputs or the workspace.
  * Tensors are 16-byte aligned, the gates and cu_seqlens 4-byte aligned.
  * Results are deterministic (partial sums are added in a fixed order).

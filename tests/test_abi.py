@@ -160,6 +160,8 @@ def test_fused_rejects(lib):
     assert call(ST=W + 4096) == -1           # S_T inside the workspace
     assert call(rms=-1.0) == -1
     assert call(it=9) == -2
+    assert call(it=0) == -2                  # fp32 inputs: intermediates are fp16
+    assert b"16-bit" in lib.gdn_last_error()
     assert lib.gdn_last_error() != b""
 
 

@@ -26,7 +26,7 @@ def _case(T, dk, dv, seed, s0=True, extreme=None):
 
 
 @pytest.mark.parametrize("T,C", [(1, 64), (63, 64), (64, 64), (65, 64), (200, 64), (130, 16),
-                                 (77, 1), (90, 90)])
+                                 (77, 1), (90, 90), (32, 32), (33, 32), (95, 32), (160, 32)])
 @pytest.mark.parametrize("extreme", [None, "no_decay", "strong_decay", "beta_one", "repeated_keys"])
 def test_chunk_model_equals_recurrence(T, C, extreme):
     q, k, v, la, b, S0 = _case(T, 16, 12, seed=T * 7 + C, extreme=extreme)
