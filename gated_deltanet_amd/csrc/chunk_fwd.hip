@@ -234,7 +234,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     const float *__restrict__ gA, const float *__restrict__ gbias,
     const float *__restrict__ S0, TOUT *__restrict__ y, float *__restrict__ S_T,
     float *__restrict__ states, const int32_t *__restrict__ cu_seqlens, int T, int H, int DV,
-    int n_vt, int n_units) {
+    int n_vt, int n_units, SegCtl seg) {
   using L = Lay<DK, NS>;
   using KO = KOps<TIN>;
   using kvec = typename KO::vec;
@@ -294,6 +294,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     len = T;
   }
   const int nc = static_cast<int>((len + kC - 1) / kC);
+  const bool write_y = y != nullptr && n < seg.y_nseq;  // (never for the states-only variant)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -369,15 +370,17 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     char *slot = ring + (c % kRing) * L::SLOT;
     const int64_t r0 = row0_of(c);
     const uint32_t rows = static_cast<uint32_t>(rows_of(c));
+    const uint32_t vrows = seg.v_zero ? 0u : rows;  // v read as zeros: an empty range
     if constexpr (!STATES) {  // the states-only variant never reads Q
-      const i32x4 rq = buffer_rsrc(q + r0 * hdk, rows * hdk * 2);
+      // Q only feeds y: a run that writes no y loads it from an empty range
+      const i32x4 rq = buffer_rsrc(q + r0 * hdk, (write_y ? rows : 0u) * hdk * 2);
 #pragma unroll
       for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           dma16(rq, kq_lane + static_cast<uint32_t>(16 * rt * hdk * 2 + 64 * kb), lds_addr(slot + L::Q_OFF + (rt * NKB + kb) * 1024));
     }
-    const i32x4 rv = buffer_rsrc(v + r0 * hdv, rows * hdv * 2);
+    const i32x4 rv = buffer_rsrc(v + r0 * hdv, vrows * hdv * 2);
 #pragma unroll
     for (int p = 0; p < L::NV; ++p) dma16(rv, v_lane(p), lds_addr(slot + L::V_OFF + p * 1024));
   };
@@ -659,12 +662,18 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   const size_t sbase = static_cast<size_t>(n * H + h) * DK * DV + v0 + slab + lc;
   if (is_state) {
     __builtin_amdgcn_s_setprio(1);
+    const bool use_s0 = S0 != nullptr && n < seg.s0_nseq;
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st[t][i] = S0 ? S0[sbase + static_cast<size_t>(state_row(t, lg, i)) * DV] : 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        const int row = state_row(t, lg, i);
+        st[t][i] = seg.s0_ident ? (row == v0 + slab + lc ? 1.0f : 0.0f)
+                   : use_s0     ? S0[sbase + static_cast<size_t>(row) * DV]
+                                : 0.0f;
+      }
   }
+
   // chunk-start states for the backward pass (optional): chunk x of sequence
   // n goes to slot floor(bos / C) + n + x, this wave's slab of the tile
   float *const st_out =
@@ -784,7 +793,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     f32x4 Yt[kNCT];
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt) Yt[rt] = mma_f16(pf[rt], eb, G4[rt] * QS[rt]);
-    if constexpr (STATES) return;
+    if (STATES || !write_y) return;
     const uint32_t rows = static_cast<uint32_t>(rows_of(x));
     const auto ry = __builtin_amdgcn_make_buffer_rsrc(y + row0_of(x) * hdv, 0,
                                                       static_cast<int>(rows * hdv * sizeof(TOUT)),
@@ -850,7 +859,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
         if (is_gram) {
           if (in_range(it + 2)) gram(it + 2);
         } else if (is_qk) {
-          if (!STATES && in_range(it + 1)) qkp(it + 1);  // P only feeds y
+          if (!STATES && write_y && in_range(it + 1)) qkp(it + 1);  // P only feeds y
         } else if (is_inv) {
           if (in_range(it + 1)) inverse(it + 1);
         } else {
@@ -861,12 +870,13 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     }
   }
 
-  if (!STATES && is_state && S_T) {
+  if (!STATES && is_state && S_T && n >= seg.st_first) {
+    const size_t obase = static_cast<size_t>((n - seg.st_first) * H + h) * DK * DV + v0 + slab + lc;
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        S_T[sbase + static_cast<size_t>(state_row(t, lg, i)) * DV] = st[t][i];
+        S_T[obase + static_cast<size_t>(state_row(t, lg, i)) * DV] = st[t][i];
   }
 }
 
@@ -881,7 +891,7 @@ hipError_t launch_bf16(const ChunkArgs &a) {
                      dim3(64 * (NS + kPrep)), 0, a.stream, static_cast<const TIN *>(a.q),
                      static_cast<const TIN *>(a.k), static_cast<const TIN *>(a.v),
                      a.log_alpha, a.beta, a.A, a.b_alpha, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.states, a.cu_seqlens,
-                     a.T, a.H, a.dv, n_vt, static_cast<int>(units));
+                     a.T, a.H, a.dv, n_vt, static_cast<int>(units), a.seg);
   return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(64 * (DVT / 16)) void chunk_fwd_f32_kernel(
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
     const float *__restrict__ gA, const float *__restrict__ gbias,
     const float *__restrict__ S0, TOUT *__restrict__ y, float *__restrict__ S_T,
-    const int32_t *__restrict__ cu_seqlens, int T, int H, int DV, int n_vt) {
+    const int32_t *__restrict__ cu_seqlens, int T, int H, int DV, int n_vt, SegCtl seg) {
   constexpr int C = kChunkF32;
   constexpr int NW = DVT / 16;
   constexpr int NT = 64 * NW;
@@ -107,11 +107,17 @@ __global__ __launch_bounds__(64 * (DVT / 16)) void chunk_fwd_f32_kernel(
   // state slab: st[it][i] = S[16*it + 4*lg + i][v0 + n0 + lc]
   f32x4 st[NKT];
   const size_t sbase = static_cast<size_t>(n * H + h) * DK * DV + v0 + n0 + lc;
+  const bool use_s0 = S0 != nullptr && n < seg.s0_nseq;
+  const bool write_y = y != nullptr && n < seg.y_nseq;
 #pragma unroll
   for (int it = 0; it < NKT; ++it)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      st[it][i] = S0 ? S0[sbase + static_cast<size_t>(16 * it + 4 * lg + i) * DV] : 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * it + 4 * lg + i;
+      st[it][i] = seg.s0_ident ? (row == v0 + n0 + lc ? 1.0f : 0.0f)
+                  : use_s0     ? S0[sbase + static_cast<size_t>(row) * DV]
+                               : 0.0f;
+    }
 
   const RawGate gate = RawGate::load(gA, gbias, h);
   const int nchunks = static_cast<int>((len + C - 1) / C);
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(64 * (DVT / 16)) void chunk_fwd_f32_kernel(
         const int r = idx / VV_PER_ROW;
         const int d0 = (idx % VV_PER_ROW) * VEC;
         float vv[VEC];
-        if (r < valid) {
+        if (r < valid && !seg.v_zero) {
           io<TIN>::load16(v + static_cast<size_t>((t0 + r) * H + h) * DV + v0 + d0, vv);
         } else {
 #pragma unroll
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(64 * (DVT / 16)) void chunk_fwd_f32_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * lg + i;
-        if (r < valid)
+        if (write_y && r < valid)
           y[static_cast<size_t>((t0 + r) * H + h) * DV + v0 + n0 + lc] = io<TOUT>::from_f32(Y[i]);
       }
     }
@@ -351,12 +357,13 @@ __global__ __launch_bounds__(64 * (DVT / 16)) void chunk_fwd_f32_kernel(
     }
   }
 
-  if (S_T) {
+  if (S_T && n >= seg.st_first) {
+    const size_t obase = static_cast<size_t>((n - seg.st_first) * H + h) * DK * DV + v0 + n0 + lc;
 #pragma unroll
     for (int it = 0; it < NKT; ++it)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        S_T[sbase + static_cast<size_t>(16 * it + 4 * lg + i) * DV] = st[it][i];
+        S_T[obase + static_cast<size_t>(16 * it + 4 * lg + i) * DV] = st[it][i];
   }
 }
 
@@ -369,7 +376,7 @@ static hipError_t launch_tile(const ChunkArgs &a) {
                      dim3(64 * (DVT / 16)), 0, a.stream, static_cast<const TIN *>(a.q),
                      static_cast<const TIN *>(a.k), static_cast<const TIN *>(a.v), a.log_alpha,
                      a.beta, a.A, a.b_alpha, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.cu_seqlens, a.T, a.H, a.dv,
-                     n_vt);
+                     n_vt, a.seg);
   return hipGetLastError();
 }
 

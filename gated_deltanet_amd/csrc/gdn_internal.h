@@ -48,6 +48,17 @@ struct DecodeArgs {
 // most tokens one decode call applies per (sequence, head)
 constexpr int kDecodeMaxTok = 8;
 
+// Controls for the runs of the segment-parallel prefill, whose "sequences"
+// are segments; the defaults make every sequence an ordinary prefill. All
+// are uniform per workgroup.
+struct SegCtl {
+  int y_nseq = 0x7fffffff;   // sequences n < y_nseq write y
+  int s0_nseq = 0x7fffffff;  // sequences n < s0_nseq start from S0[n], the others from zero
+  int s0_ident = 0;          // every sequence starts from the identity (dk == dv)
+  int v_zero = 0;            // v is read as zeros (the pointer is still a valid buffer)
+  int st_first = 0;          // sequences n >= st_first write S_T[n - st_first]
+};
+
 struct ChunkArgs {
   const void *q, *k, *v;
   const float *log_alpha, *beta;
@@ -62,6 +73,7 @@ struct ChunkArgs {
   // launch_chunk_fwd_states only: chunk-start states in the backward
   // workspace's tile order
   float *states = nullptr;
+  SegCtl seg;
 };
 
 struct FrontendArgs {
@@ -129,14 +141,8 @@ hipError_t launch_conv_state(const ConvStateArgs &a);
 // vzero_bytes of zeros (the values of the transition runs).
 struct SegPrepArgs {
   const int32_t *cu_seqlens;  // may be null
-  int N, T, H, dk, dv, P;
-  const float *S0;            // may be null
-  int32_t *cu_seg;
-  float *S0seg;
-  float *ident;
-  size_t n_ident;
-  void *vzero;
-  size_t vzero_bytes;
+  int N, T, P;
+  int32_t *cu_seg;            // [N][P + 1] segment bounds
   hipStream_t stream;
 };
 hipError_t launch_seg_prep(const SegPrepArgs &a);

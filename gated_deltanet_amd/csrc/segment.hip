@@ -43,36 +43,6 @@ __global__ void seg_bounds_kernel(const int32_t *cu, int N, int T, int P, int32_
   }
 }
 
-// Initial states of the zero-start runs: segment 0 of each sequence starts
-// from the caller's S0 (zeros when absent), the others from zero.
-__global__ void seg_s0_kernel(const float *S0, float *S0seg, int N, int nseg, size_t per) {
-  const size_t total = static_cast<size_t>(N) * nseg * per;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const size_t x = i % per;
-    const size_t e = (i / per) % nseg;
-    const size_t n = i / (per * nseg);
-    S0seg[i] = (e == 0 && S0) ? S0[n * per + x] : 0.0f;
-  }
-}
-
-// count identity matrices of size dk x dk
-__global__ void seg_ident_kernel(float *I, size_t count, int dk) {
-  const size_t per = static_cast<size_t>(dk) * dk;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count * per;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const size_t x = i % per;
-    I[i] = (x / dk == x % dk) ? 1.0f : 0.0f;
-  }
-}
-
-__global__ void seg_zero_kernel(u32x4 *p, size_t n16) {
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x)
-    p[i] = z;
-}
-
 // The chain for one sequence, in fp32: Sin[0] = N[0] and
 // Sin[e] = M[e - 1] Sin[e - 1] + N[e] for e = 1 .. P - 2 (entry e of Sin is
 // the initial state of segment e + 1, of N the zero-start final state of
@@ -120,28 +90,13 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(const float *__restric
   }
 }
 
-unsigned grid_for(size_t n, unsigned cap = 4096) {
-  const size_t g = (n + 255) / 256;
-  return static_cast<unsigned>(g < 1 ? 1 : (g > cap ? cap : g));
-}
 
 }  // namespace
 
 hipError_t launch_seg_prep(const SegPrepArgs &a) {
-  if (a.N > 0) {
+  if (a.N > 0)
     hipLaunchKernelGGL(seg_bounds_kernel, dim3((a.N + 255) / 256), dim3(256), 0, a.stream,
                        a.cu_seqlens, a.N, a.T, a.P, a.cu_seg);
-    const size_t per = static_cast<size_t>(a.H) * a.dk * a.dv;
-    const size_t n_s0 = static_cast<size_t>(a.N) * (a.P - 1) * per;
-    hipLaunchKernelGGL(seg_s0_kernel, dim3(grid_for(n_s0)), dim3(256), 0, a.stream, a.S0,
-                       a.S0seg, a.N, a.P - 1, per);
-  }
-  if (a.n_ident > 0)
-    hipLaunchKernelGGL(seg_ident_kernel, dim3(grid_for(a.n_ident * a.dk * a.dk)), dim3(256), 0,
-                       a.stream, a.ident, a.n_ident, a.dk);
-  if (a.vzero_bytes > 0)
-    hipLaunchKernelGGL(seg_zero_kernel, dim3(grid_for(a.vzero_bytes / 16)), dim3(256), 0,
-                       a.stream, static_cast<u32x4 *>(a.vzero), a.vzero_bytes / 16);
   return hipGetLastError();
 }
 

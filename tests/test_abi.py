@@ -315,13 +315,14 @@ def test_segmented_rejects(lib):
     lib.gdn_chunk_fwd_segmented_workspace_size.argtypes = [ctypes.c_int64] + [i32] * 6
     lib.gdn_chunk_fwd_segmented_workspace_size.restype = sz
     lib.gdn_chunk_fwd_segmented.argtypes = [v] * 9 + [i32] * 6 + [v, sz, i32, i32, v]
-    # rows 64, N 1, H 2, d 128, 3 segments, bf16: bounds (256 B padded), four
-    # sets of 2 states of 2 x 128 x 128 fp32 (zero-start initial and final,
-    # chained initial, rerun final), one transition and one identity, and
-    # 2 x 64 x 2 x 128 bf16 of zeros and scratch
+    # rows 64, N 1, H 2, d 128, 3 segments, bf16: bounds (256 B padded), two
+    # sets of 2 states of 2 x 128 x 128 fp32 (zero-start finals of segments
+    # 0 and 1, chained initial states of segments 1 and 2) and one transition
+    # of segment 1; nothing scales with the row count
     need = lib.gdn_chunk_fwd_segmented_workspace_size(64, 1, 2, 128, 128, 3, 1)
     per = 2 * 128 * 128 * 4
-    assert need == 256 + 4 * 2 * per + 2 * per + 2 * 64 * 2 * 128 * 2
+    assert need == 256 + 2 * 2 * per + per
+    assert need == lib.gdn_chunk_fwd_segmented_workspace_size(1 << 20, 1, 2, 128, 128, 3, 1)
     assert lib.gdn_chunk_fwd_segmented_workspace_size(64, 1, 2, 128, 128, 1, 1) == 0
     assert lib.gdn_chunk_fwd_segmented_workspace_size(64, 1, 2, 96, 128, 3, 1) == 0
 
