@@ -175,10 +175,10 @@ GDN_API int gdn_chunk_fwd_segmented(const void *q, const void *k, const void *v,
 
 /*
  * Bytes of workspace gdn_chunk_fwd_segmented needs (0 for invalid sizes):
- * segment bounds and per-segment states of all N sequences, plus zeros for
- * the transition runs' values and a scratch for their outputs
- * (2 * rows * H * dk elements of in_dtype). `rows` as for gdn_chunk_fwd:
- * N * T, or T with cu_seqlens.
+ * segment bounds and per-segment states of all N sequences, in fp32:
+ * N * H * (2 (P - 1) dk dv + (P - 2) dk dk) * 4 bytes plus the bounds,
+ * independent of the row count. `rows` as for gdn_chunk_fwd (N * T, or T
+ * with cu_seqlens) is validated but does not enter the size.
  */
 GDN_API size_t gdn_chunk_fwd_segmented_workspace_size(int64_t rows, int32_t N, int32_t H,
                                                       int32_t dk, int32_t dv,
