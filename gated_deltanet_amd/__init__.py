@@ -100,6 +100,9 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_chunk_fwd_segmented.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, ip, i32, i32, i32,
                                             i32, i32, i32, vp, sz, i32, i32, vp]
     lib.gdn_chunk_fwd_segmented.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_segmented_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, ip, i32, i32,
+                                                    i32, i32, i32, i32, i32, i32, vp]
+    lib.gdn_chunk_fwd_segmented_noalloc.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -294,6 +297,35 @@ def gdn_chunk_fwd_segmented(q, k, v, log_alpha, beta, segments, S0=None, cu_seql
                                      _dt(in_dtype),
                                      _dt(out_dtype), _stream(v.device))
     _check(rc, lib, "gdn_chunk_fwd_segmented")
+    return y, S_T
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDN_NOALLOC_SCRATCH_BYTES
+
+
+def gdn_chunk_fwd_segmented_noalloc(q, k, v, log_alpha, beta, segments, S0=None,
+                                    cu_seqlens=None, out_dtype=None, S_T=None, y=None,
+                                    want_state=True, N=None):
+    """gdn_chunk_fwd_segmented with the library's fixed per-GPU scratch as its
+    workspace (nothing allocated by the library; calls on one GPU must not
+    overlap). y and S_T are allocated here unless given."""
+    lib = load_library()
+    in_dtype = _prefill_checked(q, k, v, log_alpha, beta, ("log_alpha", "beta"))
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    N, T, H, dk, dv = _prefill_shape(q, v, S0, cu_seqlens, N)
+    _dt(out_dtype)
+    _outputs(y, v.shape, out_dtype, S_T, (N, H, dk, dv))
+    _devices((q, "q"), (k, "k"), (v, "v"), (log_alpha, "log_alpha"), (beta, "beta"), (S0, "S0"),
+             (cu_seqlens, "cu_seqlens"), (y, "y"), (S_T, "S_T"))
+    if y is None:
+        y = torch.empty(v.shape, dtype=out_dtype, device=v.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=v.device)
+    rc = lib.gdn_chunk_fwd_segmented_noalloc(_p(q), _p(k), _p(v), _p(log_alpha), _p(beta), _p(S0),
+                                             _p(y), _p(S_T), _p(cu_seqlens), N, T, H, dk, dv,
+                                             segments, _dt(in_dtype), _dt(out_dtype),
+                                             _stream(v.device))
+    _check(rc, lib, "gdn_chunk_fwd_segmented_noalloc")
     return y, S_T
 
 

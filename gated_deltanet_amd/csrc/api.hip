@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/gdn.h"
 #include "gdn_internal.h"
 
@@ -429,6 +431,64 @@ GDN_API int gdn_chunk_fwd_segmented(const void *q, const void *k, const void *v,
   return segmented_impl(q, k, v, log_alpha, beta, S0, y, S_T, cu_seqlens, N, T, H, dk, dv,
                         segments, workspace, workspace_bytes, in_dtype, out_dtype, stream,
                         "gdn_chunk_fwd_segmented");
+}
+
+// Scratch of gdn_chunk_fwd_segmented_noalloc: a fixed device array, one copy
+// on every GPU the library runs on, held until the process ends. In host code
+// `scratch` names a host-side stand-in, not a device address: its address on
+// a device comes from hipGetSymbolAddress with that device current, looked up
+// once per device and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratch = GDN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratch];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "device ordinal beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+}  // namespace
+
+GDN_API int gdn_chunk_fwd_segmented_noalloc(const void *q, const void *k, const void *v,
+                                            const float *log_alpha, const float *beta,
+                                            const float *S0, void *y, float *S_T,
+                                            const int32_t *cu_seqlens, int32_t N, int32_t T,
+                                            int32_t H, int32_t dk, int32_t dv, int32_t segments,
+                                            int32_t in_dtype, int32_t out_dtype, void *stream) {
+  g_last_error[0] = '\0';
+  if (segments < 2 || segments > 64)
+    return fail(GDN_ERR_INVALID_ARG, "%s", "segments must be in [2, 64]");
+  if (N < 0 || H <= 0) return fail(GDN_ERR_INVALID_ARG, "%s", "N must be >= 0 and H > 0");
+  if (!head_size_ok(dk) || !head_size_ok(dv))
+    return fail(GDN_ERR_UNSUPPORTED, "%s", "dk and dv must be 64 or 128");
+  const size_t need = seg_layout(N, H, dk, dv, segments).total;
+  if (need > kNoAllocScratch) {
+    char msg[160];
+    snprintf(msg, sizeof(msg), "needs %zu bytes of scratch, more than the fixed %zu "
+             "(fewer sequences, heads or segments per call)", need, kNoAllocScratch);
+    return fail(GDN_ERR_INVALID_ARG, "%s", msg);
+  }
+  void *ws = nullptr;
+  const int rc = scratch_of_current_device(&ws);
+  if (rc != GDN_OK) return rc;
+  return segmented_impl(q, k, v, log_alpha, beta, S0, y, S_T, cu_seqlens, N, T, H, dk, dv,
+                        segments, ws, kNoAllocScratch, in_dtype, out_dtype, stream,
+                        "gdn_chunk_fwd_segmented_noalloc");
 }
 
 GDN_API int gdn_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,

@@ -174,6 +174,29 @@ GDN_API int gdn_chunk_fwd_segmented(const void *q, const void *k, const void *v,
                                     int32_t out_dtype, void *stream);
 
 /*
+ * gdn_chunk_fwd_segmented for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and results, with the workspace taken from
+ * a fixed scratch array of GDN_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends. The call allocates nothing and
+ * rejects, with GDN_ERR_INVALID_ARG and nothing enqueued, a problem whose
+ * workspace (gdn_chunk_fwd_segmented_workspace_size) exceeds that size. Every
+ * call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents (every byte a call reads it first writes, so nothing needs
+ * clearing): calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller. Arguments and errors as
+ * gdn_chunk_fwd_segmented without the workspace.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+GDN_API int gdn_chunk_fwd_segmented_noalloc(const void *q, const void *k, const void *v,
+                                            const float *log_alpha, const float *beta,
+                                            const float *S0, void *y, float *S_T,
+                                            const int32_t *cu_seqlens, int32_t N, int32_t T,
+                                            int32_t H, int32_t dk, int32_t dv,
+                                            int32_t segments, int32_t in_dtype,
+                                            int32_t out_dtype, void *stream);
+
+/*
  * Bytes of workspace gdn_chunk_fwd_segmented needs (0 for invalid sizes):
  * segment bounds and per-segment states of all N sequences, in fp32:
  * N * H * (2 (P - 1) dk dv + (P - 2) dk dk) * 4 bytes plus the bounds,
