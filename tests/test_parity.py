@@ -429,8 +429,10 @@ def _multi_inputs(N, H, dk, dv, n_tok, dtype, seed):
 @pytest.mark.parametrize("n_tok", [1, 2, 4, 8])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_multi_matches_steps_and_oracle(dk, dv, n_tok, dtype):
-    """n_tok tokens in one call equal n_tok single-token calls bit for bit
-    (the same arithmetic in the same order) and the oracle to the bar."""
+    """n_tok tokens in one call equal n_tok single-token calls (bit for bit
+    for one token; for more, the call applies them as blocks of 4 in the
+    unrolled form, the same sums in another order, so to fp32 rounding) and
+    the oracle to the bar."""
     g = _lib()
     N, H = 5, 3
     inp, tm = _multi_inputs(N, H, dk, dv, n_tok, dtype, seed=dk + dv + n_tok)
@@ -442,8 +444,12 @@ def test_decode_multi_matches_steps_and_oracle(dk, dv, n_tok, dtype):
                               ("q", "k", "v", "log_alpha", "beta")), S2, out_dtype=torch.float32)
           for t in range(n_tok)]
     torch.cuda.synchronize()
-    assert torch.equal(y1, torch.stack(y2, 1))
-    assert torch.equal(S1, S2)
+    if n_tok == 1:
+        assert torch.equal(y1, torch.stack(y2, 1))
+        assert torch.equal(S1, S2)
+    else:
+        assert rel_l2(y1, torch.stack(y2, 1).double().cpu().numpy()) <= 1e-5
+        assert rel_l2(S1, S2.double().cpu().numpy()) <= 1e-5
     S_or = inp["S0"].double().numpy()
     yo = []
     for t in range(n_tok):
