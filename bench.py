@@ -261,10 +261,10 @@ def bench_decode(g, n_steps=128, reps=2):
     return dict(_check=check, workload=w.name, us_per_step=us_step, GBps=gbs,
                 frac_hbm=gbs / HBM_PEAK_GBS,
                 tokens_per_s=N / (us_step * 1e-6), bytes_per_step=bytes_step, steps=n_steps,
-                roofline=dict(kernel="decode_kernel<128,128,bf16,bf16,unfused> (n_tok = 1)", bound="hbm",
-                              achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                roofline=dict(kernel="decode_token_kernel<128,128,bf16,bf16,unfused> (n_tok = 1)",
+                              bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                               frac=gbs / HBM_PEAK_GBS,
-                              traffic=measured_traffic("decode_kernel_N256_H32_d128",
+                              traffic=measured_traffic("decode_token_kernel_N256_H32_d128",
                                                        "decode.hip")))
 
 
@@ -290,7 +290,12 @@ def bench_decode_multi(g, n_tok=4, calls=32):
     gbs = nbytes / (us * 1e-6) / 1e9
     return dict(workload=w.name, entry_point="gdn_decode_multi", n_tok=n_tok, us_per_call=us,
                 tokens_per_s=N * n_tok / (us * 1e-6), GBps=gbs, frac_hbm=gbs / HBM_PEAK_GBS,
-                bytes_per_call=nbytes)
+                bytes_per_call=nbytes,
+                roofline=dict(kernel="decode_block_kernel<128,128,bf16,bf16,unfused> (n_tok = %d)"
+                              % n_tok, bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=gbs / HBM_PEAK_GBS,
+                              traffic=measured_traffic("decode_block_kernel_N256_H32_d128_ntok4",
+                                                       "decode.hip") if n_tok == 4 else None))
 
 
 def bench_decode_fused(g, n_tok=4, calls=32):

@@ -227,7 +227,7 @@ __device__ __forceinline__ V lds_read16(const char *p) {
 // workspace) instead of y and S_T. LPT (packed batches of at most kLptMax
 // sequences): workgroups take the sequences longest first, so the short ones
 // fill in at the end instead of a long one running alone.
-template <int DK, int NS, typename TIN, typename TOUT, bool STATES, bool LPT>
+template <int DK, int NS, typename TIN, typename TOUT, bool STATES, bool LPT, bool SEG>
 __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     const TIN *__restrict__ q, const TIN *__restrict__ k, const TIN *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
@@ -294,7 +294,9 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     len = T;
   }
   const int nc = static_cast<int>((len + kC - 1) / kC);
-  const bool write_y = y != nullptr && n < seg.y_nseq;  // (never for the states-only variant)
+  // the controls of the segment runs are read only by the SEG variant, so
+  // that every other instantiation compiles as if they were absent
+  const bool write_y = !SEG || (y != nullptr && n < seg.y_nseq);  // (never for the states-only variant)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     char *slot = ring + (c % kRing) * L::SLOT;
     const int64_t r0 = row0_of(c);
     const uint32_t rows = static_cast<uint32_t>(rows_of(c));
-    const uint32_t vrows = seg.v_zero ? 0u : rows;  // v read as zeros: an empty range
+    const uint32_t vrows = SEG && seg.v_zero ? 0u : rows;  // v read as zeros: an empty range
     if constexpr (!STATES) {  // the states-only variant never reads Q
       // Q only feeds y: a run that writes no y loads it from an empty range
       const i32x4 rq = buffer_rsrc(q + r0 * hdk, (write_y ? rows : 0u) * hdk * 2);
@@ -662,15 +664,15 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   const size_t sbase = static_cast<size_t>(n * H + h) * DK * DV + v0 + slab + lc;
   if (is_state) {
     __builtin_amdgcn_s_setprio(1);
-    const bool use_s0 = S0 != nullptr && n < seg.s0_nseq;
+    const bool use_s0 = S0 != nullptr && (!SEG || n < seg.s0_nseq);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = state_row(t, lg, i);
-        st[t][i] = seg.s0_ident ? (row == v0 + slab + lc ? 1.0f : 0.0f)
-                   : use_s0     ? S0[sbase + static_cast<size_t>(row) * DV]
-                                : 0.0f;
+        st[t][i] = SEG && seg.s0_ident ? (row == v0 + slab + lc ? 1.0f : 0.0f)
+                   : use_s0            ? S0[sbase + static_cast<size_t>(row) * DV]
+                                       : 0.0f;
       }
   }
 
@@ -870,8 +872,9 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     }
   }
 
-  if (!STATES && is_state && S_T && n >= seg.st_first) {
-    const size_t obase = static_cast<size_t>((n - seg.st_first) * H + h) * DK * DV + v0 + slab + lc;
+  const int st_first = SEG ? seg.st_first : 0;
+  if (!STATES && is_state && S_T && n >= st_first) {
+    const size_t obase = static_cast<size_t>((n - st_first) * H + h) * DK * DV + v0 + slab + lc;
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
@@ -880,14 +883,15 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   }
 }
 
-template <int DK, int NS, typename TIN, typename TOUT, bool STATES = false, bool LPT = false>
+template <int DK, int NS, typename TIN, typename TOUT, bool STATES = false, bool LPT = false,
+          bool SEG = false>
 hipError_t launch_bf16(const ChunkArgs &a) {
   constexpr int DVT = 16 * NS;
   const int n_vt = a.dv / DVT;
   const int64_t units = static_cast<int64_t>(a.N) * a.H;
   const int64_t blocks = (units + 7) / 8 * 8 * n_vt;
   if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, NS, TIN, TOUT, STATES, LPT>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, NS, TIN, TOUT, STATES, LPT, SEG>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * (NS + kPrep)), 0, a.stream, static_cast<const TIN *>(a.q),
                      static_cast<const TIN *>(a.k), static_cast<const TIN *>(a.v),
                      a.log_alpha, a.beta, a.A, a.b_alpha, a.S0, static_cast<TOUT *>(a.y), a.S_T, a.states, a.cu_seqlens,
@@ -899,6 +903,11 @@ hipError_t launch_bf16(const ChunkArgs &a) {
 
 template <typename TIN, typename TOUT>
 static hipError_t launch_16(const ChunkArgs &a) {
+  // runs of the segment-parallel form (in sequence order: the ordering by
+  // length is only a scheduling aid)
+  if (!a.seg.plain())
+    return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT, false, false, true>(a)
+                       : launch_bf16<64, 2, TIN, TOUT, false, false, true>(a);
   if (a.cu_seqlens && a.N > 1 && a.N <= kLptMax)
     return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT, false, true>(a)
                        : launch_bf16<64, 2, TIN, TOUT, false, true>(a);

@@ -57,6 +57,9 @@ struct SegCtl {
   int s0_ident = 0;          // every sequence starts from the identity (dk == dv)
   int v_zero = 0;            // v is read as zeros (the pointer is still a valid buffer)
   int st_first = 0;          // sequences n >= st_first write S_T[n - st_first]
+  bool plain() const {
+    return y_nseq == 0x7fffffff && s0_nseq == 0x7fffffff && !s0_ident && !v_zero && !st_first;
+  }
 };
 
 struct ChunkArgs {
