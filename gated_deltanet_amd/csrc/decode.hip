@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(const DecodeArgs a) {
 // so the state is touched by one pass of dot products (all 2G of them) and
 // one update per block, and only 2G sums per column cross lanes.
 template <int DK, int DV, typename TIN, typename TOUT, bool FUSED>
-__global__ __launch_bounds__(256) void decode_block_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(256, FUSED ? 3 : 4) void decode_block_kernel(const DecodeArgs a) {
   constexpr int G = 4;  // tokens per block
   const TIN *__restrict__ q = static_cast<const TIN *>(a.q);
   const TIN *__restrict__ k = static_cast<const TIN *>(a.k);
@@ -449,7 +449,8 @@ __global__ __launch_bounds__(256) void decode_block_kernel(const DecodeArgs a) {
   const float *__restrict__ gb = a.beta;
   float *__restrict__ S = a.S;
   const int32_t *__restrict__ read_idx = a.read_idx;
-  const int r_stride = a.r_stride, n_slots = a.n_slots;
+  const int32_t *__restrict__ write_idx = a.write_idx;
+  const int r_stride = a.r_stride, w_stride = a.w_stride, n_slots = a.n_slots;
   TOUT *__restrict__ y = static_cast<TOUT *>(a.y);
   const int H = a.H, n_tok = a.n_tok;
   constexpr int NT = 256;
@@ -473,6 +474,7 @@ __global__ __launch_bounds__(256) void decode_block_kernel(const DecodeArgs a) {
   __shared__ __align__(16) float skT[DK][TP];
   __shared__ __align__(16) float sv[TP][DV];
   __shared__ float s_la[TP], s_beta[TP];
+  __shared__ int s_dst[TP];  // slot receiving the state after token t, or -1
   __shared__ __align__(16) float sz[FUSED ? TP : 1][DV];
   __shared__ float s_ss[FUSED ? TP : 1][NWAVE];
 
@@ -550,6 +552,11 @@ __global__ __launch_bounds__(256) void decode_block_kernel(const DecodeArgs a) {
   float la = ga[gi];
   float bt = gb[gi];
   const RawGate gate = RawGate::load(a.A, a.b_alpha, h);
+  // the slot table's write entries, read with the small loads (without a
+  // table the gates are read in their place, and the value is not used)
+  const int32_t *wtab = write_idx ? write_idx + static_cast<int64_t>(n) * w_stride
+                                  : reinterpret_cast<const int32_t *>(ga);
+  const int wraw = wtab[gj];
 
   // front-end lanes: lane f < 3 * FG owns 4 channels of one stream
   // (q, k, v); lanes past them repeat the last one
@@ -591,6 +598,8 @@ __global__ __launch_bounds__(256) void decode_block_kernel(const DecodeArgs a) {
   if (tid < TP) {
     s_la[tid] = tid < n_tok ? la : 0.0f;
     s_beta[tid] = tid < n_tok ? bt : 0.0f;
+    s_dst[tid] = write_idx ? (tid < n_tok && wraw >= 0 && wraw < n_slots ? wraw : -1)
+                           : (tid == n_tok - 1 ? slot : -1);
   }
   lds_barrier();
 
@@ -624,9 +633,11 @@ __global__ __launch_bounds__(256) void decode_block_kernel(const DecodeArgs a) {
           hist[1][c] = hist[2][c];
           hist[2][c] = x[c];
         }
-        // the convolution history after the last token goes back to the slot
-        if (j == n_tok - 1 && tid < 3 * FG) {
-          TIN *hp = cstate + ((static_cast<size_t>(slot) * H + h) * 3 + fs) * 3 * DK + fc;
+        // the convolution history after token j goes wherever the state
+        // after token j goes
+        const int dst = s_dst[j];
+        if (dst >= 0 && tid < 3 * FG) {
+          TIN *hp = cstate + ((static_cast<size_t>(dst) * H + h) * 3 + fs) * 3 * DK + fc;
 #pragma unroll
           for (int r = 0; r < 3; ++r) store4(hp + r * DK, hist[r]);
         }
@@ -749,16 +760,58 @@ __global__ __launch_bounds__(256) void decode_block_kernel(const DecodeArgs a) {
       if (col_lead && t0 + t < n_tok)
         y[((row0 + t0 + t) * H + h) * DV + col0 + cr] = io<TOUT>::from_f32(yv[t]);
 
-    // state update, stored back after the last block; each row is stored as
-    // soon as it is updated, so the stores drain while the rest of the
-    // update still runs
+    // where the state after token t goes (s_dst: its slot from the table,
+    // or without a table the starting slot after the call's last token; -1
+    // for nowhere)
+    auto dst_of = [&](int t) { return s_dst[t]; };
+    // The state after the block's last real token is the updated state
+    // (padding tokens change nothing). The states after earlier tokens of
+    // the block are needed only with a table that names slots for them; each
+    // is formed from the block's start state in a pass of its own,
+    //     S_t = Gam_t S + sum_{i<=t} D_ti beta_i e_i k_i^T.
+    const int t_end = min(t0 + G, n_tok) - 1;  // the block's last real token
+    if (write_idx) {
+#pragma unroll
+      for (int t = 0; t < G - 1; ++t) {
+        if (t0 + t >= t_end) break;
+        const int dt = dst_of(t0 + t);
+        if (dt < 0) continue;
+        float ut[G][4];
+#pragma unroll
+        for (int i = 0; i <= t; ++i) {
+          const float wi = (i == t ? 1.0f : __expf(cum[t] - cum[i])) * s_beta[t0 + i];
+          bcast_rows(wi * e[i], ut[i]);
+        }
+        const auto St = state_rsrc(dt);
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+          float kr[G];
+          lds_read<G>(&skT[rg + RGW * m][t0], kr);
+          f32x4 x;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            float acc = Gam[t] * s[m][c];
+#pragma unroll
+            for (int i = 0; i <= t; ++i) acc = fmaf(kr[i], ut[i][c], acc);
+            x[c] = acc;
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), St, s_lane,
+                                                 m * kRowStep, 2);
+        }
+      }
+    }
+
+    // state update; each row is stored as soon as it is updated, so the
+    // stores drain while the rest of the update still runs
     float u[G][4];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const float wi = (i == G - 1 ? 1.0f : __expf(cum[G - 1] - cum[i])) * s_beta[t0 + i];
       bcast_rows(wi * e[i], u[i]);
     }
-    const bool store = b == n_blk - 1;
+    const int dend = dst_of(t_end);
+    const bool store = dend >= 0;
+    const auto Sw = state_rsrc(store ? dend : slot);
     const float gl = Gam[G - 1];
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
@@ -772,7 +825,7 @@ __global__ __launch_bounds__(256) void decode_block_kernel(const DecodeArgs a) {
         s[m][c] = x;
       }
       if (store)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), Sr, s_lane,
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), Sw, s_lane,
                                                m * kRowStep, 2);
     }
   };
@@ -787,9 +840,8 @@ template <int DK, int DV, typename TIN, typename TOUT, bool FUSED>
 static hipError_t launch(const DecodeArgs &a) {
   const int units = a.N * a.H;
   if (units == 0 || a.n_tok <= 0) return hipSuccess;
-  // blocks of tokens for multi-token calls that keep only the final state;
-  // token by token for one token and for states kept after every token
-  if (a.n_tok == 1 || a.write_idx)
+  // one token: token by token; more: in blocks
+  if (a.n_tok == 1)
     hipLaunchKernelGGL((decode_token_kernel<DK, DV, TIN, TOUT, FUSED>), dim3(units), dim3(256), 0,
                        a.stream, a);
   else
