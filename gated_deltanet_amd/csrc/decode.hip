@@ -647,59 +647,64 @@ __global__ __launch_bounds__(256, FUSED ? 3 : 4) void decode_block_kernel(const 
   }
 
   const int n_blk = n_pad / G;
-  auto block = [&](const int b) __attribute__((always_inline)) {
-    const int t0 = b * G;
-    // cum_t: running sum of log alpha over the block, Gam_t = exp(cum_t)
-    float cum[G], Gam[G];
+  static_assert(TP / G <= 2, "at most two blocks per call");
+  // Per block: cum_t, the running sum of log alpha over the block, and
+  // Gam_t = exp(cum_t); the Gram entries, summed by every wave on its own
+  // (lane l takes rows l, l + 64, ...), and their coefficients
+  // D_ti beta_i (k_i . x_t). All uniform (scalar registers) and independent
+  // of the state, so they are formed while the state loads are in flight:
+  // without the front end both blocks' sets up front, with it (which holds
+  // more registers) each block's own just before it.
+  struct Coef {
+    float cum[G], Gam[G], ckk[NKK > 0 ? NKK : 1], ckq[NKQ];
+  };
+  auto coef_of = [&](const int t0) __attribute__((always_inline)) {
+    Coef cf;
     {
       float acc = 0.0f;
 #pragma unroll
       for (int t = 0; t < G; ++t) {
         acc += s_la[t0 + t];
-        cum[t] = acc;
-        Gam[t] = __expf(acc);
+        cf.cum[t] = uniform(acc);
+        cf.Gam[t] = uniform(__expf(acc));
       }
     }
-    // Gram entries, summed by every wave on its own (lane l takes rows l,
-    // l + 64, ...), then their coefficients D_ti beta_i (k_i . x_t), which
-    // are uniform. Needs no state, so for the first block it runs while the
-    // state loads are in flight.
-    float ckk[NKK > 0 ? NKK : 1], ckq[NKQ];
-    {
-      float gk[NKK > 0 ? NKK : 1], gq[NKQ];
+    float gk[NKK > 0 ? NKK : 1], gq[NKQ];
 #pragma unroll
-      for (int p = 0; p < NKK; ++p) gk[p] = 0.0f;
+    for (int p = 0; p < NKK; ++p) gk[p] = 0.0f;
 #pragma unroll
-      for (int p = 0; p < NKQ; ++p) gq[p] = 0.0f;
+    for (int p = 0; p < NKQ; ++p) gq[p] = 0.0f;
 #pragma unroll
-      for (int m = 0; m < DK / 64; ++m) {
-        float kr[G], qr[G];
-        lds_read<G>(&skT[lane + 64 * m][t0], kr);
-        lds_read<G>(&sqT[lane + 64 * m][t0], qr);
-#pragma unroll
-        for (int t = 0; t < G; ++t)
-#pragma unroll
-          for (int i = 0; i <= t; ++i) {
-            if (i < t) gk[t * (t - 1) / 2 + i] = fmaf(kr[i], kr[t], gk[t * (t - 1) / 2 + i]);
-            gq[t * (t + 1) / 2 + i] = fmaf(kr[i], qr[t], gq[t * (t + 1) / 2 + i]);
-          }
-      }
-      float bet[G];
-#pragma unroll
-      for (int i = 0; i < G; ++i) bet[i] = s_beta[t0 + i];
+    for (int m = 0; m < DK / 64; ++m) {
+      float kr[G], qr[G];
+      lds_read<G>(&skT[lane + 64 * m][t0], kr);
+      lds_read<G>(&sqT[lane + 64 * m][t0], qr);
 #pragma unroll
       for (int t = 0; t < G; ++t)
 #pragma unroll
         for (int i = 0; i <= t; ++i) {
-          // D_ti beta_i = exp(cum_t - cum_i) beta_i
-          const float db = i == t ? bet[i] : __expf(cum[t] - cum[i]) * bet[i];
-          if (i < t) ckk[t * (t - 1) / 2 + i] = uniform(db * lane_sum<0>(gk[t * (t - 1) / 2 + i]));
-          ckq[t * (t + 1) / 2 + i] = uniform(db * lane_sum<0>(gq[t * (t + 1) / 2 + i]));
+          if (i < t) gk[t * (t - 1) / 2 + i] = fmaf(kr[i], kr[t], gk[t * (t - 1) / 2 + i]);
+          gq[t * (t + 1) / 2 + i] = fmaf(kr[i], qr[t], gq[t * (t + 1) / 2 + i]);
         }
     }
-    // keep the scheduler from sinking the Gram work below the state's dot
-    // products, where it would wait for the state and hold registers
-    __builtin_amdgcn_sched_barrier(0);
+    float bet[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) bet[i] = s_beta[t0 + i];
+#pragma unroll
+    for (int t = 0; t < G; ++t)
+#pragma unroll
+      for (int i = 0; i <= t; ++i) {
+        // D_ti beta_i = exp(cum_t - cum_i) beta_i
+        const float db = i == t ? bet[i] : __expf(cf.cum[t] - cf.cum[i]) * bet[i];
+        if (i < t) cf.ckk[t * (t - 1) / 2 + i] = uniform(db * lane_sum<0>(gk[t * (t - 1) / 2 + i]));
+        cf.ckq[t * (t + 1) / 2 + i] = uniform(db * lane_sum<0>(gq[t * (t + 1) / 2 + i]));
+      }
+    return cf;
+  };
+
+  auto block = [&](const int b, const Coef &cf) __attribute__((always_inline)) {
+    const int t0 = b * G;
+    const float *cum = cf.cum, *Gam = cf.Gam, *ckk = cf.ckk, *ckq = cf.ckq;
 
     // s_j . k_t and s_j . q_t over this lane's rows, summed over row groups
     float dk_[G][4], dq_[G][4];
@@ -829,12 +834,30 @@ __global__ __launch_bounds__(256, FUSED ? 3 : 4) void decode_block_kernel(const 
                                                m * kRowStep, 2);
     }
   };
-  // block 0 is peeled off the loop: entering the loop with the freshly
-  // loaded state made the compiler copy all of it into separate
-  // loop-carried registers, which costs occupancy
-  block(0);
-  for (int b = 1; b < n_blk; ++b) block(b);
+  // the scheduler must not sink the coefficient work below the state's dot
+  // products, where it would wait for the state and hold registers
+  if constexpr (FUSED) {
+    {
+      const Coef cf = coef_of(0);
+      __builtin_amdgcn_sched_barrier(0);
+      block(0, cf);
+    }
+    if (n_blk > 1) {
+      const Coef cf = coef_of(G);
+      __builtin_amdgcn_sched_barrier(0);
+      block(1, cf);
+    }
+  } else {
+    const Coef cf0 = coef_of(0);
+    Coef cf1 = cf0;
+    if (n_blk > 1) cf1 = coef_of(G);
+    __builtin_amdgcn_sched_barrier(0);
+    block(0, cf0);
+    if (n_blk > 1) block(1, cf1);
+  }
 }
+
+constexpr unsigned kFusedLdsPad = 30000;  // bytes of dynamic LDS, see launch()
 
 template <int DK, int DV, typename TIN, typename TOUT, bool FUSED>
 static hipError_t launch(const DecodeArgs &a) {
@@ -845,8 +868,12 @@ static hipError_t launch(const DecodeArgs &a) {
     hipLaunchKernelGGL((decode_token_kernel<DK, DV, TIN, TOUT, FUSED>), dim3(units), dim3(256), 0,
                        a.stream, a);
   else
-    hipLaunchKernelGGL((decode_block_kernel<DK, DV, TIN, TOUT, FUSED>), dim3(units), dim3(256), 0,
-                       a.stream, a);
+    // The fused d = 128 variant runs faster with three workgroups per CU than
+    // with the four its registers allow (195 against 205 us for 256 x 32
+    // states and 4 tokens; the plain variant is fastest at four): unused
+    // dynamic LDS, 45 KiB per workgroup in all, keeps the fourth off.
+    hipLaunchKernelGGL((decode_block_kernel<DK, DV, TIN, TOUT, FUSED>), dim3(units), dim3(256),
+                       FUSED && DK == 128 ? kFusedLdsPad : 0u, a.stream, a);
   return hipGetLastError();
 }
 
