@@ -216,8 +216,8 @@ def bench_backward(g, steps=5, warmup=1):
     dev = torch.device("cuda", 0)
     d = {k: inp[k].to(dev) for k in ("q", "k", "v", "log_alpha", "beta")}
     dy = gi.normal((tokens, H, dv), 13, 40).to(torch.bfloat16).to(dev)
-    ws = torch.empty(g.gdn_chunk_bwd_workspace_size(tokens, N, H, dk, dv), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(g.gdn_chunk_bwd_workspace_size(tokens, N, H, dk, dv, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():

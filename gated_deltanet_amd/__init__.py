@@ -83,7 +83,7 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_decode_fused.argtypes = [vp, vp, vp, fp, vp, fp, fp, fp, fp, fp, ip, i32, vp, fp, f32,
                                      f32, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.gdn_decode_fused.restype = ctypes.c_int
-    lib.gdn_chunk_bwd_workspace_size.argtypes = [i64, i32, i32, i32, i32]
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
     lib.gdn_chunk_bwd_workspace_size.restype = sz
     lib.gdn_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, ip, i32, i32, i32, i32, i32,
                                   vp, vp, vp, fp, fp, fp, i32, i32, vp, sz, vp]
@@ -329,8 +329,11 @@ def gdn_chunk_fwd_segmented_noalloc(q, k, v, log_alpha, beta, segments, S0=None,
     return y, S_T
 
 
-def gdn_chunk_bwd_workspace_size(rows: int, N: int, H: int, dk: int, dv: int) -> int:
-    return int(load_library().gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv))
+def gdn_chunk_bwd_workspace_size(rows: int, N: int, H: int, dk: int, dv: int,
+                                 in_dtype=torch.bfloat16) -> int:
+    """Workspace bytes of gdn_chunk_bwd / gdn_chunk_bwd_gated for inputs of
+    in_dtype (fp32 inputs keep fp32 chunk-start states, 16-bit ones fp16)."""
+    return int(load_library().gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv, _dt(in_dtype)))
 
 
 def gdn_chunk_bwd(q, k, v, log_alpha, beta, dy, S0=None, dS_T=None, cu_seqlens=None, N=None,
@@ -354,7 +357,7 @@ def gdn_chunk_bwd(q, k, v, log_alpha, beta, dy, S0=None, dS_T=None, cu_seqlens=N
                    (S0, "S0"), (dy, "dy"), (dS_T, "dS_T"), (cu_seqlens, "cu_seqlens"),
                    (workspace, "workspace"))
     rows = q.numel() // (H * dk)
-    need = gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv)
+    need = gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv, in_dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     dq = torch.empty(q.shape, dtype=grad_dtype, device=dev)
@@ -391,7 +394,7 @@ def gdn_chunk_bwd_gated(q, k, v, a, b, A, dy, b_alpha=None, S0=None, dS_T=None,
                    (b_alpha, "b_alpha"), (S0, "S0"), (dy, "dy"), (dS_T, "dS_T"),
                    (cu_seqlens, "cu_seqlens"), (workspace, "workspace"))
     rows = q.numel() // (H * dk)
-    need = gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv)
+    need = gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv, in_dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     dq = torch.empty(q.shape, dtype=grad_dtype, device=dev)

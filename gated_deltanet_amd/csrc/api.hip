@@ -765,11 +765,11 @@ GDN_API int gdn_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void
 }
 
 GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t rows, int32_t N, int32_t H, int32_t dk,
-                                            int32_t dv) {
+                                            int32_t dv, int32_t in_dtype) {
   if (rows < 0 || N < 0 || H <= 0 || !head_size_ok(dk) || !head_size_ok(dv) ||
-      rows * H * (dk > dv ? dk : dv) >= (int64_t{1} << 40))
+      !dtype_ok(in_dtype) || rows * H * (dk > dv ? dk : dv) >= (int64_t{1} << 40))
     return 0;
-  return gdn::chunk_bwd_workspace_size(rows, N, H, dk, dv);
+  return gdn::chunk_bwd_workspace_size(rows, N, H, dk, dv, in_dtype);
 }
 
 }  // extern "C"
@@ -793,7 +793,7 @@ int chunk_bwd_impl(const void *q, const void *k, const void *v, const float *log
     return fail(GDN_ERR_INVALID_ARG, "%s", "N * H too large");
   if (rows * H * (dk > dv ? dk : dv) >= (int64_t{1} << 40))
     return fail(GDN_ERR_INVALID_ARG, "%s", "input too large");
-  const size_t need = gdn::chunk_bwd_workspace_size(rows, N, H, dk, dv);
+  const size_t need = gdn::chunk_bwd_workspace_size(rows, N, H, dk, dv, in_dtype);
   if (N > 0 && (!workspace || workspace_bytes < need))
     return fail(GDN_ERR_INVALID_ARG, "%s",
                 "workspace missing or smaller than gdn_chunk_bwd_workspace_size()");
@@ -869,8 +869,10 @@ int chunk_bwd_impl(const void *q, const void *k, const void *v, const float *log
   a.dbeta = dbeta;
   a.dS0 = dS0;
   a.ws_states = static_cast<float *>(workspace);
-  a.ws_part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                        gdn::chunk_bwd_states_bytes(rows, N, H, dk, dv));
+  const gdn::BwdLayout lay = gdn::chunk_bwd_layout(rows, N, H, dk, dv, in_dtype);
+  a.ws_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.part);
+  a.ws_carry = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.carry);
+  a.run_off = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + lay.table);
   a.A = A;
   a.b_alpha = A ? b_alpha : nullptr;
   a.dA = dA;

@@ -34,6 +34,7 @@
 // accumulation). The work is split into phases separated by workgroup
 // barriers, each phase's 16x16 output tiles dealt round-robin to the sixteen
 // waves (four per SIMD).
+#include <cstdlib>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -167,6 +168,93 @@ __device__ __forceinline__ void raw16_to_f32(const u32x4 r, float *x) {
   }
 }
 
+// Sequence n's rows [bos, bos + len), the offsets clamped to [0, T].
+__device__ __forceinline__ void seq_rows(const BwdArgs &a, int n, int64_t &bos, int64_t &len) {
+  if (a.cu_seqlens) {
+    int64_t s0 = a.cu_seqlens[n], s1 = a.cu_seqlens[n + 1];
+    s0 = s0 < 0 ? 0 : (s0 > a.T ? a.T : s0);
+    s1 = s1 < s0 ? s0 : (s1 > a.T ? a.T : s1);
+    bos = s0;
+    len = s1 - s0;
+  } else {
+    bos = static_cast<int64_t>(n) * a.T;
+    len = a.T;
+  }
+}
+
+// The chunks [c_lo, c_hi) of a sequence (first row bos, nc chunks) that run
+// j sweeps (see BwdArgs::runs). Every chunk falls in exactly one run, and a
+// later run never holds an earlier chunk.
+__device__ __forceinline__ void run_chunks(const BwdArgs &a, int j, int64_t bos, int nc, int &c_lo,
+                                           int &c_hi) {
+  auto first = [&](int r) -> int {  // first chunk of run r
+    if (r <= 0) return 0;
+    if (r >= a.runs) return nc;
+    if (a.run_rows == 0) return static_cast<int>(static_cast<int64_t>(r) * nc / a.runs);
+    const int64_t row = static_cast<int64_t>(r) * a.run_rows;
+    if (row <= bos) return 0;
+    if (row >= bos + static_cast<int64_t>(nc) * kC) return nc;
+    return static_cast<int>((row - bos + kC - 1) / kC);
+  };
+  c_lo = first(j);
+  c_hi = first(j + 1);
+}
+
+// Rows a sequence (len rows, nc chunks) contributes to run j.
+__device__ __forceinline__ int64_t run_seq_rows(const BwdArgs &a, int j, int64_t bos, int64_t len,
+                                                int nc) {
+  int c_lo, c_hi;
+  run_chunks(a, j, bos, nc, c_lo, c_hi);
+  if (c_lo >= c_hi) return 0;
+  const int64_t end = static_cast<int64_t>(c_hi) * kC;
+  return (end < len ? end : len) - static_cast<int64_t>(c_lo) * kC;
+}
+
+// Whether the runs' sequence offsets come from the run_off table: with
+// more than one run, unless every sequence gives every run as many rows
+// (equal lengths, proportional runs).
+__device__ __host__ __forceinline__ bool run_table(const BwdArgs &a) {
+  return a.runs > 1 && (a.cu_seqlens || a.run_rows > 0);
+}
+
+// Where sequence n's rows of run a.run start among the run's partial sums.
+__device__ __forceinline__ int64_t run_seq_offset(const BwdArgs &a, int n, int64_t bos) {
+  if (a.runs == 1) return bos;
+  if (run_table(a)) return a.run_off[static_cast<size_t>(a.run) * (a.N + 1) + n];
+  return static_cast<int64_t>(n) * run_seq_rows(a, a.run, 0, a.T, (a.T + kC - 1) / kC);
+}
+
+// Row j of the run offsets (see run_table): an exclusive scan
+// of the sequences' row counts in run j = blockIdx.x, the total last.
+__global__ __launch_bounds__(256) void run_offsets_kernel(const BwdArgs a) {
+  const int j = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ int64_t sc[256];
+  int64_t carry = 0;
+  for (int base = 0; base < a.N; base += 256) {
+    const int n = base + tid;
+    int64_t cnt = 0;
+    if (n < a.N) {
+      int64_t bos, len;
+      seq_rows(a, n, bos, len);
+      cnt = run_seq_rows(a, j, bos, len, static_cast<int>((len + kC - 1) / kC));
+    }
+    sc[tid] = cnt;
+    __syncthreads();
+    for (int w = 1; w < 256; w <<= 1) {  // inclusive scan
+      const int64_t x = tid >= w ? sc[tid - w] : 0;
+      __syncthreads();
+      sc[tid] += x;
+      __syncthreads();
+    }
+    if (n < a.N)
+      a.run_off[static_cast<size_t>(j) * (a.N + 1) + n] = static_cast<int32_t>(carry + sc[tid] - cnt);
+    carry += sc[255];
+    __syncthreads();
+  }
+  if (tid == 0) a.run_off[static_cast<size_t>(j) * (a.N + 1) + a.N] = static_cast<int32_t>(carry);
+}
+
 template <int DK, typename TIN, typename TG>
 __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   constexpr int C = kC, DVT = kDVT, LDV = kLDV, LDC = kLDC;
@@ -229,17 +317,13 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   const int h = unit % H;
   const int n = unit / H;
   int64_t bos, len;
-  if (a.cu_seqlens) {
-    int64_t s0 = a.cu_seqlens[n], s1 = a.cu_seqlens[n + 1];
-    s0 = s0 < 0 ? 0 : (s0 > a.T ? a.T : s0);
-    s1 = s1 < s0 ? s0 : (s1 > a.T ? a.T : s1);
-    bos = s0;
-    len = s1 - s0;
-  } else {
-    bos = static_cast<int64_t>(n) * a.T;
-    len = a.T;
-  }
+  seq_rows(a, n, bos, len);
   const int nc = static_cast<int>((len + C - 1) / C);
+  // this run's chunks, and the partial-sum row of sequence row t: t + pbase
+  int c_lo, c_hi;
+  run_chunks(a, a.run, bos, nc, c_lo, c_hi);
+  const int64_t pbase =
+      c_lo < c_hi ? run_seq_offset(a, n, bos) - bos - static_cast<int64_t>(c_lo) * C : 0;
   // chunk-state slots of this sequence: floor(bos / C) + n + c never
   // collide between sequences and stay below rows / C + N
   const int64_t slot0 = bos / C + n;
@@ -265,13 +349,32 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   const int v0 = vt * DVT;
   const size_t state_sz = static_cast<size_t>(DK) * DV;
   float *const ws_states = a.ws_states;
-  const size_t part_stride = static_cast<size_t>(a.rows) * H;  // per tile, in rows*H
+  const size_t part_stride = static_cast<size_t>(a.part_rows) * H;  // per tile, in rows*H
+  // the state gradient of this tile between runs, [DK][DVT]
+  float *const carry = a.ws_carry + (static_cast<size_t>(unit) * n_vt + vt) * (DK * DVT);
+  if (c_lo == c_hi) {
+    // no chunk in this run; a sequence without chunks gets dS0 = dS_T from
+    // run 0
+    if (nc == 0 && a.run == 0 && a.dS0)
+      for (int idx = tid; idx < DK * DVT; idx += kNT) {
+        const int r = idx / DVT, cc = idx % DVT;
+        const size_t o = static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc;
+        a.dS0[o] = a.dS_T ? a.dS_T[o] : 0.0f;
+      }
+    return;
+  }
 
   const RawGate gate = RawGate::load(a.A, a.b_alpha, h);
   // chunk-start state tiles in the workspace, [slot][head][column tile] blocks
-  // of DK x DVT floats in the accumulator order of state_row()
-  auto state_tile = [&](int c) {
-    return ws_states + ((static_cast<size_t>(slot0 + c) * H + h) * n_vt + vt) * (DK * DVT);
+  // of DK x DVT values in the accumulator order of state_row(): fp32 (rebuilt
+  // here) with fp32 inputs, fp16 (from the prefill kernel) with 16-bit ones
+  const size_t tile_idx0 = (static_cast<size_t>(slot0) * H + h) * n_vt + vt;
+  auto state_tile = [&](int c) {  // fp32 inputs
+    return ws_states + (tile_idx0 + static_cast<size_t>(c) * H * n_vt) * (DK * DVT);
+  };
+  auto state_tile16 = [&](int c) {  // 16-bit inputs
+    return reinterpret_cast<const _Float16 *>(ws_states) +
+           (tile_idx0 + static_cast<size_t>(c) * H * n_vt) * (DK * DVT);
   };
   // element e of the f32x4 with index idx of a state block: row and column
   auto state_rc = [&](int idx, int e, int &r, int &cc) {
@@ -302,9 +405,11 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   static_assert(VOFF + VP <= kNT && GOFF + GP <= kNT && VI == 1 && GI == 1,
                 "V and dY pieces fit the workgroup once");
   constexpr int kGateWave = kNW - 1;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   struct Pre {
     u32x4 k[KI], q[KI], v[VI], dy[GI];
-    f32x4 s[SI];
+    f32x4 s[H16 ? 1 : SI];   // fp32 state pieces
+    u32x2 sh[H16 ? SI : 1];  // fp16 state pieces (four values each)
     float la, bt;
   };
   const u32x4 zero_raw = {0u, 0u, 0u, 0u};
@@ -366,12 +471,22 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     }
     if (with_state) {
       // streamed once: non-temporal
-      const auto rs = rsrc(state_tile(c), DK * DVT * 4);
+      if constexpr (H16) {
+        const auto rs = rsrc(state_tile16(c), DK * DVT * 2);
 #pragma unroll
-      for (int i = 0; i < SI; ++i) {
-        const int idx = tid + kNT * i;
-        const uint32_t off = idx < DK * DVT / 4 ? static_cast<uint32_t>(16 * idx) : kNone;
-        p.s[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
+        for (int i = 0; i < SI; ++i) {
+          const int idx = tid + kNT * i;
+          const uint32_t off = idx < DK * DVT / 4 ? static_cast<uint32_t>(8 * idx) : kNone;
+          p.sh[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 2));
+        }
+      } else {
+        const auto rs = rsrc(state_tile(c), DK * DVT * 4);
+#pragma unroll
+        for (int i = 0; i < SI; ++i) {
+          const int idx = tid + kNT * i;
+          const uint32_t off = idx < DK * DVT / 4 ? static_cast<uint32_t>(16 * idx) : kNone;
+          p.s[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
+        }
       }
     }
     p.la = 0.0f;
@@ -436,7 +551,12 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
           for (int e = 0; e < 4; ++e) {
             int r, cc;
             state_rc(idx, e, r, cc);
-            Ss[r * LDV + cc] = p.s[i][e];
+            if constexpr (H16) {
+              typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+              Ss[r * LDV + cc] = static_cast<float>(__builtin_bit_cast(f16x4, p.sh[i])[e]);
+            } else {
+              Ss[r * LDV + cc] = p.s[i][e];
+            }
           }
         }
       }
@@ -536,6 +656,9 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
   // running state.
   Pre pf;
   if constexpr (!H16) {
+  // (once per sequence: in the run that holds its last chunk, the first of
+  // the runs that touch it)
+  if (c_hi == nc) {
   for (int idx = tid; idx < DK * DVT; idx += kNT) {
     const int r = idx / DVT, cc = idx % DVT;
     Ss[r * LDV + cc] = a.S0 ? a.S0[static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc] : 0.0f;
@@ -622,12 +745,17 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     __syncthreads();
   }
   }
+  }
 
   // ======================= backward sweep ================================
+  // from dS_T in the run that holds the sequence's last chunk, else from the
+  // state gradient the previous run left
   for (int idx = tid; idx < DK * DVT; idx += kNT) {
     const int r = idx / DVT, cc = idx % DVT;
     dSs[r * LDV + cc] =
-        a.dS_T ? a.dS_T[static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc] : 0.0f;
+        c_hi < nc ? carry[idx]
+                  : (a.dS_T ? a.dS_T[static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc]
+                            : 0.0f);
   }
   // dbeta and d log alpha of a finished chunk (first row t0c, nv valid rows,
   // gamma_C = gC) from the row and column sums its phases left in LDS; run
@@ -669,15 +797,15 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     rs += gC * sred;
     if (r < nv) {
       float *dst = a.ws_part + static_cast<size_t>(2) * n_vt * part_stride * DK;
-      dst[(static_cast<size_t>(vt) * 2) * part_stride + (t0c + r) * H + h] = s_db[r];
-      dst[(static_cast<size_t>(vt) * 2 + 1) * part_stride + (t0c + r) * H + h] = rs;
+      dst[(static_cast<size_t>(vt) * 2) * part_stride + (t0c + r + pbase) * H + h] = s_db[r];
+      dst[(static_cast<size_t>(vt) * 2 + 1) * part_stride + (t0c + r + pbase) * H + h] = rs;
     }
   };
   int64_t prev_t0 = 0;
   int prev_valid = 0;
   float prev_gamC = 0.0f;
-  if (nc > 0) fetch(pf, nc - 1, true, true, true);
-  for (int c = nc - 1; c >= 0; --c) {
+  fetch(pf, c_hi - 1, true, true, true);
+  for (int c = c_hi - 1; c >= c_lo; --c) {
     opaque_lanes();
     const int64_t t0 = bos + static_cast<int64_t>(c) * C;
     const int valid = rows_valid(c);
@@ -714,7 +842,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       }
     };
     if (wave == 15) {
-      if (c < nc - 1) gate_grads(prev_t0, prev_valid, prev_gamC);
+      if (c < c_hi - 1) gate_grads(prev_t0, prev_valid, prev_gamC);
     } else if (wave == 11 || wave == 13) {
       prio(true);
       gram_tile(wave == 11 ? 0 : 2);
@@ -911,7 +1039,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     // the next chunk's inputs, fetched before this phase's partial stores:
     // a later wait for a store (before its data registers are reused) would
     // also wait for loads issued after it
-    if (c > 0) fetch(pf, c - 1, true, true, true);
+    if (c > c_lo) fetch(pf, c - 1, true, true, true);
 
     // ---- P5: partial dQ and dK, one (row tile, key tile) pair per wave --
     // The pair's dQ and dK tiles share the S row fragment (dY S^T, dX S^T)
@@ -961,7 +1089,7 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
       ld_row(fa, Mm, LDC, r, 0);
       mma(acc2, fK, fa);
       if (r < valid) {
-        const size_t o = ((t0 + r) * H + h) * DK + k4;
+        const size_t o = ((t0 + r + pbase) * H + h) * DK + k4;
         *reinterpret_cast<f32x4 *>(a.ws_part + static_cast<size_t>(vt) * part_stride * DK + o) = acc;
         *reinterpret_cast<f32x4 *>(a.ws_part + (static_cast<size_t>(n_vt) + vt) * part_stride * DK +
                                    o) = acc2;
@@ -1025,26 +1153,65 @@ __global__ __launch_bounds__(kNT) void chunk_bwd_kernel(const BwdArgs a) {
     prev_gamC = gamC;
     __syncthreads();
   }
-  if (nc > 0 && wave == kNW - 1) gate_grads(prev_t0, prev_valid, prev_gamC);
-  // dS0 for this tile
-  if (a.dS0) {
+  if (wave == kNW - 1) gate_grads(prev_t0, prev_valid, prev_gamC);
+  // dS0 for this tile after the sequence's first chunk, else the carry to
+  // the next run
+  if (c_lo == 0) {
+    if (a.dS0)
+      for (int idx = tid; idx < DK * DVT; idx += kNT) {
+        const int r = idx / DVT, cc = idx % DVT;
+        a.dS0[static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc] = dSs[r * LDV + cc];
+      }
+  } else {
     for (int idx = tid; idx < DK * DVT; idx += kNT) {
       const int r = idx / DVT, cc = idx % DVT;
-      a.dS0[static_cast<size_t>(unit) * state_sz + r * DV + v0 + cc] = dSs[r * LDV + cc];
+      carry[idx] = dSs[r * LDV + cc];
     }
   }
 }
 
+// The sequence row of partial-sum row p of run a.run, or -1 for a row that
+// holds nothing.
+__device__ __forceinline__ int64_t run_row(const BwdArgs &a, int64_t p) {
+  if (a.runs == 1) return p < a.rows ? p : -1;
+  int n;
+  int64_t off;
+  if (run_table(a)) {
+    // the last sequence whose rows start at or before p
+    const int32_t *o = a.run_off + static_cast<size_t>(a.run) * (a.N + 1);
+    if (p >= o[a.N]) return -1;
+    int lo = 0, hi = a.N;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (o[mid] <= p) lo = mid;
+      else hi = mid;
+    }
+    n = lo;
+    off = o[lo];
+  } else {
+    const int64_t per = run_seq_rows(a, a.run, 0, a.T, (a.T + kC - 1) / kC);
+    if (per == 0 || p >= per * a.N) return -1;
+    n = static_cast<int>(p / per);
+    off = per * n;
+  }
+  int64_t bos, len;
+  seq_rows(a, n, bos, len);
+  int c_lo, c_hi;
+  run_chunks(a, a.run, bos, static_cast<int>((len + kC - 1) / kC), c_lo, c_hi);
+  return bos + static_cast<int64_t>(c_lo) * kC + (p - off);
+}
+
 // Sum of the column tiles' partial dq, dk (C x dk rows) and dbeta, dlog
-// alpha, in tile order.
+// alpha, in tile order, for the rows of one run.
 template <int DK, int NVT, typename TG>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
   constexpr int n_vt = NVT;  // column tiles (dv / 32)
-  const size_t part_stride = static_cast<size_t>(a.rows) * a.H;
+  const size_t part_stride = static_cast<size_t>(a.part_rows) * a.H;
   const size_t total_k = part_stride * DK;
   const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   // dq, dk: four consecutive elements per thread (16-byte partial loads)
-  if (4 * i < total_k) {
+  const int64_t rk = 4 * i < total_k ? run_row(a, static_cast<int64_t>(4 * i / (a.H * DK))) : -1;
+  if (rk >= 0) {
     // every partial is read once: all loads issued before the sums, streamed
     f32x4 pq[NVT], pk[NVT];
 #pragma unroll
@@ -1060,8 +1227,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
       sq += pq[t];
       sk += pk[t];
     }
-    TG *dq = static_cast<TG *>(a.dq) + 4 * i;
-    TG *dk = static_cast<TG *>(a.dk) + 4 * i;
+    const size_t o = static_cast<size_t>(rk) * a.H * DK + 4 * i % (static_cast<size_t>(a.H) * DK);
+    TG *dq = static_cast<TG *>(a.dq) + o;
+    TG *dk = static_cast<TG *>(a.dk) + o;
     if constexpr (sizeof(TG) == 4) {
       *reinterpret_cast<f32x4 *>(dq) = sq;
       *reinterpret_cast<f32x4 *>(dk) = sk;
@@ -1079,6 +1247,13 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
   }
   if (i < part_stride) {
     float *g = a.ws_part + static_cast<size_t>(2) * n_vt * total_k;
+    const int64_t rg = run_row(a, static_cast<int64_t>(i / a.H));
+    if (rg < 0) {
+      // rows that hold nothing add nothing to the per-head sums
+      if (a.A) g[i] = g[part_stride + i] = 0.0f;
+      return;
+    }
+    const size_t gi = static_cast<size_t>(rg) * a.H + i % a.H;
     float sb = 0.0f, sl = 0.0f;
     for (int t = 0; t < n_vt; ++t) {
       sb += g[(static_cast<size_t>(t) * 2) * part_stride + i];
@@ -1088,19 +1263,19 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
       // chain rule through log alpha = -e^A softplus(a + b_alpha) and
       // beta = sigmoid(b); the per-row terms of dA and db_alpha go over
       // tile 0's partials (this thread has read them) for the head sums
-      const int h = static_cast<int>(i % a.H);
+      const int h = static_cast<int>(gi % a.H);
       const RawGate gate = RawGate::load(a.A, a.b_alpha, h);
-      const float x = a.log_alpha[i] + gate.bias;
+      const float x = a.log_alpha[gi] + gate.bias;
       const float sig = 1.0f / (1.0f + expf(-x));
       const float da = sl * (-gate.scale * sig);
-      const float bt = RawGate::beta(a.beta[i]);
-      a.dbeta[i] = sb * bt * (1.0f - bt);
-      a.dlog_alpha[i] = da;
-      g[i] = sl * gate.log_alpha(a.log_alpha[i]);
+      const float bt = RawGate::beta(a.beta[gi]);
+      a.dbeta[gi] = sb * bt * (1.0f - bt);
+      a.dlog_alpha[gi] = da;
+      g[i] = sl * gate.log_alpha(a.log_alpha[gi]);
       g[part_stride + i] = da;
     } else {
-      a.dbeta[i] = sb;
-      a.dlog_alpha[i] = sl;
+      a.dbeta[gi] = sb;
+      a.dlog_alpha[gi] = sl;
     }
   }
 }
@@ -1110,10 +1285,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a) {
 __global__ __launch_bounds__(256) void head_sum_kernel(const BwdArgs a) {
   const int h = blockIdx.x;
   const int n_vt = a.dv_size / kDVT;
-  const size_t part_stride = static_cast<size_t>(a.rows) * a.H;
+  const size_t part_stride = static_cast<size_t>(a.part_rows) * a.H;
   const float *g = a.ws_part + static_cast<size_t>(2) * n_vt * part_stride * a.dk_size;
   float s0 = 0.0f, s1 = 0.0f;
-  for (int64_t r = threadIdx.x; r < a.rows; r += 256) {
+  for (int64_t r = threadIdx.x; r < a.part_rows; r += 256) {
     s0 += g[r * a.H + h];
     s1 += g[part_stride + r * a.H + h];
   }
@@ -1128,11 +1303,60 @@ __global__ __launch_bounds__(256) void head_sum_kernel(const BwdArgs a) {
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    a.dA[h] = red[0][0];
-    a.db_alpha[h] = red[1][0];
+  if (threadIdx.x == 0) {  // the runs' sums are added in run order
+    const bool first = a.run == a.runs - 1;
+    a.dA[h] = (first ? 0.0f : a.dA[h]) + red[0][0];
+    a.db_alpha[h] = (first ? 0.0f : a.db_alpha[h]) + red[1][0];
   }
 }
+
+}  // namespace
+
+// Runs of the backward: the column tiles' partial sums are kept for one run
+// at a time, at most about kBwdPartBytes of them (some 2 000 rows at H = 16,
+// d = 128); a problem whose partials fit is one run. Runs that take the same
+// share of every sequence keep every sequence busy in every run; they are
+// used while a chunk of every sequence is a small part of a run, and runs of
+// consecutive rows (which hold many short sequences each) otherwise.
+constexpr size_t kBwdPartBytes = size_t{128} << 20;
+
+BwdSegPlan bwd_seg_plan(int64_t rows, int N, int H, int dk, int dv) {
+  const size_t per_row = static_cast<size_t>(dv / kDVT) * H * (2 * dk + 2) * sizeof(float);
+  BwdSegPlan p{1, 0, rows < 0 ? 0 : rows};
+  if (rows <= 0 || N <= 0 || per_row == 0) return p;
+  // GDN_BWD_RUNS (proportional runs) or GDN_BWD_SEGMENT_ROWS (runs of that
+  // many rows, rounded down to whole chunks) set the runs instead, so that
+  // tests reach both forms on small problems
+  int64_t runs = 0, seg = 0;
+  if (const char *e = getenv("GDN_BWD_RUNS")) runs = atoll(e);
+  if (const char *e = getenv("GDN_BWD_SEGMENT_ROWS")) seg = atoll(e) / kC * kC;
+  const int64_t cap = static_cast<int64_t>(kBwdPartBytes / per_row);
+  const int64_t padded = rows + static_cast<int64_t>(N) * (kC - 1);  // rows in whole chunks, at most
+  if (runs <= 0 && seg <= 0) {
+    if (rows <= cap) return p;
+    if (2 * static_cast<int64_t>(N) * kC <= cap)
+      runs = (padded + cap - static_cast<int64_t>(N) * kC - 1) / (cap - static_cast<int64_t>(N) * kC);
+    else
+      seg = cap - kC;
+  }
+  if (runs > 0) {
+    if (runs == 1) return p;
+    // a sequence gives a run at most ceil(nc / runs) chunks
+    p.runs = static_cast<int>(runs);
+    const int64_t bound = (padded + runs - 1) / runs + static_cast<int64_t>(N) * kC;
+    p.part_rows = bound < rows ? bound : rows;
+    return p;
+  }
+  seg = seg < kC ? kC : seg / kC * kC;
+  if (seg >= rows) return p;
+  p.run_rows = seg;
+  p.runs = static_cast<int>((rows + seg - 1) / seg);
+  // a chunk that starts in a run's rows may end up to C - 1 rows past them
+  p.part_rows = seg + kC < rows ? seg + kC : rows;
+  return p;
+}
+
+namespace {
 
 template <int DK, typename TIN, typename TG>
 hipError_t launch_bwd_t(const BwdArgs &a) {
@@ -1165,26 +1389,46 @@ hipError_t launch_bwd_t(const BwdArgs &a) {
       const hipError_t e = launch_chunk_fwd_states(f);
       if (e != hipSuccess) return e;
     }
-    const int64_t blocks = (units + 7) / 8 * 8 * n_vt;
-    hipLaunchKernelGGL((chunk_bwd_kernel<DK, TIN, TG>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kNT), 0, a.stream, a);
+  }
+  // the sweep, the tile reduction and the per-head sums once per run, the
+  // last chunks first (the state gradient flows backwards)
+  const BwdSegPlan sp = bwd_seg_plan(a.rows, a.N, a.H, DK, a.dv_size);
+  BwdArgs r = a;
+  r.runs = sp.runs;
+  r.run_rows = sp.run_rows;
+  r.part_rows = sp.part_rows;
+  if (run_table(r) && a.N > 0) {
+    hipLaunchKernelGGL(run_offsets_kernel, dim3(sp.runs), dim3(256), 0, a.stream, r);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t total = static_cast<size_t>(a.rows) * a.H * DK;
-  if (total > 0) {
-    // one thread per four dq/dk elements, which also covers the rows * H
-    // gate rows (DK >= 4)
-    const dim3 grid(static_cast<unsigned>((total / 4 + 255) / 256));
-    if (a.dv_size == 128)
-      hipLaunchKernelGGL((bwd_reduce_kernel<DK, 128 / kDVT, TG>), grid, dim3(256), 0, a.stream, a);
-    else
-      hipLaunchKernelGGL((bwd_reduce_kernel<DK, 64 / kDVT, TG>), grid, dim3(256), 0, a.stream, a);
+  for (int j = sp.runs - 1; j >= 0; --j) {
+    BwdArgs b = r;
+    b.run = j;
+    if (units > 0) {
+      const int64_t blocks = (units + 7) / 8 * 8 * n_vt;
+      hipLaunchKernelGGL((chunk_bwd_kernel<DK, TIN, TG>), dim3(static_cast<unsigned>(blocks)),
+                         dim3(kNT), 0, b.stream, b);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    const size_t total = static_cast<size_t>(b.part_rows) * b.H * DK;
+    if (total > 0) {
+      // one thread per four dq/dk elements, which also covers the rows * H
+      // gate rows (DK >= 4)
+      const dim3 grid(static_cast<unsigned>((total / 4 + 255) / 256));
+      if (b.dv_size == 128)
+        hipLaunchKernelGGL((bwd_reduce_kernel<DK, 128 / kDVT, TG>), grid, dim3(256), 0, b.stream, b);
+      else
+        hipLaunchKernelGGL((bwd_reduce_kernel<DK, 64 / kDVT, TG>), grid, dim3(256), 0, b.stream, b);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (b.A) hipLaunchKernelGGL(head_sum_kernel, dim3(b.H), dim3(256), 0, b.stream, b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.A) hipLaunchKernelGGL(head_sum_kernel, dim3(a.H), dim3(256), 0, a.stream, a);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 template <typename TIN, typename TG>
@@ -1204,18 +1448,31 @@ hipError_t launch_bwd_g(const BwdArgs &a) {
 }  // namespace
 
 // Workspace: the chunk-start states (one slot per chunk, floor(bos / C) + n
-// + c for chunk c of sequence n), then the column tiles' partial sums.
-size_t chunk_bwd_states_bytes(int64_t rows, int N, int H, int dk, int dv) {
+// + c for chunk c of sequence n), then the column tiles' partial sums of one
+// run, then (with more than one run) the state gradients carried between
+// runs and the runs' sequence offsets.
+size_t chunk_bwd_states_bytes(int64_t rows, int N, int H, int dk, int dv, int in_dtype) {
   const size_t slots = static_cast<size_t>(rows / kC + N);
-  const size_t states = slots * H * dk * dv * sizeof(float);
+  // fp32 states for fp32 inputs, fp16 for 16-bit inputs
+  const size_t states = slots * H * dk * dv * (in_dtype == 0 ? sizeof(float) : sizeof(_Float16));
   return (states + 255) / 256 * 256;
 }
 
-size_t chunk_bwd_workspace_size(int64_t rows, int N, int H, int dk, int dv) {
-  if (rows < 0 || N < 0 || H <= 0) return 0;
+BwdLayout chunk_bwd_layout(int64_t rows, int N, int H, int dk, int dv, int in_dtype) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const BwdSegPlan p = bwd_seg_plan(rows, N, H, dk, dv);
+  BwdLayout l;
+  l.part = chunk_bwd_states_bytes(rows, N, H, dk, dv, in_dtype);
   const size_t n_vt = static_cast<size_t>(dv / kDVT);
-  const size_t parts = n_vt * static_cast<size_t>(rows) * H * (2 * dk + 2) * sizeof(float);
-  return chunk_bwd_states_bytes(rows, N, H, dk, dv) + (parts + 255) / 256 * 256;
+  l.carry = l.part + up(n_vt * static_cast<size_t>(p.part_rows) * H * (2 * dk + 2) * sizeof(float));
+  l.table = l.carry + (p.runs > 1 ? up(static_cast<size_t>(N) * H * dk * dv * sizeof(float)) : 0);
+  l.total = l.table + (p.runs > 1 ? up(static_cast<size_t>(p.runs) * (N + 1) * sizeof(int32_t)) : 0);
+  return l;
+}
+
+size_t chunk_bwd_workspace_size(int64_t rows, int N, int H, int dk, int dv, int in_dtype) {
+  if (rows < 0 || N < 0 || H <= 0) return 0;
+  return chunk_bwd_layout(rows, N, H, dk, dv, in_dtype).total;
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs &a) {

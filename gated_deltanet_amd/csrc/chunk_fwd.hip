@@ -223,7 +223,7 @@ __device__ __forceinline__ V lds_read16(const char *p) {
   return *reinterpret_cast<const V *>(p);
 }
 
-// STATES: write every chunk-start state to `states` (the backward pass's
+// STATES: write every chunk-start state, in fp16, to `states` (the backward pass's
 // workspace) instead of y and S_T. LPT (packed batches of at most kLptMax
 // sequences): workgroups take the sequences longest first, so the short ones
 // fill in at the end instead of a long one running alone.
@@ -677,9 +677,11 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   }
 
   // chunk-start states for the backward pass (optional): chunk x of sequence
-  // n goes to slot floor(bos / C) + n + x, this wave's slab of the tile
-  float *const st_out =
-      STATES ? states + ((static_cast<size_t>(bos / kC + n) * H + h) * n_vt + vt) * DK * DVT +
+  // n goes to slot floor(bos / C) + n + x, this wave's slab of the tile, in
+  // fp16 (the backward's 16-bit products round the state to fp16 anyway)
+  _Float16 *const st_out =
+      STATES ? reinterpret_cast<_Float16 *>(states) +
+                   ((static_cast<size_t>(bos / kC + n) * H + h) * n_vt + vt) * DK * DVT +
                    (static_cast<size_t>(wave) * NST * 64 + lane) * 4
              : nullptr;
   // byte offset of this lane's first y element inside a chunk's rows
@@ -688,9 +690,15 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
 
   auto state_step = [&](int x) {
     if constexpr (STATES) {
-      float *dst = st_out + static_cast<size_t>(x) * H * n_vt * DK * DVT;
+      typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+      _Float16 *dst = st_out + static_cast<size_t>(x) * H * n_vt * DK * DVT;
 #pragma unroll
-      for (int t = 0; t < NST; ++t) *reinterpret_cast<f32x4 *>(dst + t * 256) = st[t];
+      for (int t = 0; t < NST; ++t) {
+        f16x4 h4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h4[i] = static_cast<_Float16>(st[t][i]);
+        *reinterpret_cast<f16x4 *>(dst + t * 256) = h4;
+      }
     }
     const char *slot = ring + (x % kRing) * L::SLOT;
     const char *pb = procb + (x & 1) * L::PROC;

@@ -117,6 +117,22 @@ struct BwdArgs {
   float *dlog_alpha, *dbeta;      // [rows, H]
   float *dS0;                     // may be null
   float *ws_states, *ws_part;     // workspace (see chunk_bwd_workspace_size)
+  // Runs: the sweep, reduction and head sums run `runs` times, run = runs - 1
+  // first. With run_rows == 0 run j covers chunks floor(j nc / runs) ..
+  // floor((j + 1) nc / runs) - 1 of every sequence (nc its chunk count), so
+  // that every run has work for every long sequence; otherwise it covers the
+  // chunks whose first row lies in [j run_rows, (j + 1) run_rows). A run's
+  // partial sums are kept for part_rows rows, sequence after sequence: with
+  // one run at the sequence's own rows, else from sequence n's offset in
+  // row j of run_off ([runs][N + 1], the last entry the run's row count;
+  // varlen) or from n times the run's common row count (equal lengths).
+  // ws_carry holds the state gradient of every (sequence, head, column
+  // tile) from one run to the next.
+  int runs = 1, run = 0;
+  int64_t run_rows = 0;
+  int32_t *run_off = nullptr;
+  int64_t part_rows = 0;
+  float *ws_carry = nullptr;
   // raw gates: log_alpha / beta then hold a / b, dlog_alpha / dbeta receive
   // da / db, and dA, db_alpha [H] the per-head sums
   const float *A = nullptr, *b_alpha = nullptr;
@@ -154,8 +170,21 @@ hipError_t launch_seg_combine(const float *Nst, const float *Mst, float *Sin, in
                               int dv, int P, hipStream_t stream);
 hipError_t launch_decode_step(const DecodeArgs &a);
 hipError_t launch_chunk_bwd(const BwdArgs &a);
-size_t chunk_bwd_workspace_size(int64_t rows, int N, int H, int dk, int dv);
-size_t chunk_bwd_states_bytes(int64_t rows, int N, int H, int dk, int dv);
+size_t chunk_bwd_workspace_size(int64_t rows, int N, int H, int dk, int dv, int in_dtype);
+size_t chunk_bwd_states_bytes(int64_t rows, int N, int H, int dk, int dv, int in_dtype);
+// Runs of the backward sweep (see BwdArgs::runs).
+struct BwdSegPlan {
+  int runs;           // number of runs
+  int64_t run_rows;   // 0: proportional runs; else rows per run
+  int64_t part_rows;  // rows of partial sums kept per run
+};
+BwdSegPlan bwd_seg_plan(int64_t rows, int N, int H, int dk, int dv);
+// byte offsets of the workspace's parts: partial sums, carried state
+// gradients, run offsets (each 256-byte aligned)
+struct BwdLayout {
+  size_t part, carry, table, total;
+};
+BwdLayout chunk_bwd_layout(int64_t rows, int N, int H, int dk, int dv, int in_dtype);
 hipError_t launch_decode_fused(const DecodeArgs &a);  // dk == dv
 hipError_t launch_frontend(const FrontendArgs &a);
 hipError_t launch_output_gate(const GateArgs &a);

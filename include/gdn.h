@@ -415,9 +415,24 @@ GDN_API int gdn_decode_fused(const void *q_raw, const void *k_raw,
  *   dlog_alpha, dbeta   float32 [rows, H].
  *   dS0           float32 [N, H, dk, dv] or NULL (not written).
  *   workspace     device memory, 256-byte aligned, at least
- *                 gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv) bytes,
- *                 overwritten (it holds the state at every chunk start and
- *                 per-column-tile partial sums).
+ *                 gdn_chunk_bwd_workspace_size(rows, N, H, dk, dv, in_dtype)
+ *                 bytes, overwritten. It holds the state at every chunk start
+ *                 ((rows / 32 + N) * H * dk * dv values: fp32 for fp32
+ *                 inputs, fp16 for 16-bit inputs, whose products round the
+ *                 state to fp16 in any case), the per-column-
+ *                 tile partial sums of dq, dk, dbeta and dlog_alpha for the
+ *                 rows of one run (dv / 32 * H * (2 dk + 2) * 4 bytes per
+ *                 row, about 128 MiB at most: longer problems run the
+ *                 backward sweep several times, the last chunks first,
+ *                 each run taking the same share of every sequence's chunks
+ *                 while 64 N rows fit in the bound, else consecutive rows)
+ *                 and, with more than one run, the state gradient carried
+ *                 between runs (N * H * dk * dv * 4 bytes) and a table of
+ *                 the runs' sequence offsets (runs * (N + 1) * 4 bytes).
+ *                 The environment variables GDN_BWD_RUNS (that many
+ *                 proportional runs) and GDN_BWD_SEGMENT_ROWS (runs of that
+ *                 many rows) set the runs instead: test hooks, to be set
+ *                 before both calls.
  * The states are recomputed from S0 (the forward's outputs are not needed).
  * Precision: with fp32 inputs every product runs in fp32 (fp32 MFMA) and the
  * gradients meet the fp32 bar (relative L2 1e-5); with bf16/fp16 inputs the
@@ -429,7 +444,7 @@ GDN_API int gdn_decode_fused(const void *q_raw, const void *k_raw,
  * Results are deterministic (partial sums are added in a fixed order).
  */
 GDN_API size_t gdn_chunk_bwd_workspace_size(int64_t rows, int32_t N, int32_t H,
-                                            int32_t dk, int32_t dv);
+                                            int32_t dk, int32_t dv, int32_t in_dtype);
 GDN_API int gdn_chunk_bwd(const void *q, const void *k, const void *v,
                           const float *log_alpha, const float *beta,
                           const float *S0, const void *dy, const float *dS_T,

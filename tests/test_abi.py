@@ -252,15 +252,61 @@ def test_decode_fused_rejects(lib):
     assert dec(cs=B + (1 << 28) + 8) == -3
 
 
+def test_chunk_bwd_workspace_run_hooks(lib, monkeypatch):
+    """The run hooks size the partial sums: GDN_BWD_SEGMENT_ROWS (whole
+    chunks) keeps segment + 32 rows, GDN_BWD_RUNS the proportional bound
+    ceil((rows + 31 N) / runs) + 32 N rows; more than one run adds the
+    carried state gradients and the runs' offset table."""
+    i32, sz = ctypes.c_int32, ctypes.c_size_t
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int64, i32, i32, i32, i32, i32]
+    lib.gdn_chunk_bwd_workspace_size.restype = sz
+    monkeypatch.delenv("GDN_BWD_RUNS", raising=False)
+    monkeypatch.delenv("GDN_BWD_SEGMENT_ROWS", raising=False)
+    up = lambda x: (x + 255) // 256 * 256
+    states = (500 // 32 + 3) * 2 * 64 * 64 * 4
+    per_row = 2 * 2 * 130 * 4
+    carry = 3 * 2 * 64 * 64 * 4
+    one = states + up(500 * per_row)
+    assert lib.gdn_chunk_bwd_workspace_size(500, 3, 2, 64, 64, 0) == one
+    monkeypatch.setenv("GDN_BWD_SEGMENT_ROWS", "100")  # -> 96 rows, 6 runs
+    assert lib.gdn_chunk_bwd_workspace_size(500, 3, 2, 64, 64, 0) == (
+        states + up(128 * per_row) + carry + up(6 * 4 * 4))
+    monkeypatch.setenv("GDN_BWD_SEGMENT_ROWS", "1000")  # longer than the problem: one run
+    assert lib.gdn_chunk_bwd_workspace_size(500, 3, 2, 64, 64, 0) == one
+    monkeypatch.delenv("GDN_BWD_SEGMENT_ROWS")
+    monkeypatch.setenv("GDN_BWD_RUNS", "4")  # ceil(593 / 4) + 96 = 245 rows
+    assert lib.gdn_chunk_bwd_workspace_size(500, 3, 2, 64, 64, 0) == (
+        states + up(245 * per_row) + carry + up(4 * 4 * 4))
+    monkeypatch.setenv("GDN_BWD_RUNS", "1")
+    assert lib.gdn_chunk_bwd_workspace_size(500, 3, 2, 64, 64, 0) == one
+
+
 def test_chunk_bwd_rejects(lib):
     v, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-    lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int64, i32, i32, i32, i32]
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int64, i32, i32, i32, i32, i32]
     lib.gdn_chunk_bwd_workspace_size.restype = sz
     lib.gdn_chunk_bwd.argtypes = [v] * 9 + [i32] * 5 + [v] * 6 + [i32, i32, v, sz, v]
-    need = lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 128, 128)
-    # states: (64/32 + 1) slots x 2 heads x 64 KiB; partials: 4 tiles x 64 x 2 x 258 x 4 B
-    assert need == 3 * 2 * 65536 + 4 * 64 * 2 * 258 * 4
-    assert lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 96, 128) == 0
+    need = lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 128, 128, 1)
+    # states: (64/32 + 1) slots x 2 heads x 128 x 128 in fp16 for 16-bit
+    # inputs (fp32 for fp32 inputs); partials: 4 tiles x 64 x 2 x 258 x 4 B
+    assert need == 3 * 2 * 32768 + 4 * 64 * 2 * 258 * 4
+    assert lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 128, 128, 0) == 3 * 2 * 65536 + 4 * 64 * 2 * 258 * 4
+    assert lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 96, 128, 1) == 0
+    assert lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 128, 128, 5) == 0
+    # long problems keep the partial sums of one run at a time (<= 128 MiB)
+    # plus the carried state gradients: B4 H16 T4096 d128 takes 9 runs of
+    # 14 or 15 chunks of every sequence (bound ceil(16508 / 9) + 128 = 1963
+    # rows of partials); with bf16 inputs the whole workspace stays under
+    # 0.5 GB
+    per_row = 4 * 16 * 258 * 4
+    ws = lib.gdn_chunk_bwd_workspace_size(16384, 4, 16, 128, 128, 1)
+    assert ws == 516 * 16 * 32768 + 1963 * per_row + 4 * 16 * 65536 + 256
+    assert ws < 500e6
+    # many short sequences: 34 runs of 1984 consecutive rows (2000 rounded
+    # down to whole chunks), 2016 rows of partials
+    ws = lib.gdn_chunk_bwd_workspace_size(65536, 512, 16, 128, 128, 1)
+    assert ws == ((2048 + 512) * 16 * 32768 + 2016 * per_row + 512 * 16 * 65536 +
+                  (34 * 513 * 4 + 255) // 256 * 256)
 
     def bwd(**kw):
         a = dict(q=A, k=A + (1 << 26), v=A + (2 << 26), la=A + (3 << 26), b=A + (4 << 26),
@@ -297,9 +343,9 @@ def test_conv_state_and_gated_bwd_reject(lib):
     assert lib.gdn_conv_state_from_prefill(A, A + (1 << 20), A + (2 << 20), None, 2, 10, 2, 64,
                                            B, -1, B, 1, None) == -1  # slot table, n_slots < 0
     lib.gdn_chunk_bwd_gated.argtypes = [v] * 11 + [i32] * 5 + [v] * 8 + [i32, i32, v, sz, v]
-    lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int64, i32, i32, i32, i32]
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int64, i32, i32, i32, i32, i32]
     lib.gdn_chunk_bwd_workspace_size.restype = sz
-    need = lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 128, 128)
+    need = lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 128, 128, 1)
     args = [A, A + (1 << 26), A + (2 << 26), A + (3 << 26), A + (4 << 26), None, None, None,
             A + (5 << 26), None, None, 1, 64, 2, 128, 128, B, B + (1 << 24), B + (2 << 24),
             B + (3 << 24), B + (4 << 24), B + (5 << 24), B + (5 << 24) + 64, None, 1, 1,

@@ -764,6 +764,83 @@ def test_chunk_bwd_gated(with_bias):
         assert e <= TOL["bf16"], (nm, e)
 
 
+_RUN_HOOKS = ("GDN_BWD_RUNS", "GDN_BWD_SEGMENT_ROWS")
+
+
+def _one_run_vs_split(monkeypatch, run, hook, value):
+    """run() once as a single run and once split by the hook."""
+    for h in _RUN_HOOKS:
+        monkeypatch.delenv(h, raising=False)
+    one = run()
+    monkeypatch.setenv(hook, str(value))
+    split = run()
+    monkeypatch.delenv(hook)
+    return one, split
+
+
+@gpu
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("hook,value", [("GDN_BWD_RUNS", 3), ("GDN_BWD_RUNS", 9),
+                                        ("GDN_BWD_SEGMENT_ROWS", 32),
+                                        ("GDN_BWD_SEGMENT_ROWS", 96)])
+@pytest.mark.parametrize("varlen", [True, False])
+def test_chunk_bwd_runs_equal_one_run(dtype, hook, value, varlen, monkeypatch):
+    """A backward split into runs (forced small by the hooks; long problems
+    are split to bound the workspace) gives the one-run gradients bit for
+    bit: proportional runs (every sequence in every run, sequences with
+    fewer chunks than runs leaving some runs empty) and runs of consecutive
+    rows (sequences straddling runs), a sequence without rows included, and
+    the oracle's to the bar."""
+    g = _lib()
+    if varlen:
+        inp, dy, dST = _bwd_inputs([1, 31, 32, 33, 100, 0, 65, 200], 2, 64, 64, dtype, seed=150)
+    else:  # equal lengths with a ragged last chunk
+        inp = gi.prefill_inputs(3, 2, 200, 64, 64, dtype, s0_std=0.02, seed=151)
+        dy = gi.normal((600, 2, 64), 151, 40)
+        dST = gi.normal((3, 2, 64, 64), 151, 41)
+    d = to_dev(inp)
+
+    def run():
+        out = g.gdn_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], dy.cuda(),
+                              S0=d["S0"], dS_T=dST.cuda(), cu_seqlens=d["cu_seqlens"],
+                              N=d["N"])
+        torch.cuda.synchronize()
+        return [t.cpu() for t in out]
+
+    one, split = _one_run_vs_split(monkeypatch, run, hook, value)
+    for nm, a, b in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0"), one, split):
+        assert torch.equal(a, b), nm
+    _check_bwd(inp, dy, dST, tol=TOL[dtype])
+
+
+@gpu
+@pytest.mark.parametrize("hook,value", [("GDN_BWD_RUNS", 4), ("GDN_BWD_SEGMENT_ROWS", 64)])
+def test_chunk_bwd_gated_runs(hook, value, monkeypatch):
+    """The raw-gate backward split into runs: per-row gradients as one run
+    bit for bit, the per-head sums dA and db_alpha (added run by run) to
+    fp32 rounding."""
+    g = _lib()
+    inp, dy, dST = _bwd_inputs([70, 33, 1, 130], 2, 64, 64, "bf16", seed=160)
+    rows = inp["q"].shape[0]
+    a, b, A, b_alpha = gi.raw_gates(rows, 2, 161)
+    d = to_dev(inp)
+
+    def run():
+        out = g.gdn_chunk_bwd_gated(d["q"], d["k"], d["v"], a.cuda(), b.cuda(), A.cuda(),
+                                    dy.cuda(), b_alpha=b_alpha.cuda(), S0=d["S0"],
+                                    dS_T=dST.cuda(), cu_seqlens=d["cu_seqlens"])
+        torch.cuda.synchronize()
+        return [t.cpu() for t in out]
+
+    one, split = _one_run_vs_split(monkeypatch, run, hook, value)
+    names = ("dq", "dk", "dv", "da", "db", "dA", "db_alpha", "dS0")
+    for nm, x, y in zip(names, one, split):
+        if nm in ("dA", "db_alpha"):
+            assert rel_l2(y, x.double().numpy()) <= 1e-5, nm
+        else:
+            assert torch.equal(x, y), nm
+
+
 # ---------------------------------------------- prefill -> decode handoff -----
 @gpu
 def test_conv_state_from_prefill_is_the_last_raw_rows():
