@@ -44,6 +44,7 @@
 // rows land that way straight from HBM, the key dimension inside each
 // 32-slice is visited in the order 8*lg + j for lane group lg and slot j, and
 // the state rows are stored in the matching order (see state_row()).
+#include <cstdlib>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -57,7 +58,6 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 32;     // tokens per chunk
 constexpr int kNCT = 2;    // 16-token tiles per chunk
-constexpr int kRing = 6;   // raw-tile ring slots
 constexpr int kPrep = 6;   // prep waves per workgroup (four compute, two load)
 constexpr int kLptMax = 256;  // packed batches up to this many sequences are run longest first
 
@@ -73,6 +73,8 @@ struct Lay {
   static constexpr int V_OFF = Q_OFF + kNCT * NKB * 1024;
   static constexpr int G_OFF = V_OFF + kC * DVT * 2;  // log_alpha[32], beta[32]
   static constexpr int SLOT = G_OFF + 256;
+  // raw-tile ring slots: six, five with four state waves (wider V tiles)
+  static constexpr int RING_N = NS <= 2 ? 6 : 5;
   // per-chunk gate values (four buffers), 32 floats each:
   //   G2 running log2 decay, BT beta, GAM gamma = 2^G2, RA 2^(G2 - G2[m]),
   //   CB 2^(G2[m] - G2), KD 2^(G2[C-1] - G2), BR beta * RA, MISC[0] fast flag
@@ -89,7 +91,7 @@ struct Lay {
   static constexpr int LDT = kC + 4;  // T row stride (floats), rows 16-byte aligned
   static constexpr int AMTB = kC * LDA * 4;
   static constexpr int RING = 0;
-  static constexpr int PROCB = RING + kRing * SLOT;
+  static constexpr int PROCB = RING + RING_N * SLOT;
   static constexpr int GATEB = PROCB + 2 * PROC;
   static constexpr int AMT = GATEB + 4 * GATE;
   static constexpr int TMP = AMT + 2 * AMTB;
@@ -242,6 +244,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   constexpr int NST = L::NST;
   constexpr int DVT = L::DVT;
   constexpr int NTHR = 64 * (NS + kPrep);
+  constexpr int kRing = L::RING_N;
   __shared__ __attribute__((aligned(1024))) char smem[L::TOTAL];
 
   // Workgroups are dealt to the 8 XCDs round-robin by id. The n_vt column
@@ -677,12 +680,14 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   }
 
   // chunk-start states for the backward pass (optional): chunk x of sequence
-  // n goes to slot floor(bos / C) + n + x, this wave's slab of the tile, in
-  // fp16 (the backward's 16-bit products round the state to fp16 anyway)
+  // n goes to slot floor(bos / C) + n + x, in fp16 (the backward's 16-bit
+  // products round the state to fp16 anyway), in blocks of 32 columns (the
+  // backward's column tiles) of two 16-column slabs each
   _Float16 *const st_out =
       STATES ? reinterpret_cast<_Float16 *>(states) +
-                   ((static_cast<size_t>(bos / kC + n) * H + h) * n_vt + vt) * DK * DVT +
-                   (static_cast<size_t>(wave) * NST * 64 + lane) * 4
+                   ((static_cast<size_t>(bos / kC + n) * H + h) * (DV / 32) + (v0 + slab) / 32) *
+                       DK * 32 +
+                   (static_cast<size_t>(wave % 2) * NST * 64 + lane) * 4
              : nullptr;
   // byte offset of this lane's first y element inside a chunk's rows
   const uint32_t y_lane =
@@ -691,7 +696,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   auto state_step = [&](int x) {
     if constexpr (STATES) {
       typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-      _Float16 *dst = st_out + static_cast<size_t>(x) * H * n_vt * DK * DVT;
+      _Float16 *dst = st_out + static_cast<size_t>(x) * H * DK * DV;
 #pragma unroll
       for (int t = 0; t < NST; ++t) {
         f16x4 h4;
@@ -909,6 +914,23 @@ hipError_t launch_bf16(const ChunkArgs &a) {
 
 }  // namespace
 
+// State waves per workgroup. Each column tile of a head repeats the head's
+// prep work (gates, Gram, inverse, Q K^T). When the 32-column tiles of two
+// state waves would not all run at once (one workgroup per CU), four state
+// waves (64 columns, half the tiles, a step about 1.3 times as long) finish
+// sooner; otherwise two keep more CUs busy. GDN_PREFILL_NS = 2 or 4 sets it
+// instead (a test hook).
+static int prefill_ns(const ChunkArgs &a) {
+  if (a.dk != 128 || a.dv % 64 != 0) return 2;
+  if (const char *e = getenv("GDN_PREFILL_NS")) {
+    const int ns = atoi(e);
+    if (ns == 2 || ns == 4) return ns;
+  }
+  constexpr int64_t kCUs = 256;
+  const int64_t units = static_cast<int64_t>(a.N) * a.H;
+  return units * (a.dv / 32) > kCUs ? 4 : 2;
+}
+
 template <typename TIN, typename TOUT>
 static hipError_t launch_16(const ChunkArgs &a) {
   // runs of the segment-parallel form (in sequence order: the ordering by
@@ -916,9 +938,13 @@ static hipError_t launch_16(const ChunkArgs &a) {
   if (!a.seg.plain())
     return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT, false, false, true>(a)
                        : launch_bf16<64, 2, TIN, TOUT, false, false, true>(a);
-  if (a.cu_seqlens && a.N > 1 && a.N <= kLptMax)
+  const bool wide = prefill_ns(a) == 4;
+  if (a.cu_seqlens && a.N > 1 && a.N <= kLptMax) {
+    if (wide) return launch_bf16<128, 4, TIN, TOUT, false, true>(a);
     return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT, false, true>(a)
                        : launch_bf16<64, 2, TIN, TOUT, false, true>(a);
+  }
+  if (wide) return launch_bf16<128, 4, TIN, TOUT>(a);
   return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT>(a) : launch_bf16<64, 2, TIN, TOUT>(a);
 }
 
@@ -936,9 +962,13 @@ hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a) {
 }
 
 hipError_t launch_chunk_fwd_states(const ChunkArgs &a) {
-  if (a.in_dtype == 2)
+  const bool wide = prefill_ns(a) == 4;
+  if (a.in_dtype == 2) {
+    if (wide) return launch_bf16<128, 4, _Float16, _Float16, true>(a);
     return a.dk == 128 ? launch_bf16<128, 2, _Float16, _Float16, true>(a)
                        : launch_bf16<64, 2, _Float16, _Float16, true>(a);
+  }
+  if (wide) return launch_bf16<128, 4, bf16_t, bf16_t, true>(a);
   return a.dk == 128 ? launch_bf16<128, 2, bf16_t, bf16_t, true>(a)
                      : launch_bf16<64, 2, bf16_t, bf16_t, true>(a);
 }

@@ -133,6 +133,32 @@ def test_chunk_varlen(dtype):
 
 
 @gpu
+@pytest.mark.parametrize("case", ["varlen", "equal", "rect", "strong_decay"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_chunk_four_state_waves(case, dtype, monkeypatch):
+    """The prefill with four state waves per workgroup (64 columns; chosen
+    for batches with many (sequence, head) pairs, forced here by
+    GDN_PREFILL_NS) gives the two-wave result bit for bit: each column's
+    arithmetic is the same, only the columns' grouping into workgroups
+    differs. Checked against the oracle as well."""
+    if case == "varlen":
+        inp = gi.prefill_inputs(0, 2, 0, 128, 128, dtype, s0_std=0.02, seed=33,
+                                lengths=[1, 2, 63, 64, 65, 1000, 0, 130])
+    elif case == "rect":
+        inp = gi.prefill_inputs(2, 2, 130, 128, 64, dtype, s0_std=0.02, seed=34)
+    else:
+        inp = gi.prefill_inputs(3, 2, 200, 128, 128, dtype, s0_std=0.02, seed=35)
+        if case == "strong_decay":
+            inp["log_alpha"][::3] = -30.0
+    monkeypatch.setenv("GDN_PREFILL_NS", "2")
+    y2, S2 = _run_chunk(inp, torch.float32)
+    monkeypatch.setenv("GDN_PREFILL_NS", "4")
+    y4, S4 = _run_chunk(inp, torch.float32)
+    assert torch.equal(y2.cpu(), y4.cpu()) and torch.equal(S2.cpu(), S4.cpu())
+    _check(inp, out_dtype=torch.float32)
+
+
+@gpu
 def test_chunk_in_place_state():
     g = _lib()
     inp = to_dev(gi.prefill_inputs(2, 2, 100, 128, 128, "bf16", s0_std=0.02, seed=41))
@@ -762,6 +788,31 @@ def test_chunk_bwd_gated(with_bias):
         e = rel_l2(got, w)
         print(nm, "%.2e" % e, flush=True)
         assert e <= TOL["bf16"], (nm, e)
+
+
+@gpu
+@pytest.mark.parametrize("dv", [64, 128])
+def test_chunk_bwd_states_from_four_state_waves(dv, monkeypatch):
+    """The backward's chunk-start states written by the four-state-wave
+    prefill (64-column workgroups, stored as the backward's 32-column tiles)
+    give the two-wave gradients bit for bit."""
+    g = _lib()
+    inp, dy, dST = _bwd_inputs([1, 31, 32, 33, 100, 0, 65, 200], 2, 128, dv, "bf16", seed=152)
+    d = to_dev(inp)
+
+    def run():
+        out = g.gdn_chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], dy.cuda(),
+                              S0=d["S0"], dS_T=dST.cuda(), cu_seqlens=d["cu_seqlens"],
+                              N=d["N"])
+        torch.cuda.synchronize()
+        return [t.cpu() for t in out]
+
+    monkeypatch.setenv("GDN_PREFILL_NS", "2")
+    two = run()
+    monkeypatch.setenv("GDN_PREFILL_NS", "4")
+    four = run()
+    for nm, a, b in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0"), two, four):
+        assert torch.equal(a, b), nm
 
 
 _RUN_HOOKS = ("GDN_BWD_RUNS", "GDN_BWD_SEGMENT_ROWS")
