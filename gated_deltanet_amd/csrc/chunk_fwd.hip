@@ -73,8 +73,9 @@ struct Lay {
   static constexpr int V_OFF = Q_OFF + kNCT * NKB * 1024;
   static constexpr int G_OFF = V_OFF + kC * DVT * 2;  // log_alpha[32], beta[32]
   static constexpr int SLOT = G_OFF + 256;
-  // raw-tile ring slots: six, five with four state waves (wider V tiles)
-  static constexpr int RING_N = NS <= 2 ? 6 : 5;
+  // raw-tile ring slots: six; five with four state waves and four with
+  // eight (wider V tiles)
+  static constexpr int RING_N = NS <= 2 ? 6 : NS == 4 ? 5 : 4;
   // per-chunk gate values (four buffers), 32 floats each:
   //   G2 running log2 decay, BT beta, GAM gamma = 2^G2, RA 2^(G2 - G2[m]),
   //   CB 2^(G2[m] - G2), KD 2^(G2[C-1] - G2), BR beta * RA, MISC[0] fast flag
@@ -915,20 +916,35 @@ hipError_t launch_bf16(const ChunkArgs &a) {
 }  // namespace
 
 // State waves per workgroup. Each column tile of a head repeats the head's
-// prep work (gates, Gram, inverse, Q K^T). When the 32-column tiles of two
-// state waves would not all run at once (one workgroup per CU), four state
-// waves (64 columns, half the tiles, a step about 1.3 times as long) finish
-// sooner; otherwise two keep more CUs busy. GDN_PREFILL_NS = 2 or 4 sets it
-// instead (a test hook).
+// prep work (gate scan, Gram, inverse, Q K^T), so wider tiles do less work
+// in all but take longer per step (more waves share the SIMDs) and give
+// fewer workgroups. With one workgroup per CU the time is about (rounds of
+// workgroups) x (step time); relative step times measured on the varlen
+// front-end workload: 2 waves 1, 4 waves 1.29, 8 waves 2.06. The count with
+// the least estimate is taken (ties to fewer waves). GDN_PREFILL_NS = 2, 4
+// or 8 sets it instead (a test hook).
 static int prefill_ns(const ChunkArgs &a) {
   if (a.dk != 128 || a.dv % 64 != 0) return 2;
   if (const char *e = getenv("GDN_PREFILL_NS")) {
     const int ns = atoi(e);
-    if (ns == 2 || ns == 4) return ns;
+    if (ns == 2 || ns == 4 || (ns == 8 && a.dv % 128 == 0)) return ns;
   }
   constexpr int64_t kCUs = 256;
-  const int64_t units = static_cast<int64_t>(a.N) * a.H;
-  return units * (a.dv / 32) > kCUs ? 4 : 2;
+  const int64_t slabs = static_cast<int64_t>(a.N) * a.H * (a.dv / 16);
+  int best = 2;
+  double best_t = 0.0;
+  const int cand[3] = {2, 4, 8};
+  const double step[3] = {1.0, 1.29, 2.06};
+  for (int i = 0; i < 3; ++i) {
+    if (a.dv % (16 * cand[i]) != 0) continue;
+    const int64_t wgs = slabs / cand[i];
+    const double t = static_cast<double>((wgs + kCUs - 1) / kCUs) * step[i];
+    if (i == 0 || t < best_t) {
+      best = cand[i];
+      best_t = t;
+    }
+  }
+  return best;
 }
 
 template <typename TIN, typename TOUT>
@@ -938,13 +954,15 @@ static hipError_t launch_16(const ChunkArgs &a) {
   if (!a.seg.plain())
     return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT, false, false, true>(a)
                        : launch_bf16<64, 2, TIN, TOUT, false, false, true>(a);
-  const bool wide = prefill_ns(a) == 4;
+  const int ns = prefill_ns(a);
   if (a.cu_seqlens && a.N > 1 && a.N <= kLptMax) {
-    if (wide) return launch_bf16<128, 4, TIN, TOUT, false, true>(a);
+    if (ns == 8) return launch_bf16<128, 8, TIN, TOUT, false, true>(a);
+    if (ns == 4) return launch_bf16<128, 4, TIN, TOUT, false, true>(a);
     return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT, false, true>(a)
                        : launch_bf16<64, 2, TIN, TOUT, false, true>(a);
   }
-  if (wide) return launch_bf16<128, 4, TIN, TOUT>(a);
+  if (ns == 8) return launch_bf16<128, 8, TIN, TOUT>(a);
+  if (ns == 4) return launch_bf16<128, 4, TIN, TOUT>(a);
   return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT>(a) : launch_bf16<64, 2, TIN, TOUT>(a);
 }
 
@@ -962,13 +980,15 @@ hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a) {
 }
 
 hipError_t launch_chunk_fwd_states(const ChunkArgs &a) {
-  const bool wide = prefill_ns(a) == 4;
+  const int ns = prefill_ns(a);
   if (a.in_dtype == 2) {
-    if (wide) return launch_bf16<128, 4, _Float16, _Float16, true>(a);
+    if (ns == 8) return launch_bf16<128, 8, _Float16, _Float16, true>(a);
+    if (ns == 4) return launch_bf16<128, 4, _Float16, _Float16, true>(a);
     return a.dk == 128 ? launch_bf16<128, 2, _Float16, _Float16, true>(a)
                        : launch_bf16<64, 2, _Float16, _Float16, true>(a);
   }
-  if (wide) return launch_bf16<128, 4, bf16_t, bf16_t, true>(a);
+  if (ns == 8) return launch_bf16<128, 8, bf16_t, bf16_t, true>(a);
+  if (ns == 4) return launch_bf16<128, 4, bf16_t, bf16_t, true>(a);
   return a.dk == 128 ? launch_bf16<128, 2, bf16_t, bf16_t, true>(a)
                      : launch_bf16<64, 2, bf16_t, bf16_t, true>(a);
 }
