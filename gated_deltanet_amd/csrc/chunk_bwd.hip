@@ -1313,12 +1313,14 @@ __global__ __launch_bounds__(256) void head_sum_kernel(const BwdArgs a) {
 }  // namespace
 
 // Runs of the backward: the column tiles' partial sums are kept for one run
-// at a time, at most about kBwdPartBytes of them (some 2 000 rows at H = 16,
-// d = 128); a problem whose partials fit is one run. Runs that take the same
+// at a time, at most about kBwdPartBytes of them (some 3 000 rows at H = 16,
+// d = 128); a problem whose partials fit is one run. Each run costs about
+// one chunk step more (the sweep's pipeline refills), so the bound trades
+// workspace against time. Runs that take the same
 // share of every sequence keep every sequence busy in every run; they are
 // used while a chunk of every sequence is a small part of a run, and runs of
 // consecutive rows (which hold many short sequences each) otherwise.
-constexpr size_t kBwdPartBytes = size_t{128} << 20;
+constexpr size_t kBwdPartBytes = size_t{192} << 20;
 
 BwdSegPlan bwd_seg_plan(int64_t rows, int N, int H, int dk, int dv) {
   const size_t per_row = static_cast<size_t>(dv / kDVT) * H * (2 * dk + 2) * sizeof(float);

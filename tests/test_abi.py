@@ -293,20 +293,20 @@ def test_chunk_bwd_rejects(lib):
     assert lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 128, 128, 0) == 3 * 2 * 65536 + 4 * 64 * 2 * 258 * 4
     assert lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 96, 128, 1) == 0
     assert lib.gdn_chunk_bwd_workspace_size(64, 1, 2, 128, 128, 5) == 0
-    # long problems keep the partial sums of one run at a time (<= 128 MiB)
-    # plus the carried state gradients: B4 H16 T4096 d128 takes 9 runs of
-    # 14 or 15 chunks of every sequence (bound ceil(16508 / 9) + 128 = 1963
-    # rows of partials); with bf16 inputs the whole workspace stays under
-    # 0.5 GB
+    # long problems keep the partial sums of one run at a time (<= 192 MiB:
+    # 3048 rows here) plus the carried state gradients: B4 H16 T4096 d128
+    # takes 6 runs of 21 or 22 chunks of every sequence (bound
+    # ceil(16508 / 6) + 128 = 2880 rows of partials); with bf16 inputs the
+    # whole workspace stays under 0.5 GB
     per_row = 4 * 16 * 258 * 4
     ws = lib.gdn_chunk_bwd_workspace_size(16384, 4, 16, 128, 128, 1)
-    assert ws == 516 * 16 * 32768 + 1963 * per_row + 4 * 16 * 65536 + 256
+    assert ws == 516 * 16 * 32768 + 2880 * per_row + 4 * 16 * 65536 + 256
     assert ws < 500e6
-    # many short sequences: 34 runs of 1984 consecutive rows (2000 rounded
-    # down to whole chunks), 2016 rows of partials
+    # many short sequences: 22 runs of 3008 consecutive rows (3016 rounded
+    # down to whole chunks), 3040 rows of partials
     ws = lib.gdn_chunk_bwd_workspace_size(65536, 512, 16, 128, 128, 1)
-    assert ws == ((2048 + 512) * 16 * 32768 + 2016 * per_row + 512 * 16 * 65536 +
-                  (34 * 513 * 4 + 255) // 256 * 256)
+    assert ws == ((2048 + 512) * 16 * 32768 + 3040 * per_row + 512 * 16 * 65536 +
+                  (22 * 513 * 4 + 255) // 256 * 256)
 
     def bwd(**kw):
         a = dict(q=A, k=A + (1 << 26), v=A + (2 << 26), la=A + (3 << 26), b=A + (4 << 26),
