@@ -73,8 +73,8 @@ struct Lay {
   static constexpr int V_OFF = Q_OFF + kNCT * NKB * 1024;
   static constexpr int G_OFF = V_OFF + kC * DVT * 2;  // log_alpha[32], beta[32]
   static constexpr int SLOT = G_OFF + 256;
-  // raw-tile ring slots: six; five with four state waves and four with
-  // eight (wider V tiles)
+  // raw-tile ring slots: six with one or two state waves, five with four
+  // and four with eight (wider V tiles)
   static constexpr int RING_N = NS <= 2 ? 6 : NS == 4 ? 5 : 4;
   // per-chunk gate values (four buffers), 32 floats each:
   //   G2 running log2 decay, BT beta, GAM gamma = 2^G2, RA 2^(G2 - G2[m]),
@@ -688,7 +688,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       STATES ? reinterpret_cast<_Float16 *>(states) +
                    ((static_cast<size_t>(bos / kC + n) * H + h) * (DV / 32) + (v0 + slab) / 32) *
                        DK * 32 +
-                   (static_cast<size_t>(wave % 2) * NST * 64 + lane) * 4
+                   (static_cast<size_t>((v0 + slab) / 16 % 2) * NST * 64 + lane) * 4
              : nullptr;
   // byte offset of this lane's first y element inside a chunk's rows
   const uint32_t y_lane =
@@ -920,22 +920,23 @@ hipError_t launch_bf16(const ChunkArgs &a) {
 // in all but take longer per step (more waves share the SIMDs) and give
 // fewer workgroups. With one workgroup per CU the time is about (rounds of
 // workgroups) x (step time); relative step times measured on the varlen
-// front-end workload: 2 waves 1, 4 waves 1.29, 8 waves 2.06. The count with
-// the least estimate is taken (ties to fewer waves). GDN_PREFILL_NS = 2, 4
-// or 8 sets it instead (a test hook).
+// front-end and the B4 H16 T4096 / B1 H32 T65536 workloads: 1 wave 0.92,
+// 2 waves 1, 4 waves 1.29, 8 waves 2.06. The count with the least estimate
+// is taken (ties to fewer waves). GDN_PREFILL_NS = 1, 2, 4 or 8 sets it
+// instead (a test hook).
 static int prefill_ns(const ChunkArgs &a) {
   if (a.dk != 128 || a.dv % 64 != 0) return 2;
   if (const char *e = getenv("GDN_PREFILL_NS")) {
     const int ns = atoi(e);
-    if (ns == 2 || ns == 4 || (ns == 8 && a.dv % 128 == 0)) return ns;
+    if (ns == 1 || ns == 2 || ns == 4 || (ns == 8 && a.dv % 128 == 0)) return ns;
   }
   constexpr int64_t kCUs = 256;
   const int64_t slabs = static_cast<int64_t>(a.N) * a.H * (a.dv / 16);
   int best = 2;
   double best_t = 0.0;
-  const int cand[3] = {2, 4, 8};
-  const double step[3] = {1.0, 1.29, 2.06};
-  for (int i = 0; i < 3; ++i) {
+  const int cand[4] = {1, 2, 4, 8};
+  const double step[4] = {0.92, 1.0, 1.29, 2.06};
+  for (int i = 0; i < 4; ++i) {
     if (a.dv % (16 * cand[i]) != 0) continue;
     const int64_t wgs = slabs / cand[i];
     const double t = static_cast<double>((wgs + kCUs - 1) / kCUs) * step[i];
@@ -958,11 +959,13 @@ static hipError_t launch_16(const ChunkArgs &a) {
   if (a.cu_seqlens && a.N > 1 && a.N <= kLptMax) {
     if (ns == 8) return launch_bf16<128, 8, TIN, TOUT, false, true>(a);
     if (ns == 4) return launch_bf16<128, 4, TIN, TOUT, false, true>(a);
+    if (ns == 1) return launch_bf16<128, 1, TIN, TOUT, false, true>(a);
     return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT, false, true>(a)
                        : launch_bf16<64, 2, TIN, TOUT, false, true>(a);
   }
   if (ns == 8) return launch_bf16<128, 8, TIN, TOUT>(a);
   if (ns == 4) return launch_bf16<128, 4, TIN, TOUT>(a);
+  if (ns == 1) return launch_bf16<128, 1, TIN, TOUT>(a);
   return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT>(a) : launch_bf16<64, 2, TIN, TOUT>(a);
 }
 
@@ -984,11 +987,13 @@ hipError_t launch_chunk_fwd_states(const ChunkArgs &a) {
   if (a.in_dtype == 2) {
     if (ns == 8) return launch_bf16<128, 8, _Float16, _Float16, true>(a);
     if (ns == 4) return launch_bf16<128, 4, _Float16, _Float16, true>(a);
+    if (ns == 1) return launch_bf16<128, 1, _Float16, _Float16, true>(a);
     return a.dk == 128 ? launch_bf16<128, 2, _Float16, _Float16, true>(a)
                        : launch_bf16<64, 2, _Float16, _Float16, true>(a);
   }
   if (ns == 8) return launch_bf16<128, 8, bf16_t, bf16_t, true>(a);
   if (ns == 4) return launch_bf16<128, 4, bf16_t, bf16_t, true>(a);
+  if (ns == 1) return launch_bf16<128, 1, bf16_t, bf16_t, true>(a);
   return a.dk == 128 ? launch_bf16<128, 2, bf16_t, bf16_t, true>(a)
                      : launch_bf16<64, 2, bf16_t, bf16_t, true>(a);
 }

@@ -133,15 +133,15 @@ def test_chunk_varlen(dtype):
 
 
 @gpu
-@pytest.mark.parametrize("ns", [4, 8])
+@pytest.mark.parametrize("ns", [1, 4, 8])
 @pytest.mark.parametrize("case", ["varlen", "equal", "rect", "strong_decay"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_chunk_wide_state_tiles(ns, case, dtype, monkeypatch):
-    """The prefill with four or eight state waves per workgroup (64 or 128
-    columns; chosen for batches with many (sequence, head) pairs, forced here
-    by GDN_PREFILL_NS) gives the two-wave result bit for bit: each column's
-    arithmetic is the same, only the columns' grouping into workgroups
-    differs. Checked against the oracle as well."""
+    """The prefill with one, four or eight state waves per workgroup (16, 64
+    or 128 columns; chosen by batch size, forced here by GDN_PREFILL_NS)
+    gives the two-wave result bit for bit: each column's arithmetic is the
+    same, only the columns' grouping into workgroups differs. Checked
+    against the oracle as well."""
     if ns == 8 and case == "rect":
         pytest.skip("eight state waves need dv = 128")
     if case == "varlen":
@@ -794,11 +794,12 @@ def test_chunk_bwd_gated(with_bias):
 
 
 @gpu
-@pytest.mark.parametrize("ns,dv", [(4, 64), (4, 128), (8, 128)])
+@pytest.mark.parametrize("ns,dv", [(1, 64), (1, 128), (4, 64), (4, 128), (8, 128)])
 def test_chunk_bwd_states_from_wide_state_tiles(ns, dv, monkeypatch):
-    """The backward's chunk-start states written by the prefill with four or
-    eight state waves (64- or 128-column workgroups, stored as the
-    backward's 32-column tiles) give the two-wave gradients bit for bit."""
+    """The backward's chunk-start states written by the prefill with one,
+    four or eight state waves (16-, 64- or 128-column workgroups, stored as
+    the backward's 32-column tiles) give the two-wave gradients bit for
+    bit."""
     g = _lib()
     inp, dy, dST = _bwd_inputs([1, 31, 32, 33, 100, 0, 65, 200], 2, 128, dv, "bf16", seed=152)
     d = to_dev(inp)
