@@ -90,7 +90,11 @@ enum gdn_status_e {
  *
  * Empty sequences (length 0) copy S0 to S_T. Inputs must not alias outputs.
  * q, k, v, y, S0 and S_T must be 16-byte aligned; log_alpha, beta and
- * cu_seqlens 4-byte aligned.
+ * cu_seqlens 4-byte aligned. With 16-bit inputs and dk = 128, the number of
+ * state columns per workgroup (16, 32, 64 or 128) follows from N * H * dv;
+ * results do not depend on it (each column's arithmetic is the same). The
+ * environment variable GDN_PREFILL_NS (1, 2, 4 or 8 state waves of 16
+ * columns) sets it instead: a test hook.
  */
 GDN_API int gdn_chunk_fwd(const void *q, const void *k, const void *v,
                           const float *log_alpha, const float *beta,
