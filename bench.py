@@ -342,7 +342,9 @@ def bench_longctx(g, steps=3, warmup=1):
     return dict(workload=w.name, ms_per_call=ms, tokens_per_s=tokens / (ms * 1e-3),
                 pct_bf16_mfma_peak=100.0 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                 hbm_GBps=nbytes / (ms * 1e-3) / 1e9,
-                roofline=_roofline("chunk_fwd_bf16_kernel<128,2,bf16,bf16>", nbytes, flops, ms))
+                # 32 heads x 128 columns = 256 16-column slabs: one state wave
+                # per workgroup, one workgroup per CU
+                roofline=_roofline("chunk_fwd_bf16_kernel<128,1,bf16,bf16>", nbytes, flops, ms))
 
 
 def bench_longctx_segmented(g, segment_counts=(2, 3, 4), steps=3, warmup=1):
