@@ -142,6 +142,13 @@ def time_launches(fn, steps, warmup, stream):
     return start.elapsed_time(end)  # ms
 
 
+def prefill_kernel_name(g, N, H, dk, dv):
+    """The prefill kernel instance the library launches for this bf16 shape
+    (its state waves per workgroup = columns / 16)."""
+    ns = g.gdn_prefill_state_columns(N, H, dk, dv, torch.bfloat16) // 16
+    return "chunk_fwd_bf16_kernel<%d,%d,bf16,bf16>" % (dk, ns)
+
+
 def bench_prefill(g, steps, warmup, copies=3):
     w = gi.WORKLOADS[1]
     inp = gi.workload_inputs(1)
@@ -342,9 +349,8 @@ def bench_longctx(g, steps=3, warmup=1):
     return dict(workload=w.name, ms_per_call=ms, tokens_per_s=tokens / (ms * 1e-3),
                 pct_bf16_mfma_peak=100.0 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                 hbm_GBps=nbytes / (ms * 1e-3) / 1e9,
-                # 32 heads x 128 columns = 256 16-column slabs: one state wave
-                # per workgroup, one workgroup per CU
-                roofline=_roofline("chunk_fwd_bf16_kernel<128,1,bf16,bf16>", nbytes, flops, ms))
+                roofline=_roofline(prefill_kernel_name(g, w.B, w.H, w.dk, w.dv), nbytes,
+                                   flops, ms))
 
 
 def bench_longctx_segmented(g, segment_counts=(2, 3, 4), steps=3, warmup=1):
@@ -562,7 +568,7 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic("chunk_fwd_bf16_kernel_B4_H16_T4096_d128", "chunk_fwd.hip")
     mfma = measured_mfma("chunk_fwd_bf16_kernel_B4_H16_T4096_d128", "chunk_fwd.hip")
-    roofline = dict(kernel="chunk_fwd_bf16_kernel<128,2,bf16,bf16>", bound="hbm",
+    roofline = dict(kernel=prefill_kernel_name(g, N, H, dk, dv), bound="hbm",
                     achieved=achieved_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=achieved_gbs / HBM_PEAK_GBS, traffic=traffic,
                     alg_bytes_per_launch=nbytes, alg_flops_per_launch=flops,

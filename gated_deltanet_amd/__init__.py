@@ -109,6 +109,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_version.argtypes = []
     lib.gdn_version.restype = ctypes.c_int
+    lib.gdn_prefill_state_columns.argtypes = [i32] * 5
+    lib.gdn_prefill_state_columns.restype = ctypes.c_int32
     _lib = lib
     return lib
 
@@ -327,6 +329,12 @@ def gdn_chunk_fwd_segmented_noalloc(q, k, v, log_alpha, beta, segments, S0=None,
                                              _stream(v.device))
     _check(rc, lib, "gdn_chunk_fwd_segmented_noalloc")
     return y, S_T
+
+
+def gdn_prefill_state_columns(N: int, H: int, dk: int, dv: int, in_dtype=torch.bfloat16) -> int:
+    """State columns per workgroup that gdn_chunk_fwd uses for this shape
+    (16, 32, 64 or 128; a query, nothing is launched)."""
+    return int(load_library().gdn_prefill_state_columns(N, H, dk, dv, _dt(in_dtype)))
 
 
 def gdn_chunk_bwd_workspace_size(rows: int, N: int, H: int, dk: int, dv: int,

@@ -60,6 +60,18 @@ GDN_API const char *gdn_last_error(void) { return g_last_error; }
 
 GDN_API int gdn_version(void) { return 100; }
 
+GDN_API int32_t gdn_prefill_state_columns(int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                          int32_t in_dtype) {
+  if (N < 0 || H <= 0 || !head_size_ok(dk) || !head_size_ok(dv) || !dtype_ok(in_dtype)) return 0;
+  gdn::ChunkArgs a{};
+  a.N = N;
+  a.H = H;
+  a.dk = dk;
+  a.dv = dv;
+  a.in_dtype = in_dtype;
+  return gdn::chunk_fwd_state_columns(a);
+}
+
 }  // extern "C"
 
 namespace {

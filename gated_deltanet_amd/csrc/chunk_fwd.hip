@@ -948,6 +948,10 @@ static int prefill_ns(const ChunkArgs &a) {
   return best;
 }
 
+int chunk_fwd_state_columns(const ChunkArgs &a) {
+  return a.in_dtype == 0 ? 32 : 16 * prefill_ns(a);
+}
+
 template <typename TIN, typename TOUT>
 static hipError_t launch_16(const ChunkArgs &a) {
   // runs of the segment-parallel form (in sequence order: the ordering by

@@ -193,5 +193,7 @@ hipError_t launch_chunk_fwd_f32(const ChunkArgs &a);  // fp32 inputs
 hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a); // bf16 inputs
 // 16-bit inputs: chunk-start states only (a.states; y and S_T not written)
 hipError_t launch_chunk_fwd_states(const ChunkArgs &a);
+// state columns per workgroup of the plain prefill for a's shape and dtype
+int chunk_fwd_state_columns(const ChunkArgs &a);
 
 }  // namespace gdn

@@ -506,6 +506,17 @@ GDN_API const char *gdn_last_error(void);
 /* Library version, major * 10000 + minor * 100 + patch. */
 GDN_API int gdn_version(void);
 
+/*
+ * State columns per workgroup that gdn_chunk_fwd (and the chunk-start
+ * states of gdn_chunk_bwd) would use for a batch of N sequences, H heads and
+ * head sizes dk, dv with the given input dtype: 16, 32, 64 or 128 (32 for
+ * fp32 inputs, dk = 64 and the segmented form). A query for profiling and
+ * tests; it launches nothing. Results never depend on it. Returns 0 for
+ * invalid sizes or dtypes.
+ */
+GDN_API int32_t gdn_prefill_state_columns(int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                          int32_t in_dtype);
+
 #ifdef __cplusplus
 }
 #endif

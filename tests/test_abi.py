@@ -281,6 +281,29 @@ def test_chunk_bwd_workspace_run_hooks(lib, monkeypatch):
     assert lib.gdn_chunk_bwd_workspace_size(500, 3, 2, 64, 64, 0) == one
 
 
+def test_prefill_state_columns(lib, monkeypatch):
+    """The prefill's column-tile width by batch shape (the rounds-times-step
+    estimate): the timed shapes, an intermediate batch, fp32 inputs, dk = 64,
+    the test hook, and invalid sizes."""
+    i32 = ctypes.c_int32
+    lib.gdn_prefill_state_columns.argtypes = [i32] * 5
+    lib.gdn_prefill_state_columns.restype = i32
+    monkeypatch.delenv("GDN_PREFILL_NS", raising=False)
+    cols = lib.gdn_prefill_state_columns
+    assert cols(4, 16, 128, 128, 1) == 32     # B4 H16: 256 workgroups, one round
+    assert cols(1, 32, 128, 128, 1) == 16     # B1 H32: 16 columns fill the 256 CUs
+    assert cols(64, 16, 128, 128, 2) == 128   # varlen front-end batch: whole heads
+    assert cols(8, 16, 128, 128, 1) == 64     # 256 workgroups of 64 columns
+    assert cols(64, 16, 128, 128, 0) == 32    # fp32 inputs: their own kernel
+    assert cols(64, 16, 64, 64, 1) == 32      # dk = 64: two state waves
+    assert cols(4, 16, 128, 64, 1) == 16      # dv = 64: 256 slabs, one round
+    monkeypatch.setenv("GDN_PREFILL_NS", "4")
+    assert cols(4, 16, 128, 128, 1) == 64
+    assert cols(4, 16, 96, 128, 1) == 0
+    assert cols(4, 0, 128, 128, 1) == 0
+    assert cols(4, 16, 128, 128, 7) == 0
+
+
 def test_chunk_bwd_rejects(lib):
     v, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int64, i32, i32, i32, i32, i32]
