@@ -268,6 +268,53 @@ def test_backward_B4_H16_T4096_sampled():
 
 
 @gpu
+def test_backward_many_short_sequences_sampled():
+    """gdn_chunk_bwd on a packed batch of 512 sequences of 1-256 tokens (about
+    65 000 rows, H = 16, d = 128, bf16) as the library plans it by itself:
+    the partial sums of all rows exceed the workspace bound, so the sweep
+    runs over consecutive rows in many runs, and sequences that straddle a
+    run boundary carry their state gradient from run to run. Sampled
+    sequences (the shortest, the longest, and those holding rows at run
+    boundaries) against the oracle's backward of that sequence alone."""
+    g = _lib()
+    H, d = 16, 128
+    lengths = gi.seq_lengths(512, 1, 256, seed=17).tolist()
+    inp = gi.prefill_inputs(0, H, 0, d, d, "bf16", s0_std=0.02, seed=17, lengths=lengths)
+    rows = inp["q"].shape[0]
+    per_row = (d // 32) * H * (2 * d + 2) * 4
+    ws = g.gdn_chunk_bwd_workspace_size(rows, 512, H, d, d, torch.bfloat16)
+    assert ws < rows * per_row  # the partial sums are kept for one run at a time
+    dy = gi.normal((rows, H, d), 17, 40).to(torch.bfloat16)
+    dST = gi.normal((512, H, d, d), 17, 41)
+    dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    grads = g.gdn_chunk_bwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
+                            dy.cuda(), S0=dev["S0"], dS_T=dST.cuda(),
+                            cu_seqlens=dev["cu_seqlens"], N=512)
+    torch.cuda.synchronize()
+    grads = [x.cpu() for x in grads]
+    cu = inp["cu_seqlens"].tolist()
+    order = sorted(range(512), key=lambda n: lengths[n])
+
+    def holding(row):  # the sequence that holds a row
+        return max(n for n in range(512) if cu[n] <= row and cu[n + 1] > row)
+
+    picks = {order[0], order[-1]} | {holding(r) for r in (3008, 6016, 30080, 60160)}
+    for i, n in enumerate(sorted(picks)):
+        h = (5 * i + 1) % H
+        s0, e0 = cu[n], cu[n + 1]
+        unit = [inp[key][s0:e0, h:h + 1].contiguous()
+                for key in ("q", "k", "v", "log_alpha", "beta")]
+        ref = oracle.gdn_bwd(*unit, inp["S0"][n:n + 1, h:h + 1], dy[s0:e0, h:h + 1],
+                             dST[n:n + 1, h:h + 1], N=1)
+        got = [grads[0][s0:e0, h:h + 1], grads[1][s0:e0, h:h + 1], grads[2][s0:e0, h:h + 1],
+               grads[3][s0:e0, h:h + 1], grads[4][s0:e0, h:h + 1], grads[5][n:n + 1, h:h + 1]]
+        for nm, gg, rr in zip(("dq", "dk", "dv", "dla", "dbeta", "dS0"), got, ref):
+            e = rel_l2(gg, rr)
+            print("sequence", n, "len", e0 - s0, "head", h, nm, "%.2e" % e, flush=True)
+            assert e <= TOL, (n, h, nm, e)
+
+
+@gpu
 def test_decode_multi_N256_H32_sampled():
     """gdn_decode_multi at the decode workload's size with 4 tokens per call
     (next_n = 4), sampled units against 4 oracle decode steps."""
