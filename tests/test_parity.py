@@ -392,6 +392,36 @@ def test_chunk_gated(d, dtype, with_bias):
 
 
 @gpu
+@pytest.mark.parametrize("ns", [1, 4, 8])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_chunk_gated_wide_state_tiles(ns, dtype, monkeypatch):
+    """The raw-gate prefill with one, four or eight state waves per
+    workgroup (forced by GDN_PREFILL_NS) equals the two-wave result bit for
+    bit, and the oracle to the bar; varlen with an empty sequence, biases."""
+    g = _lib()
+    inp, a, b, A, b_alpha = _raw_case([1, 33, 100, 0, 65, 200], 3, 128, dtype, seed=66)
+    dv_ = to_dev(inp)
+
+    def run():
+        y, S = g.gdn_chunk_fwd_gated(dv_["q"], dv_["k"], dv_["v"], a.cuda(), b.cuda(), A.cuda(),
+                                     b_alpha.cuda(), dv_["S0"], cu_seqlens=dv_["cu_seqlens"],
+                                     out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        return y.cpu(), S.cpu()
+
+    monkeypatch.setenv("GDN_PREFILL_NS", "2")
+    y2, S2 = run()
+    monkeypatch.setenv("GDN_PREFILL_NS", str(ns))
+    y, S = run()
+    assert torch.equal(y, y2) and torch.equal(S, S2)
+    la, bt = oracle.gates_from_raw(a, b, A, b_alpha)
+    yo, So = oracle.gdn_fwd(inp["q"], inp["k"], inp["v"], la, bt, inp["S0"],
+                            cu_seqlens=inp["cu_seqlens"], N=inp["N"])
+    ey, es = rel_l2(_flat(inp, y), yo), rel_l2(S, So)
+    assert ey <= TOL[dtype] and es <= TOL[dtype], (ey, es)
+
+
+@gpu
 def test_chunk_gated_matches_precomputed_gates():
     """The in-kernel gate map and gates precomputed in fp32 by torch drive
     the same recurrence: the two outputs agree to fp32 rounding."""
