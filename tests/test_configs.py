@@ -315,6 +315,44 @@ def test_backward_many_short_sequences_sampled():
 
 
 @gpu
+def test_prefill_and_backward_B16_H16_T2048_sampled():
+    """A large equal-length batch (B = 16, H = 16, T = 2048, bf16): the
+    prefill takes whole-head workgroups (eight state waves, 128 columns) and
+    the backward's chunk-start states come from the same kernel, while the
+    backward sweep runs in proportional runs. Sampled units of y, S_T and of
+    every gradient against the oracle on that unit alone."""
+    g = _lib()
+    B, H, T, d = 16, 16, 2048, 128
+    assert g.gdn_prefill_state_columns(B, H, d, d, torch.bfloat16) == 128
+    inp = gi.prefill_inputs(B, H, T, d, d, "bf16", s0_std=0.02, seed=23)
+    dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
+    y, S = g.gdn_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
+                           dev["S0"], N=B)
+    dy = gi.normal((B * T, H, d), 23, 40).to(torch.bfloat16)
+    grads = g.gdn_chunk_bwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
+                            dy.cuda(), S0=dev["S0"], N=B)
+    torch.cuda.synchronize()
+    y, S = y.cpu(), S.cpu()
+    grads = [x.cpu() for x in grads]
+    for n, h in [(0, 0), (7, 9), (15, 15)]:
+        q, k, v, la, b = _unit(inp, n, h, T)
+        S0u = inp["S0"][n:n + 1, h:h + 1]
+        rows = slice(n * T, (n + 1) * T)
+        yo, So = oracle.gdn_fwd(q, k, v, la, b, S0u, col_blocks=8)
+        ey, es = rel_l2(y[rows, h], yo[:, 0]), rel_l2(S[n, h], So[0, 0])
+        print("unit (%d, %d): y %.3e S %.3e" % (n, h, ey, es), flush=True)
+        assert ey <= TOL and es <= TOL
+        _rows_ok(y[rows, h], yo[:, 0], "unit (%d, %d) y" % (n, h))
+        ref = oracle.gdn_bwd(q, k, v, la, b, S0u, dy[rows, h:h + 1], None, N=1)
+        got = [grads[0][rows, h:h + 1], grads[1][rows, h:h + 1], grads[2][rows, h:h + 1],
+               grads[3][rows, h:h + 1], grads[4][rows, h:h + 1], grads[5][n:n + 1, h:h + 1]]
+        for nm, gg, rr in zip(("dq", "dk", "dv", "dla", "dbeta", "dS0"), got, ref):
+            e = rel_l2(gg, rr)
+            print("unit", n, h, nm, "%.2e" % e, flush=True)
+            assert e <= TOL, (n, h, nm, e)
+
+
+@gpu
 def test_decode_multi_N256_H32_sampled():
     """gdn_decode_multi at the decode workload's size with 4 tokens per call
     (next_n = 4), sampled units against 4 oracle decode steps."""
