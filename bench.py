@@ -85,6 +85,15 @@ def measured_mfma(key, source):
     return dict(mfma_busy=rec["mfma_busy"], issued_flops=rec["issued_flops"])
 
 
+def fused_traffic():
+    """HBM bytes of the varlen fused call: its three kernels' counters, or
+    None unless all three are current."""
+    parts = [measured_traffic("frontend_kernel_varlen64_H16_d128", "frontend.hip"),
+             measured_traffic("chunk_fwd_bf16_kernel_varlen64_H16_d128", "chunk_fwd.hip"),
+             measured_traffic("output_gate_kernel_varlen64_H16_d128", "frontend.hip")]
+    return None if any(x is None for x in parts) else sum(parts)
+
+
 def rel_l2(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
@@ -107,12 +116,13 @@ def row_errors(got, ref, block=32, floor_frac=0.05):
     return row, worst
 
 
-def _roofline(kernel, nbytes, flops, ms):
-    """HBM roofline record of one call from its algorithmic bytes and flops."""
+def _roofline(kernel, nbytes, flops, ms, traffic=None):
+    """HBM roofline record of one call from its algorithmic bytes and flops;
+    traffic: HBM bytes per call from rocprofv3 counters, or None."""
     gbs = nbytes / (ms * 1e-3) / 1e9
     tf = flops / (ms * 1e-3) / 1e12
     return dict(kernel=kernel, bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=gbs / HBM_PEAK_GBS, alg_bytes_per_launch=nbytes,
+                frac=gbs / HBM_PEAK_GBS, traffic=traffic, alg_bytes_per_launch=nbytes,
                 alg_flops_per_launch=flops, mfma_tflops=tf, mfma_frac_bf16_peak=tf / BF16_PEAK_TFLOPS)
 
 
@@ -350,7 +360,9 @@ def bench_longctx(g, steps=3, warmup=1):
                 pct_bf16_mfma_peak=100.0 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                 hbm_GBps=nbytes / (ms * 1e-3) / 1e9,
                 roofline=_roofline(prefill_kernel_name(g, w.B, w.H, w.dk, w.dv), nbytes,
-                                   flops, ms))
+                                   flops, ms,
+                                   measured_traffic("chunk_fwd_bf16_kernel_B1_H32_T65536_d128",
+                                                    "chunk_fwd.hip")))
 
 
 def bench_longctx_segmented(g, segment_counts=(2, 3, 4), steps=3, warmup=1):
@@ -419,7 +431,8 @@ def bench_varlen_frontend(g, steps=3, warmup=1):
                 tokens_per_s=rows / (ms * 1e-3),
                 pct_bf16_mfma_peak=100.0 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                 hbm_GBps_of_fused_bytes=fused_bytes / (ms * 1e-3) / 1e9,
-                roofline=_roofline("gdn_chunk_fwd_fused (whole call)", fused_bytes, flops, ms),
+                roofline=_roofline("gdn_chunk_fwd_fused (whole call)", fused_bytes, flops, ms,
+                                   fused_traffic()),
                 entry_point="gdn_chunk_fwd_fused")
 
 
