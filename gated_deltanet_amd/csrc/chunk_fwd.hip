@@ -956,10 +956,14 @@ template <typename TIN, typename TOUT>
 static hipError_t launch_16(const ChunkArgs &a) {
   // runs of the segment-parallel form (in sequence order: the ordering by
   // length is only a scheduling aid)
-  if (!a.seg.plain())
+  const int ns = prefill_ns(a);
+  if (!a.seg.plain()) {
+    if (ns == 8) return launch_bf16<128, 8, TIN, TOUT, false, false, true>(a);
+    if (ns == 4) return launch_bf16<128, 4, TIN, TOUT, false, false, true>(a);
+    if (ns == 1) return launch_bf16<128, 1, TIN, TOUT, false, false, true>(a);
     return a.dk == 128 ? launch_bf16<128, 2, TIN, TOUT, false, false, true>(a)
                        : launch_bf16<64, 2, TIN, TOUT, false, false, true>(a);
-  const int ns = prefill_ns(a);
+  }
   if (a.cu_seqlens && a.N > 1 && a.N <= kLptMax) {
     if (ns == 8) return launch_bf16<128, 8, TIN, TOUT, false, true>(a);
     if (ns == 4) return launch_bf16<128, 4, TIN, TOUT, false, true>(a);

@@ -76,14 +76,16 @@ def test_prefill_B1_H32_T65536_sampled():
 
 
 @gpu
-def test_prefill_B1_H32_T65536_segmented_sampled():
-    """The long-context workload through the segment-parallel form (4
-    segments of 16 384 tokens), on two heads the oracle recomputes."""
+@pytest.mark.parametrize("segments", [4, 8])
+def test_prefill_B1_H32_T65536_segmented_sampled(segments):
+    """The long-context workload through the segment-parallel form (4 or 8
+    segments of 16 384 or 8 192 tokens; the runs take their own column-tile
+    width), on two heads the oracle recomputes."""
     g = _lib()
     inp = gi.workload_inputs(2)
     dev = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor)}
     y, S = g.gdn_chunk_fwd_segmented(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
-                                     4, dev["S0"])
+                                     segments, dev["S0"])
     torch.cuda.synchronize()
     y, S = y.cpu(), S.cpu()
     T = 65536
