@@ -17,7 +17,7 @@
 namespace gdn {
 namespace {
 
-constexpr int kSegTile = 32;  // state columns per combine workgroup
+constexpr int kSegTile = 16;  // state columns per combine workgroup
 
 // Segment bounds of every sequence: segment p of sequence n covers rows
 // [bos + min(p L, len), bos + min((p + 1) L, len)) with L = len / P rounded
@@ -46,50 +46,80 @@ __global__ void seg_bounds_kernel(const int32_t *cu, int N, int T, int P, int32_
 // The chain for one sequence, in fp32: Sin[0] = N[0] and
 // Sin[e] = M[e - 1] Sin[e - 1] + N[e] for e = 1 .. P - 2 (entry e of Sin is
 // the initial state of segment e + 1, of N the zero-start final state of
-// segment e, of M the transition of segment e + 1). One workgroup per (head,
-// 32-column tile); the tile of the running state and the head's M stay in
-// LDS, each thread owns one column and DK / 8 rows.
+// segment e, of M the transition of segment e + 1). The columns of the state
+// are independent, so one workgroup takes one (head, 16-column tile): 256
+// workgroups for 32 heads of 128 columns. The tile of the running state is
+// kept transposed in LDS (a 16-byte read gives four k of one column) and the
+// head's M row-major (a 16-byte read gives four k of one row); thread (i0, j)
+// owns column j and rows i0 + 16 m. M of the next link is read into
+// registers while the current product runs (it does not depend on the chain).
 template <int DK>
 __global__ __launch_bounds__(256) void seg_combine_kernel(const float *__restrict__ Nst,
                                                           const float *__restrict__ Mst,
                                                           float *__restrict__ Sin, int H, int DV,
                                                           int P) {
-  __shared__ float Sl[DK][kSegTile + 1];
-  __shared__ float Ml[DK][DK + 1];
+  constexpr int LD = DK + 4;          // padded row length (floats)
+  constexpr int NR = DK / 16;         // rows per thread
+  constexpr int MV = DK * DK / 4 / 256;  // 16-byte pieces of M per thread
+  __shared__ __attribute__((aligned(16))) float St[kSegTile][LD];  // St[j][k] = S[k][j]
+  __shared__ __attribute__((aligned(16))) float Ml[DK][LD];
   const int h = blockIdx.x;
   const int j0 = blockIdx.y * kSegTile;
   const int t = threadIdx.x, j = t % kSegTile, i0 = t / kSegTile;
-  constexpr int RS = 256 / kSegTile;  // row stride
   const size_t st = static_cast<size_t>(H) * DK * DV;
   const size_t mt = static_cast<size_t>(H) * DK * DK;
   auto sidx = [&](int i) { return (static_cast<size_t>(h) * DK + i) * DV + j0 + j; };
-  for (int i = i0; i < DK; i += RS) {
+  for (int m = 0; m < NR; ++m) {
+    const int i = i0 + 16 * m;
     const float v = Nst[sidx(i)];
-    Sl[i][j] = v;
+    St[j][i] = v;
     Sin[sidx(i)] = v;
   }
+  if (P <= 2) return;
+  f32x4 mreg[MV];
+  auto fetch_m = [&](int e) {  // M[e - 1] of this head, 16 bytes per piece
+    const f32x4 *M = reinterpret_cast<const f32x4 *>(Mst + (e - 1) * mt +
+                                                     static_cast<size_t>(h) * DK * DK);
+#pragma unroll
+    for (int q = 0; q < MV; ++q) mreg[q] = M[t + 256 * q];
+  };
+  auto stage_m = [&]() {
+#pragma unroll
+    for (int q = 0; q < MV; ++q) {
+      const int idx = t + 256 * q;  // piece idx: row idx / (DK / 4), columns 4 (idx % (DK / 4))
+      *reinterpret_cast<f32x4 *>(&Ml[idx / (DK / 4)][4 * (idx % (DK / 4))]) = mreg[q];
+    }
+  };
+  fetch_m(1);
+  stage_m();
+  __syncthreads();
   for (int e = 1; e <= P - 2; ++e) {
-    const float *M = Mst + (e - 1) * mt + static_cast<size_t>(h) * DK * DK;
-    for (int idx = t; idx < DK * DK; idx += 256) Ml[idx / DK][idx % DK] = M[idx];
-    __syncthreads();
-    float acc[DK / RS];
+    if (e + 1 <= P - 2) fetch_m(e + 1);
+    float acc[NR];
 #pragma unroll
-    for (int m = 0; m < DK / RS; ++m) acc[m] = Nst[e * st + sidx(i0 + RS * m)];
-    for (int k = 0; k < DK; ++k) {
-      const float s = Sl[k][j];
+    for (int m = 0; m < NR; ++m) acc[m] = Nst[e * st + sidx(i0 + 16 * m)];
+#pragma unroll 4
+    for (int k = 0; k < DK; k += 4) {
+      const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&St[j][k]);
 #pragma unroll
-      for (int m = 0; m < DK / RS; ++m) acc[m] = fmaf(Ml[i0 + RS * m][k], s, acc[m]);
+      for (int m = 0; m < NR; ++m) {
+        const f32x4 m4 = *reinterpret_cast<const f32x4 *>(&Ml[i0 + 16 * m][k]);
+        acc[m] = fmaf(m4[0], s4[0], acc[m]);
+        acc[m] = fmaf(m4[1], s4[1], acc[m]);
+        acc[m] = fmaf(m4[2], s4[2], acc[m]);
+        acc[m] = fmaf(m4[3], s4[3], acc[m]);
+      }
     }
-    __syncthreads();
+    __syncthreads();  // every read of St and Ml for this link is done
 #pragma unroll
-    for (int m = 0; m < DK / RS; ++m) {
-      Sl[i0 + RS * m][j] = acc[m];
-      Sin[e * st + sidx(i0 + RS * m)] = acc[m];
+    for (int m = 0; m < NR; ++m) {
+      St[j][i0 + 16 * m] = acc[m];
+      Sin[e * st + sidx(i0 + 16 * m)] = acc[m];
     }
+    if (e + 1 <= P - 2) stage_m();
     __syncthreads();
   }
 }
-
 
 }  // namespace
 
