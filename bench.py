@@ -365,7 +365,7 @@ def bench_longctx(g, steps=3, warmup=1):
                                                     "chunk_fwd.hip")))
 
 
-def bench_longctx_segmented(g, segment_counts=(2, 4, 8), steps=3, warmup=1):
+def bench_longctx_segmented(g, segment_counts=(2, 4, 9), steps=3, warmup=1):
     """The long-context workload through gdn_chunk_fwd_segmented (each
     sequence cut into P pieces whose state summaries are chained), per P."""
     w = gi.WORKLOADS[2]

@@ -155,9 +155,12 @@ GDN_API int gdn_chunk_fwd_gated(const void *q, const void *k, const void *v,
  * `segments` pieces of whole 32-token chunks; the summaries (M, N) of the
  * pieces are computed independently, chained into each piece's true initial
  * state, and every piece after the first is run again from it for y. This
- * is the one-GPU form of splitting a long sequence over several GPUs; on
- * one GPU it does more work than gdn_chunk_fwd and is not faster (it cannot
- * shorten the serial chain inside each workgroup).
+ * is the one-GPU form of splitting a long sequence over several GPUs. It
+ * does about three times the work of gdn_chunk_fwd over 1/segments of the
+ * chain, with each launch's workgroups holding whole heads. On one GPU it
+ * beats gdn_chunk_fwd when N * H is small: best near segments =
+ * 256 / (N * H) + 1, where each launch fills the 256 CUs once (B1 H32
+ * T65536: 9 segments, 0.80x the time of gdn_chunk_fwd).
  *
  *   segments   2 .. 64.
  *   workspace  device memory of at least
