@@ -49,10 +49,9 @@ __global__ void seg_bounds_kernel(const int32_t *cu, int N, int T, int P, int32_
 // segment e, of M the transition of segment e + 1). The columns of the state
 // are independent, so one workgroup takes one (head, 16-column tile): 256
 // workgroups for 32 heads of 128 columns. The tile of the running state is
-// kept transposed in LDS (a 16-byte read gives four k of one column) and the
-// head's M row-major (a 16-byte read gives four k of one row); thread (i0, j)
-// owns column j and rows i0 + 16 m. M of the next link is read into
-// registers while the current product runs (it does not depend on the chain).
+// kept transposed in LDS and the head's M row-major; each link's product
+// runs on the fp32 matrix cores, and M of the next link is read into
+// registers while it runs (M does not depend on the chain).
 template <int DK>
 __global__ __launch_bounds__(256) void seg_combine_kernel(const float *__restrict__ Nst,
                                                           const float *__restrict__ Mst,
@@ -93,29 +92,38 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(const float *__restric
   fetch_m(1);
   stage_m();
   __syncthreads();
+  // the product M S on the matrix cores (fp32 16x16x4): wave w forms row
+  // tiles w and w + 4 (w + 4 only for DK = 128) of the 16-column result; lane
+  // l holds rows 4 (l / 16) + i of its tile, column l % 16
+  const int lane = t & 63, wv = t >> 6;
+  const int lr = lane & 15, lk = lane >> 4;
+  constexpr int TPW = DK / 16 / 4;  // row tiles per wave
   for (int e = 1; e <= P - 2; ++e) {
     if (e + 1 <= P - 2) fetch_m(e + 1);
-    float acc[NR];
+    f32x4 acc[TPW];
 #pragma unroll
-    for (int m = 0; m < NR; ++m) acc[m] = Nst[e * st + sidx(i0 + 16 * m)];
+    for (int u = 0; u < TPW; ++u) acc[u] = zero4();
 #pragma unroll 4
-    for (int k = 0; k < DK; k += 4) {
-      const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&St[j][k]);
+    for (int k0 = 0; k0 < DK; k0 += 4) {
+      const float b = St[lr][k0 + lk];  // S[k0 + lk][j0 + lr]
 #pragma unroll
-      for (int m = 0; m < NR; ++m) {
-        const f32x4 m4 = *reinterpret_cast<const f32x4 *>(&Ml[i0 + 16 * m][k]);
-        acc[m] = fmaf(m4[0], s4[0], acc[m]);
-        acc[m] = fmaf(m4[1], s4[1], acc[m]);
-        acc[m] = fmaf(m4[2], s4[2], acc[m]);
-        acc[m] = fmaf(m4[3], s4[3], acc[m]);
+      for (int u = 0; u < TPW; ++u) {
+        const float a = Ml[16 * (wv + 4 * u) + lr][k0 + lk];
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[u], 0, 0, 0);
       }
     }
     __syncthreads();  // every read of St and Ml for this link is done
+    // plus N, written back transposed for the next link
 #pragma unroll
-    for (int m = 0; m < NR; ++m) {
-      St[j][i0 + 16 * m] = acc[m];
-      Sin[e * st + sidx(i0 + 16 * m)] = acc[m];
-    }
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * (wv + 4 * u) + 4 * lk + i;
+        const size_t o = e * st + (static_cast<size_t>(h) * DK + r) * DV + j0 + lr;
+        const float v = acc[u][i] + Nst[o];
+        St[lr][r] = v;
+        Sin[o] = v;
+      }
     if (e + 1 <= P - 2) stage_m();
     __syncthreads();
   }
