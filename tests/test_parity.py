@@ -1076,6 +1076,38 @@ def _check_segmented(inp, segments, out_dtype=None, tol=None):
 
 
 @gpu
+@pytest.mark.parametrize("ns", [1, 4, 8])
+@pytest.mark.parametrize("varlen", [False, True])
+def test_chunk_segmented_tile_widths(ns, varlen, monkeypatch):
+    """The segmented prefill's runs with one, four or eight state waves per
+    workgroup (each launch picks its width; forced here by GDN_PREFILL_NS)
+    give the two-wave result bit for bit: equal lengths and varlen with an
+    empty sequence, 4 segments, bf16."""
+    g = _lib()
+    if varlen:
+        inp = gi.prefill_inputs(0, 2, 0, 128, 128, "bf16", s0_std=0.02, seed=44,
+                                lengths=[700, 0, 65, 1000, 33])
+    else:
+        inp = gi.prefill_inputs(3, 2, 640, 128, 128, "bf16", s0_std=0.02, seed=45)
+    d = to_dev(inp)
+
+    def run():
+        y, S = g.gdn_chunk_fwd_segmented(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], 4,
+                                         d["S0"], cu_seqlens=d["cu_seqlens"],
+                                         out_dtype=torch.float32, N=d["N"])
+        torch.cuda.synchronize()
+        return y.cpu(), S.cpu()
+
+    monkeypatch.setenv("GDN_PREFILL_NS", "2")
+    y2, S2 = run()
+    monkeypatch.setenv("GDN_PREFILL_NS", str(ns))
+    y, S = run()
+    assert torch.equal(y, y2) and torch.equal(S, S2)
+    yo, So = _oracle_chunk(inp)
+    assert rel_l2(_flat(inp, y), yo) <= TOL["bf16"] and rel_l2(S, So) <= TOL["bf16"]
+
+
+@gpu
 @pytest.mark.parametrize("segments", [2, 3, 5])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_chunk_segmented_equal_length(segments, dtype):
