@@ -694,7 +694,11 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   const uint32_t y_lane =
       static_cast<uint32_t>((4 * lg * hdv + h * DV + v0 + slab + lc) * sizeof(TOUT));
 
-  auto state_step = [&](int x) {
+  // One chunk of the state waves. WITH_Y false (segment runs that write no
+  // y: summaries and transitions) keeps only the chain X = K S -> R ->
+  // E = T R -> S update and leaves out Q S, P E and the y stores.
+  auto state_step = [&](int x, auto with_y) {
+    constexpr bool WITH_Y = decltype(with_y)::value;
     if constexpr (STATES) {
       typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
       _Float16 *dst = st_out + static_cast<size_t>(x) * H * DK * DV;
@@ -732,17 +736,19 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
 #pragma unroll
     for (int t = 0; t < NST; ++t) ktf[t] = lds_read16<f16x8>(pb + L::KT_OFF + t * 1024 + 16 * lane);
     kvec qraw[kNCT][NKB];
+    if constexpr (WITH_Y) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int rt = 0; rt < kNCT; ++rt) {
-        if constexpr (KO::kConvertQ)
-          qraw[rt][kb] = lds_read16<kvec>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
-        else
-          qf[rt][kb] = lds_read16<f16x8>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
-      }
+        for (int rt = 0; rt < kNCT; ++rt) {
+          if constexpr (KO::kConvertQ)
+            qraw[rt][kb] = lds_read16<kvec>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+          else
+            qf[rt][kb] = lds_read16<f16x8>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+        }
 #pragma unroll
-    for (int rt = 0; rt < kNCT; ++rt) pf[rt] = lds_read16<f16x8>(pb + L::P_OFF + rt * 1024 + 16 * lane);
+      for (int rt = 0; rt < kNCT; ++rt) pf[rt] = lds_read16<f16x8>(pb + L::P_OFF + rt * 1024 + 16 * lane);
+    }
 
     // the state as B operand: bf16 against the raw bf16 keys for X = K S,
     // fp16 against the fp16 queries for Q S (Q S feeds y directly, so it gets
@@ -752,7 +758,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       sb[kb] = KO::pack(st[2 * kb], st[2 * kb + 1]);
-      sh[kb] = pack_f16(st[2 * kb], st[2 * kb + 1]);
+      if constexpr (WITH_Y) sh[kb] = pack_f16(st[2 * kb], st[2 * kb + 1]);
     }
     // serial chain: X = K S -> R -> E = T R -> S update. X is summed in two
     // halves so that no MFMA waits on the one just before it.
@@ -774,7 +780,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     // tile already has, so the matrix cores only widen it (exact), and the
     // rounding to fp16 is exact for all but tiny values. Off the X -> R -> E
     // chain, so these products fill issue gaps of the state waves.
-    if constexpr (KO::kConvertQ) {
+    if constexpr (WITH_Y && KO::kConvertQ) {
       const kvec sel[2] = {selector(0), selector(1)};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -786,10 +792,12 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     f32x4 QS[kNCT];
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt) QS[rt] = zero4();
+    if constexpr (WITH_Y) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int rt = 0; rt < kNCT; ++rt) QS[rt] = mma_f16(qf[rt][kb], sh[kb], QS[rt]);
+        for (int rt = 0; rt < kNCT; ++rt) QS[rt] = mma_f16(qf[rt][kb], sh[kb], QS[rt]);
+    }
     f32x4 R[kNCT];
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt)
@@ -804,6 +812,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     const f16x8 eb = pack_f16(E[0], E[1]);
 #pragma unroll
     for (int t = 0; t < NST; ++t) st[t] = mma_f16(ktf[t], eb, st[t] * gC);
+    if constexpr (!WITH_Y) return;
     // output: Y = gamma o (Q S) + P E; rows past the end of the sequence fall
     // outside the buffer resource and are dropped
     f32x4 Yt[kNCT];
@@ -842,10 +851,18 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       step_barrier();
       step_barrier();
       step_barrier();
+      if (SEG && !write_y) {
 #pragma unroll 1
-      for (int x = 0; x < nc; ++x) {
-        state_step(x);
-        step_barrier();
+        for (int x = 0; x < nc; ++x) {
+          state_step(x, std::false_type{});
+          step_barrier();
+        }
+      } else {
+#pragma unroll 1
+        for (int x = 0; x < nc; ++x) {
+          state_step(x, std::true_type{});
+          step_barrier();
+        }
       }
     } else if (is_ldk) {
 #pragma unroll 1
