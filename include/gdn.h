@@ -160,7 +160,7 @@ GDN_API int gdn_chunk_fwd_gated(const void *q, const void *k, const void *v,
  * chain, with each launch's workgroups holding whole heads. On one GPU it
  * beats gdn_chunk_fwd when N * H is small: best near segments =
  * 256 / (N * H) + 1, where each launch fills the 256 CUs once (B1 H32
- * T65536: 9 segments, 0.79x the time of gdn_chunk_fwd).
+ * T65536: 9 segments, 0.75x the time of gdn_chunk_fwd).
  *
  *   segments   2 .. 64.
  *   workspace  device memory of at least
