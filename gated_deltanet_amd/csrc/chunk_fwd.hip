@@ -307,6 +307,27 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   const int lc = lane & 15;
   const int lg = lane >> 4;
   const int v0 = vt * DVT;
+  // Layout of the raw K and Q tiles in the ring. With one or two state waves
+  // (kRowBlocks) a tile is stored in 1 KiB blocks of 8 tokens x 64 keys, so
+  // that each direct-to-LDS load fetches 8 whole 128-byte lines (8 rows, half
+  // a row each at d = 128) instead of 16 half lines: lane L of a block holds
+  // row L % 8, keys 8 (L / 8) .. 8 (L / 8) + 7. Otherwise each 1 KiB block is
+  // one 16 x 32 MFMA operand slice, lane L's 16 bytes at 16 L. Either way the
+  // 16 bytes lane (lg, lc) reads for row tile rt and 32-key slice kb (row
+  // 16 rt + lc, keys 32 kb + 8 lg .. 32 kb + 8 lg + 7) sit at a per-lane base
+  // plus a constant per (rt, kb), so the operand reads need no per-slice
+  // address arithmetic, and 8 consecutive lanes read distinct banks.
+  constexpr bool kRowBlocks = NS <= 2;
+  constexpr int kHalves = DK / 64;  // 64-key halves per row
+  int frag_lane = kRowBlocks ? 1024 * kHalves * (lc >> 3) + 128 * lg + 16 * (lc & 7) : 0;
+  if constexpr (kRowBlocks)
+    asm volatile("" : "+v"(frag_lane));  // opaque: kept apart from the other per-lane offsets
+  auto frag = [&](int rt, int kb) -> int {
+    if constexpr (kRowBlocks)
+      return frag_lane + 1024 * (2 * kHalves * rt + (kb >> 1)) + 512 * (kb & 1);
+    else
+      return (rt * NKB + kb) * 1024 + 16 * lane;
+  };
   // roles; wave w runs on SIMD w % 4, so the two helpers that share a SIMD
   // with a state wave (gram, kt) are the lighter ones
   const bool is_state = wave < NS;
@@ -347,8 +368,17 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     const int64_t r = static_cast<int64_t>(c) * kC;
     return bos + (r < len ? r : len);
   };
-  // per-lane byte offsets of this lane's K/Q and V pieces inside a chunk
+  // per-lane byte offsets of this lane's K/Q and V pieces inside a chunk:
+  // load j of a K or Q tile fills block j of the tile (the layout above)
   const uint32_t kq_lane = static_cast<uint32_t>((lc * hdk + h * DK + 8 * lg) * 2);
+  auto kq_load = [&](int j) -> uint32_t {
+    if constexpr (kRowBlocks) {
+      const int r = 8 * (j / kHalves) + (lane & 7);
+      return static_cast<uint32_t>((r * hdk + h * DK) * 2 + 128 * (j % kHalves) + 16 * (lane >> 3));
+    } else {
+      return kq_lane + static_cast<uint32_t>(16 * (j / NKB) * hdk * 2 + 64 * (j % NKB));
+    }
+  };
   auto v_lane = [&](int p) -> uint32_t {
     const int qi = 64 * p + lane;
     const int r = qi / (DVT / 8);
@@ -366,7 +396,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        dma16(rk, kq_lane + static_cast<uint32_t>(16 * rt * hdk * 2 + 64 * kb), lds_addr(slot + L::K_OFF + (rt * NKB + kb) * 1024));
+        dma16(rk, kq_load(rt * NKB + kb), lds_addr(slot + L::K_OFF + (rt * NKB + kb) * 1024));
     const i32x4 rla = buffer_rsrc(log_alpha + r0 * H, rows * H * 4);
     const i32x4 rb = buffer_rsrc(beta + r0 * H, rows * H * 4);
     if (lane < 32) dma4(rla, g_off, lds_addr(slot + L::G_OFF));
@@ -384,7 +414,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
       for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          dma16(rq, kq_lane + static_cast<uint32_t>(16 * rt * hdk * 2 + 64 * kb), lds_addr(slot + L::Q_OFF + (rt * NKB + kb) * 1024));
+          dma16(rq, kq_load(rt * NKB + kb), lds_addr(slot + L::Q_OFF + (rt * NKB + kb) * 1024));
     }
     const i32x4 rv = buffer_rsrc(v + r0 * hdv, vrows * hdv * 2);
 #pragma unroll
@@ -445,7 +475,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + frag(rt, kb));
     const bool fast = __builtin_amdgcn_readfirstlane(
                           __builtin_bit_cast(int, gt[L::GB_MISC / 4])) != 0;
     f32x4 gm[3];
@@ -582,8 +612,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
-        qf[rt][kb] = lds_read16<kvec>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + frag(rt, kb));
+        qf[rt][kb] = lds_read16<kvec>(slot + L::Q_OFF + frag(rt, kb));
       }
     const bool fast = __builtin_amdgcn_readfirstlane(
                           __builtin_bit_cast(int, gt[L::GB_MISC / 4])) != 0;
@@ -648,7 +678,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     for (int rt = 0; rt < kNCT; ++rt)
 #pragma unroll
       for (int kb = half * (NKB / 2); kb < (half + 1) * (NKB / 2); ++kb)
-        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + frag(rt, kb));
     const kvec sel[2] = {selector(0), selector(1)};
     // slot j of the A operand <-> token 16 (j >> 2) + 4 lg + (j & 3)
     const f32x4 kd0 = *reinterpret_cast<const f32x4 *>(gt + L::GB_KD / 4 + 4 * lg);
@@ -723,7 +753,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int rt = 0; rt < kNCT; ++rt)
-        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+        kf[rt][kb] = lds_read16<kvec>(slot + L::K_OFF + frag(rt, kb));
 #pragma unroll
     for (int rt = 0; rt < kNCT; ++rt) {
       G4[rt] = *reinterpret_cast<const f32x4 *>(gt + L::GB_GAM / 4 + 16 * rt + 4 * lg);
@@ -742,9 +772,9 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
 #pragma unroll
         for (int rt = 0; rt < kNCT; ++rt) {
           if constexpr (KO::kConvertQ)
-            qraw[rt][kb] = lds_read16<kvec>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+            qraw[rt][kb] = lds_read16<kvec>(slot + L::Q_OFF + frag(rt, kb));
           else
-            qf[rt][kb] = lds_read16<f16x8>(slot + L::Q_OFF + (rt * NKB + kb) * 1024 + 16 * lane);
+            qf[rt][kb] = lds_read16<f16x8>(slot + L::Q_OFF + frag(rt, kb));
         }
 #pragma unroll
       for (int rt = 0; rt < kNCT; ++rt) pf[rt] = lds_read16<f16x8>(pb + L::P_OFF + rt * 1024 + 16 * lane);
