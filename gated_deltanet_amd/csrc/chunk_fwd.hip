@@ -307,7 +307,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   const int lc = lane & 15;
   const int lg = lane >> 4;
   const int v0 = vt * DVT;
-  // Layout of the raw K and Q tiles in the ring. With one or two state waves
+  // Layout of the raw K and Q tiles in the ring. With two state waves
   // (kRowBlocks) a tile is stored in 1 KiB blocks of 8 tokens x 64 keys, so
   // that each direct-to-LDS load fetches 8 whole 128-byte lines (8 rows, half
   // a row each at d = 128) instead of 16 half lines: lane L of a block holds
@@ -316,8 +316,10 @@ __global__ __launch_bounds__(64 * (NS + kPrep)) void chunk_fwd_bf16_kernel(
   // 16 bytes lane (lg, lc) reads for row tile rt and 32-key slice kb (row
   // 16 rt + lc, keys 32 kb + 8 lg .. 32 kb + 8 lg + 7) sit at a per-lane base
   // plus a constant per (rt, kb), so the operand reads need no per-slice
-  // address arithmetic, and 8 consecutive lanes read distinct banks.
-  constexpr bool kRowBlocks = NS <= 2;
+  // address arithmetic, and 8 consecutive lanes read distinct banks. (With
+  // one state wave the eight column tiles of a head then shared their K and Q
+  // reads less well in L2: 35% more HBM reads on B1 H32 T65536.)
+  constexpr bool kRowBlocks = NS == 2;
   constexpr int kHalves = DK / 64;  // 64-key halves per row
   int frag_lane = kRowBlocks ? 1024 * kHalves * (lc >> 3) + 128 * lg + 16 * (lc & 7) : 0;
   if constexpr (kRowBlocks)
