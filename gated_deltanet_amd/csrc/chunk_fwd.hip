@@ -43,7 +43,10 @@
 // every operand read is one conflict-free ds_read_b128. To make the raw K/Q
 // rows land that way straight from HBM, the key dimension inside each
 // 32-slice is visited in the order 8*lg + j for lane group lg and slot j, and
-// the state rows are stored in the matching order (see state_row()).
+// the state rows are stored in the matching order (see state_row()). With two
+// state waves the raw K and Q tiles are instead kept in blocks of 8 tokens,
+// so that each load fetches whole cache lines; their fragment reads are still
+// one ds_read_b128 per lane at a per-lane base plus a constant (see frag()).
 #include <cstdlib>
 #include <type_traits>
 
